@@ -1,0 +1,227 @@
+"""CPU oracle for the dequantize-inside-the-matmul decode path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library (``quantized_transformer_decode_amd``) and imports
+nothing from it.
+
+The arithmetic lives in ``qd_oracle.c`` (IEEE double dot products with a
+sequential sum; a step-by-step IEEE single emulation of the Q4_0 encoder).
+This module only builds that file with gcc, loads it with ctypes and marshals
+numpy arrays.  ``reference_np`` holds an independent numpy restatement used to
+cross-check the C code on small shapes.
+
+Sources (page title -- section):
+  turbospark-runtime 0.3.0, src/qwen3_asr_metal.rs -- PackedLinear::resident,
+      load_packed_linear, embed_row_bytes (affine-INT8 g64 format and dequant).
+  fuel-transformers 0.19.1, src/models/lazy_quantized_whisper.rs -- module
+      documentation, quantize_in_out_to_q4_0, q_linear (Q4_0 format, bake and
+      matmul).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libqd_oracle.so")
+
+GROUP = 64
+QK = 32
+BLOCK_BYTES = 18
+
+
+def build(force: bool = True) -> str:
+    """Compile qd_oracle.c with gcc (no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = [
+            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+            _SRC, "-o", tmp, "-lm",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
+        L.qdo_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.qdo_f16_to_f64.restype = D
+        L.qdo_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.qdo_bf16_to_f64.restype = D
+        L.qdo_f32_to_f16_rne.argtypes = [ctypes.c_float]
+        L.qdo_f32_to_f16_rne.restype = ctypes.c_uint16
+        for name in ("qdo_affine_scales_offset", "qdo_affine_biases_offset",
+                     "qdo_affine_bytes", "qdo_q4_0_bytes"):
+            getattr(L, name).argtypes = [I64, I64]
+            getattr(L, name).restype = I64
+        L.qdo_affine_pack.argtypes = [P, P, P, I64, I64, P]
+        L.qdo_affine_pack.restype = None
+        L.qdo_affine_weight.argtypes = [P, I64, I64, I64, I64]
+        L.qdo_affine_weight.restype = D
+        L.qdo_affine_gemv.argtypes = [P, I64, I64, P, I64, P, I64, P, I64, P]
+        L.qdo_affine_gemv.restype = None
+        L.qdo_q4_0_weight.argtypes = [P, I64, I64, I64]
+        L.qdo_q4_0_weight.restype = D
+        L.qdo_q4_0_gemm.argtypes = [P, I64, I64, P, ctypes.c_int, I64, P, I64,
+                                    P, I64, P]
+        L.qdo_q4_0_gemm.restype = None
+        L.qdo_q4_0_quantize.argtypes = [P, I64, I64, P]
+        L.qdo_q4_0_quantize.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _sel(sel, n):
+    if sel is None:
+        return None, n
+    a = np.ascontiguousarray(np.asarray(sel, dtype=np.int64))
+    return a, a.size
+
+
+# ---- scalar decoders ------------------------------------------------------
+
+def f16_to_f64(bits: int) -> float:
+    return lib().qdo_f16_to_f64(int(bits))
+
+
+def bf16_to_f64(bits: int) -> float:
+    return lib().qdo_bf16_to_f64(int(bits))
+
+
+def f32_to_f16_rne(x: float) -> int:
+    return int(lib().qdo_f32_to_f16_rne(float(np.float32(x))))
+
+
+# ---- affine-INT8 g64 ------------------------------------------------------
+
+def affine_scales_offset(rows: int, cols: int) -> int:
+    return int(lib().qdo_affine_scales_offset(rows, cols))
+
+
+def affine_biases_offset(rows: int, cols: int) -> int:
+    return int(lib().qdo_affine_biases_offset(rows, cols))
+
+
+def affine_bytes(rows: int, cols: int) -> int:
+    return int(lib().qdo_affine_bytes(rows, cols))
+
+
+def affine_pack(codes_u32: np.ndarray, scales_bf16: np.ndarray,
+                biases_bf16: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Concatenate the checkpoint triplet into one resident blob (u8)."""
+    codes = np.ascontiguousarray(codes_u32).view(np.uint8).reshape(-1)
+    sc = np.ascontiguousarray(scales_bf16).view(np.uint8).reshape(-1)
+    bi = np.ascontiguousarray(biases_bf16).view(np.uint8).reshape(-1)
+    assert codes.size == rows * cols
+    assert sc.size == bi.size == rows * (cols // GROUP) * 2
+    out = np.empty(affine_bytes(rows, cols), dtype=np.uint8)
+    lib().qdo_affine_pack(_ptr(codes), _ptr(sc), _ptr(bi), rows, cols, _ptr(out))
+    return out
+
+
+def affine_weight(blob: np.ndarray, rows: int, cols: int, r: int, c: int) -> float:
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    return float(lib().qdo_affine_weight(_ptr(blob), rows, cols, r, c))
+
+
+def affine_gemv(blob: np.ndarray, rows: int, cols: int, x_bf16: np.ndarray,
+                m_sel=None, row_sel=None) -> np.ndarray:
+    """f64 y[len(m_sel), len(row_sel)] for x BF16 bits [m, cols]."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, cols)
+    m = x.shape[0]
+    ms, n_m = _sel(m_sel, m)
+    rs, n_r = _sel(row_sel, rows)
+    if ms is not None:
+        assert ms.min(initial=0) >= 0 and ms.max(initial=0) < max(m, 1)
+    if rs is not None:
+        assert rs.min(initial=0) >= 0 and rs.max(initial=0) < max(rows, 1)
+    y = np.zeros((n_m, n_r), dtype=np.float64)
+    lib().qdo_affine_gemv(_ptr(blob), rows, cols, _ptr(x), m, _ptr(ms), n_m,
+                          _ptr(rs), n_r, _ptr(y))
+    return y
+
+
+# ---- ggml Q4_0 -------------------------------------------------------------
+
+def q4_0_bytes(rows: int, cols: int) -> int:
+    return int(lib().qdo_q4_0_bytes(rows, cols))
+
+
+def q4_0_quantize(w_f32: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """f32 [rows=out, cols=in] -> Q4_0 byte stream including the zero pad."""
+    w = np.ascontiguousarray(w_f32, dtype=np.float32).reshape(-1)
+    assert w.size == rows * cols and cols % QK == 0
+    out = np.empty(q4_0_bytes(rows, cols), dtype=np.uint8)
+    lib().qdo_q4_0_quantize(_ptr(w), rows, cols, _ptr(out))
+    return out
+
+
+def q4_0_quantize_in_out(w_in_out: np.ndarray, in_features: int,
+                         out_features: int) -> np.ndarray:
+    """The bake as the Whisper page states it: the weight arrives as
+    [in_features, out_features], is transposed to [out, in], then encoded."""
+    w = np.asarray(w_in_out, dtype=np.float32).reshape(in_features, out_features)
+    return q4_0_quantize(np.ascontiguousarray(w.T), out_features, in_features)
+
+
+def q4_0_weight(wq: np.ndarray, cols: int, n: int, k: int) -> float:
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    return float(lib().qdo_q4_0_weight(_ptr(wq), cols, n, k))
+
+
+def q4_0_gemm(wq: np.ndarray, rows: int, cols: int, x: np.ndarray,
+              m_sel=None, row_sel=None) -> np.ndarray:
+    """f64 y[len(m_sel), len(row_sel)]; x is float32 [m, cols] or BF16 bits
+    (uint16) [m, cols]."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    if x.dtype == np.uint16:
+        kind = 1
+        xa = np.ascontiguousarray(x).reshape(-1, cols)
+    else:
+        kind = 0
+        xa = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, cols)
+    m = xa.shape[0]
+    ms, n_m = _sel(m_sel, m)
+    rs, n_r = _sel(row_sel, rows)
+    if ms is not None:
+        assert ms.min(initial=0) >= 0 and ms.max(initial=0) < max(m, 1)
+    if rs is not None:
+        assert rs.min(initial=0) >= 0 and rs.max(initial=0) < max(rows, 1)
+    y = np.zeros((n_m, n_r), dtype=np.float64)
+    lib().qdo_q4_0_gemm(_ptr(wq), rows, cols, _ptr(xa), kind, m, _ptr(ms), n_m,
+                        _ptr(rs), n_r, _ptr(y))
+    return y
+
+
+# ---- tolerance metric -------------------------------------------------------
+
+def normwise_error(got: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |got_i - ref_i| / max_i |ref_i| (0 when both are all zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den
