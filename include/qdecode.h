@@ -1,0 +1,161 @@
+/*
+ * qdecode.h -- C ABI of libqdecode.so: dequantize-inside-the-matmul kernels
+ * for token-by-token transformer decoders on AMD Instinct MI355X (gfx950).
+ *
+ * Two weight formats, both defined by the pages this library follows:
+ *
+ *  affine-INT8 g64  (turbospark-runtime 0.3.0, src/qwen3_asr_metal.rs --
+ *     PackedLinear::resident, load_packed_linear, embed_row_bytes)
+ *     One resident buffer [codes | scales | biases] for a [rows, cols] matrix:
+ *       codes   rows*cols bytes, code of (r, c) at byte r*cols + c (the
+ *               checkpoint's U32 words [rows, cols/4] viewed little-endian);
+ *       scales  BF16 [rows, cols/64] at byte offset rows*cols;
+ *       biases  BF16 [rows, cols/64] at byte offset rows*cols + rows*(cols/64)*2;
+ *     w[r, c] = q * scale[r, c/64] + bias[r, c/64].
+ *
+ *  ggml Q4_0  (fuel-transformers 0.19.1, src/models/lazy_quantized_whisper.rs
+ *     -- module documentation, quantize_in_out_to_q4_0)
+ *     A row-major stream of 18-byte blocks, block (n, b) for output row n and
+ *     32-column block b at byte 18*(n*cols/32 + b): f16 delta d (little-endian)
+ *     then 16 bytes whose low nibble is element j and high nibble element
+ *     j+16; w = d * (q - 8).  The stream is zero-padded to a multiple of 4
+ *     bytes (2 bytes when the block count is odd).
+ *
+ * Conventions for every entry point:
+ *  - All matrix/vector pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or retains them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; results are valid once the caller has
+ *    synchronised the stream.  Device faults surface at that synchronisation.
+ *  - Every argument is validated on the host before any HIP call, so a host
+ *    without a GPU can exercise every error path.  On error nothing is
+ *    enqueued and the output is untouched.
+ *  - Matrices are row-major; activations x are [m, cols] and outputs y are
+ *    [m, rows], both row-major and contiguous.  Outputs must not overlap
+ *    inputs.  Inputs are never written.
+ *  - Functions are reentrant and thread-safe; the only global state is a
+ *    per-device cache of the architecture check.
+ *  - None of the matmuls takes a bias input: the pages apply biases outside
+ *    the matmul (q_linear) or refuse biased linears (load_packed_linear).
+ */
+#ifndef QDECODE_H
+#define QDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QD_OK = 0,
+  QD_EINVAL = 1,  /* null pointer, m or rows out of range, overlapping output */
+  QD_ESHAPE = 2,  /* divisibility requirement on cols violated               */
+  QD_EALIGN = 3,  /* pointer misaligned for the kernel's vector loads/stores  */
+  QD_EDEVICE = 4, /* no current HIP device, or it is not gfx950               */
+  QD_EHIP = 5     /* the HIP runtime reported an error; see qd_last_hip_error */
+} qd_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *qd_status_string(int status);
+
+/* The hipError_t of the most recent QD_EHIP on the calling thread (0 if none). */
+int qd_last_hip_error(void);
+
+/* Library version string, e.g. "qdecode 0.1.0 gfx950". */
+const char *qd_version(void);
+
+/* ---- layout helpers (pure host arithmetic; 0 on invalid arguments) ------ */
+
+/* Byte size of the affine blob: rows*cols + 2 * rows*(cols/64)*2.
+ * Requires rows >= 1, cols >= 64, cols % 64 == 0. */
+size_t affine_i8_g64_bytes(int64_t rows, int64_t cols);
+/* Byte offset of the BF16 scales inside the blob: rows*cols. */
+size_t affine_i8_g64_scales_offset(int64_t rows, int64_t cols);
+/* Byte offset of the BF16 biases inside the blob: rows*cols + rows*(cols/64)*2. */
+size_t affine_i8_g64_biases_offset(int64_t rows, int64_t cols);
+/* Byte size of a Q4_0 stream for [rows, cols]: rows*cols/32*18 rounded up
+ * to a multiple of 4.  Requires rows >= 1, cols >= 32, cols % 32 == 0. */
+size_t q4_0_bytes(int64_t rows, int64_t cols);
+
+/* ---- affine-INT8 g64 ------------------------------------------------------ */
+
+/* Packed-weight loader (turbospark-runtime 0.3.0, qwen3_asr_metal.rs --
+ * load_packed_linear): validates the checkpoint triplet's shape and writes
+ * the resident blob codes | scales | biases.
+ *   codes_u32   device, U32 [rows, cols/4]   (rows*cols bytes)
+ *   scales_bf16 device, BF16 [rows, cols/64]
+ *   biases_bf16 device, BF16 [rows, cols/64]
+ *   blob        device, affine_i8_g64_bytes(rows, cols) bytes, 16-byte aligned
+ * Requires cols % 64 == 0 (QD_ESHAPE), rows >= 1, no overlap between blob and
+ * the sources (QD_EINVAL).  Bit-exact byte copy. */
+qd_status affine_i8_g64_pack(const void *codes_u32, const void *scales_bf16,
+                             const void *biases_bf16, int64_t rows,
+                             int64_t cols, void *blob, void *stream);
+
+/* y = x W^T with W dequantised inside the kernel (w = q*scale + bias), fp32
+ * accumulation, BF16 output rounded to nearest even
+ * (turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::gemv,
+ * embed_row_bytes for the dequantisation).
+ *   w_packed  device, the affine blob for [rows, cols], 16-byte aligned
+ *   x_bf16    device, BF16 [m, cols], 16-byte aligned
+ *   y_bf16    device, BF16 [m, rows], 2-byte aligned (may sit at an offset
+ *             inside a larger buffer, e.g. a K/V cache row)
+ *   m         number of token rows, 1 <= m <= 16
+ * Requires cols % 64 == 0 and 64 <= cols <= 65536 (QD_ESHAPE),
+ * 1 <= rows < 2^31 (QD_EINVAL). */
+qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
+                              const void *x_bf16, void *y_bf16, int64_t m,
+                              void *stream);
+
+/* ---- ggml Q4_0 ------------------------------------------------------------ */
+
+/* y = x W^T over a Q4_0 stream, f32 activations and f32 output
+ * (fuel-transformers 0.19.1, lazy_quantized_whisper.rs -- q_linear /
+ * WeightStorage::apply_linear; the bias is applied outside).
+ *   w_q4_0  device, the Q4_0 stream for [rows = out_features, cols =
+ *           in_features], 16-byte aligned
+ *   x       device, f32 [m, cols], 16-byte aligned
+ *   y       device, f32 [m, rows], 4-byte aligned
+ *   m       1 <= m <= 16
+ * Requires cols % 256 == 0 and 256 <= cols <= 65536 (QD_ESHAPE): every row
+ * then starts on a 16-byte boundary (8 blocks = 144 bytes). */
+qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
+                     const float *x, float *y, int64_t m, void *stream);
+
+/* Prefill GEMM y = x W^T over a Q4_0 stream on the matrix cores: BF16
+ * activations, exact integer codes (q - 8) as BF16 MFMA operands, the f16
+ * delta applied per block in fp32, f32 output
+ * (fuel-transformers 0.19.1, lazy_quantized_whisper.rs -- forward_encoder /
+ * encoder_layer, which run every projection over all encoder frames).
+ *   w_q4_0  device, Q4_0 stream for [rows, cols], 16-byte aligned
+ *   x_bf16  device, BF16 [m, cols], 16-byte aligned
+ *   y       device, f32 [m, rows], 16-byte aligned
+ *   m       any m >= 1 (the tail tile is masked), m < 2^31
+ * Requires cols % 256 == 0, 256 <= cols <= 65536 (QD_ESHAPE). */
+qd_status qgemm_q4_0_prefill(const void *w_q4_0, int64_t rows, int64_t cols,
+                             const void *x_bf16, float *y, int64_t m,
+                             void *stream);
+
+/* f32 -> Q4_0 bake (fuel-transformers 0.19.1, lazy_quantized_whisper.rs --
+ * quantize_in_out_to_q4_0 with ggml's BlockQ4_0::from_float): per block of
+ * 32, d = (element of largest magnitude, first index on ties) / -8 in f32,
+ * id = 1/d correctly rounded (0 if d == 0), nibble = min(15, trunc(x*id +
+ * 8.5)) with the product and the sum rounded separately (no FMA), d stored
+ * as f16 round-to-nearest-even; blocks row-major; 2 zero bytes appended when
+ * the block count is odd.  Bit-exact.  Non-finite inputs, or a block whose
+ * |max|/8 overflows f16, are outside the contract (not checked).
+ *   w    device, f32 [rows = out_features, cols = in_features], 16-byte
+ *        aligned (callers holding [in, out] weights transpose first)
+ *   out  device, q4_0_bytes(rows, cols) bytes, 4-byte aligned
+ * Requires cols % 32 == 0 (QD_ESHAPE), rows >= 1 and rows*cols/32 < 2^31
+ * (QD_EINVAL). */
+qd_status q4_0_quantize(const float *w, int64_t rows, int64_t cols, void *out,
+                        void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDECODE_H */

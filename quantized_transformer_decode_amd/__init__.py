@@ -1,0 +1,143 @@
+"""Python binding of libqdecode.so (include/qdecode.h).
+
+Argument marshalling only: every function here forwards torch tensors' device
+pointers, the sizes and the current HIP stream to the C entry point of the
+same name and turns a non-zero status into ``QDError``.  No step of the
+computation runs in Python or PyTorch, and there is no fallback: if the
+shared library is missing the first call raises.
+
+Weight formats (see include/qdecode.h):
+  * affine-INT8 g64 -- turbospark-runtime 0.3.0, src/qwen3_asr_metal.rs
+    (PackedLinear::resident, load_packed_linear, embed_row_bytes);
+  * ggml Q4_0 -- fuel-transformers 0.19.1,
+    src/models/lazy_quantized_whisper.rs (quantize_in_out_to_q4_0, q_linear).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqdecode.so")
+
+QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_EDEVICE, QD_EHIP = range(6)
+
+# every function declared in include/qdecode.h
+EXPORTS = (
+    "qd_status_string", "qd_last_hip_error", "qd_version",
+    "affine_i8_g64_bytes", "affine_i8_g64_scales_offset",
+    "affine_i8_g64_biases_offset", "q4_0_bytes",
+    "affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
+    "qgemm_q4_0_prefill", "q4_0_quantize",
+)
+
+
+class QDError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip: int = 0):
+        self.status = status
+        self.hip_error = hip
+        msg = lib().qd_status_string(status).decode()
+        if status == QD_EHIP:
+            msg += f" (hipError {hip})"
+        super().__init__(f"{fn}: {msg}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqdecode.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python quantized_transformer_decode_amd/build.py` "
+                "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        L.qd_status_string.argtypes = [I]
+        L.qd_status_string.restype = ctypes.c_char_p
+        L.qd_last_hip_error.argtypes = []
+        L.qd_last_hip_error.restype = I
+        L.qd_version.argtypes = []
+        L.qd_version.restype = ctypes.c_char_p
+        for n in ("affine_i8_g64_bytes", "affine_i8_g64_scales_offset",
+                  "affine_i8_g64_biases_offset", "q4_0_bytes"):
+            getattr(L, n).argtypes = [I64, I64]
+            getattr(L, n).restype = SZ
+        L.affine_i8_g64_pack.argtypes = [P, P, P, I64, I64, P, P]
+        L.qgemv_affine_i8_g64.argtypes = [P, I64, I64, P, P, I64, P]
+        L.qgemv_q4_0.argtypes = [P, I64, I64, P, P, I64, P]
+        L.qgemm_q4_0_prefill.argtypes = [P, I64, I64, P, P, I64, P]
+        L.q4_0_quantize.argtypes = [P, I64, I64, P, P]
+        for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
+                  "qgemm_q4_0_prefill", "q4_0_quantize"):
+            getattr(L, n).restype = I
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != QD_OK:
+        raise QDError(fn, status, lib().qd_last_hip_error() if status == QD_EHIP else 0)
+
+
+# ---- layout helpers ----------------------------------------------------------
+
+def affine_i8_g64_bytes(rows: int, cols: int) -> int:
+    return int(lib().affine_i8_g64_bytes(rows, cols))
+
+
+def affine_i8_g64_scales_offset(rows: int, cols: int) -> int:
+    return int(lib().affine_i8_g64_scales_offset(rows, cols))
+
+
+def affine_i8_g64_biases_offset(rows: int, cols: int) -> int:
+    return int(lib().affine_i8_g64_biases_offset(rows, cols))
+
+
+def q4_0_bytes(rows: int, cols: int) -> int:
+    return int(lib().q4_0_bytes(rows, cols))
+
+
+# ---- entry points ------------------------------------------------------------
+
+def affine_i8_g64_pack(codes_u32, scales_bf16, biases_bf16, rows: int, cols: int,
+                       blob, stream=None) -> None:
+    _check("affine_i8_g64_pack", lib().affine_i8_g64_pack(
+        _ptr(codes_u32), _ptr(scales_bf16), _ptr(biases_bf16), rows, cols,
+        _ptr(blob), _stream(stream)))
+
+
+def qgemv_affine_i8_g64(w_packed, rows: int, cols: int, x_bf16, y_bf16, m: int,
+                        stream=None) -> None:
+    _check("qgemv_affine_i8_g64", lib().qgemv_affine_i8_g64(
+        _ptr(w_packed), rows, cols, _ptr(x_bf16), _ptr(y_bf16), m, _stream(stream)))
+
+
+def qgemv_q4_0(w_q4_0, rows: int, cols: int, x, y, m: int, stream=None) -> None:
+    _check("qgemv_q4_0", lib().qgemv_q4_0(
+        _ptr(w_q4_0), rows, cols, _ptr(x), _ptr(y), m, _stream(stream)))
+
+
+def qgemm_q4_0_prefill(w_q4_0, rows: int, cols: int, x_bf16, y, m: int,
+                       stream=None) -> None:
+    _check("qgemm_q4_0_prefill", lib().qgemm_q4_0_prefill(
+        _ptr(w_q4_0), rows, cols, _ptr(x_bf16), _ptr(y), m, _stream(stream)))
+
+
+def q4_0_quantize(w, rows: int, cols: int, out, stream=None) -> None:
+    _check("q4_0_quantize", lib().q4_0_quantize(
+        _ptr(w), rows, cols, _ptr(out), _stream(stream)))

@@ -1,0 +1,26 @@
+// qd_internal.h -- launchers between the validated C entry points
+// (qd_api.hip) and the kernels.  Arguments reaching these functions have
+// already passed every host-side check; each launcher only enqueues work on
+// `stream` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qd {
+
+hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
+                              const uint16_t *x, uint16_t *y, int m,
+                              hipStream_t stream);
+
+hipError_t launch_q4_0_gemv(const uint8_t *w, int rows, int cols,
+                            const float *x, float *y, int m,
+                            hipStream_t stream);
+
+hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,
+                            const uint16_t *x, float *y, int m,
+                            hipStream_t stream);
+
+hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
+                                hipStream_t stream);
+
+}  // namespace qd

@@ -1,0 +1,141 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/qdecode.h declares, computes the layout helpers, and rejects every
+invalid argument with the documented status before touching the GPU.
+
+Pointers passed here are fake (never dereferenced): validation runs on the
+host before any HIP call.  The one test that gets past validation runs only
+where no GPU is visible, so the call stops at the device check.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_transformer_decode_amd as qd
+from conftest import ROOT
+
+P = ctypes.c_void_p
+A = 0x7f0000000000  # fake, 256-byte aligned device address
+B = 0x7f1000000000
+C = 0x7f2000000000
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "qdecode.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"}
+
+
+def test_header_symbols_exported():
+    L = qd.lib()
+    names = _declared()
+    assert names == set(qd.EXPORTS), names ^ set(qd.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = qd.lib()
+    for s in range(6):
+        assert L.qd_status_string(s).decode().startswith(
+            ["QD_OK", "QD_EINVAL", "QD_ESHAPE", "QD_EALIGN", "QD_EDEVICE", "QD_EHIP"][s])
+    assert L.qd_status_string(99) == b"QD_UNKNOWN"
+    assert b"gfx950" in L.qd_version()
+    assert L.qd_last_hip_error() == 0
+
+
+def test_layout_helpers():
+    # turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- PackedLinear::resident
+    assert qd.affine_i8_g64_scales_offset(1024, 1024) == 1048576
+    assert qd.affine_i8_g64_biases_offset(1024, 1024) == 1048576 + 32768
+    assert qd.affine_i8_g64_bytes(1024, 1024) == 1114112
+    assert qd.affine_i8_g64_bytes(151936, 1024) == 155582464 + 2 * 4861952
+    assert qd.affine_i8_g64_bytes(1024, 100) == 0
+    assert qd.affine_i8_g64_bytes(0, 64) == 0
+    # fuel-transformers 0.19.1, lazy_quantized_whisper.rs -- 18-byte blocks
+    # padded to a multiple of 4
+    assert qd.q4_0_bytes(1, 32) == 20
+    assert qd.q4_0_bytes(2, 32) == 36
+    assert qd.q4_0_bytes(2048, 512) == 589824
+    assert qd.q4_0_bytes(1, 48) == 0
+
+
+def _call(fn, *args):
+    return getattr(qd.lib(), fn)(*args)
+
+
+def test_errors_affine_gemv():
+    f = "qgemv_affine_i8_g64"
+    ok = (A, 64, 1024, B, C, 1, None)
+    assert _call(f, None, 64, 1024, B, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, None, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, B, None, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 0, 1024, B, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, B, C, 0, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, B, C, 17, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1000, B, C, 1, None) == qd.QD_ESHAPE
+    assert _call(f, A, 64, 32, B, C, 1, None) == qd.QD_ESHAPE
+    assert _call(f, A, 64, 16384, B, C, 1, None) == qd.QD_ESHAPE
+    assert _call(f, A + 8, 64, 1024, B, C, 1, None) == qd.QD_EALIGN
+    assert _call(f, A, 64, 1024, B + 2, C, 1, None) == qd.QD_EALIGN
+    assert _call(f, A, 64, 1024, B, C + 1, 1, None) == qd.QD_EALIGN
+    # output overlapping the weights or x
+    assert _call(f, A, 64, 1024, B, A + 64, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, B, B + 2, 1, None) == qd.QD_EINVAL
+    assert ok  # the valid form is exercised by test_valid_args_reach_device_check
+
+
+def test_errors_q4_0_gemv_and_gemm():
+    for f in ("qgemv_q4_0", "qgemm_q4_0_prefill"):
+        assert _call(f, None, 64, 512, B, C, 1, None) == qd.QD_EINVAL
+        assert _call(f, A, 64, 512, None, C, 1, None) == qd.QD_EINVAL
+        assert _call(f, A, 64, 512, B, None, 1, None) == qd.QD_EINVAL
+        assert _call(f, A, -1, 512, B, C, 1, None) == qd.QD_EINVAL
+        assert _call(f, A, 64, 512, B, C, 0, None) == qd.QD_EINVAL
+        assert _call(f, A, 64, 480, B, C, 1, None) == qd.QD_ESHAPE   # % 256
+        assert _call(f, A, 64, 128, B, C, 1, None) == qd.QD_ESHAPE
+        assert _call(f, A + 4, 64, 512, B, C, 1, None) == qd.QD_EALIGN
+        assert _call(f, A, 64, 512, B + 4, C, 1, None) == qd.QD_EALIGN
+        assert _call(f, A, 64, 512, B, C + 2, 1, None) == qd.QD_EALIGN
+        assert _call(f, A, 64, 512, B, B, 1, None) == qd.QD_EINVAL
+    assert _call("qgemv_q4_0", A, 64, 512, B, C, 17, None) == qd.QD_EINVAL
+    assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C + 4, 1, None) == qd.QD_EALIGN
+    assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, (1 << 22) + 1, None) == qd.QD_EINVAL
+
+
+def test_errors_quantize_and_pack():
+    f = "q4_0_quantize"
+    assert _call(f, None, 4, 64, C, None) == qd.QD_EINVAL
+    assert _call(f, A, 4, 64, None, None) == qd.QD_EINVAL
+    assert _call(f, A, 0, 64, C, None) == qd.QD_EINVAL
+    assert _call(f, A, 4, 48, C, None) == qd.QD_ESHAPE
+    assert _call(f, A + 4, 4, 64, C, None) == qd.QD_EALIGN
+    assert _call(f, A, 4, 64, C + 2, None) == qd.QD_EALIGN
+    assert _call(f, A, 4, 64, A + 16, None) == qd.QD_EINVAL
+    g = "affine_i8_g64_pack"
+    assert _call(g, None, B, C, 4, 64, A, None) == qd.QD_EINVAL
+    assert _call(g, A, B, C, 4, 96, A + (1 << 20), None) == qd.QD_ESHAPE
+    assert _call(g, A, B, C, 4, 64, A + (1 << 20) + 8, None) == qd.QD_EALIGN
+    assert _call(g, A, B, C, 4, 64, A + 128, None) == qd.QD_EINVAL  # overlaps codes
+
+
+def _gpu_visible():
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        n = ctypes.c_int(0)
+        return hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0
+    except OSError:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers must never reach a real GPU")
+def test_valid_args_reach_device_check():
+    # with every argument valid, the only remaining failure on a host with no
+    # GPU is the device check -- proving validation passed and nothing launched
+    assert _call("qgemv_affine_i8_g64", A, 64, 1024, B, C, 1, None) == qd.QD_EDEVICE
+    assert _call("qgemv_q4_0", A, 64, 512, B, C, 4, None) == qd.QD_EDEVICE
+    assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, 1500, None) == qd.QD_EDEVICE
+    assert _call("q4_0_quantize", A, 3, 32, C, None) == qd.QD_EDEVICE
+    assert _call("affine_i8_g64_pack", A, B, C, 4, 64, A + (1 << 20), None) == qd.QD_EDEVICE
