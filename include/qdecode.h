@@ -54,7 +54,8 @@ typedef enum {
   QD_ESHAPE = 2,  /* divisibility requirement on cols violated               */
   QD_EALIGN = 3,  /* pointer misaligned for the kernel's vector loads/stores  */
   QD_EDEVICE = 4, /* no current HIP device, or it is not gfx950               */
-  QD_EHIP = 5     /* the HIP runtime reported an error; see qd_last_hip_error */
+  QD_EHIP = 5,    /* the HIP runtime reported an error; see qd_last_hip_error */
+  QD_ESTEP = 6    /* a decode-step launch reported an error word (see _step_check) */
 } qd_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -103,11 +104,69 @@ qd_status affine_i8_g64_pack(const void *codes_u32, const void *scales_bf16,
  *   y_bf16    device, BF16 [m, rows], 2-byte aligned (may sit at an offset
  *             inside a larger buffer, e.g. a K/V cache row)
  *   m         number of token rows, 1 <= m <= 16
- * Requires cols % 64 == 0 and 64 <= cols <= 65536 (QD_ESHAPE),
+ * Requires cols % 64 == 0 and 64 <= cols <= 8192 (QD_ESHAPE),
  * 1 <= rows < 2^31 (QD_EINVAL). */
 qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
                               const void *x_bf16, void *y_bf16, int64_t m,
                               void *stream);
+
+/* ---- one decode step of affine GEMVs in a single launch ------------------ */
+
+/* One GEMV of a decode step: y[m, rows] = x[m, cols] W^T (same operation,
+ * layouts and rounding as qgemv_affine_i8_g64).  `stage` orders the GEMVs:
+ * stages are numbered 0, 1, 2, ... in op-array order; GEMVs of one stage may
+ * run concurrently (e.g. q, k, v, or gate and up, which read the same
+ * input), and no GEMV of stage s+1 reads its input before every GEMV of
+ * stage s has finished -- the decoder order of turbospark-runtime 0.3.0,
+ * qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step. */
+typedef struct {
+  const void *w_packed; /* device, affine blob [rows, cols], 16-byte aligned */
+  const void *x_bf16;   /* device, BF16 [m, cols], 2-byte aligned          */
+  void *y_bf16;         /* device, BF16 [m, rows], 2-byte aligned          */
+  int64_t rows, cols;   /* rows >= 1; cols % 64 == 0, 64 <= cols <= 8192   */
+  int64_t stage;
+} qd_affine_gemv_op;
+
+/* Host-side handle filled by _step_plan (caller-owned plain data). */
+typedef struct {
+  void *workspace;
+  int32_t nwg;        /* workgroups = CUs of the planning device */
+  int32_t lds_bytes;
+  int32_t n_ops, n_stages, m;
+  uint32_t magic;
+} qd_step_plan;
+
+/* Workspace bytes needed by _step_plan for these ops (0 if invalid). */
+size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
+                                                int64_t n_ops, int64_t m);
+
+/* Validates the ops (host array), writes the step tables into `workspace`
+ * (device memory owned by the caller, 256-byte aligned, at least
+ * _step_workspace_bytes) and fills *plan.  Synchronises `stream` before
+ * returning.  Requirements beyond those of each op: m == 1; ops[0].stage ==
+ * 0 and each op's stage equals its predecessor's or one more; ops of one
+ * stage share cols; per stage sum(m*ceil(cols/1024)*1024) <= 16384; no op's output overlaps
+ * any op's weights or input, or the workspace (QD_EINVAL / QD_ESHAPE /
+ * QD_EALIGN as for the single GEMV).  The workspace, weights and inputs must
+ * stay valid while runs are in flight. */
+qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
+                                        int64_t n_ops, int64_t m,
+                                        void *workspace, size_t workspace_bytes,
+                                        qd_step_plan *plan, void *stream);
+
+/* Enqueues the whole step as ONE persistent kernel (one workgroup per CU;
+ * every workgroup must be able to be resident, so do not run it concurrently
+ * with kernels that occupy whole CUs indefinitely).  Launches nothing else,
+ * allocates nothing, and may be captured in a HIP graph.  Runs planned on
+ * the same workspace must not overlap in time. */
+qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream);
+
+/* Synchronises `stream`, reads the workspace's error word into *error_bits
+ * (0 = every wait completed) and returns QD_ESTEP if it is non-zero.  Bits:
+ * 1 input poll timed out, 2/4 intra-workgroup wait timed out, 8 grid size did
+ * not match the plan. */
+qd_status qgemv_affine_i8_g64_step_check(const qd_step_plan *plan,
+                                         uint32_t *error_bits, void *stream);
 
 /* ---- ggml Q4_0 ------------------------------------------------------------ */
 
@@ -119,7 +178,7 @@ qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
  *   x       device, f32 [m, cols], 16-byte aligned
  *   y       device, f32 [m, rows], 4-byte aligned
  *   m       1 <= m <= 16
- * Requires cols % 256 == 0 and 256 <= cols <= 65536 (QD_ESHAPE): every row
+ * Requires cols % 256 == 0 and 256 <= cols <= 8192 (QD_ESHAPE): every row
  * then starts on a 16-byte boundary (8 blocks = 144 bytes). */
 qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
                      const float *x, float *y, int64_t m, void *stream);
@@ -132,7 +191,7 @@ qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
  *   w_q4_0  device, Q4_0 stream for [rows, cols], 16-byte aligned
  *   x_bf16  device, BF16 [m, cols], 16-byte aligned
  *   y       device, f32 [m, rows], 16-byte aligned
- *   m       any m >= 1 (the tail tile is masked), m < 2^31
+ *   m       any 1 <= m <= 2^22 (the tail tile is masked)
  * Requires cols % 256 == 0, 256 <= cols <= 65536 (QD_ESHAPE). */
 qd_status qgemm_q4_0_prefill(const void *w_q4_0, int64_t rows, int64_t cols,
                              const void *x_bf16, float *y, int64_t m,

@@ -20,7 +20,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqdecode.so")
 
-QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_EDEVICE, QD_EHIP = range(6)
+QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_EDEVICE, QD_EHIP, QD_ESTEP = range(7)
 
 # every function declared in include/qdecode.h
 EXPORTS = (
@@ -29,7 +29,24 @@ EXPORTS = (
     "affine_i8_g64_biases_offset", "q4_0_bytes",
     "affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
     "qgemm_q4_0_prefill", "q4_0_quantize",
+    "qgemv_affine_i8_g64_step_workspace_bytes", "qgemv_affine_i8_g64_step_plan",
+    "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
 )
+
+
+class AffineGemvOp(ctypes.Structure):
+    """qd_affine_gemv_op"""
+    _fields_ = [("w_packed", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
+                ("y_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("stage", ctypes.c_int64)]
+
+
+class StepPlan(ctypes.Structure):
+    """qd_step_plan (filled by the library, kept by the caller)"""
+    _fields_ = [("workspace", ctypes.c_void_p), ("nwg", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("n_ops", ctypes.c_int32),
+                ("n_stages", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("magic", ctypes.c_uint32)]
 
 
 class QDError(RuntimeError):
@@ -71,8 +88,16 @@ def lib() -> ctypes.CDLL:
         L.qgemv_q4_0.argtypes = [P, I64, I64, P, P, I64, P]
         L.qgemm_q4_0_prefill.argtypes = [P, I64, I64, P, P, I64, P]
         L.q4_0_quantize.argtypes = [P, I64, I64, P, P]
+        OPS = ctypes.POINTER(AffineGemvOp)
+        PLAN = ctypes.POINTER(StepPlan)
+        L.qgemv_affine_i8_g64_step_workspace_bytes.argtypes = [OPS, I64, I64]
+        L.qgemv_affine_i8_g64_step_workspace_bytes.restype = SZ
+        L.qgemv_affine_i8_g64_step_plan.argtypes = [OPS, I64, I64, P, SZ, PLAN, P]
+        L.qgemv_affine_i8_g64_step_run.argtypes = [PLAN, P]
+        L.qgemv_affine_i8_g64_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
-                  "qgemm_q4_0_prefill", "q4_0_quantize"):
+                  "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
+                  "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -141,3 +166,45 @@ def qgemm_q4_0_prefill(w_q4_0, rows: int, cols: int, x_bf16, y, m: int,
 def q4_0_quantize(w, rows: int, cols: int, out, stream=None) -> None:
     _check("q4_0_quantize", lib().q4_0_quantize(
         _ptr(w), rows, cols, _ptr(out), _stream(stream)))
+
+
+# ---- decode step in one launch -------------------------------------------------
+
+def make_ops(specs):
+    """specs: iterable of (w_packed, x_bf16, y_bf16, rows, cols, stage) with
+    tensors or raw device addresses -> ctypes array of AffineGemvOp."""
+    specs = list(specs)
+    arr = (AffineGemvOp * len(specs))()
+    for i, (w, x, y, rows, cols, stage) in enumerate(specs):
+        arr[i] = AffineGemvOp(_ptr(w), _ptr(x), _ptr(y), rows, cols, stage)
+    return arr
+
+
+def qgemv_affine_i8_g64_step_workspace_bytes(ops, m: int = 1) -> int:
+    return int(lib().qgemv_affine_i8_g64_step_workspace_bytes(ops, len(ops), m))
+
+
+def qgemv_affine_i8_g64_step_plan(ops, m, workspace, workspace_bytes: int,
+                                  stream=None) -> StepPlan:
+    plan = StepPlan()
+    _check("qgemv_affine_i8_g64_step_plan", lib().qgemv_affine_i8_g64_step_plan(
+        ops, len(ops), m, _ptr(workspace), workspace_bytes, ctypes.byref(plan),
+        _stream(stream)))
+    return plan
+
+
+def qgemv_affine_i8_g64_step_run(plan: StepPlan, stream=None) -> None:
+    _check("qgemv_affine_i8_g64_step_run",
+           lib().qgemv_affine_i8_g64_step_run(ctypes.byref(plan), _stream(stream)))
+
+
+def qgemv_affine_i8_g64_step_check(plan: StepPlan, stream=None) -> int:
+    """Synchronise and return the step's error word (raises QDError if set)."""
+    bits = ctypes.c_uint32(0)
+    st = lib().qgemv_affine_i8_g64_step_check(ctypes.byref(plan), ctypes.byref(bits),
+                                              _stream(stream))
+    if st not in (QD_OK, QD_ESTEP):
+        _check("qgemv_affine_i8_g64_step_check", st)
+    if st == QD_ESTEP:
+        raise QDError(f"qgemv_affine_i8_g64_step_check (error bits {bits.value:#x})", st)
+    return bits.value

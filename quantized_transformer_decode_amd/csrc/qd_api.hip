@@ -12,6 +12,9 @@
 
 #include "../../include/qdecode.h"
 #include "qd_internal.h"
+#include "qd_step.h"
+
+#include <vector>
 
 namespace {
 
@@ -24,6 +27,28 @@ thread_local int g_last_hip = 0;
 
 // 0 = unknown, 1 = gfx950, 2 = other
 std::atomic<int> g_arch[64];
+
+std::atomic<int> g_cus[64];
+
+// Compute units of the current device (0 on failure).
+int current_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev < 64) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -71,6 +96,87 @@ bool affine_shape_ok(int64_t rows, int64_t cols) {
   return rows >= 1 && cols >= 64 && cols % 64 == 0;
 }
 
+constexpr int kMaxStageWords = 16384;  // LDS: two fp32 copies of a stage input
+constexpr int kMinStepWgs = 32;        // smallest grid a plan supports
+constexpr int kStepReplicas = 8;       // copies of each published slice (kernel's kReplicas)
+
+// log2 of the slice length for a stage input of `words` words over `nwg`
+// publishers: the smallest power of two >= ceil(words / nwg), within [2, 64].
+int step_lg(int64_t words, int nwg) {
+  const int64_t per = (words + nwg - 1) / nwg;
+  int lg = 1;
+  while ((int64_t(1) << lg) < per) ++lg;
+  return lg;
+}
+int64_t step_slices(int64_t words, int nwg) {
+  return (words + (int64_t(1) << step_lg(words, nwg)) - 1) >> step_lg(words, nwg);
+}
+constexpr int64_t kMaxStepOps = 65536;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Validates a decode-step op list; on success fills the layout sizes.
+qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
+                        size_t *ws_bytes, int *n_stages, int *xmax) {
+  if (!ops || n_ops < 1 || n_ops > kMaxStepOps || m != 1) return QD_EINVAL;
+  int stages = 0, cur_words = 0, max_words = 0;
+  size_t staging = 0;
+  for (int64_t i = 0; i < n_ops; ++i) {
+    const qd_affine_gemv_op &o = ops[i];
+    if (!o.w_packed || !o.x_bf16 || !o.y_bf16) return QD_EINVAL;
+    if (o.rows < 1 || o.rows > kMaxRows || o.cols < 1) return QD_EINVAL;
+    if (o.cols % 64 != 0 || o.cols > kMaxGemvCols) return QD_ESHAPE;
+    if (!aligned(o.w_packed, 16) || !aligned(o.x_bf16, 2) || !aligned(o.y_bf16, 2))
+      return QD_EALIGN;
+    if (i == 0) {
+      if (o.stage != 0) return QD_EINVAL;
+      stages = 1;
+      cur_words = 0;
+    } else if (o.stage == ops[i - 1].stage + 1) {
+      stages += 1;
+      cur_words = 0;
+    } else if (o.stage == ops[i - 1].stage) {
+      if (o.cols != ops[i - 1].cols) return QD_ESHAPE;
+    } else {
+      return QD_EINVAL;
+    }
+    // LDS holds each op's input in whole 1024-column chunks
+    cur_words += (int)(m * ((o.cols + 1023) / 1024) * 1024);
+    if (cur_words > kMaxStageWords) return QD_ESHAPE;
+    if (cur_words > max_words) max_words = cur_words;
+  }
+  // outputs may not overlap any weights or inputs of the step
+  for (int64_t i = 0; i < n_ops; ++i) {
+    const size_t ny = (size_t)m * ops[i].rows * 2;
+    for (int64_t j = 0; j < n_ops; ++j) {
+      if (overlap(ops[i].y_bf16, ny, ops[j].w_packed, affine_bytes(ops[j].rows, ops[j].cols)) ||
+          overlap(ops[i].y_bf16, ny, ops[j].x_bf16, (size_t)m * ops[j].cols * 2))
+        return QD_EINVAL;
+      if (j > i && overlap(ops[i].y_bf16, ny, ops[j].y_bf16, (size_t)m * ops[j].rows * 2))
+        return QD_EINVAL;
+    }
+  }
+  *n_stages = stages;
+  *xmax = max_words;
+  *ws_bytes = sizeof(qd::StepHeader) + align256(sizeof(qd::StepOp) * n_ops) +
+              align256(sizeof(qd::StepStage) * stages) + staging;
+  return QD_OK;
+}
+
+// Staging bytes for a grid of nwg workgroups: each stage's input in slices of
+// 2^lg words, one 256-byte line per slice.
+size_t step_staging_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
+  size_t bytes = 0;
+  int64_t i = 0;
+  while (i < n_ops) {
+    int64_t j = i, words = 0;
+    while (j < n_ops && ops[j].stage == ops[i].stage) words += m * ops[j++].cols;
+    bytes += (size_t)step_slices(words, nwg) * 256 * kStepReplicas;
+    i = j;
+  }
+  return bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +189,7 @@ const char *qd_status_string(int status) {
     case QD_EALIGN: return "QD_EALIGN: pointer not aligned as the kernel requires";
     case QD_EDEVICE: return "QD_EDEVICE: no current HIP device, or it is not gfx950";
     case QD_EHIP: return "QD_EHIP: the HIP runtime reported an error";
+    case QD_ESTEP: return "QD_ESTEP: a decode-step launch reported a wait time-out or grid mismatch";
     default: return "QD_UNKNOWN";
   }
 }
@@ -209,6 +316,150 @@ qd_status q4_0_quantize(const float *w, int64_t rows, int64_t cols, void *out,
   hipError_t e = qd::launch_q4_0_quantize(w, nb, (uint8_t *)out,
                                           (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
+                                                int64_t n_ops, int64_t m) {
+  size_t bytes = 0;
+  int ns = 0, xmax = 0;
+  if (step_validate(ops, n_ops, m, &bytes, &ns, &xmax) != QD_OK) return 0;
+  // the staging layout depends on the grid: one workgroup per CU of the
+  // current device
+  if (check_device() != QD_OK) return 0;
+  const int nwg = current_cus();
+  if (nwg < kMinStepWgs) return 0;
+  return bytes + step_staging_bytes(ops, n_ops, m, nwg);
+}
+
+qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
+                                        int64_t n_ops, int64_t m,
+                                        void *workspace, size_t workspace_bytes,
+                                        qd_step_plan *plan, void *stream) {
+  if (!workspace || !plan) return QD_EINVAL;
+  size_t need = 0;
+  int ns = 0, xmax = 0;
+  qd_status st = step_validate(ops, n_ops, m, &need, &ns, &xmax);
+  if (st != QD_OK) return st;
+  if (!aligned(workspace, 256)) return QD_EALIGN;
+  if (workspace_bytes < need) return QD_EINVAL;  // tables alone; staging checked below
+  for (int64_t i = 0; i < n_ops; ++i) {
+    const qd_affine_gemv_op &o = ops[i];
+    if (overlap(workspace, workspace_bytes, o.w_packed, affine_bytes(o.rows, o.cols)) ||
+        overlap(workspace, workspace_bytes, o.x_bf16, (size_t)m * o.cols * 2) ||
+        overlap(workspace, workspace_bytes, o.y_bf16, (size_t)m * o.rows * 2))
+      return QD_EINVAL;
+  }
+  st = check_device();
+  if (st != QD_OK) return st;
+  const int nwg = current_cus();
+  if (nwg < kMinStepWgs) return QD_EDEVICE;
+  need += step_staging_bytes(ops, n_ops, m, nwg);
+  if (workspace_bytes < need) return QD_EINVAL;
+
+  // host image of header + tables; staging words start zeroed (tag 0 is
+  // never expected: the epoch starts at 1)
+  const size_t ops_off = sizeof(qd::StepHeader);
+  const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * n_ops);
+  const size_t stg_off = stages_off + align256(sizeof(qd::StepStage) * ns);
+  std::vector<uint8_t> img(stg_off, 0);
+  qd::StepHeader *h = (qd::StepHeader *)img.data();
+  qd::StepOp *dops = (qd::StepOp *)(img.data() + ops_off);
+  qd::StepStage *dst = (qd::StepStage *)(img.data() + stages_off);
+  h->magic = qd::kStepMagic;
+  h->n_ops = (int32_t)n_ops;
+  h->n_stages = ns;
+  h->m = (int32_t)m;
+  h->nwg = nwg;
+  h->xmax = xmax;
+  h->ops_off = (uint32_t)ops_off;
+  h->stages_off = (uint32_t)stages_off;
+  h->lds_bytes = (uint32_t)(2 * (size_t)xmax * 4);
+  h->epoch = 1;
+  h->error = 0;
+  size_t stg = stg_off;
+  int s = -1;
+  for (int64_t i = 0; i < n_ops; ++i) {
+    const qd_affine_gemv_op &o = ops[i];
+    if ((int)o.stage != s) {
+      s = (int)o.stage;
+      int64_t words = 0;
+      for (int64_t j = i; j < n_ops && ops[j].stage == o.stage; ++j) words += m * ops[j].cols;
+      dst[s].stg = (uint32_t *)((uint8_t *)workspace + stg);
+      dst[s].op0 = (int32_t)i;
+      dst[s].nops = 0;
+      dst[s].rows_total = 0;
+      dst[s].cols = (int32_t)o.cols;
+      dst[s].chunks = (int32_t)((o.cols + 1023) / 1024);
+      dst[s].words = (uint16_t)words;
+      dst[s].lg = (uint16_t)step_lg(words, nwg);
+      stg += (size_t)step_slices(words, nwg) * 256 * kStepReplicas;
+    }
+    qd::StepOp &d = dops[i];
+    d.w = (const uint8_t *)o.w_packed;
+    d.x = (const uint16_t *)o.x_bf16;
+    d.y = (uint16_t *)o.y_bf16;
+    d.stg = (uint32_t *)((uint8_t *)workspace + stg);
+    d.rows = (int32_t)o.rows;
+    d.cols = (int32_t)o.cols;
+    d.stage = s;
+    d.row_base = dst[s].rows_total;
+    dst[s].rows_total += (int32_t)o.rows;
+    dst[s].nops += 1;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, hs);
+  if (e == hipSuccess)
+    e = hipMemsetAsync((uint8_t *)workspace + stg_off, 0, need - stg_off, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e);
+  plan->workspace = workspace;
+  plan->nwg = nwg;
+  plan->lds_bytes = (int32_t)h->lds_bytes;
+  plan->n_ops = (int32_t)n_ops;
+  plan->n_stages = ns;
+  plan->m = (int32_t)m;
+  plan->magic = qd::kStepMagic;
+  return QD_OK;
+}
+
+qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream) {
+  if (!plan || !plan->workspace || plan->magic != qd::kStepMagic || plan->nwg < 1 ||
+      plan->lds_bytes < 8 || plan->lds_bytes > 2 * kMaxStageWords * 4 ||
+      plan->lds_bytes % 8 != 0 || plan->n_ops < 1 || plan->n_stages < 1 ||
+      plan->n_stages > plan->n_ops || plan->m != 1)
+    return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  if (current_cus() != plan->nwg) return QD_EDEVICE;
+  uint8_t *ws = (uint8_t *)plan->workspace;
+  const size_t ops_off = sizeof(qd::StepHeader);
+  const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * plan->n_ops);
+  qd::StepHeader *h = (qd::StepHeader *)ws;  // device address; never dereferenced here
+  hipError_t e = qd::launch_affine_step(
+      (const qd::StepOp *)(ws + ops_off), (const qd::StepStage *)(ws + stages_off),
+      plan->n_stages, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch, &h->error,
+      (size_t)plan->lds_bytes, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status qgemv_affine_i8_g64_step_check(const qd_step_plan *plan,
+                                         uint32_t *error_bits, void *stream) {
+  if (!plan || !plan->workspace || plan->magic != qd::kStepMagic || !error_bits)
+    return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  uint32_t v = 0;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&v, (uint8_t *)plan->workspace + offsetof(qd::StepHeader, error),
+                                4, hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e);
+  *error_bits = v;
+  return v ? QD_ESTEP : QD_OK;
 }
 
 }  // extern "C"

@@ -23,4 +23,12 @@ hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,
 hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
                                 hipStream_t stream);
 
+// Persistent decode-step kernel (decode_step.hip): one workgroup per CU.
+struct StepOp;
+struct StepStage;
+int step_threads();
+hipError_t launch_affine_step(const StepOp *ops, const StepStage *stages, int n_stages, int m,
+                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *err,
+                              size_t lds_bytes, hipStream_t stream);
+
 }  // namespace qd
