@@ -1,18 +1,26 @@
 #!/usr/bin/env python
-"""Decode-step throughput of the dequant-GEMV path on one MI355X.
+"""Throughput of the dequantize-inside-the-matmul decode path on one MI355X.
 
-A step is one batch-1 decode step of a 28-layer Qwen3-0.6B-shaped text
-decoder: its 197 affine-INT8 g64 projection GEMVs in decoder order (per layer
-q, k, v -> o -> gate, up -> down; then the tied 151936 x 1024 LM head), every
-weight resident in HBM (633,233,408 bytes), a fresh BF16 N(0,1) input per
-GEMV (turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::
-step runs exactly this GEMV sequence once per generated token).
+Headline step: one batch-1 decode step of a 28-layer Qwen3-0.6B-shaped text
+decoder -- its 197 affine-INT8 g64 projection GEMVs in decoder order (per
+layer q, k, v -> o -> gate, up -> down, then the tied 151936 x 1024 LM head),
+every weight resident in HBM (633,233,408 bytes), a fresh BF16 N(0,1) input
+per GEMV (turbospark-runtime 0.3.0, qwen3_asr_metal.rs --
+Qwen3AsrMetalEngine::step runs this GEMV sequence once per generated token).
 
-Prints one JSON line.  `value` is decoder tokens/s (batch 1, so 1000 /
-ms_per_step); the same line carries weight GB/s and the fraction of the
-8 TB/s HBM peak, the roofline of the dominant kernel measured with HIP events
-on its stream, and the CPU oracle timed on the host (which also re-checks
-sampled outputs of the timed buffers).
+Prints one JSON line.  `value` is decoder tokens/s at batch 1 (1000 /
+ms_per_step).  The line also carries weight GB/s and the fraction of the
+8 TB/s HBM peak, the roofline of the dominant kernel (HIP events on its
+stream), the CPU oracle timed on the host (it also re-checks the outputs of
+the timed buffers), and under "rows" a measurement of every other part of
+the path on its own workload:
+  affine_gemv_1024       single 1024x1024 affine GEMV, batch 1
+  q4_0_ffn_pair          Whisper-base FFN pair (fc1 2048x512, fc2 512x2048), M = 1, 4
+  qwen3_1_7b_step        Qwen3-1.7B-shaped decode step at M = 1, 4, 10, 16
+  whisper_large_prefill  one Whisper-large layer's six projections at 1500 frames
+  whisper_large_decoder  32 layers x 6 Q4_0 GEMVs at batch 1
+  q4_0_bake              f32 -> Q4_0 of one Whisper-large layer
+All inputs are seeded synthetic data of the pages' shapes (see synth/).
 """
 from __future__ import annotations
 
@@ -27,8 +35,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix cores
 METRIC = "dequant-GEMV weight GB/s & % HBM peak; decoder-step tokens/s at batch 1"
+DEV = "cuda:0"
 
 
 def parse():
@@ -37,85 +47,318 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rows", default="all",
+                   help="comma-separated extra rows to measure, 'all' or 'none'")
     p.add_argument("--variant", default="step", choices=["step", "graph"],
                    help="step: the whole step as one persistent launch (default); "
                         "graph: 197 GEMV launches captured in a HIP graph")
     return p.parse_args()
 
 
-class DecodeStep:
-    """All weights, inputs and outputs of one decode step, resident on the GPU."""
+# ---- helpers -------------------------------------------------------------------
 
-    def __init__(self, spec, dev):
+def u8dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to(DEV)
+
+
+def bf16dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to(DEV).view(
+        torch.bfloat16)
+
+
+def event_time(fn, iters, warmup, stream=None):
+    """Average ms per call of fn(), HIP events on the current stream."""
+    import torch
+    cur = stream or torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(iters):
+        fn()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def capture(fn):
+    """Capture fn() (which launches on the current stream) into a HIP graph."""
+    import torch
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def affine_blob(qd, rows, cols, key):
+    import torch
+    import synth
+    tr = synth.affine_triplet(rows, cols, key=key)
+    blob = torch.empty(qd.affine_i8_g64_bytes(rows, cols), dtype=torch.uint8, device=DEV)
+    qd.affine_i8_g64_pack(u8dev(tr.codes), u8dev(tr.scales), u8dev(tr.biases), rows, cols, blob)
+    return blob
+
+
+# ---- the headline step ---------------------------------------------------------
+
+class DecodeStep:
+    """All weights, inputs and outputs of one affine decode step on the GPU."""
+
+    def __init__(self, spec, m=1, cfg=3):
         import torch
 
         import quantized_transformer_decode_amd as qd
         import synth
         self.qd = qd
-        self.spec = spec
+        self.m = m
         self.mats = synth.decode_step_matrices(spec)
         self.blobs, self.xs, self.ys, self.x_host = [], [], [], []
         self.weight_bytes = 0
         for i, (layer, name, rows, cols, stage) in enumerate(self.mats):
-            tr = synth.affine_triplet(rows, cols, key=(3, layer, i))
-            blob = torch.empty(qd.affine_i8_g64_bytes(rows, cols), dtype=torch.uint8, device=dev)
-            qd.affine_i8_g64_pack(
-                torch.from_numpy(tr.codes.view(np.uint8).reshape(-1)).to(dev),
-                torch.from_numpy(tr.scales.view(np.uint8).reshape(-1)).to(dev),
-                torch.from_numpy(tr.biases.view(np.uint8).reshape(-1)).to(dev),
-                rows, cols, blob)
-            xb = synth.x_bf16(1, cols, key=(3, layer, 1000 + i))
+            self.blobs.append(affine_blob(qd, rows, cols, (cfg, layer, i)))
+            xb = synth.x_bf16(m, cols, key=(cfg, layer, 1000 + i))
             self.x_host.append(xb)
-            self.xs.append(torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16))
-            self.ys.append(torch.empty((1, rows), dtype=torch.bfloat16, device=dev))
-            self.blobs.append(blob)
+            self.xs.append(bf16dev(xb))
+            self.ys.append(torch.empty((m, rows), dtype=torch.bfloat16, device=DEV))
             self.weight_bytes += qd.affine_i8_g64_bytes(rows, cols)
         torch.cuda.synchronize()
 
-    def launches(self):
-        return len(self.mats)
-
-    def plan_step(self, dev):
+    def plan_step(self):
         import torch
         qd = self.qd
         self.ops = qd.make_ops((b, x, y, rows, cols, stage) for (_, _, rows, cols, stage), b, x, y
                                in zip(self.mats, self.blobs, self.xs, self.ys))
-        nbytes = qd.qgemv_affine_i8_g64_step_workspace_bytes(self.ops, 1)
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        self.plan = qd.qgemv_affine_i8_g64_step_plan(self.ops, 1, self.ws, nbytes)
+        nbytes = qd.qgemv_affine_i8_g64_step_workspace_bytes(self.ops, self.m)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        self.plan = qd.qgemv_affine_i8_g64_step_plan(self.ops, self.m, self.ws, nbytes)
 
     def run_step(self, stream=None):
         self.qd.qgemv_affine_i8_g64_step_run(self.plan, stream)
 
     def run_eager(self, stream=None):
-        for (layer, name, rows, cols, stage), blob, x, y in zip(self.mats, self.blobs, self.xs, self.ys):
-            self.qd.qgemv_affine_i8_g64(blob, rows, cols, x, y, 1, stream)
+        for (_, _, rows, cols, _), blob, x, y in zip(self.mats, self.blobs, self.xs, self.ys):
+            self.qd.qgemv_affine_i8_g64(blob, rows, cols, x, y, self.m, stream)
+
+    def free(self):
+        self.blobs = self.xs = self.ys = None
 
 
 def cpu_baseline(step: DecodeStep):
-    """The oracle on one full decode step (all 197 GEMVs, every row), on all
+    """The oracle on one full decode step (all 197 GEMVs, every row) on all
     host cores; its outputs are compared with the GPU's timed buffers."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     blobs = [b.cpu().numpy() for b in step.blobs]
     ys = [y.float().cpu().numpy().astype(np.float64) for y in step.ys]
     t0 = time.perf_counter()
-    refs = []
-    for (layer, name, rows, cols, stage), blob, xh in zip(step.mats, blobs, step.x_host):
-        refs.append(oracle.affine_gemv(blob, rows, cols, xh))
+    refs = [oracle.affine_gemv(blob, rows, cols, xh)
+            for (_, _, rows, cols, _), blob, xh in zip(step.mats, blobs, step.x_host)]
     dt = time.perf_counter() - t0
     worst = 0.0
     for got, ref in zip(ys, refs):
+        # each output must be the BF16 rounding of the exact value up to fp32
+        # accumulation noise
         half = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126))) - 8)
-        excess = float(np.maximum(np.abs(got - ref) - half, 0).max() / np.abs(ref).max())
-        worst = max(worst, excess)
-    ok = worst <= 1e-5
+        worst = max(worst, float(np.maximum(np.abs(got - ref) - half, 0).max() / np.abs(ref).max()))
     return {
         "value": 1.0 / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": "one full decode step: all 197 GEMVs, every output row, f64 (%.1f s wall)" % dt,
+        "sample": "one full decode step: all 197 GEMVs, every output row, f64 (%.2f s wall)" % dt,
         "weight_GBps": step.weight_bytes / dt / 1e9,
-        "parity_vs_timed_gpu_buffers": "ok" if ok else "FAIL (excess %.3g)" % worst,
+        "parity_vs_timed_gpu_buffers": "ok" if worst <= 1e-5 else "FAIL (excess %.3g)" % worst,
     }
+
+
+# ---- rows ------------------------------------------------------------------------
+
+def row_affine_gemv_1024(qd):
+    """Single 1024x1024 GEMV at batch 1: warm (same weights every launch) and
+    cold (rotating over 482 distinct copies, 537 MB, past the 256 MB MALL)."""
+    import torch
+    import synth
+    rows = cols = 1024
+    nbytes = qd.affine_i8_g64_bytes(rows, cols)
+    ncopy = 482
+    base = affine_blob(qd, rows, cols, (1, 0, 0))
+    copies = base.repeat(ncopy).view(ncopy, -1)
+    x = bf16dev(synth.x_bf16(1, cols, key=(1, 0, 1)))
+    y = torch.empty((1, rows), dtype=torch.bfloat16, device=DEV)
+    gw = capture(lambda: [qd.qgemv_affine_i8_g64(base, rows, cols, x, y, 1) for _ in range(ncopy)])
+    gc = capture(lambda: [qd.qgemv_affine_i8_g64(copies[i], rows, cols, x, y, 1)
+                          for i in range(ncopy)])
+    warm = event_time(gw.replay, 5, 2) / ncopy
+    cold = event_time(gc.replay, 5, 2) / ncopy
+    return {"shape": "1024x1024, M=1", "weight_bytes": nbytes,
+            "us_per_gemv_warm": warm * 1e3, "us_per_gemv_cold": cold * 1e3,
+            "GBps_cold": nbytes / (cold * 1e-3) / 1e9,
+            "hbm_peak_frac_cold": nbytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "note": "back-to-back launches in one HIP graph; cold rotates 482 copies (537 MB)"}
+
+
+def q4_0_from_f32(qd, w_host, rows, cols):
+    import torch
+    wq = torch.empty(qd.q4_0_bytes(rows, cols), dtype=torch.uint8, device=DEV)
+    qd.q4_0_quantize(torch.from_numpy(w_host).to(DEV), rows, cols, wq)
+    return wq
+
+
+def row_q4_0_ffn_pair(qd):
+    """Whisper-base FFN pair baked to Q4_0 on the GPU, GEMV at M = 1 and 4,
+    cold over 455 distinct pairs (537 MB)."""
+    import torch
+    import synth
+    npair = 455
+    mats = []
+    for name, rows, cols in synth.WHISPER_BASE_FFN:
+        wq = q4_0_from_f32(qd, synth.w_f32(rows, cols, key=(2, 0, rows)), rows, cols)
+        mats.append((rows, cols, wq, wq.repeat(npair).view(npair, -1)))
+    pair_bytes = sum(qd.q4_0_bytes(r, c) for r, c, _, _ in mats)
+    out = {"shapes": "fc1 2048x512 + fc2 512x2048", "pair_weight_bytes": pair_bytes}
+    for m in (1, 4):
+        xs = [torch.from_numpy(synth.x_f32(m, c, key=(2, m, c))).to(DEV) for r, c, _, _ in mats]
+        ys = [torch.empty((m, r), device=DEV) for r, c, _, _ in mats]
+
+        def launch(cold):
+            for i in range(npair):
+                for k, (r, c, wq, cp) in enumerate(mats):
+                    qd.qgemv_q4_0(cp[i] if cold else wq, r, c, xs[k], ys[k], m)
+        gw, gc = capture(lambda: launch(False)), capture(lambda: launch(True))
+        warm = event_time(gw.replay, 3, 1) / npair
+        cold = event_time(gc.replay, 3, 1) / npair
+        out[f"M{m}"] = {"us_per_pair_warm": warm * 1e3, "us_per_pair_cold": cold * 1e3,
+                        "GBps_cold": pair_bytes / (cold * 1e-3) / 1e9}
+    return out
+
+
+def row_qwen3_1_7b_step(qd):
+    """Qwen3-1.7B-shaped decode step (1,827,979,264 weight bytes) at M rows:
+    M = 1 as one persistent launch, M > 1 as 197 GEMV launches in a graph."""
+    import synth
+    out = {}
+    step = DecodeStep(synth.QWEN3_1_7B, m=1, cfg=4)
+    wb = step.weight_bytes
+    step.plan_step()
+    ms1 = event_time(step.run_step, 20, 5)
+    out["M1"] = {"ms_per_step": ms1, "tokens_per_s": 1000.0 / ms1,
+                 "weight_GBps": wb / (ms1 * 1e-3) / 1e9, "variant": "persistent step"}
+    ys_keep = step.ys
+    for m in (4, 10, 16):
+        import torch
+        step.m = m
+        step.xs = [bf16dev(synth.x_bf16(m, cols, key=(4, layer, 2000 + i)))
+                   for i, (layer, _, rows, cols, _) in enumerate(step.mats)]
+        step.ys = [torch.empty((m, rows), dtype=torch.bfloat16, device=DEV)
+                   for (_, _, rows, _, _) in step.mats]
+        g = capture(step.run_eager)
+        ms = event_time(g.replay, 5, 2)
+        out[f"M{m}"] = {"ms_per_step": ms, "tokens_per_s": m * 1000.0 / ms,
+                        "weight_GBps": wb / (ms * 1e-3) / 1e9,
+                        "variant": "197 GEMV launches in a HIP graph"}
+    del ys_keep
+    step.free()
+    out["weight_bytes"] = wb
+    return out
+
+
+def whisper_large_layers(qd, nlayers):
+    """Q4_0 weights of `nlayers` Whisper-large layers, baked on the GPU."""
+    import synth
+    layers = []
+    for layer in range(nlayers):
+        layers.append([(name, rows, cols,
+                        q4_0_from_f32(qd, synth.w_f32(rows, cols, key=(5, layer, k)), rows, cols))
+                       for k, (name, rows, cols) in enumerate(synth.WHISPER_LARGE_LAYER)])
+    return layers
+
+
+def row_whisper_large_prefill(qd, layers):
+    """One encoder layer's six Q4_0 projections at M = 1500 frames (MFMA)."""
+    import torch
+    import synth
+    m = synth.WHISPER_LARGE_FRAMES
+    lay = layers[0]
+    xs = {c: bf16dev(synth.x_bf16(m, c, key=(5, 99, c))) for c in (1280, 5120)}
+    ys = [torch.empty((m, r), device=DEV) for _, r, _, _ in lay]
+    flops = sum(2 * m * r * c for _, r, c, _ in lay)
+    g = capture(lambda: [qd.qgemm_q4_0_prefill(wq, r, c, xs[c], ys[k], m)
+                         for k, (_, r, c, wq) in enumerate(lay)])
+    ms = event_time(g.replay, 10, 3)
+    per = {}
+    for k, (name, r, c, wq) in enumerate(lay):
+        gk = capture(lambda k=k, r=r, c=c, wq=wq: qd.qgemm_q4_0_prefill(wq, r, c, xs[c], ys[k], m))
+        mk = event_time(gk.replay, 20, 3)
+        per[name] = {"us": mk * 1e3, "TFLOPs": 2 * m * r * c / (mk * 1e-3) / 1e12,
+                     "mfma_frac": 2 * m * r * c / (mk * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"frames": m, "flops_per_layer": flops, "ms_per_layer": ms,
+            "ms_32_layers": 32 * ms, "TFLOPs": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
+            "per_matrix": per}
+
+
+def row_whisper_large_decoder(qd, layers):
+    """32 layers x (q, k, v, o, fc1, fc2) Q4_0 GEMVs at batch 1, f32."""
+    import torch
+    import synth
+    ops = []
+    wb = 0
+    for layer, lay in enumerate(layers):
+        for k, (name, r, c, wq) in enumerate(lay):
+            x = torch.from_numpy(synth.x_f32(1, c, key=(5, layer, 100 + k))).to(DEV)
+            ops.append((wq, r, c, x, torch.empty((1, r), device=DEV)))
+            wb += qd.q4_0_bytes(r, c)
+    g = capture(lambda: [qd.qgemv_q4_0(wq, r, c, x, y, 1) for wq, r, c, x, y in ops])
+    ms = event_time(g.replay, 20, 3)
+    return {"gemvs": len(ops), "weight_bytes": wb, "ms_per_step": ms,
+            "tokens_per_s": 1000.0 / ms, "weight_GBps": wb / (ms * 1e-3) / 1e9,
+            "hbm_peak_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "variant": "192 GEMV launches in a HIP graph"}
+
+
+def row_q4_0_bake(qd):
+    """f32 -> Q4_0 of one Whisper-large layer (19.7 M weights)."""
+    import torch
+    import synth
+    mats = [(r, c, torch.from_numpy(synth.w_f32(r, c, key=(5, 77, k))).to(DEV),
+             torch.empty(qd.q4_0_bytes(r, c), dtype=torch.uint8, device=DEV))
+            for k, (_, r, c) in enumerate(synth.WHISPER_LARGE_LAYER)]
+    n = sum(r * c for r, c, _, _ in mats)
+    g = capture(lambda: [qd.q4_0_quantize(w, r, c, o) for r, c, w, o in mats])
+    ms = event_time(g.replay, 20, 3)
+    moved = n * 4 + sum(qd.q4_0_bytes(r, c) for r, c, _, _ in mats)
+    return {"weights": n, "ms": ms, "Gweights_per_s": n / (ms * 1e-3) / 1e9,
+            "GBps": moved / (ms * 1e-3) / 1e9,
+            "hbm_peak_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
+ROWS = ("affine_gemv_1024", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
+        "whisper_large_decoder", "q4_0_bake")
+
+
+def run_rows(qd, names):
+    import torch
+    out = {}
+    layers = None
+    for name in names:
+        t0 = time.perf_counter()
+        try:
+            if name in ("whisper_large_prefill", "whisper_large_decoder") and layers is None:
+                import synth
+                layers = whisper_large_layers(qd, synth.WHISPER_LARGE_LAYERS)
+            fn = globals()["row_" + name]
+            out[name] = fn(qd, layers) if "whisper_large" in name else fn(qd)
+        except Exception as e:  # a failing row is reported, not hidden
+            out[name] = {"error": repr(e)}
+        out[name]["bench_wall_s"] = time.perf_counter() - t0
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -126,59 +369,33 @@ def main():
                           "design notes, not launched)"}))
         return 2
     import torch
+
     import synth
-    dev = "cuda:0"
     torch.cuda.set_device(0)
-    step = DecodeStep(synth.QWEN3_0_6B, dev)
-
-    # warm (also fills the library's per-device architecture cache)
-    step.run_eager()
-    torch.cuda.synchronize()
-
-    s = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        step.run_eager()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            step.run_eager()
+    step = DecodeStep(synth.QWEN3_0_6B)
+    qd = step.qd
+    step.run_eager()  # warm (also fills the library's per-device caches)
     torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
 
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(cur)
-        for _ in range(steps):
-            fn()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
-
-    # the launch-per-GEMV graph, kept as a reference point
-    ms_graph, _ = timed(g.replay, max(10, args.steps // 4), max(2, args.warmup // 4))
+    g = capture(step.run_eager)  # the launch-per-GEMV graph, kept as a reference point
+    ms_graph = event_time(g.replay, max(10, args.steps // 4), max(2, args.warmup // 4))
 
     if args.variant == "step":
-        step.plan_step(dev)
-        ms, wall = timed(lambda: step.run_step(cur), args.steps, args.warmup)
-        err = step.qd.qgemv_affine_i8_g64_step_check(step.plan)
-        assert err == 0
+        step.plan_step()
+        t0 = time.perf_counter()
+        ms = event_time(lambda: step.run_step(cur), args.steps, args.warmup, cur)
+        wall = time.perf_counter() - t0
+        assert qd.qgemv_affine_i8_g64_step_check(step.plan) == 0
         variant = ("one persistent launch per step (one workgroup per CU); stage s+1 "
                    "reads its inputs only after every workgroup finished stage s")
-        kernel = "affine_step_kernel"
-        launches = 1
+        kernel, launches = "affine_step_kernel", 1
     else:
         ms, wall = ms_graph, None
         variant = "hipgraph: 197 GEMV launches in decoder order"
-        kernel = "affine_gemv_kernel<1,4>"
-        launches = step.launches()
+        kernel, launches = "affine_gemv_m1_kernel", len(step.mats)
     tok_s = 1000.0 / ms
     gbps = step.weight_bytes / (ms * 1e-3) / 1e9
-
     avg_launch_s = ms * 1e-3 / launches
     bytes_per_launch = step.weight_bytes / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
@@ -199,27 +416,26 @@ def main():
             "workload": "qwen3-0.6b-shaped decode step, batch 1: 197 affine-INT8 g64 "
                         "GEMVs (28 x q,k,v,o,gate,up,down + 151936x1024 LM head)",
             "batch": 1, "weight_bytes": step.weight_bytes,
-            "activations": "bf16 in/out, fp32 accumulate",
+            "activations": "bf16 in/out, u8 codes, fp32 accumulate",
             "variant": variant,
         },
-        "graph_of_197_launches_ms_per_step": ms_graph,
         "weight_GBps": gbps,
         "hbm_peak_frac": gbps / HBM_PEAK_GBPS,
+        "graph_of_197_launches_ms_per_step": ms_graph,
         "wall_s_timed": wall,
         "roofline": {
-            "kernel": kernel,
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
-            "bytes_per_launch": bytes_per_launch,
-            "avg_launch_us": avg_launch_s * 1e6,
+            "kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
         },
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(step)
+    step.free()
+    torch.cuda.empty_cache()
+    names = ROWS if args.rows == "all" else [] if args.rows == "none" else args.rows.split(",")
+    if names:
+        out["rows"] = run_rows(qd, names)
     print(json.dumps(out))
     return 0
 

@@ -179,6 +179,8 @@ size_t step_staging_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m
 
 }  // namespace
 
+int qd::device_cus() { return current_cus(); }
+
 extern "C" {
 
 const char *qd_status_string(int status) {

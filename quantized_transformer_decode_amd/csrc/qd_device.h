@@ -40,6 +40,69 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Pointers that are not kernel arguments are generic; casting them to the
+// global address space makes their accesses global_* instructions (flat_*
+// would also count against the LDS wait counter).
+#define QD_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ QD_GLOBAL T *gp(T *p) {
+  return (QD_GLOBAL T *)p;
+}
+
+// Wave-uniform value forced into a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sum over the 64 lanes with DPP row operations; the total ends in lane 63
+// and is broadcast with readlane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  int x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));  // quad [1,0,3,2]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));  // quad [2,3,0,1]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true)); // row half mirror
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true)); // row mirror
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false)); // row bcast 15
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false)); // row bcast 31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// 16 u8 codes (one 16-byte load) against 16 activations.
+__device__ __forceinline__ float dot16(const uint4 q, const float4 a, const float4 b,
+                                       const float4 c, const float4 d) {
+  float s = ubyte<0>(q.x) * a.x;
+  s = fmaf(ubyte<1>(q.x), a.y, s);
+  s = fmaf(ubyte<2>(q.x), a.z, s);
+  s = fmaf(ubyte<3>(q.x), a.w, s);
+  s = fmaf(ubyte<0>(q.y), b.x, s);
+  s = fmaf(ubyte<1>(q.y), b.y, s);
+  s = fmaf(ubyte<2>(q.y), b.z, s);
+  s = fmaf(ubyte<3>(q.y), b.w, s);
+  s = fmaf(ubyte<0>(q.z), c.x, s);
+  s = fmaf(ubyte<1>(q.z), c.y, s);
+  s = fmaf(ubyte<2>(q.z), c.z, s);
+  s = fmaf(ubyte<3>(q.z), c.w, s);
+  s = fmaf(ubyte<0>(q.w), d.x, s);
+  s = fmaf(ubyte<1>(q.w), d.y, s);
+  s = fmaf(ubyte<2>(q.w), d.z, s);
+  s = fmaf(ubyte<3>(q.w), d.w, s);
+  return s;
+}
+
+// LDS layout of an activation vector for the wave-per-1KiB-chunk GEMVs:
+// within each 1024-column chunk, column 16*l + 4*q + t (lane l's q-th float4)
+// is stored at float (q*64 + l)*4 + t, so each of a wave's four float4
+// reads is lane-contiguous (no bank conflicts).
+__device__ __forceinline__ int xswz(int e) {
+  const int chunk = e & ~1023, r = e & 1023;
+  return chunk + ((((r >> 2) & 3) * 64 + (r >> 4)) << 2) + (r & 3);
+}
+
 // Sum over aligned groups of W lanes (W = 2, 4, 8, 16, 32).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {

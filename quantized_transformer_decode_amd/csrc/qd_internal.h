@@ -8,6 +8,9 @@
 
 namespace qd {
 
+// Compute units of the current device, cached per device (0 if unknown).
+int device_cus();
+
 hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
                               const uint16_t *x, uint16_t *y, int m,
                               hipStream_t stream);
