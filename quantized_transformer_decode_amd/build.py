@@ -3,8 +3,10 @@
 Every .hip file under csrc/ is compiled to an object (in parallel), then the
 objects are linked into ``quantized_transformer_decode_amd/libqdecode.so``.
 The quantize kernel is compiled with -ffp-contract=off (its encoding must
-match ggml's f32 rounding bit for bit).  Packed-fp32 VALU instructions are
-disabled for all device code.
+match ggml's f32 rounding bit for bit).  The prefill GEMM keeps its MFMA
+results in ordinary VGPRs (fewer registers than the AGPR form, so two
+workgroups fit per CU).  Packed-fp32 VALU instructions are disabled for all
+device code.
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ COMMON = [
 ]
 PER_FILE = {
     "q4_0_quantize.hip": ["-ffp-contract=off"],
+    "q4_0_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -6,139 +6,241 @@
 // (q - 8) in [-8, 7] are exact in BF16, so each 16x16x32 BF16 MFMA computes
 // one block's partial product P exactly up to fp32 accumulation; the f16
 // delta is applied to P in fp32 (rounding d*(q-8) to BF16 instead would cost
-// up to 2^-9 relative error per weight).
+// up to 2^-9 relative error per weight).  One fp32 multiply-add per output
+// per block is exactly the VALU rate that matches the MFMA rate, so the
+// kernel interleaves the MFMAs of block b with the delta scaling of block
+// b-1's partial products.
 //
-// Tiling: a 256-thread workgroup owns a 64 (tokens) x 64 (weight rows) output
-// tile; its four wavefronts each own 32 x 32 (2 x 2 MFMA tiles).  Each K step
-// is one Q4_0 block (32 columns): x [64][32] BF16 and the dequantised codes
-// [64][32] BF16 are staged in LDS, the deltas as fp32.
+// Tiling: a 256-thread workgroup owns a BM (frames) x BN (weight rows)
+// output tile, 64 x 64 by default; its four waves are 2 x 2, each
+// BM/2 x BN/2.  Each LDS stage covers 128 columns of K (four Q4_0 blocks):
+// x [BM][128] BF16 and the dequantised codes [BN][128] BF16, rows padded by
+// 16 bytes so the 16 rows a fragment read touches fall in different banks;
+// the deltas [BN][4] fp32.  Stages are double-buffered: the global loads of
+// stage s+1 are in flight while stage s is computed.  64 x 64 tiles give
+// ~2 workgroups per CU on a 1500 x 1280 output (the LDS, 70 KiB per
+// workgroup, allows two) -- larger tiles leave the chip underfilled at
+// Whisper-large shapes and smaller ones repeat the dequantisation.
 #include "qd_device.h"
 #include "qd_internal.h"
+
+#ifndef QD_GEMM_BM
+#define QD_GEMM_BM 64
+#define QD_GEMM_BN 64
+#endif
 
 namespace qd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 64;
-constexpr int BN = 64;
-constexpr int kLd = 40;  // LDS row stride in bf16 (32 + 8 pad, 80 bytes)
+constexpr int BK = 128;                 // K columns per stage (4 blocks)
+constexpr int NB = BK / 32;             // Q4_0 blocks per stage
+constexpr int LDA = BK + 8;             // LDS row stride in bf16 (272 bytes)
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+template <int BM, int BN>
+struct Tile {
+  static constexpr int A_ELEMS = BM * LDA;
+  static constexpr int B_ELEMS = BN * LDA;
+  static constexpr int STAGE_BYTES = (A_ELEMS + B_ELEMS) * 2 + BN * NB * 4;
+  static constexpr int TM = BM / 32;    // 16x16 MFMA tiles per wave along M
+  static constexpr int TN = BN / 32;    // ... along N (waves are 2 x 2)
+  static constexpr int XCH = BM * 16 / kThreads;  // x 16-byte chunks per thread
+  static constexpr int WB = BN * NB / kThreads;   // weight blocks per thread (<= 1)
+};
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// (q - 8) of 8 nibbles (the low or high nibbles of two dwords) as BF16:
+// small integers are exact in BF16.
+__device__ __forceinline__ uint32_t bf16x2_of(int a, int b) {
+  return (uint32_t)f32_to_bf16((float)a) | ((uint32_t)f32_to_bf16((float)b) << 16);
 }
 
-__global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
-    const uint8_t *__restrict__ w, int rows, int cols,
-    const uint16_t *__restrict__ x, float *__restrict__ y, int m) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * kLd];
-  __shared__ float Ds[BN];
+template <int BM, int BN>
+struct Stage {
+  uint4 xa[Tile<BM, BN>::XCH];  // this thread's x chunks (16 bytes each)
+  uint32_t w[5];                // this thread's Q4_0 block window
+  uint32_t fb;                  // flat index parity | 2 if the row is past the end
+  bool has_w;                   // this thread loads a weight block
+};
 
+// Global loads of one stage: x rows m0.., columns k0..k0+127; the weight
+// block (row n0 + tid/4, block kb0 + tid%4).
+template <int BM, int BN>
+__device__ __forceinline__ void stage_load(Stage<BM, BN> &st, const QD_GLOBAL uint16_t *x,
+                                           const QD_GLOBAL uint8_t *w, int m, int rows,
+                                           int cols, int m0, int n0, int kb0, int tid) {
+#pragma unroll
+  for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
+    const int c = tid + i * kThreads;  // 16-byte chunk of the 128 x 256-byte tile
+    const int r = c >> 4, ch = c & 15;
+    int row = m0 + r;
+    const bool ok = row < m;
+    if (!ok) row = m - 1;
+    const u32x4 v = *(const QD_GLOBAL u32x4 *)(x + (size_t)row * cols + kb0 * 32 + ch * 8);
+    st.xa[i] = ok ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0, 0, 0, 0);
+  }
+  st.has_w = tid < BN * NB;
+  const int r = (tid >> 2) % BN, b = tid & 3;
+  int n = n0 + r;
+  if (n >= rows) n = rows - 1;  // clamped rows are zeroed at the store
+  const size_t flat = (size_t)n * (cols >> 5) + kb0 + b;
+  // 20-byte window holding the block's 18 bytes: starts 2 bytes early for
+  // odd flat indices (still inside the previous block) and on the block for
+  // even ones (the 2 bytes past it exist: an even block is never the last
+  // one, the block count per row being a multiple of 8)
+  const QD_GLOBAL uint32_t *p =
+      (const QD_GLOBAL uint32_t *)(w + 18 * flat - 2 * (flat & 1));
+#pragma unroll
+  for (int i = 0; i < 5; ++i) st.w[i] = p[i];
+  st.fb = (uint32_t)(flat & 1) | (n0 + r >= rows ? 2u : 0u);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void stage_store(const Stage<BM, BN> &st, uint16_t *As, uint16_t *Bs,
+                                            float *Ds, int tid) {
+#pragma unroll
+  for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
+    const int c = tid + i * kThreads;
+    const int r = c >> 4, ch = c & 15;
+    *(uint4 *)(As + r * LDA + ch * 8) = st.xa[i];
+  }
+  if (!st.has_w) return;
+  const int r = tid >> 2, b = tid & 3;
+  const bool odd = st.fb & 1, dead = st.fb & 2;
+  // d: bytes 0-1 of the block; nibble bytes 2..17
+  const uint32_t dbits = odd ? (st.w[0] >> 16) : (st.w[0] & 0xffffu);
+  uint32_t nib[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    nib[k] = odd ? st.w[k + 1] : __builtin_amdgcn_alignbyte(st.w[k + 1], st.w[k], 2);
+  uint32_t lo[8], hi[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t v = dead ? 0x88888888u : nib[k];
+    lo[2 * k] = bf16x2_of((int)(v & 15u) - 8, (int)((v >> 8) & 15u) - 8);
+    lo[2 * k + 1] = bf16x2_of((int)((v >> 16) & 15u) - 8, (int)((v >> 24) & 15u) - 8);
+    hi[2 * k] = bf16x2_of((int)((v >> 4) & 15u) - 8, (int)((v >> 12) & 15u) - 8);
+    hi[2 * k + 1] = bf16x2_of((int)((v >> 20) & 15u) - 8, (int)((v >> 28) & 15u) - 8);
+  }
+  uint4 *dst = (uint4 *)(Bs + r * LDA + b * 32);
+  dst[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);  // elements 0..7
+  dst[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);  // 8..15
+  dst[2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);  // 16..23
+  dst[3] = make_uint4(hi[4], hi[5], hi[6], hi[7]);  // 24..31
+  Ds[r * NB + b] = dead ? 0.f : f16_to_f32(dbits);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
+    const uint8_t *__restrict__ w_, int rows, int cols, const uint16_t *__restrict__ x_,
+    float *__restrict__ y_, int m) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const QD_GLOBAL uint8_t *w = gp(w_);
+  const QD_GLOBAL uint16_t *x = gp(x_);
+  QD_GLOBAL float *y = gp((float *)y_);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uni(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
-  const int bpr = cols >> 5;
+  const int nstages = cols / BK;
 
-  floatx4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  using T = Tile<BM, BN>;
+  constexpr int TM = T::TM, TN = T::TN;
+  auto As = [&](int buf) { return (uint16_t *)(smem + buf * T::STAGE_BYTES); };
+  auto Bs = [&](int buf) { return (uint16_t *)(smem + buf * T::STAGE_BYTES) + T::A_ELEMS; };
+  auto Ds = [&](int buf) {
+    return (float *)(smem + buf * T::STAGE_BYTES + (T::A_ELEMS + T::B_ELEMS) * 2);
+  };
 
-  for (int kb = 0; kb < bpr; ++kb) {
-    // x tile: 64 rows x 64 bytes; thread -> (row tid/4, 16-byte chunk tid%4)
-    {
-      const int r = tid >> 2, ch = tid & 3;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + r < m)
-        v = *(const uint4 *)(x + (size_t)(m0 + r) * cols + kb * 32 + ch * 8);
-      *(uint4 *)(As + r * kLd + ch * 8) = v;
-    }
-    // weight tile: threads 0..63 dequantise one block each
-    if (tid < BN) {
-      const int n = n0 + tid;
-      uint32_t nib[4] = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-      float d = 0.f;
-      if (n < rows) {
-        const size_t flat = (size_t)n * bpr + kb;
-        const size_t nb = 18 * flat + 2;
-        const uint32_t *p = (const uint32_t *)(w + (nb & ~(size_t)3));
-        const uint32_t sh = (uint32_t)(nb & 3);
-        const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
-        const uint32_t v4 = sh ? p[4] : 0u;
-        nib[0] = __builtin_amdgcn_alignbyte(v1, v0, sh);
-        nib[1] = __builtin_amdgcn_alignbyte(v2, v1, sh);
-        nib[2] = __builtin_amdgcn_alignbyte(v3, v2, sh);
-        nib[3] = __builtin_amdgcn_alignbyte(v4, v3, sh);
-        d = f16_to_f32(*(const uint16_t *)(w + 18 * flat));
-      }
-      uint32_t lo[8], hi[8];
+  floatx4 acc[TM][TN];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t v = nib[k];
-        const float e0 = (float)((int)(v & 15u) - 8);
-        const float e1 = (float)((int)((v >> 8) & 15u) - 8);
-        const float e2 = (float)((int)((v >> 16) & 15u) - 8);
-        const float e3 = (float)((int)((v >> 24) & 15u) - 8);
-        const float f0 = (float)((int)((v >> 4) & 15u) - 8);
-        const float f1 = (float)((int)((v >> 12) & 15u) - 8);
-        const float f2 = (float)((int)((v >> 20) & 15u) - 8);
-        const float f3 = (float)((int)((v >> 28) & 15u) - 8);
-        lo[2 * k] = pack_bf16x2(e0, e1);
-        lo[2 * k + 1] = pack_bf16x2(e2, e3);
-        hi[2 * k] = pack_bf16x2(f0, f1);
-        hi[2 * k + 1] = pack_bf16x2(f2, f3);
-      }
-      uint4 *dst = (uint4 *)(Bs + tid * kLd);
-      dst[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);  // elements 0..7
-      dst[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);  // 8..15
-      dst[2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);  // 16..23
-      dst[3] = make_uint4(hi[4], hi[5], hi[6], hi[7]);  // 24..31
-      Ds[tid] = d;
-    }
-    __syncthreads();
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int kq = (lane >> 4) * 8;  // this lane's 8 K indices
-    bf16x8 a[2], b[2];
+  Stage<BM, BN> st;
+  stage_load(st, x, w, m, rows, cols, m0, n0, 0, tid);
+  stage_store(st, As(0), Bs(0), Ds(0), tid);
+  __syncthreads();
+
+  const int kq = (lane >> 4) * 8;  // this lane's 8 K indices within a block
+  const int arow = wm * (BM / 2) + (lane & 15);
+  const int bcol = wn * (BN / 2) + (lane & 15);
+
+  for (int s = 0; s < nstages; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nstages) stage_load(st, x, w, m, rows, cols, m0, n0, (s + 1) * NB, tid);
+    const uint16_t *A = As(buf);
+    const uint16_t *Bm = Bs(buf);
+    const float *D = Ds(buf);
+    floatx4 p[2][TM][TN];  // partial products of two blocks in flight
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wm * 32 + i * 16 + (lane & 15);
-      a[i] = *(const bf16x8 *)(As + r * kLd + kq);
-    }
+    for (int b = 0; b < NB; ++b) {
+      bf16x8 af[TM], bfr[TN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = wn * 32 + j * 16 + (lane & 15);
-      b[j] = *(const bf16x8 *)(Bs + c * kLd + kq);
-    }
+      for (int i = 0; i < TM; ++i)
+        af[i] = *(const bf16x8 *)(A + (arow + i * 16) * LDA + b * 32 + kq);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float dj = Ds[wn * 32 + j * 16 + (lane & 15)];
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *(const bf16x8 *)(Bm + (bcol + j * 16) * LDA + b * 32 + kq);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const floatx4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a[i], b[j], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        acc[i][j] += dj * p;
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          p[b & 1][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af[i], bfr[j], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      if (b > 0) {  // scale the previous block while this block's MFMAs run
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float dj = D[(bcol + j * 16) * NB + (b - 1)];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[i][j] += dj * p[(b - 1) & 1][i][j];
+        }
       }
     }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float dj = D[(bcol + j * 16) * NB + (NB - 1)];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i][j] += dj * p[(NB - 1) & 1][i][j];
+    }
+    if (s + 1 < nstages) stage_store(st, As(buf ^ 1), Bs(buf ^ 1), Ds(buf ^ 1), tid);
     __syncthreads();
   }
 
   // C layout of a 16x16 f32 MFMA tile: lane holds rows 4*(lane/16)+v of
   // column lane%16.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int t = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + v;
+        const int t = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + v;
         if (t < m && n < rows) y[(size_t)t * rows + n] = acc[i][j][v];
       }
     }
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const uint8_t *w, int rows, int cols, const uint16_t *x, float *y,
+                       int m, hipStream_t stream) {
+  const size_t lds = 2 * (size_t)Tile<BM, BN>::STAGE_BYTES;
+  static bool attr_set = false;  // the limit is per function; setting it twice is harmless
+  if (!attr_set && lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemm_kernel<BM, BN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((rows + BN - 1) / BN, (m + BM - 1) / BM);
+  hipLaunchKernelGGL((q4_0_gemm_kernel<BM, BN>), grid, dim3(kThreads), lds, stream, w, rows,
+                     cols, x, y, m);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -146,10 +248,7 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
 hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,
                             const uint16_t *x, float *y, int m,
                             hipStream_t stream) {
-  dim3 grid((rows + BN - 1) / BN, (m + BM - 1) / BM);
-  hipLaunchKernelGGL(q4_0_gemm_kernel, grid, dim3(kThreads), 0, stream, w,
-                     rows, cols, x, y, m);
-  return hipGetLastError();
+  return launch_tile<QD_GEMM_BM, QD_GEMM_BN>(w, rows, cols, x, y, m, stream);
 }
 
 }  // namespace qd
