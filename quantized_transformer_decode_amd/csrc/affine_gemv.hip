@@ -2,115 +2,328 @@
 //
 // Computes y[t, r] = sum_c (q[r,c] * s[r,c/64] + b[r,c/64]) * x[t,c]
 // (turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- embed_row_bytes for the
-// dequantisation, Qwen3AsrMetalEngine::gemv for the GEMV), regrouped as
-//   y[t, r] = sum_{16-col chunk j} s * (sum_{c in j} q*x) + b * X[t, j]
-// where X[t, j] is the sum of x over chunk j (a 16-column chunk never
-// straddles a 64-column group).  Codes are exact in fp32, accumulation is
-// fp32, the output is rounded once to BF16 (nearest even).
+// dequantisation, Qwen3AsrMetalEngine::gemv for the GEMV), regrouped per
+// 64-column group g as
+//   y[t, r] = sum_g s[r,g] * (sum_{c in g} q*x) + b[r,g] * (sum_{c in g} x)
+// Codes are exact in fp32 and in BF16, accumulation is fp32, the output is
+// rounded once to BF16 (nearest even).
 //
-// Layout on the chip: one wavefront streams R rows at a time; lane l reads
-// the 16-byte code chunks l, l+64, ... of each row (a full 1 KiB of one row
-// per load instruction, fully coalesced), converts the bytes with
-// v_cvt_f32_ubyteN and multiplies against x, which every workgroup stages
-// once in LDS as fp32 together with the per-chunk sums X.
+// Two kernels: batch 1 streams rows through the VALU (one wave per row
+// range, lane l holding bytes [16l, 16l+16) of each 1 KiB chunk, x in LDS as
+// fp32); batches of 2..16 tokens use the matrix cores, where one MFMA pair
+// per group covers all 16 token rows and the VALU only converts codes and
+// applies the group's scale and bias.
 #include "qd_device.h"
 #include "qd_internal.h"
 
 namespace qd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kLdsBudget = 64 * 1024;
+// ---- small batch: matrix cores ----------------------------------------------
+//
+// A tile y^T[16 tokens][16 rows] = X[16][K] W^T[K][16] on
+// v_mfma_f32_16x16x32_bf16: the A operand is x as given (BF16), the B
+// operand the u8 codes converted exactly to BF16.  Per 64-column group g:
+//   P[t,n] = sum_{k in g} q[n,k] x[t,k]          (two MFMAs)
+//   S[t]   = sum_{k in g} x[t,k]                 (two MFMAs against ones)
+//   acc[t,n] += s[n,g] P[t,n] + b[n,g] S[t]      (fp32)
+// A lane's four C values (tokens 4*(lane/16)+v, weight row lane%16) share
+// one scale and one bias.  K order inside a group: lane quarter g4 = lane/16
+// holds columns 16*g4..+7 for the first MFMA and 16*g4+8..+15 for the
+// second, for x and codes alike, so each lane reads 16 contiguous code bytes
+// and 32 contiguous x bytes per group.  Token rows past m read row m-1 and
+// their outputs are dropped.
+//
+// Work split: a "tile" is 16*R weight rows over all of K.  A workgroup of
+// kMW waves has kMW/KS slots of KS waves; the waves of a slot take
+// contiguous ranges of the groups and their partial tiles are summed in LDS
+// (KS > 1, for matrices with few tiles).  With KS = 1 each wave owns whole
+// tiles, walks them grid-stride and stores its own outputs; its loads run
+// ahead across tile boundaries (double-buffered, U groups per buffer, always
+// issued unconditionally -- past the end the last group is loaded again --
+// so the compiler waits only for the buffer being consumed).
 
-// Tokens t0 .. t0+MT-1 (those < m) against all rows.
-template <int MT, int R>
-__global__ __launch_bounds__(kThreads) void affine_gemv_kernel(
-    const uint8_t *__restrict__ w, int rows, int cols,
-    const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int t0, int m) {
-  extern __shared__ float lds[];
-  float *xs = lds;                 // [MT][cols]
-  float *xsum = lds + MT * cols;   // [MT][cols/16]
-  const int nch = cols >> 4;
-  for (int i = threadIdx.x; i < MT * cols; i += kThreads) {
-    const int t = i / cols;
-    const int c = i - t * cols;
-    xs[i] = (t0 + t < m) ? bf16_to_f32(x[(size_t)(t0 + t) * cols + c]) : 0.f;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < MT * nch; i += kThreads) {
-    const float *p = xs + (size_t)i * 16;
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) s += p[k];
-    xsum[i] = s;
-  }
-  __syncthreads();
+constexpr int kMW = 8;
+constexpr int kMThreads = kMW * kWave;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int groups = cols >> 6;
-  const uint16_t *scales = (const uint16_t *)(w + (size_t)rows * cols);
-  const uint16_t *biases = scales + (size_t)rows * groups;
+// Scales and biases: with CH (the group count a multiple of 4) each buffer
+// of U = 4 groups also loads, per 16-row block, one 8-byte piece per lane --
+// lanes n and 32+n the scales of row n for the buffer's four groups, lanes
+// 16+n and 48+n its biases -- and ds_bpermute hands each lane the pair it
+// needs; without CH every lane loads its row's scale and bias per group.
+template <int R, int U, bool CH>
+struct MGroup {
+  u32x4 q[U][R];
+  bf16x8 xa[U], xb[U];
+  uint16_t sc[CH ? 1 : U][R], bi[CH ? 1 : U][R];
+  u32x2 sbv[R];
+};
 
-  for (int row0 = (blockIdx.x * kWaves + wave) * R; row0 < rows;
-       row0 += gridDim.x * kWaves * R) {
-    float acc[R][MT];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
+// Walk position: item (j, g) = group g of the wave's j-th tile (wave-uniform).
+struct MCursor {
+  int j, g;
+};
 
-    for (int u = lane; u < nch; u += kWave) {
-      uint4 q[R];
-      float s[R], b[R];
+struct MShape {
+  const QD_GLOBAL uint8_t *w;
+  const QD_GLOBAL uint16_t *sc;
+  size_t boff;     // biases - scales, in elements
+  int rows, cols, groups;
+  int ts0, stride; // the wave's first tile and the tile stride
+  int ga, gb;      // the wave's group range
+};
+
+// Advance by one item without branches; `left` counts the items still to
+// walk (the cursor stays on the last item once it is 0).
+__device__ __forceinline__ void mc_next(MCursor &c, const MShape &S, int &left) {
+  const int adv = left > 1;
+  left = adv ? left - 1 : 0;
+  const int g = c.g + adv;
+  const int wrap = g == S.gb;
+  c.g = wrap ? S.ga : g;
+  c.j += wrap;
+}
+
+// Addresses are a wave-uniform base (the tile's first row, the group) plus a
+// 32-bit per-lane offset, so the loads take the scalar-base form.  Rows past
+// the end of the matrix are clamped to its last row.
+template <int R, int U, bool CH>
+__device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const MShape &S,
+                                         const QD_GLOBAL uint16_t *x, uint32_t xoff, int lane,
+                                         int &left) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = row0 + r;
-        if (row < rows) {
-          q[r] = *(const uint4 *)(w + (size_t)row * cols + 16 * u);
-          const size_t g = (size_t)row * groups + (u >> 2);
-          s[r] = bf16_to_f32(scales[g]);
-          b[r] = bf16_to_f32(biases[g]);
-        } else {
-          q[r] = make_uint4(0, 0, 0, 0);
-          s[r] = 0.f;
-          b[r] = 0.f;
-        }
-      }
+  for (int u = 0; u < U; ++u) {
+    const QD_GLOBAL uint8_t *xg = (const QD_GLOBAL uint8_t *)(x + 64 * c.g);
+    G.xa[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff));
+    G.xb[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
+    const int trow = (S.ts0 + c.j * S.stride) * 16 * R;
+    const int lim = S.rows - 1 - trow;  // last valid row offset inside the tile
+    const QD_GLOBAL uint8_t *cb = S.w + (size_t)trow * S.cols + 64 * c.g;
+    const QD_GLOBAL uint8_t *sb =
+        (const QD_GLOBAL uint8_t *)(S.sc + (size_t)trow * S.groups + c.g);
+    const QD_GLOBAL uint8_t *bb = sb + 2 * S.boff;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float4 *xp = (const float4 *)(xs + t * cols + 16 * u);
-        const float4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
-        const float xc = xsum[t * nch + u];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float d = dot16(q[r], x0, x1, x2, x3);
-          acc[r][t] = fmaf(s[r], d, fmaf(b[r], xc, acc[r][t]));
-        }
+    for (int r = 0; r < R; ++r) {
+      // codes: adjacent lanes read adjacent 16-byte pieces (row lane/4,
+      // quarter lane%4); mg_compute moves them into the MFMA layout
+      const uint32_t co = (uint32_t)min(16 * r + (lane >> 2), lim) * (uint32_t)S.cols +
+                          16u * (lane & 3);
+      G.q[u][r] = __builtin_nontemporal_load((const QD_GLOBAL u32x4 *)(cb + co));
+      const uint32_t so = (uint32_t)min(16 * r + (lane & 15), lim) * (uint32_t)(2 * S.groups);
+      if constexpr (CH) {
+        if (u == 0)  // the buffer's first group starts a 4-group chunk
+          G.sbv[r] = *(const QD_GLOBAL u32x2 *)(((lane >> 4) & 1 ? bb : sb) + so);
+      } else {
+        G.sc[u][r] = *(const QD_GLOBAL uint16_t *)(sb + so);
+        G.bi[u][r] = *(const QD_GLOBAL uint16_t *)(bb + so);
       }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float v = wave_sum(acc[r][t]);
-        if (lane == 0 && row0 + r < rows && t0 + t < m)
-          y[(size_t)(t0 + t) * rows + row0 + r] = f32_to_bf16(v);
-      }
+    mc_next(c, S, left);
   }
 }
 
-template <int MT, int R>
-hipError_t launch_pass(const uint8_t *w, int rows, int cols, const uint16_t *x,
-                       uint16_t *y, int t0, int m, hipStream_t stream) {
-  const size_t lds = (size_t)MT * cols * 4 + (size_t)MT * (cols / 16) * 4;
-  const int per_block = kWaves * R;
-  int grid = (rows + per_block - 1) / per_block;
-  if (grid > 2048) grid = 2048;
-  hipLaunchKernelGGL((affine_gemv_kernel<MT, R>), dim3(grid), dim3(kThreads),
-                     lds, stream, w, rows, cols, x, y, t0, m);
+// Output of one finished tile (KS = 1): lane holds tokens 4*(lane/16)+v of
+// weight row lane%16 of each 16-row block.
+template <int R>
+__device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S, int j, int m,
+                                         QD_GLOBAL uint16_t *y, int lane) {
+  const int base = (S.ts0 + j * S.stride) * 16 * R + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = base + 16 * r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * (lane >> 4) + v;
+      if (t < m && n < S.rows) y[(size_t)t * S.rows + n] = f32_to_bf16(acc[r][v]);
+      acc[r][v] = 0.f;
+    }
+  }
+}
+
+// Items past the end of the walk (padding up to a whole buffer) are
+// computed with zero scale and bias.
+template <int R, int U, bool CH, bool STORE>
+__device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&acc)[R],
+                                           MCursor &c, const MShape &S, int &left, int m,
+                                           QD_GLOBAL uint16_t *y, int lane, bf16x8 ones) {
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  const int src4 = (4 * (lane & 15) + (lane >> 4)) * 4;
+  const int srcs = (lane & 15) * 4, srcb = srcs + 64;
+  uint32_t sp[R], bp[R];  // scale / bias pair of the current two groups (CH)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int valid = left > 0;  // wave-uniform
+    floatx4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xa[u], ones, z, 0, 0, 0);
+    Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xb[u], ones, Sx, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // lane 16*g4 + n takes row n's quarter g4 from lane 4*n + g4
+      const u32x4 ql = G.q[u][r];
+      const u32x4 q = {(uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.x),
+                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.y),
+                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.z),
+                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.w)};
+      floatx4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xa[u], codes8_bf16(q.x, q.y), z,
+                                                          0, 0, 0);
+      P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xb[u], codes8_bf16(q.z, q.w), P, 0, 0, 0);
+      float s, b;
+      if constexpr (CH) {
+        if ((u & 1) == 0) {
+          const uint32_t d = u < 2 ? G.sbv[r].x : G.sbv[r].y;
+          sp[r] = (uint32_t)__builtin_amdgcn_ds_bpermute(srcs, (int)d);
+          bp[r] = (uint32_t)__builtin_amdgcn_ds_bpermute(srcb, (int)d);
+        }
+        s = __uint_as_float(u & 1 ? sp[r] & 0xffff0000u : sp[r] << 16);
+        b = __uint_as_float(u & 1 ? bp[r] & 0xffff0000u : bp[r] << 16);
+      } else {
+        s = bf16_to_f32(G.sc[u][r]);
+        b = bf16_to_f32(G.bi[u][r]);
+      }
+      s = valid ? s : 0.f;
+      b = valid ? b : 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[r][v] = fmaf(s, P[v], fmaf(b, Sx[v], acc[r][v]));
+    }
+    if (STORE && valid && c.g == S.gb - 1) mg_store(acc, S, c.j, m, y, lane);
+    left -= valid;
+    const int g = c.g + valid;
+    const int wrap = g == S.gb;
+    c.g = wrap ? S.ga : g;
+    c.j += wrap;
+  }
+}
+
+template <int R, int U, int KS, bool CH>
+__global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
+    const uint8_t *__restrict__ w_, int rows, int cols, const uint16_t *__restrict__ x_,
+    uint16_t *__restrict__ y_, int m) {
+  constexpr int SLOTS = kMW / KS;
+  __shared__ float red[KS > 1 ? kMW * R * kWave * 4 : 1];
+  QD_GLOBAL uint16_t *y = gp(y_);
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(threadIdx.x >> 6);
+  const int slot = wave / KS, split = wave % KS;
+  MShape S;
+  S.w = gp(w_);
+  S.rows = rows;
+  S.cols = cols;
+  S.groups = cols >> 6;
+  S.sc = (const QD_GLOBAL uint16_t *)(S.w + (size_t)rows * cols);
+  S.boff = (size_t)rows * S.groups;
+  // group ranges in whole buffers of U groups when the scales come in chunks
+  const int unit = CH ? U : 1;
+  const int units = S.groups / unit;
+  S.ga = uni(unit * (units * split / KS));
+  S.gb = uni(unit * (units * (split + 1) / KS));
+  S.ts0 = blockIdx.x * SLOTS + slot;
+  S.stride = gridDim.x * SLOTS;
+  const int ntiles = (rows + 16 * R - 1) / (16 * R);
+  int tiles_mine = 0;
+  if (S.ts0 < ntiles) tiles_mine = KS == 1 ? (ntiles - 1 - S.ts0) / S.stride + 1 : 1;
+  const int n = uni(tiles_mine * (S.gb - S.ga));
+  const int t = (lane & 15) < m ? (lane & 15) : m - 1;
+  const QD_GLOBAL uint16_t *x = gp(x_);
+  const uint32_t xoff = 2u * ((uint32_t)t * (uint32_t)cols + 16u * (lane >> 4));  // bytes
+
+  floatx4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (n > 0) {
+    const bf16x8 ones = __builtin_bit_cast(
+        bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    MCursor ci, cc;  // issue and compute cursors
+    ci.j = cc.j = 0;
+    ci.g = cc.g = S.ga;
+    int li = n, lc = n;
+    // Loads are never conditional (the compiler then waits for exactly the
+    // buffer it consumes); the branches only choose whether another buffer
+    // is issued before the current one is consumed.
+    MGroup<R, U, CH> A, B;
+    mg_issue(A, ci, S, x, xoff, lane, li);
+    for (;;) {
+      if (lc <= U) {
+        mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, lc, m, y, lane, ones);
+        break;
+      }
+      mg_issue(B, ci, S, x, xoff, lane, li);
+      mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, lc, m, y, lane, ones);
+      if (lc <= U) {
+        mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, lc, m, y, lane, ones);
+        break;
+      }
+      mg_issue(A, ci, S, x, xoff, lane, li);
+      mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, lc, m, y, lane, ones);
+    }
+  }
+  if constexpr (KS > 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((wave * R + r) * kWave + lane) * 4 + v] = acc[r][v];
+    __syncthreads();
+    for (int i = threadIdx.x; i < SLOTS * R * kWave * 4; i += kMThreads) {
+      const int sl = i / (R * kWave * 4), rem = i - sl * (R * kWave * 4);
+      const int r = rem >> 8, l = (rem >> 2) & 63, v = rem & 3;
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) sum += red[(((sl * KS + k) * R + r) * kWave + l) * 4 + v];
+      const int tt = 4 * (l >> 4) + v;
+      const int nn = (blockIdx.x * SLOTS + sl) * 16 * R + 16 * r + (l & 15);
+      if (tt < m && nn < rows) y[(size_t)tt * rows + nn] = f32_to_bf16(sum);
+    }
+  }
+}
+
+#ifndef QD_AFFINE_MFMA_R
+#define QD_AFFINE_MFMA_R 1
+#endif
+#ifndef QD_AFFINE_TARGET_WAVES
+#define QD_AFFINE_TARGET_WAVES 4096
+#define QD_AFFINE_STREAM_WGS 2
+#endif
+
+template <int KS, bool CH>
+hipError_t launch_mfma_ks(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
+                          int m, int grid, hipStream_t stream) {
+  constexpr int R = QD_AFFINE_MFMA_R;
+  constexpr int U = CH ? 4 : 2;
+  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH>), dim3(grid), dim3(kMThreads), 0,
+                     stream, w, rows, cols, x, y, m);
   return hipGetLastError();
+}
+
+template <bool CH>
+hipError_t launch_mfma_ch(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
+                          int m, hipStream_t stream) {
+  // KS: split K over up to 8 waves until the matrix gives about
+  // kTargetWaves waves (each wave keeping at least two buffers of groups);
+  // KS = 1 walks tiles grid-stride with kStreamWgsPerCu workgroups per CU.
+  constexpr int kTargetWaves = QD_AFFINE_TARGET_WAVES;
+  constexpr int kStreamWgsPerCu = QD_AFFINE_STREAM_WGS;
+  constexpr int R = QD_AFFINE_MFMA_R;
+  const int units = (cols / 64) / (CH ? 4 : 1);
+  const long ntiles = (rows + 16 * R - 1) / (16 * R);
+  int ks = 1;
+  while (ks < 8 && ntiles * ks < kTargetWaves && units / (2 * ks) >= (CH ? 1 : 2)) ks *= 2;
+  if (ks == 1) {
+    int cus = device_cus();
+    if (cus < 1) cus = 256;
+    long grid = (ntiles + kMW - 1) / kMW;
+    if (grid > (long)kStreamWgsPerCu * cus) grid = (long)kStreamWgsPerCu * cus;
+    return launch_mfma_ks<1, CH>(w, rows, cols, x, y, m, (int)grid, stream);
+  }
+  const int grid = (int)((ntiles * ks + kMW - 1) / kMW);
+  switch (ks) {
+    case 2: return launch_mfma_ks<2, CH>(w, rows, cols, x, y, m, grid, stream);
+    case 4: return launch_mfma_ks<4, CH>(w, rows, cols, x, y, m, grid, stream);
+    default: return launch_mfma_ks<8, CH>(w, rows, cols, x, y, m, grid, stream);
+  }
+}
+
+hipError_t launch_mfma(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
+                       int m, hipStream_t stream) {
+  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true>(w, rows, cols, x, y, m, stream);
+  return launch_mfma_ch<false>(w, rows, cols, x, y, m, stream);
 }
 
 // ---- batch 1: streaming kernel ---------------------------------------------
@@ -242,23 +455,7 @@ hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
                        stream, w, rows, cols, x, y);
     return hipGetLastError();
   }
-  // Tokens per pass limited by the LDS copy of x (fp32 plus chunk sums).
-  const int cap = kLdsBudget / (cols * 4 + cols / 4);
-  int t0 = 0;
-  while (t0 < m) {
-    const int left = m - t0;
-    const int lim = left < cap ? left : cap;
-    hipError_t e;
-    int mt;
-    if (lim >= 16) { mt = 16; e = launch_pass<16, 1>(w, rows, cols, x, y, t0, m, stream); }
-    else if (lim >= 8) { mt = 8; e = launch_pass<8, 1>(w, rows, cols, x, y, t0, m, stream); }
-    else if (lim >= 4) { mt = 4; e = launch_pass<4, 2>(w, rows, cols, x, y, t0, m, stream); }
-    else if (lim >= 2) { mt = 2; e = launch_pass<2, 4>(w, rows, cols, x, y, t0, m, stream); }
-    else { mt = 1; e = launch_pass<1, 4>(w, rows, cols, x, y, t0, m, stream); }
-    if (e != hipSuccess) return e;
-    t0 += mt;
-  }
-  return hipSuccess;
+  return launch_mfma(w, rows, cols, x, y, m, stream);
 }
 
 }  // namespace qd

@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -41,6 +42,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Pointers that are not kernel arguments are generic; casting them to the
 // global address space makes their accesses global_* instructions (flat_*
@@ -92,6 +94,14 @@ __device__ __forceinline__ float dot16(const uint4 q, const float4 a, const floa
   s = fmaf(ubyte<2>(q.w), d.z, s);
   s = fmaf(ubyte<3>(q.w), d.w, s);
   return s;
+}
+
+// Eight u8 codes (two dwords, byte order) as an MFMA BF16 fragment: integers
+// 0..255 are exact in BF16 (v_cvt_f32_ubyteN + v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 codes8_bf16(uint32_t a, uint32_t b) {
+  const floatx8 f = {ubyte<0>(a), ubyte<1>(a), ubyte<2>(a), ubyte<3>(a),
+                     ubyte<0>(b), ubyte<1>(b), ubyte<2>(b), ubyte<3>(b)};
+  return __builtin_convertvector(f, bf16x8);
 }
 
 // LDS layout of an activation vector for the wave-per-1KiB-chunk GEMVs:
