@@ -1,4 +1,4 @@
-// affine_gemv.hip -- affine-INT8 g64 dequant GEMV for gfx950, M <= 16 rows.
+// affine_gemv.hip -- affine-INT8 g64 dequant GEMV for gfx950, M <= 16 token rows.
 //
 // Computes y[t, r] = sum_c (q[r,c] * s[r,c/64] + b[r,c/64]) * x[t,c]
 // (turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- embed_row_bytes for the
@@ -8,11 +8,11 @@
 // Codes are exact in fp32 and in BF16, accumulation is fp32, the output is
 // rounded once to BF16 (nearest even).
 //
-// Two kernels: batch 1 streams rows through the VALU (one wave per row
-// range, lane l holding bytes [16l, 16l+16) of each 1 KiB chunk, x in LDS as
-// fp32); batches of 2..16 tokens use the matrix cores, where one MFMA pair
-// per group covers all 16 token rows and the VALU only converts codes and
-// applies the group's scale and bias.
+// Two kernels: the matrix-core kernel serves every batch size (one MFMA pair
+// per group covers all 16 token rows; the VALU only converts codes and
+// applies the group's scale and bias); batch 1 on very large matrices
+// streams rows through the VALU instead (one wave per row range, lane l
+// holding bytes [16l, 16l+16) of each 1 KiB chunk, x in LDS as fp32).
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -87,15 +87,22 @@ __device__ __forceinline__ void mc_next(MCursor &c, const MShape &S, int &left) 
 // Addresses are a wave-uniform base (the tile's first row, the group) plus a
 // 32-bit per-lane offset, so the loads take the scalar-base form.  Rows past
 // the end of the matrix are clamped to its last row.
-template <int R, int U, bool CH>
+template <int R, int U, bool CH, bool XL>
 __device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const MShape &S,
-                                         const QD_GLOBAL uint16_t *x, uint32_t xoff, int lane,
+                                         const QD_GLOBAL uint16_t *x, uint32_t xoff,
+                                         const uint8_t *xl, uint32_t xloff, int lane,
                                          int &left) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const QD_GLOBAL uint8_t *xg = (const QD_GLOBAL uint8_t *)(x + 64 * c.g);
-    G.xa[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff));
-    G.xb[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
+    if constexpr (XL) {
+      const uint8_t *xp = xl + xloff + 128 * c.g;
+      G.xa[u] = *(const bf16x8 *)(xp);
+      G.xb[u] = *(const bf16x8 *)(xp + 16);
+    } else {
+      const QD_GLOBAL uint8_t *xg = (const QD_GLOBAL uint8_t *)(x + 64 * c.g);
+      G.xa[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff));
+      G.xb[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
+    }
     const int trow = (S.ts0 + c.j * S.stride) * 16 * R;
     const int lim = S.rows - 1 - trow;  // last valid row offset inside the tile
     const QD_GLOBAL uint8_t *cb = S.w + (size_t)trow * S.cols + 64 * c.g;
@@ -193,12 +200,40 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&
   }
 }
 
-template <int R, int U, int KS, bool CH>
+// x [m][cols] BF16 into LDS, rows padded to 2*cols + 16 bytes (the 16
+// token rows of a fragment read then start in different banks).
+__device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x, int m,
+                                        int cols) {
+  const int per_row = cols >> 3;  // 16-byte chunks per row
+  const int chunks = m * per_row;
+  const uint32_t stride = 2u * cols + 16u;
+  for (int base = 0; base < chunks; base += 8 * kMThreads) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = min(base + k * kMThreads + (int)threadIdx.x, chunks - 1);
+      const int row = i / per_row;
+      v[k] = *(const QD_GLOBAL u32x4 *)(x + (size_t)row * cols + 8 * (i - row * per_row));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = base + k * kMThreads + (int)threadIdx.x;
+      if (i < chunks) {
+        const int row = i / per_row;
+        *(u32x4 *)(xl + row * stride + 16 * (i - row * per_row)) = v[k];
+      }
+    }
+  }
+}
+
+template <int R, int U, int KS, bool CH, bool XL>
 __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     const uint8_t *__restrict__ w_, int rows, int cols, const uint16_t *__restrict__ x_,
     uint16_t *__restrict__ y_, int m) {
   constexpr int SLOTS = kMW / KS;
   __shared__ float red[KS > 1 ? kMW * R * kWave * 4 : 1];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xsh[];  // x (XL)
+  uint8_t *xl = xsh;
   QD_GLOBAL uint16_t *y = gp(y_);
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
@@ -224,34 +259,41 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   const int t = (lane & 15) < m ? (lane & 15) : m - 1;
   const QD_GLOBAL uint16_t *x = gp(x_);
   const uint32_t xoff = 2u * ((uint32_t)t * (uint32_t)cols + 16u * (lane >> 4));  // bytes
+  const uint32_t xloff = (uint32_t)t * (2u * cols + 16u) + 32u * (lane >> 4);
 
   floatx4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = __builtin_bit_cast(
+      bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  MCursor ci, cc;  // issue and compute cursors
+  ci.j = cc.j = 0;
+  ci.g = cc.g = S.ga;
+  int li = n, lc = n;
+  MGroup<R, U, CH> A, B;
+  // the first buffer's codes and scales are in flight while x is staged
+  if (n > 0) mg_issue<R, U, CH, false>(A, ci, S, x, xoff, xl, xloff, lane, li);
+  if constexpr (XL) {
+    stage_x(xl, x, m, cols);
+    // LDS writes done, then the barrier (global loads stay in flight)
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   if (n > 0) {
-    const bf16x8 ones = __builtin_bit_cast(
-        bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-    MCursor ci, cc;  // issue and compute cursors
-    ci.j = cc.j = 0;
-    ci.g = cc.g = S.ga;
-    int li = n, lc = n;
     // Loads are never conditional (the compiler then waits for exactly the
     // buffer it consumes); the branches only choose whether another buffer
     // is issued before the current one is consumed.
-    MGroup<R, U, CH> A, B;
-    mg_issue(A, ci, S, x, xoff, lane, li);
     for (;;) {
       if (lc <= U) {
         mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, lc, m, y, lane, ones);
         break;
       }
-      mg_issue(B, ci, S, x, xoff, lane, li);
+      mg_issue<R, U, CH, XL>(B, ci, S, x, xoff, xl, xloff, lane, li);
       mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, lc, m, y, lane, ones);
       if (lc <= U) {
         mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, lc, m, y, lane, ones);
         break;
       }
-      mg_issue(A, ci, S, x, xoff, lane, li);
+      mg_issue<R, U, CH, XL>(A, ci, S, x, xoff, xl, xloff, lane, li);
       mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, lc, m, y, lane, ones);
     }
   }
@@ -282,21 +324,46 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
 #define QD_AFFINE_STREAM_WGS 2
 #endif
 
-template <int KS, bool CH>
+// x goes to LDS when its padded copy fits this budget (two workgroups per
+// CU then still fit the 160 KiB of LDS).
+constexpr int kXlBudget = 72 * 1024;
+
+template <int KS, bool CH, bool XL>
 hipError_t launch_mfma_ks(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
                           int m, int grid, hipStream_t stream) {
   constexpr int R = QD_AFFINE_MFMA_R;
   constexpr int U = CH ? 4 : 2;
-  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH>), dim3(grid), dim3(kMThreads), 0,
-                     stream, w, rows, cols, x, y, m);
+  const size_t lds = XL ? (size_t)m * (2 * cols + 16) : 0;
+  if (lds > 48 * 1024) {  // above the default dynamic-LDS limit: raise it once
+    static bool raised = false;
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute(
+          (const void *)affine_gemv_mfma_kernel<R, U, KS, CH, XL>,
+          hipFuncAttributeMaxDynamicSharedMemorySize, kXlBudget);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL>), dim3(grid), dim3(kMThreads),
+                     lds, stream, w, rows, cols, x, y, m);
   return hipGetLastError();
+}
+
+// Only the streaming walk (KS = 1) stages x: there a workgroup reuses it over
+// many tiles, while a split workgroup reads each element of x once anyway.
+template <int KS, bool CH>
+hipError_t launch_mfma_xl(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
+                          int m, int grid, hipStream_t stream) {
+  if (KS == 1 && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
+    return launch_mfma_ks<KS, CH, true>(w, rows, cols, x, y, m, grid, stream);
+  return launch_mfma_ks<KS, CH, false>(w, rows, cols, x, y, m, grid, stream);
 }
 
 template <bool CH>
 hipError_t launch_mfma_ch(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
                           int m, hipStream_t stream) {
   // KS: split K over up to 8 waves until the matrix gives about
-  // kTargetWaves waves (each wave keeping at least two buffers of groups);
+  // kTargetWaves waves (each wave keeping at least one buffer of groups);
   // KS = 1 walks tiles grid-stride with kStreamWgsPerCu workgroups per CU.
   constexpr int kTargetWaves = QD_AFFINE_TARGET_WAVES;
   constexpr int kStreamWgsPerCu = QD_AFFINE_STREAM_WGS;
@@ -310,13 +377,13 @@ hipError_t launch_mfma_ch(const uint8_t *w, int rows, int cols, const uint16_t *
     if (cus < 1) cus = 256;
     long grid = (ntiles + kMW - 1) / kMW;
     if (grid > (long)kStreamWgsPerCu * cus) grid = (long)kStreamWgsPerCu * cus;
-    return launch_mfma_ks<1, CH>(w, rows, cols, x, y, m, (int)grid, stream);
+    return launch_mfma_xl<1, CH>(w, rows, cols, x, y, m, (int)grid, stream);
   }
   const int grid = (int)((ntiles * ks + kMW - 1) / kMW);
   switch (ks) {
-    case 2: return launch_mfma_ks<2, CH>(w, rows, cols, x, y, m, grid, stream);
-    case 4: return launch_mfma_ks<4, CH>(w, rows, cols, x, y, m, grid, stream);
-    default: return launch_mfma_ks<8, CH>(w, rows, cols, x, y, m, grid, stream);
+    case 2: return launch_mfma_xl<2, CH>(w, rows, cols, x, y, m, grid, stream);
+    case 4: return launch_mfma_xl<4, CH>(w, rows, cols, x, y, m, grid, stream);
+    default: return launch_mfma_xl<8, CH>(w, rows, cols, x, y, m, grid, stream);
   }
 }
 
@@ -441,7 +508,10 @@ __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
 hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
                               const uint16_t *x, uint16_t *y, int m,
                               hipStream_t stream) {
-  if (m == 1) {
+  // Batch 1 takes the VALU streaming kernel only for very large matrices
+  // (LM heads), where its 1 KiB-per-row loads keep the most bytes in flight;
+  // below that the matrix-core kernel's K split gives more waves per matrix.
+  if (m == 1 && (int64_t)rows * cols >= ((int64_t)1 << 28)) {
     // waves: about two register groups of items each, at most 4 workgroups
     // of 8 waves per CU
     int cus = device_cus();

@@ -68,6 +68,27 @@ def test_lm_head_full_size_sampled():
     check_bf16_output(y[:, sel], ref, "lm head")
 
 
+# Large matrices on sampled rows, one per kernel path: the batch-1 VALU
+# streaming kernel (151936 x 2048), the matrix-core streaming walk with x in
+# LDS (LM head at M=16), without chunked scales (cols % 256 != 0), and with x
+# too large for LDS (M=16, 4608 columns).
+BIG = [(151936, 2048, 1), (151936, 1024, 16), (65536, 320, 4), (65600, 4608, 16)]
+
+
+@pytest.mark.parametrize("rows,cols,m", BIG)
+def test_large_sampled(rows, cols, m):
+    print(f"affine gemv sampled rows={rows} cols={cols} m={m}", flush=True)
+    tr = synth.affine_triplet(rows, cols, key=(6, rows, cols))
+    blob = pack_on_device(tr)
+    x = synth.x_bf16(m, cols, key=(6, rows, cols + m))
+    y = host_bf16_f64(_run_gemv(tr, blob, x, m))
+    sel = np.unique(np.concatenate([np.random.default_rng(1).integers(0, rows, 1024),
+                                    np.arange(16), np.arange(rows - 40, rows)]))
+    ref = oracle.affine_gemv(blob.cpu().numpy(), rows, cols, x, row_sel=sel)
+    check_bf16_output(y[:, sel], ref, f"{rows}x{cols} m={m} sampled")
+    del blob
+
+
 def test_closed_forms_on_device():
     # zero scales: y = sum_g bias_g * X_g; constant codes q0: y = sum_g
     # (s_g q0 + b_g) X_g -- compared with the oracle, which is pinned to
