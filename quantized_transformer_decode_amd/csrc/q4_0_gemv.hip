@@ -1,141 +1,316 @@
-// q4_0_gemv.hip -- ggml Q4_0 dequant GEMV for gfx950, M <= 16 rows, f32.
+// q4_0_gemv.hip -- ggml Q4_0 dequant GEMV for gfx950, M <= 16 token rows, f32.
 //
 // y[t, n] = sum_b d[n,b] * (sum_j q[n,b,j] * x[t,32b+j] - 8 * X[t,b])
 // with X[t,b] the sum of x over block b: the "-8" of w = d*(q-8)
 // (fuel-transformers 0.19.1, lazy_quantized_whisper.rs -- module
 // documentation / quantize_in_out_to_q4_0 for the block format, q_linear for
-// the matmul) is folded into one multiply-add per block.
+// the matmul) is folded into one multiply-add per block.  fp32 throughout.
 //
-// Layout on the chip: eight lanes share an output row and walk its blocks
-// b = sub, sub+8, ...; eight lanes therefore read 8 consecutive 18-byte
-// blocks (144 contiguous bytes) per load.  A block's 16 nibble bytes start
-// at byte 18*flat+2, which is 4-byte aligned for odd flat block indices and
-// 2 bytes off for even ones; the lane reads the enclosing dwords and
-// realigns them with v_alignbyte_b32.  Each lane handles R rows at once so
-// the 32 x values it reads from LDS serve R blocks.
+// Layout on the chip: a wave covers 8R weight rows; the 8 lanes of a row take
+// the blocks b = 8s + lane%8 of step s, so a load instruction reads 8 rows x
+// 144 contiguous bytes, and each lane holds R rows whose blocks share its
+// reads of x.  A block sits at byte 18*flat (flat = n*bpr + b);
+// each lane reads the 4-byte-aligned 20-byte window holding it (starting 2
+// bytes early for odd flat -- an even block is never the stream's last, the
+// block count per row being a multiple of 8) and realigns the nibbles with
+// v_alignbyte_b32.  Loads are unconditional (clamped rows), double-buffered
+// in register groups of U steps.  x and the block sums X sit in LDS (fp32);
+// up to MT tokens share one pass over the weights.  Small matrices split the
+// steps of a row over KS waves of a workgroup (partial sums through LDS).
 #include "qd_device.h"
 #include "qd_internal.h"
 
 namespace qd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kLdsBudget = 64 * 1024;
+constexpr int kQW = 8;                 // waves per workgroup
+constexpr int kQThreads = kQW * kWave;
+constexpr int kQU = 2;                 // steps per register group
+constexpr int kQLdsBudget = 64 * 1024;
 
-__device__ __forceinline__ float nib_dot8(uint32_t v, const float *xp) {
-  // v holds elements j..j+3 (low nibbles) and j+16..j+19 (high nibbles)
-  const uint32_t lo = v & 0x0f0f0f0fu;
-  const uint32_t hi = (v >> 4) & 0x0f0f0f0fu;
-  float s = ubyte<0>(lo) * xp[0];
-  s = fmaf(ubyte<1>(lo), xp[1], s);
-  s = fmaf(ubyte<2>(lo), xp[2], s);
-  s = fmaf(ubyte<3>(lo), xp[3], s);
-  s = fmaf(ubyte<0>(hi), xp[16], s);
-  s = fmaf(ubyte<1>(hi), xp[17], s);
-  s = fmaf(ubyte<2>(hi), xp[18], s);
-  s = fmaf(ubyte<3>(hi), xp[19], s);
-  return s;
+template <int R>
+struct QGroup {
+  uint32_t w[kQU][R][5];  // the block windows
+  uint32_t odd[kQU][R];   // flat index parities
+};
+
+struct QShape {
+  const QD_GLOBAL uint8_t *w;
+  int rows, bpr;
+  int rg0, stride;      // the wave's first row group and the stride
+  int sa, sb;           // the wave's step range
+};
+
+struct QCursor {
+  int j, s;             // j-th row group of the wave, step s
+};
+
+__device__ __forceinline__ void qc_next(QCursor &c, const QShape &S, int &left) {
+  const int adv = left > 1;
+  left = adv ? left - 1 : 0;
+  const int s = c.s + adv;
+  const int wrap = s == S.sb;
+  c.s = wrap ? S.sa : s;
+  c.j += wrap;
 }
 
-template <int MT, int R>
-__global__ __launch_bounds__(kThreads) void q4_0_gemv_kernel(
-    const uint8_t *__restrict__ w, int rows, int cols,
-    const float *__restrict__ x, float *__restrict__ y, int t0, int m) {
-  extern __shared__ float lds[];
-  const int bpr = cols >> 5;
-  float *xs = lds;                // [MT][cols]
-  float *xsum = lds + MT * cols;  // [MT][cols/32]
-  for (int i = threadIdx.x; i < MT * cols; i += kThreads) {
-    const int t = i / cols;
-    const int c = i - t * cols;
-    xs[i] = (t0 + t < m) ? x[(size_t)(t0 + t) * cols + c] : 0.f;
+// Row r of a lane's R rows in row group g: 8R*g + 8r + lane/8.
+template <int R>
+__device__ __forceinline__ void qg_issue(QGroup<R> &G, QCursor &c, const QShape &S, int lane,
+                                         int &left) {
+#pragma unroll
+  for (int u = 0; u < kQU; ++u) {
+    const int base = (S.rg0 + c.j * S.stride) * 8 * R + (lane >> 3);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = min(base + 8 * r, S.rows - 1);
+      const size_t flat = (size_t)n * S.bpr + 8 * c.s + (lane & 7);
+      const uint32_t odd = (uint32_t)(flat & 1);
+      const QD_GLOBAL uint32_t *p =
+          (const QD_GLOBAL uint32_t *)(S.w + 18 * flat - 2 * odd);
+      const u32x4 v = __builtin_nontemporal_load((const QD_GLOBAL u32x4 *)p);
+      G.w[u][r][0] = v.x;
+      G.w[u][r][1] = v.y;
+      G.w[u][r][2] = v.z;
+      G.w[u][r][3] = v.w;
+      G.w[u][r][4] = __builtin_nontemporal_load(p + 4);
+      G.odd[u][r] = odd;
+    }
+    qc_next(c, S, left);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < MT * bpr; i += kThreads) {
-    const float *p = xs + (size_t)i * 32;
-    float s = 0.f;
+}
+
+// sum_j q_j x_j over a block for one token and R rows (x read once): nibble
+// dword k holds elements 4k..4k+3 (low nibbles) and 16+4k..16+4k+3 (high).
+template <int R>
+__device__ __forceinline__ void block_dot(const uint32_t (&nib)[R][4], const float *xb,
+                                          float (&s)[R]) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) s += p[k];
-    xsum[i] = s;
+  for (int r = 0; r < R; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 a = *(const float4 *)(xb + 4 * k);
+    const float4 b = *(const float4 *)(xb + 16 + 4 * k);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t lo = nib[r][k] & 0x0f0f0f0fu, hi = (nib[r][k] >> 4) & 0x0f0f0f0fu;
+      s[r] = fmaf(ubyte<0>(lo), a.x, s[r]);
+      s[r] = fmaf(ubyte<1>(lo), a.y, s[r]);
+      s[r] = fmaf(ubyte<2>(lo), a.z, s[r]);
+      s[r] = fmaf(ubyte<3>(lo), a.w, s[r]);
+      s[r] = fmaf(ubyte<0>(hi), b.x, s[r]);
+      s[r] = fmaf(ubyte<1>(hi), b.y, s[r]);
+      s[r] = fmaf(ubyte<2>(hi), b.z, s[r]);
+      s[r] = fmaf(ubyte<3>(hi), b.w, s[r]);
+    }
   }
-  __syncthreads();
+}
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int sg = lane >> 3;
-  const int sub = lane & 7;
-  const int rows_per_wave = 8 * R;
-
-  for (int row0 = (blockIdx.x * kWaves + wave) * rows_per_wave; row0 < rows;
-       row0 += gridDim.x * kWaves * rows_per_wave) {
-    float acc[R][MT];
+// Items past the end of the walk are computed with d = 0.
+template <int MT, int R, bool STORE>
+__device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][R], QCursor &c,
+                                           const QShape &S, int &left, int lane, const float *xs,
+                                           const float *xsum, int cols, int t0, int m,
+                                           QD_GLOBAL float *y) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int u = 0; u < kQU; ++u) {
+    const int valid = left > 0;  // wave-uniform
+    uint32_t nib[R][4];
+    float d[R];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[r][t] = 0.f;
-
-    for (int b = sub; b < bpr; b += 8) {
-      uint32_t nib[R][4];
-      float d[R];
+    for (int r = 0; r < R; ++r) {
+      const bool odd = G.odd[u][r];
+      const uint32_t dbits = odd ? (G.w[u][r][0] >> 16) : (G.w[u][r][0] & 0xffffu);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = row0 + sg * R + r;
-        if (n < rows) {
-          const size_t flat = (size_t)n * bpr + b;
-          const size_t nb = 18 * flat + 2;
-          const uint32_t *p = (const uint32_t *)(w + (nb & ~(size_t)3));
-          const uint32_t sh = (uint32_t)(nb & 3);  // 0 or 2
-          const uint32_t v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
-          // Only the 2-byte-offset case needs the fifth dword; it lies inside
-          // the stream (the next block, or the pad of an odd block count).
-          const uint32_t v4 = sh ? p[4] : 0u;
-          nib[r][0] = __builtin_amdgcn_alignbyte(v1, v0, sh);
-          nib[r][1] = __builtin_amdgcn_alignbyte(v2, v1, sh);
-          nib[r][2] = __builtin_amdgcn_alignbyte(v3, v2, sh);
-          nib[r][3] = __builtin_amdgcn_alignbyte(v4, v3, sh);
-          d[r] = f16_to_f32(*(const uint16_t *)(w + 18 * flat));
-        } else {
-          nib[r][0] = nib[r][1] = nib[r][2] = nib[r][3] = 0x88888888u;
-          d[r] = 0.f;
-        }
-      }
+      for (int k = 0; k < 4; ++k)
+        nib[r][k] = odd ? G.w[u][r][k + 1]
+                        : __builtin_amdgcn_alignbyte(G.w[u][r][k + 1], G.w[u][r][k], 2);
+      d[r] = valid ? f16_to_f32(dbits) : 0.f;
+    }
+    const int b = 8 * c.s + (lane & 7);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float *xp = xs + t * cols + 32 * b;
-        const float xb = xsum[t * bpr + b];
+    for (int t = 0; t < MT; ++t) {
+      float dot[R];
+      block_dot<R>(nib, xs + t * cols + 32 * b, dot);
+      const float corr = -8.f * xsum[t * S.bpr + b];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[t][r] = fmaf(d[r], dot[r] + corr, acc[t][r]);
+    }
+    if (STORE && valid && c.s == S.sb - 1) {
+      const int base = (S.rg0 + c.j * S.stride) * 8 * R + (lane >> 3);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          float s = nib_dot8(nib[r][0], xp);
-          s += nib_dot8(nib[r][1], xp + 4);
-          s += nib_dot8(nib[r][2], xp + 8);
-          s += nib_dot8(nib[r][3], xp + 12);
-          acc[r][t] = fmaf(d[r], fmaf(-8.f, xb, s), acc[r][t]);
+          const float v = group_sum<8>(acc[t][r]);
+          const int n = base + 8 * r;
+          if ((lane & 7) == 0 && n < S.rows && t0 + t < m)
+            y[(size_t)(t0 + t) * S.rows + n] = v;
+          acc[t][r] = 0.f;
         }
-      }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float v = group_sum<8>(acc[r][t]);
-        const int n = row0 + sg * R + r;
-        if (sub == 0 && n < rows && t0 + t < m)
-          y[(size_t)(t0 + t) * rows + n] = v;
-      }
+    left -= valid;
+    const int s = c.s + valid;
+    const int wrap = s == S.sb;
+    c.s = wrap ? S.sa : s;
+    c.j += wrap;
   }
 }
 
-template <int MT, int R>
-hipError_t launch_pass(const uint8_t *w, int rows, int cols, const float *x,
-                       float *y, int t0, int m, hipStream_t stream) {
+template <int MT, int R, int KS>
+__global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
+    const uint8_t *__restrict__ w_, int rows, int cols, const float *__restrict__ x_,
+    float *__restrict__ y_, int t0, int m) {
+  constexpr int SLOTS = kQW / KS;
+  __shared__ float red[KS > 1 ? kQW * MT * R * 8 : 1];
+  extern __shared__ __attribute__((aligned(16))) float qsh[];
+  float *xs = qsh;                    // [MT][cols]
+  const int bpr = cols >> 5;
+  float *xsum = qsh + MT * cols;      // [MT][bpr]
+  const QD_GLOBAL float *x = gp(x_);
+  QD_GLOBAL float *y = gp(y_);
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(threadIdx.x >> 6);
+  const int slot = wave / KS, split = wave % KS;
+  const int steps = bpr >> 3;
+  QShape S;
+  S.w = gp(w_);
+  S.rows = rows;
+  S.bpr = bpr;
+  S.sa = uni(steps * split / KS);
+  S.sb = uni(steps * (split + 1) / KS);
+  S.rg0 = blockIdx.x * SLOTS + slot;
+  S.stride = gridDim.x * SLOTS;
+  const int ngroups = (rows + 8 * R - 1) / (8 * R);
+  int mine = 0;
+  if (S.rg0 < ngroups) mine = KS == 1 ? (ngroups - 1 - S.rg0) / S.stride + 1 : 1;
+  const int n = uni(mine * (S.sb - S.sa));
+
+  QCursor ci, cc;
+  ci.j = cc.j = 0;
+  ci.s = cc.s = S.sa;
+  int li = n, lc = n;
+  QGroup<R> A, B;
+  // x staging: thread i copies block i of x (8 x 16 bytes) and its sum;
+  // MT * bpr <= 512 by the LDS budget.  The first register group of weights
+  // is issued between the x loads and their use, so both are in flight.
+  const int nblk = MT * bpr;
+  const int bi = min((int)threadIdx.x, nblk - 1);
+  const int bt = bi / bpr, bb = bi - bt * bpr;
+  const QD_GLOBAL floatx4 *xp =
+      (const QD_GLOBAL floatx4 *)(x + (size_t)min(t0 + bt, m - 1) * cols + 32 * bb);
+  floatx4 xv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) xv[k] = xp[k];
+  if (n > 0) qg_issue<R>(A, ci, S, lane, li);
+  if ((int)threadIdx.x < nblk) {
+    const bool live = t0 + bt < m;
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const floatx4 v = live ? xv[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+      sum += (v[0] + v[1]) + (v[2] + v[3]);
+      *(floatx4 *)(xs + 32 * bi + 4 * k) = v;
+    }
+    xsum[bi] = sum;
+  }
+  // LDS writes done, then the barrier (the weight loads stay in flight)
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  float acc[MT][R];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[t][r] = 0.f;
+  if (n > 0) {
+    // Loads are never conditional; the branches only choose whether another
+    // register group is issued before the current one is consumed.
+    for (;;) {
+      if (lc <= kQU) {
+        qg_compute<MT, R, KS == 1>(A, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+        break;
+      }
+      qg_issue<R>(B, ci, S, lane, li);
+      qg_compute<MT, R, KS == 1>(A, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+      if (lc <= kQU) {
+        qg_compute<MT, R, KS == 1>(B, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+        break;
+      }
+      qg_issue<R>(A, ci, S, lane, li);
+      qg_compute<MT, R, KS == 1>(B, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+    }
+  }
+  if constexpr (KS > 1) {
+    // red[wave][t][row of the group]: the 8-lane sums, written by lane%8 == 0
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = group_sum<8>(acc[t][r]);
+        if ((lane & 7) == 0) red[(wave * MT + t) * 8 * R + 8 * r + (lane >> 3)] = v;
+      }
+    __syncthreads();
+    // one thread per (slot, token, row of the group)
+    for (int i = threadIdx.x; i < SLOTS * MT * 8 * R; i += kQThreads) {
+      const int sl = i / (MT * 8 * R), rem = i - sl * (MT * 8 * R);
+      const int t = rem / (8 * R), rr = rem - t * (8 * R);
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) sum += red[((sl * KS + k) * MT + t) * 8 * R + rr];
+      const int nn = (blockIdx.x * SLOTS + sl) * 8 * R + rr;
+      if (nn < rows && t0 + t < m) y[(size_t)(t0 + t) * rows + nn] = sum;
+    }
+  }
+}
+
+template <int MT, int R, int KS>
+hipError_t launch_q_ks(const uint8_t *w, int rows, int cols, const float *x, float *y, int t0,
+                       int m, int grid, hipStream_t stream) {
   const size_t lds = (size_t)MT * cols * 4 + (size_t)MT * (cols / 32) * 4;
-  const int per_block = kWaves * 8 * R;
-  int grid = (rows + per_block - 1) / per_block;
-  if (grid > 2048) grid = 2048;
-  hipLaunchKernelGGL((q4_0_gemv_kernel<MT, R>), dim3(grid), dim3(kThreads),
-                     lds, stream, w, rows, cols, x, y, t0, m);
+  if (lds > 48 * 1024) {  // above the default dynamic-LDS limit: raise it once
+    static bool raised = false;
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemv_kernel<MT, R, KS>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         kQLdsBudget + 4096);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL((q4_0_gemv_kernel<MT, R, KS>), dim3(grid), dim3(kQThreads), lds, stream,
+                     w, rows, cols, x, y, t0, m);
   return hipGetLastError();
+}
+
+// KS: split a row's steps over up to 8 waves until the matrix gives about
+// kQTargetWaves waves (each wave keeping at least one register group);
+// KS = 1 walks row groups grid-stride with kQStreamWgsPerCu workgroups per CU.
+constexpr int kQTargetWaves = 4096;
+constexpr int kQStreamWgsPerCu = 2;
+
+// R rows per lane share each read of x: one for a single token (the loads
+// then dominate), more as tokens multiply the x reads.
+template <int MT>
+hipError_t launch_q_mt(const uint8_t *w, int rows, int cols, const float *x, float *y, int t0,
+                       int m, hipStream_t stream) {
+  constexpr int R = 1;
+  const int steps = cols / 256;
+  const long ngroups = (rows + 8 * R - 1) / (8 * R);
+  int ks = 1;
+  while (ks < 8 && ngroups * ks < kQTargetWaves && steps / (2 * ks) >= kQU) ks *= 2;
+  if (ks == 1) {
+    int cus = device_cus();
+    if (cus < 1) cus = 256;
+    long grid = (ngroups + kQW - 1) / kQW;
+    if (grid > (long)kQStreamWgsPerCu * cus) grid = (long)kQStreamWgsPerCu * cus;
+    return launch_q_ks<MT, R, 1>(w, rows, cols, x, y, t0, m, (int)grid, stream);
+  }
+  const int grid = (int)((ngroups * ks + kQW - 1) / kQW);
+  switch (ks) {
+    case 2: return launch_q_ks<MT, R, 2>(w, rows, cols, x, y, t0, m, grid, stream);
+    case 4: return launch_q_ks<MT, R, 4>(w, rows, cols, x, y, t0, m, grid, stream);
+    default: return launch_q_ks<MT, R, 8>(w, rows, cols, x, y, t0, m, grid, stream);
+  }
 }
 
 }  // namespace
@@ -143,17 +318,19 @@ hipError_t launch_pass(const uint8_t *w, int rows, int cols, const float *x,
 hipError_t launch_q4_0_gemv(const uint8_t *w, int rows, int cols,
                             const float *x, float *y, int m,
                             hipStream_t stream) {
-  const int cap = kLdsBudget / (cols * 4 + cols / 8);
+  // tokens per pass limited by the LDS copy of x (fp32 plus block sums) and
+  // by one x block per thread for the staging
+  int cap = kQLdsBudget / (cols * 4 + cols / 8);
+  if (cap * (cols / 32) > kQThreads) cap = kQThreads / (cols / 32);
   int t0 = 0;
   while (t0 < m) {
     const int left = m - t0;
     const int lim = left < cap ? left : cap;
     hipError_t e;
     int mt;
-    if (lim >= 8) { mt = 8; e = launch_pass<8, 1>(w, rows, cols, x, y, t0, m, stream); }
-    else if (lim >= 4) { mt = 4; e = launch_pass<4, 1>(w, rows, cols, x, y, t0, m, stream); }
-    else if (lim >= 2) { mt = 2; e = launch_pass<2, 2>(w, rows, cols, x, y, t0, m, stream); }
-    else { mt = 1; e = launch_pass<1, 2>(w, rows, cols, x, y, t0, m, stream); }
+    if (lim >= 4) { mt = 4; e = launch_q_mt<4>(w, rows, cols, x, y, t0, m, stream); }
+    else if (lim >= 2) { mt = 2; e = launch_q_mt<2>(w, rows, cols, x, y, t0, m, stream); }
+    else { mt = 1; e = launch_q_mt<1>(w, rows, cols, x, y, t0, m, stream); }
     if (e != hipSuccess) return e;
     t0 += mt;
   }
