@@ -15,6 +15,8 @@ stream), the CPU oracle timed on the host (it also re-checks the outputs of
 the timed buffers), and under "rows" a measurement of every other part of
 the path on its own workload:
   affine_gemv_1024       single 1024x1024 affine GEMV, batch 1
+  affine_lm_head         the tied LM heads (151936 x 1024 / x 2048) at M = 1, 4, 16:
+                         single large GEMVs, weights streamed past the 256 MB MALL
   q4_0_ffn_pair          Whisper-base FFN pair (fc1 2048x512, fc2 512x2048), M = 1, 4
   qwen3_1_7b_step        Qwen3-1.7B-shaped decode step at M = 1, 4, 10, 16
   whisper_large_prefill  one Whisper-large layer's six projections at 1500 frames
@@ -49,6 +51,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rows", default="all",
                    help="comma-separated extra rows to measure, 'all' or 'none'")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="first run one device-to-device copy of this many MiB (the "
+                        "reference dispatch for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
     p.add_argument("--variant", default="step", choices=["step", "graph"],
                    help="step: the whole step as one persistent launch (default); "
                         "graph: 197 GEMV launches captured in a HIP graph")
@@ -203,6 +208,33 @@ def row_affine_gemv_1024(qd):
             "note": "back-to-back launches in one HIP graph; cold rotates 482 copies (537 MB)"}
 
 
+def row_affine_lm_head(qd):
+    """The tied LM heads of the two decoders as single GEMVs at M = 1, 4, 16:
+    151936 x 1024 (165 MB) and 151936 x 2048 (330 MB); two copies of each are
+    alternated so every launch streams its weights from HBM (the pair exceeds
+    the 256 MB MALL)."""
+    import torch
+    import synth
+    out = {}
+    for cols in (1024, 2048):
+        rows = 151936
+        nbytes = qd.affine_i8_g64_bytes(rows, cols)
+        blobs = [affine_blob(qd, rows, cols, (3, 28, 7 + k)) for k in range(2)]
+        res = {"weight_bytes": nbytes}
+        for m in (1, 4, 16):
+            x = bf16dev(synth.x_bf16(m, cols, key=(3, 29, m)))
+            y = torch.empty((m, rows), dtype=torch.bfloat16, device=DEV)
+            g = capture(lambda: [qd.qgemv_affine_i8_g64(blobs[i % 2], rows, cols, x, y, m)
+                                 for i in range(8)])
+            ms = event_time(g.replay, 5, 2) / 8
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            res[f"M{m}"] = {"us": ms * 1e3, "GBps": gbps, "hbm_peak_frac": gbps / HBM_PEAK_GBPS}
+        out[f"{rows}x{cols}"] = res
+        del blobs
+        torch.cuda.empty_cache()
+    return out
+
+
 def q4_0_from_f32(qd, w_host, rows, cols):
     import torch
     wq = torch.empty(qd.q4_0_bytes(rows, cols), dtype=torch.uint8, device=DEV)
@@ -338,8 +370,45 @@ def row_q4_0_bake(qd):
             "hbm_peak_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
-ROWS = ("affine_gemv_1024", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
+ROWS = ("affine_gemv_1024", "affine_lm_head", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
         "whisper_large_decoder", "q4_0_bake")
+
+
+# HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) of this script scaled by the same counters of a
+# device-to-device copy of known size; the summary records the sha256 of the
+# kernel's sources at measurement time and is ignored once they change.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "affine_step_kernel_qwen3_0_6b_traffic.md")
+STEP_SOURCES = ("decode_step.hip", "qd_step.h", "qd_device.h")
+
+
+def step_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        with open(os.path.join(ROOT, "quantized_transformer_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """bytes per launch of affine_step_kernel, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != step_source_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def run_rows(qd, names):
@@ -372,6 +441,13 @@ def main():
 
     import synth
     torch.cuda.set_device(0)
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=DEV)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     step = DecodeStep(synth.QWEN3_0_6B)
     qd = step.qd
     step.run_eager()  # warm (also fills the library's per-device caches)
@@ -393,7 +469,7 @@ def main():
     else:
         ms, wall = ms_graph, None
         variant = "hipgraph: 197 GEMV launches in decoder order"
-        kernel, launches = "affine_gemv_m1_kernel", len(step.mats)
+        kernel, launches = "affine_gemv_mfma_kernel", len(step.mats)
     tok_s = 1000.0 / ms
     gbps = step.weight_bytes / (ms * 1e-3) / 1e9
     avg_launch_s = ms * 1e-3 / launches
@@ -425,7 +501,8 @@ def main():
         "wall_s_timed": wall,
         "roofline": {
             "kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": recorded_traffic() if kernel == "affine_step_kernel" else None,
             "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
         },
     }
