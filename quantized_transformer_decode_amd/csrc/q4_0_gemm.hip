@@ -48,12 +48,15 @@ struct Tile {
   static constexpr int WB = BN * NB / kThreads;   // weight blocks per thread (<= 1)
 };
 
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 
-// (q - 8) of 8 nibbles (the low or high nibbles of two dwords) as BF16:
-// small integers are exact in BF16.
-__device__ __forceinline__ uint32_t bf16x2_of(int a, int b) {
-  return (uint32_t)f32_to_bf16((float)a) | ((uint32_t)f32_to_bf16((float)b) << 16);
+// (q - 8) of four nibbles (one nibble per byte of `v`, bytes in element
+// order) as four BF16 in two dwords: small integers are exact in BF16.
+__device__ __forceinline__ u32x2v codes4_bf16(uint32_t v) {
+  const floatx4 f = {ubyte<0>(v) - 8.f, ubyte<1>(v) - 8.f, ubyte<2>(v) - 8.f,
+                     ubyte<3>(v) - 8.f};
+  return __builtin_bit_cast(u32x2v, __builtin_convertvector(f, bf16x4));
 }
 
 template <int BM, int BN>
@@ -74,11 +77,11 @@ __device__ __forceinline__ void stage_load(Stage<BM, BN> &st, const QD_GLOBAL ui
   for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
     const int c = tid + i * kThreads;  // 16-byte chunk of the 128 x 256-byte tile
     const int r = c >> 4, ch = c & 15;
-    int row = m0 + r;
-    const bool ok = row < m;
-    if (!ok) row = m - 1;
+    // frames past m read frame m-1: they only feed output rows that are
+    // never stored
+    const int row = min(m0 + r, m - 1);
     const u32x4 v = *(const QD_GLOBAL u32x4 *)(x + (size_t)row * cols + kb0 * 32 + ch * 8);
-    st.xa[i] = ok ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0, 0, 0, 0);
+    st.xa[i] = make_uint4(v.x, v.y, v.z, v.w);
   }
   st.has_w = tid < BN * NB;
   const int r = (tid >> 2) % BN, b = tid & 3;
@@ -117,11 +120,13 @@ __device__ __forceinline__ void stage_store(const Stage<BM, BN> &st, uint16_t *A
   uint32_t lo[8], hi[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
+    // dword k: elements 4k..4k+3 in the low nibbles, 16+4k.. in the high
     const uint32_t v = dead ? 0x88888888u : nib[k];
-    lo[2 * k] = bf16x2_of((int)(v & 15u) - 8, (int)((v >> 8) & 15u) - 8);
-    lo[2 * k + 1] = bf16x2_of((int)((v >> 16) & 15u) - 8, (int)((v >> 24) & 15u) - 8);
-    hi[2 * k] = bf16x2_of((int)((v >> 4) & 15u) - 8, (int)((v >> 12) & 15u) - 8);
-    hi[2 * k + 1] = bf16x2_of((int)((v >> 20) & 15u) - 8, (int)((v >> 28) & 15u) - 8);
+    const u32x2v cl = codes4_bf16(v & 0x0f0f0f0fu), ch = codes4_bf16((v >> 4) & 0x0f0f0f0fu);
+    lo[2 * k] = cl.x;
+    lo[2 * k + 1] = cl.y;
+    hi[2 * k] = ch.x;
+    hi[2 * k + 1] = ch.y;
   }
   uint4 *dst = (uint4 *)(Bs + r * LDA + b * 32);
   dst[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);  // elements 0..7
@@ -161,18 +166,13 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  Stage<BM, BN> st;
-  stage_load(st, x, w, m, rows, cols, m0, n0, 0, tid);
-  stage_store(st, As(0), Bs(0), Ds(0), tid);
-  __syncthreads();
-
   const int kq = (lane >> 4) * 8;  // this lane's 8 K indices within a block
   const int arow = wm * (BM / 2) + (lane & 15);
   const int bcol = wn * (BN / 2) + (lane & 15);
 
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nstages) stage_load(st, x, w, m, rows, cols, m0, n0, (s + 1) * NB, tid);
+  // One stage from LDS buffer `buf`: per block, TM x TN MFMAs of the exact
+  // codes, then the previous block's partial products scaled by its deltas.
+  auto compute = [&](int buf) {
     const uint16_t *A = As(buf);
     const uint16_t *Bm = Bs(buf);
     const float *D = Ds(buf);
@@ -207,6 +207,18 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < TM; ++i) acc[i][j] += dj * p[(NB - 1) & 1][i][j];
     }
+  };
+
+  // Double-buffered: the global loads of stage s+1 are in flight while stage
+  // s is computed from LDS, then go to the other LDS buffer.
+  Stage<BM, BN> st;
+  stage_load(st, x, w, m, rows, cols, m0, n0, 0, tid);
+  stage_store(st, As(0), Bs(0), Ds(0), tid);
+  __syncthreads();
+  for (int s = 0; s < nstages; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nstages) stage_load(st, x, w, m, rows, cols, m0, n0, (s + 1) * NB, tid);
+    compute(buf);
     if (s + 1 < nstages) stage_store(st, As(buf ^ 1), Bs(buf ^ 1), Ds(buf ^ 1), tid);
     __syncthreads();
   }
