@@ -146,6 +146,27 @@ class DecodeStep:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
         self.plan = qd.qgemv_affine_i8_g64_step_plan(self.ops, self.m, self.ws, nbytes)
 
+    def plan_sweep(self):
+        """Upper bound, not a decode step: the same GEMVs with the order
+        ignored -- ops grouped by input width into as few stages as the plan
+        allows (at most 16384 staged input words per stage)."""
+        import torch
+        qd = self.qd
+        order = sorted(range(len(self.mats)), key=lambda i: self.mats[i][3])
+        specs, stage, words, cols = [], -1, 0, None
+        for i in order:
+            _, _, rows, c, _ = self.mats[i]
+            w = self.m * ((c + 1023) // 1024) * 1024
+            if c != cols or words + w > 16384:
+                stage, words, cols = stage + 1, 0, c
+            words += w
+            specs.append((self.blobs[i], self.xs[i], self.ys[i], rows, c, stage))
+        ops = qd.make_ops(specs)
+        nbytes = qd.qgemv_affine_i8_g64_step_workspace_bytes(ops, self.m)
+        self.sweep_ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        self.sweep_plan = qd.qgemv_affine_i8_g64_step_plan(ops, self.m, self.sweep_ws, nbytes)
+        return stage + 1
+
     def run_step(self, stream=None):
         self.qd.qgemv_affine_i8_g64_step_run(self.plan, stream)
 
@@ -463,11 +484,16 @@ def main():
         ms = event_time(lambda: step.run_step(cur), args.steps, args.warmup, cur)
         wall = time.perf_counter() - t0
         assert qd.qgemv_affine_i8_g64_step_check(step.plan) == 0
+        n_sweep = step.plan_sweep()
+        ms_sweep = event_time(lambda: qd.qgemv_affine_i8_g64_step_run(step.sweep_plan, cur),
+                              max(10, args.steps // 4), max(2, args.warmup // 4), cur)
+        assert qd.qgemv_affine_i8_g64_step_check(step.sweep_plan) == 0
         variant = ("one persistent launch per step (one workgroup per CU); stage s+1 "
                    "reads its inputs only after every workgroup finished stage s")
         kernel, launches = "affine_step_kernel", 1
     else:
         ms, wall = ms_graph, None
+        ms_sweep, n_sweep = None, None
         variant = "hipgraph: 197 GEMV launches in decoder order"
         kernel, launches = "affine_gemv_mfma_kernel", len(step.mats)
     tok_s = 1000.0 / ms
@@ -498,6 +524,12 @@ def main():
         "weight_GBps": gbps,
         "hbm_peak_frac": gbps / HBM_PEAK_GBPS,
         "graph_of_197_launches_ms_per_step": ms_graph,
+        "independent_sweep": None if ms_sweep is None else {
+            "note": "upper bound, not a decode step: the same 197 GEMVs in one persistent "
+                    "launch with their order ignored (grouped by input width)",
+            "stages": n_sweep, "ms": ms_sweep,
+            "weight_GBps": step.weight_bytes / (ms_sweep * 1e-3) / 1e9,
+            "hbm_peak_frac": step.weight_bytes / (ms_sweep * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "wall_s_timed": wall,
         "roofline": {
             "kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,

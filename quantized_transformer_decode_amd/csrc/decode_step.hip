@@ -343,7 +343,6 @@ struct StagePlan {
   const uint64_t *src;  // this workgroup's replica of the staging, 64-bit words
   uint32_t *stg;        // staging, as words (publishing)
   int f0, f1;           // 64-bit words this workgroup polls: [f0, f1)
-  int sh;               // 64-bit words per slice = 2^sh
   int k0, k1;           // ops (within the stage) those words belong to
   int wpo;              // words per op
   int xstride;          // LDS floats per op (whole 1024-column chunks)
@@ -353,14 +352,14 @@ struct StagePlan {
 
 __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepStage &st, int m) {
   StagePlan p;
-  // slices (lines of 64 words) per replica
+  // replicas are spaced by one 64-word line per slice; within a replica the
+  // words are dense (word i at offset i)
   const int nsl = ((int)st.words + (1 << st.lg) - 1) >> st.lg;
   p.rstride = nsl * 64;
   // workgroups are dispatched round-robin over the XCDs: blockIdx % 8 reads
   // the replica that only the workgroups of its own XCD read
   p.src = (const uint64_t *)(st.stg + (blockIdx.x % kReplicas) * p.rstride);
   p.stg = st.stg;
-  p.sh = st.lg - 1;
   p.wpo = m * st.cols;
   p.xstride = st.chunks * 1024;
   int lo, hi, lo2, hi2;
@@ -397,7 +396,7 @@ __device__ bool poll_stage(const StagePlan &pp, uint32_t tag, float *dst, int la
         // would pile every lane's extra loads onto a single cache line
         const int f = base + b * 64 + lane;
         v[b] = f < pp.f1
-                   ? ld_agent64(pp.src + ((f >> pp.sh) << 5) + (f & ((1 << pp.sh) - 1)))
+                   ? ld_agent64(pp.src + f)
                    : ((uint64_t)tag << 48) | ((uint64_t)tag << 16);
       }
       bool ready = true;
@@ -450,7 +449,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
       const uint32_t w = ((epoch & 0xffffu) << 16) | p0.v;
 #pragma unroll
       for (int r = 0; r < kReplicas; ++r)
-        st_agent(q0.stg + r * q0.rstride + (int)blockIdx.x * 64 + lane, w);
+        st_agent(q0.stg + r * q0.rstride + q0.pa + lane, w);
     }
   }
   PubSlice pending;
@@ -494,7 +493,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
         const uint32_t w = t1 | sh->pub[(s + 1) % kPubRing][lane];
 #pragma unroll
         for (int r = 0; r < kReplicas; ++r)
-          st_agent(nxt.stg + r * nxt.rstride + (int)blockIdx.x * 64 + lane, w);
+          st_agent(nxt.stg + r * nxt.rstride + nxt.pa + lane, w);
       }
     }
     cur = nxt;

@@ -163,8 +163,9 @@ qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
   return QD_OK;
 }
 
-// Staging bytes for a grid of nwg workgroups: each stage's input in slices of
-// 2^lg words, one 256-byte line per slice.
+// Staging bytes for a grid of nwg workgroups: per stage and replica, room for
+// one 256-byte line per slice of 2^lg words (the words themselves are
+// stored densely at the start of that room).
 size_t step_staging_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
   size_t bytes = 0;
   int64_t i = 0;

@@ -22,11 +22,12 @@ struct StepOp {            // 64 bytes
 };
 
 // A stage's input (its ops' inputs back to back, `words` words) is split
-// into slices of 2^lg words; slice j is published by workgroup j into its
-// own 256-byte line of staging (words [64*j, 64*j + 2^lg)), so no two
-// publishers write the same cache line.
+// into slices of 2^lg words; slice j is published by workgroup j as words
+// [j*2^lg, (j+1)*2^lg) of each staging replica, so the words lie densely and
+// a consumer reads whole lines.  Publishers that share a line write disjoint
+// 32-bit words (stores carry byte masks; nothing is read back and merged).
 struct StepStage {         // 32 bytes
-  uint32_t *stg;           // staging: ceil(words / 2^lg) lines of 64 words
+  uint32_t *stg;           // staging: replicas of ceil(words / 2^lg) * 64 words
   int32_t op0, nops;       // ops [op0, op0 + nops)
   int32_t rows_total;      // sum of the ops' rows
   int32_t cols;            // shared input width
