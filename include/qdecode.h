@@ -110,6 +110,27 @@ qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
                               const void *x_bf16, void *y_bf16, int64_t m,
                               void *stream);
 
+/* GEMVs that read the same input in one launch (the q, k, v projections, or
+ * gate and up, of a decoder layer: turbospark-runtime 0.3.0,
+ * qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step issues them on one input):
+ * y_k = x W_k^T for k < n_items, each exactly as qgemv_affine_i8_g64 with
+ * (items[k].w_packed, items[k].rows, cols, x_bf16, items[k].y_bf16, m).
+ *   items     host array of n_items entries, 1 <= n_items <= 4; each
+ *             w_packed: device affine blob [rows, cols], 16-byte aligned;
+ *             y_bf16: device BF16 [m, rows], 2-byte aligned; rows >= 1
+ *   x_bf16    device, BF16 [m, cols], 16-byte aligned, shared by all items
+ * Requirements and errors as qgemv_affine_i8_g64; in addition no output may
+ * overlap another item's output or weights (QD_EINVAL). */
+typedef struct {
+  const void *w_packed;
+  void *y_bf16;
+  int64_t rows;
+} qd_affine_gemv_item;
+
+qd_status qgemv_affine_i8_g64_group(const qd_affine_gemv_item *items, int64_t n_items,
+                                    int64_t cols, const void *x_bf16, int64_t m,
+                                    void *stream);
+
 /* ---- one decode step of affine GEMVs in a single launch ------------------ */
 
 /* One GEMV of a decode step: y[m, rows] = x[m, cols] W^T (same operation,
@@ -182,6 +203,26 @@ qd_status qgemv_affine_i8_g64_step_check(const qd_step_plan *plan,
  * then starts on a 16-byte boundary (8 blocks = 144 bytes). */
 qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
                      const float *x, float *y, int64_t m, void *stream);
+
+/* Q4_0 GEMVs that read the same input in one launch (the self-attention q,
+ * k, v projections of a Whisper decoder layer: fuel-transformers 0.19.1,
+ * lazy_quantized_whisper.rs -- decoder_layer applies them to one input):
+ * y_k = x W_k^T for k < n_items, each exactly as qgemv_q4_0 with
+ * (items[k].w_q4_0, items[k].rows, cols, x, items[k].y, m).
+ *   items   host array of n_items entries, 1 <= n_items <= 4; each w_q4_0:
+ *           device Q4_0 stream [rows, cols], 16-byte aligned; y: device f32
+ *           [m, rows], 4-byte aligned; rows >= 1
+ *   x       device, f32 [m, cols], 16-byte aligned, shared by all items
+ * Requirements and errors as qgemv_q4_0; in addition no output may overlap
+ * another item's output or weights (QD_EINVAL). */
+typedef struct {
+  const void *w_q4_0;
+  float *y;
+  int64_t rows;
+} qd_q4_0_gemv_item;
+
+qd_status qgemv_q4_0_group(const qd_q4_0_gemv_item *items, int64_t n_items, int64_t cols,
+                           const float *x, int64_t m, void *stream);
 
 /* Prefill GEMM y = x W^T over a Q4_0 stream on the matrix cores: BF16
  * activations, exact integer codes (q - 8) as BF16 MFMA operands, the f16

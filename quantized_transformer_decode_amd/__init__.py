@@ -27,8 +27,8 @@ EXPORTS = (
     "qd_status_string", "qd_last_hip_error", "qd_version",
     "affine_i8_g64_bytes", "affine_i8_g64_scales_offset",
     "affine_i8_g64_biases_offset", "q4_0_bytes",
-    "affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
-    "qgemm_q4_0_prefill", "q4_0_quantize",
+    "affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_affine_i8_g64_group",
+    "qgemv_q4_0", "qgemv_q4_0_group", "qgemm_q4_0_prefill", "q4_0_quantize",
     "qgemv_affine_i8_g64_step_workspace_bytes", "qgemv_affine_i8_g64_step_plan",
     "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
 )
@@ -39,6 +39,17 @@ class AffineGemvOp(ctypes.Structure):
     _fields_ = [("w_packed", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
                 ("y_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("stage", ctypes.c_int64)]
+
+
+class AffineGemvItem(ctypes.Structure):
+    """qd_affine_gemv_item"""
+    _fields_ = [("w_packed", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p),
+                ("rows", ctypes.c_int64)]
+
+
+class Q40GemvItem(ctypes.Structure):
+    """qd_q4_0_gemv_item"""
+    _fields_ = [("w_q4_0", ctypes.c_void_p), ("y", ctypes.c_void_p), ("rows", ctypes.c_int64)]
 
 
 class StepPlan(ctypes.Structure):
@@ -86,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.affine_i8_g64_pack.argtypes = [P, P, P, I64, I64, P, P]
         L.qgemv_affine_i8_g64.argtypes = [P, I64, I64, P, P, I64, P]
         L.qgemv_q4_0.argtypes = [P, I64, I64, P, P, I64, P]
+        L.qgemv_affine_i8_g64_group.argtypes = [ctypes.POINTER(AffineGemvItem), I64, I64, P,
+                                                I64, P]
+        L.qgemv_q4_0_group.argtypes = [ctypes.POINTER(Q40GemvItem), I64, I64, P, I64, P]
         L.qgemm_q4_0_prefill.argtypes = [P, I64, I64, P, P, I64, P]
         L.q4_0_quantize.argtypes = [P, I64, I64, P, P]
         OPS = ctypes.POINTER(AffineGemvOp)
@@ -96,6 +110,7 @@ def lib() -> ctypes.CDLL:
         L.qgemv_affine_i8_g64_step_run.argtypes = [PLAN, P]
         L.qgemv_affine_i8_g64_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
+                  "qgemv_affine_i8_g64_group", "qgemv_q4_0_group",
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
                   "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check"):
             getattr(L, n).restype = I
@@ -155,6 +170,26 @@ def qgemv_affine_i8_g64(w_packed, rows: int, cols: int, x_bf16, y_bf16, m: int,
 def qgemv_q4_0(w_q4_0, rows: int, cols: int, x, y, m: int, stream=None) -> None:
     _check("qgemv_q4_0", lib().qgemv_q4_0(
         _ptr(w_q4_0), rows, cols, _ptr(x), _ptr(y), m, _stream(stream)))
+
+
+def qgemv_affine_i8_g64_group(items, cols: int, x_bf16, m: int, stream=None) -> None:
+    """items: sequence of (w_packed, y_bf16, rows) sharing the input x_bf16."""
+    items = list(items)
+    arr = (AffineGemvItem * max(1, len(items)))()
+    for i, (w, y, rows) in enumerate(items):
+        arr[i] = AffineGemvItem(_ptr(w), _ptr(y), rows)
+    _check("qgemv_affine_i8_g64_group", lib().qgemv_affine_i8_g64_group(
+        arr, len(items), cols, _ptr(x_bf16), m, _stream(stream)))
+
+
+def qgemv_q4_0_group(items, cols: int, x, m: int, stream=None) -> None:
+    """items: sequence of (w_q4_0, y, rows) sharing the input x."""
+    items = list(items)
+    arr = (Q40GemvItem * max(1, len(items)))()
+    for i, (w, y, rows) in enumerate(items):
+        arr[i] = Q40GemvItem(_ptr(w), _ptr(y), rows)
+    _check("qgemv_q4_0_group", lib().qgemv_q4_0_group(
+        arr, len(items), cols, _ptr(x), m, _stream(stream)))
 
 
 def qgemm_q4_0_prefill(w_q4_0, rows: int, cols: int, x_bf16, y, m: int,

@@ -65,13 +65,39 @@ struct MCursor {
 };
 
 struct MShape {
-  const QD_GLOBAL uint8_t *w;
-  const QD_GLOBAL uint16_t *sc;
-  size_t boff;     // biases - scales, in elements
-  int rows, cols, groups;
+  int cols, groups;
   int ts0, stride; // the wave's first tile and the tile stride
   int ga, gb;      // the wave's group range
 };
+
+// One matrix of a launch, resolved from a tile index: the tiles of the
+// group's matrices are numbered back to back (matrix k owns tiles
+// [tile0[k], tile0[k+1])).
+struct MItem {
+  const QD_GLOBAL uint8_t *w;
+  const QD_GLOBAL uint16_t *sc;  // scales; biases at sc + boff
+  QD_GLOBAL uint16_t *y;
+  size_t boff;
+  int rows;
+  int trow;                      // first row of the tile in its matrix
+};
+
+template <int R>
+__device__ __forceinline__ MItem item_of_tile(const AffineGroup &grp, int cols, int groups,
+                                              int tile) {
+  int k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < grp.n && tile >= grp.tile0[i]) k = i;
+  MItem it;
+  it.rows = grp.rows[k];
+  it.w = gp(grp.w[k]);
+  it.sc = (const QD_GLOBAL uint16_t *)(it.w + (size_t)it.rows * cols);
+  it.y = gp(grp.y[k]);
+  it.boff = (size_t)it.rows * groups;
+  it.trow = (tile - grp.tile0[k]) * 16 * R;
+  return it;
+}
 
 // Advance by one item without branches; `left` counts the items still to
 // walk (the cursor stays on the last item once it is 0).
@@ -89,6 +115,7 @@ __device__ __forceinline__ void mc_next(MCursor &c, const MShape &S, int &left) 
 // the end of the matrix are clamped to its last row.
 template <int R, int U, bool CH, bool XL>
 __device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const MShape &S,
+                                         const AffineGroup &grp,
                                          const QD_GLOBAL uint16_t *x, uint32_t xoff,
                                          const uint8_t *xl, uint32_t xloff, int lane,
                                          int &left) {
@@ -103,12 +130,13 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const 
       G.xa[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff));
       G.xb[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
     }
-    const int trow = (S.ts0 + c.j * S.stride) * 16 * R;
-    const int lim = S.rows - 1 - trow;  // last valid row offset inside the tile
-    const QD_GLOBAL uint8_t *cb = S.w + (size_t)trow * S.cols + 64 * c.g;
+    const MItem it = item_of_tile<R>(grp, S.cols, S.groups, S.ts0 + c.j * S.stride);
+    const int trow = it.trow;
+    const int lim = it.rows - 1 - trow;  // last valid row offset inside the tile
+    const QD_GLOBAL uint8_t *cb = it.w + (size_t)trow * S.cols + 64 * c.g;
     const QD_GLOBAL uint8_t *sb =
-        (const QD_GLOBAL uint8_t *)(S.sc + (size_t)trow * S.groups + c.g);
-    const QD_GLOBAL uint8_t *bb = sb + 2 * S.boff;
+        (const QD_GLOBAL uint8_t *)(it.sc + (size_t)trow * S.groups + c.g);
+    const QD_GLOBAL uint8_t *bb = sb + 2 * it.boff;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // codes: adjacent lanes read adjacent 16-byte pieces (row lane/4,
@@ -132,16 +160,17 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const 
 // Output of one finished tile (KS = 1): lane holds tokens 4*(lane/16)+v of
 // weight row lane%16 of each 16-row block.
 template <int R>
-__device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S, int j, int m,
-                                         QD_GLOBAL uint16_t *y, int lane) {
-  const int base = (S.ts0 + j * S.stride) * 16 * R + (lane & 15);
+__device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S,
+                                         const AffineGroup &grp, int j, int m, int lane) {
+  const MItem it = item_of_tile<R>(grp, S.cols, S.groups, S.ts0 + j * S.stride);
+  const int base = it.trow + (lane & 15);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int n = base + 16 * r;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 4 * (lane >> 4) + v;
-      if (t < m && n < S.rows) y[(size_t)t * S.rows + n] = f32_to_bf16(acc[r][v]);
+      if (t < m && n < it.rows) it.y[(size_t)t * it.rows + n] = f32_to_bf16(acc[r][v]);
       acc[r][v] = 0.f;
     }
   }
@@ -151,8 +180,8 @@ __device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S, int
 // computed with zero scale and bias.
 template <int R, int U, bool CH, bool STORE>
 __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&acc)[R],
-                                           MCursor &c, const MShape &S, int &left, int m,
-                                           QD_GLOBAL uint16_t *y, int lane, bf16x8 ones) {
+                                           MCursor &c, const MShape &S, const AffineGroup &grp,
+                                           int &left, int m, int lane, bf16x8 ones) {
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   const int src4 = (4 * (lane & 15) + (lane >> 4)) * 4;
   const int srcs = (lane & 15) * 4, srcb = srcs + 64;
@@ -191,7 +220,7 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[r][v] = fmaf(s, P[v], fmaf(b, Sx[v], acc[r][v]));
     }
-    if (STORE && valid && c.g == S.gb - 1) mg_store(acc, S, c.j, m, y, lane);
+    if (STORE && valid && c.g == S.gb - 1) mg_store(acc, S, grp, c.j, m, lane);
     left -= valid;
     const int g = c.g + valid;
     const int wrap = g == S.gb;
@@ -228,23 +257,17 @@ __device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x
 
 template <int R, int U, int KS, bool CH, bool XL>
 __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
-    const uint8_t *__restrict__ w_, int rows, int cols, const uint16_t *__restrict__ x_,
-    uint16_t *__restrict__ y_, int m) {
+    const AffineGroup grp, int cols, const uint16_t *__restrict__ x_, int m) {
   constexpr int SLOTS = kMW / KS;
   __shared__ float red[KS > 1 ? kMW * R * kWave * 4 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t xsh[];  // x (XL)
   uint8_t *xl = xsh;
-  QD_GLOBAL uint16_t *y = gp(y_);
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int slot = wave / KS, split = wave % KS;
   MShape S;
-  S.w = gp(w_);
-  S.rows = rows;
   S.cols = cols;
   S.groups = cols >> 6;
-  S.sc = (const QD_GLOBAL uint16_t *)(S.w + (size_t)rows * cols);
-  S.boff = (size_t)rows * S.groups;
   // group ranges in whole buffers of U groups when the scales come in chunks
   const int unit = CH ? U : 1;
   const int units = S.groups / unit;
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   S.gb = uni(unit * (units * (split + 1) / KS));
   S.ts0 = blockIdx.x * SLOTS + slot;
   S.stride = gridDim.x * SLOTS;
-  const int ntiles = (rows + 16 * R - 1) / (16 * R);
+  const int ntiles = grp.tile0[grp.n];
   int tiles_mine = 0;
   if (S.ts0 < ntiles) tiles_mine = KS == 1 ? (ntiles - 1 - S.ts0) / S.stride + 1 : 1;
   const int n = uni(tiles_mine * (S.gb - S.ga));
@@ -272,7 +295,7 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   int li = n, lc = n;
   MGroup<R, U, CH> A, B;
   // the first buffer's codes and scales are in flight while x is staged
-  if (n > 0) mg_issue<R, U, CH, false>(A, ci, S, x, xoff, xl, xloff, lane, li);
+  if (n > 0) mg_issue<R, U, CH, false>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
   if constexpr (XL) {
     stage_x(xl, x, m, cols);
     // LDS writes done, then the barrier (global loads stay in flight)
@@ -284,17 +307,17 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     // is issued before the current one is consumed.
     for (;;) {
       if (lc <= U) {
-        mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, lc, m, y, lane, ones);
+        mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, grp, lc, m, lane, ones);
         break;
       }
-      mg_issue<R, U, CH, XL>(B, ci, S, x, xoff, xl, xloff, lane, li);
-      mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, lc, m, y, lane, ones);
+      mg_issue<R, U, CH, XL>(B, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, grp, lc, m, lane, ones);
       if (lc <= U) {
-        mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, lc, m, y, lane, ones);
+        mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, grp, lc, m, lane, ones);
         break;
       }
-      mg_issue<R, U, CH, XL>(A, ci, S, x, xoff, xl, xloff, lane, li);
-      mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, lc, m, y, lane, ones);
+      mg_issue<R, U, CH, XL>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, grp, lc, m, lane, ones);
     }
   }
   if constexpr (KS > 1) {
@@ -309,9 +332,12 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
       float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < KS; ++k) sum += red[(((sl * KS + k) * R + r) * kWave + l) * 4 + v];
+      const int tile = blockIdx.x * SLOTS + sl;
+      if (tile >= ntiles) continue;
+      const MItem it = item_of_tile<R>(grp, cols, S.groups, tile);
       const int tt = 4 * (l >> 4) + v;
-      const int nn = (blockIdx.x * SLOTS + sl) * 16 * R + 16 * r + (l & 15);
-      if (tt < m && nn < rows) y[(size_t)tt * rows + nn] = f32_to_bf16(sum);
+      const int nn = it.trow + 16 * r + (l & 15);
+      if (tt < m && nn < it.rows) it.y[(size_t)tt * it.rows + nn] = f32_to_bf16(sum);
     }
   }
 }
@@ -329,8 +355,8 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
 constexpr int kXlBudget = 72 * 1024;
 
 template <int KS, bool CH, bool XL>
-hipError_t launch_mfma_ks(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
-                          int m, int grid, hipStream_t stream) {
+hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
+                          hipStream_t stream) {
   constexpr int R = QD_AFFINE_MFMA_R;
   constexpr int U = CH ? 4 : 2;
   const size_t lds = XL ? (size_t)m * (2 * cols + 16) : 0;
@@ -345,31 +371,34 @@ hipError_t launch_mfma_ks(const uint8_t *w, int rows, int cols, const uint16_t *
     }
   }
   hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL>), dim3(grid), dim3(kMThreads),
-                     lds, stream, w, rows, cols, x, y, m);
+                     lds, stream, g, cols, x, m);
   return hipGetLastError();
 }
 
 // Only the streaming walk (KS = 1) stages x: there a workgroup reuses it over
 // many tiles, while a split workgroup reads each element of x once anyway.
 template <int KS, bool CH>
-hipError_t launch_mfma_xl(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
-                          int m, int grid, hipStream_t stream) {
+hipError_t launch_mfma_xl(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
+                          hipStream_t stream) {
   if (KS == 1 && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
-    return launch_mfma_ks<KS, CH, true>(w, rows, cols, x, y, m, grid, stream);
-  return launch_mfma_ks<KS, CH, false>(w, rows, cols, x, y, m, grid, stream);
+    return launch_mfma_ks<KS, CH, true>(g, cols, x, m, grid, stream);
+  return launch_mfma_ks<KS, CH, false>(g, cols, x, m, grid, stream);
 }
 
 template <bool CH>
-hipError_t launch_mfma_ch(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
-                          int m, hipStream_t stream) {
-  // KS: split K over up to 8 waves until the matrix gives about
+hipError_t launch_mfma_ch(AffineGroup g, int cols, const uint16_t *x, int m,
+                          hipStream_t stream) {
+  // KS: split K over up to 8 waves until the launch gives about
   // kTargetWaves waves (each wave keeping at least one buffer of groups);
   // KS = 1 walks tiles grid-stride with kStreamWgsPerCu workgroups per CU.
   constexpr int kTargetWaves = QD_AFFINE_TARGET_WAVES;
   constexpr int kStreamWgsPerCu = QD_AFFINE_STREAM_WGS;
   constexpr int R = QD_AFFINE_MFMA_R;
+  g.tile0[0] = 0;
+  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + 16 * R - 1) / (16 * R);
+  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
   const int units = (cols / 64) / (CH ? 4 : 1);
-  const long ntiles = (rows + 16 * R - 1) / (16 * R);
+  const long ntiles = g.tile0[g.n];
   int ks = 1;
   while (ks < 8 && ntiles * ks < kTargetWaves && units / (2 * ks) >= (CH ? 1 : 2)) ks *= 2;
   if (ks == 1) {
@@ -377,20 +406,20 @@ hipError_t launch_mfma_ch(const uint8_t *w, int rows, int cols, const uint16_t *
     if (cus < 1) cus = 256;
     long grid = (ntiles + kMW - 1) / kMW;
     if (grid > (long)kStreamWgsPerCu * cus) grid = (long)kStreamWgsPerCu * cus;
-    return launch_mfma_xl<1, CH>(w, rows, cols, x, y, m, (int)grid, stream);
+    return launch_mfma_xl<1, CH>(g, cols, x, m, (int)grid, stream);
   }
   const int grid = (int)((ntiles * ks + kMW - 1) / kMW);
   switch (ks) {
-    case 2: return launch_mfma_xl<2, CH>(w, rows, cols, x, y, m, grid, stream);
-    case 4: return launch_mfma_xl<4, CH>(w, rows, cols, x, y, m, grid, stream);
-    default: return launch_mfma_xl<8, CH>(w, rows, cols, x, y, m, grid, stream);
+    case 2: return launch_mfma_xl<2, CH>(g, cols, x, m, grid, stream);
+    case 4: return launch_mfma_xl<4, CH>(g, cols, x, m, grid, stream);
+    default: return launch_mfma_xl<8, CH>(g, cols, x, m, grid, stream);
   }
 }
 
-hipError_t launch_mfma(const uint8_t *w, int rows, int cols, const uint16_t *x, uint16_t *y,
-                       int m, hipStream_t stream) {
-  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true>(w, rows, cols, x, y, m, stream);
-  return launch_mfma_ch<false>(w, rows, cols, x, y, m, stream);
+hipError_t launch_mfma(const AffineGroup &g, int cols, const uint16_t *x, int m,
+                       hipStream_t stream) {
+  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true>(g, cols, x, m, stream);
+  return launch_mfma_ch<false>(g, cols, x, m, stream);
 }
 
 // ---- batch 1: streaming kernel ---------------------------------------------
@@ -505,13 +534,15 @@ __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
 
 }  // namespace
 
-hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
-                              const uint16_t *x, uint16_t *y, int m,
+hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
                               hipStream_t stream) {
-  // Batch 1 takes the VALU streaming kernel only for very large matrices
-  // (LM heads), where its 1 KiB-per-row loads keep the most bytes in flight;
-  // below that the matrix-core kernel's K split gives more waves per matrix.
-  if (m == 1 && (int64_t)rows * cols >= ((int64_t)1 << 28)) {
+  // Batch 1 takes the VALU streaming kernel only for a single very large
+  // matrix (LM heads), where its 1 KiB-per-row loads keep the most bytes in
+  // flight; below that the matrix-core kernel's K split gives more waves.
+  if (g.n == 1 && m == 1 && (int64_t)g.rows[0] * cols >= ((int64_t)1 << 28)) {
+    const uint8_t *w = g.w[0];
+    uint16_t *y = g.y[0];
+    const int rows = g.rows[0];
     // waves: about two register groups of items each, at most 4 workgroups
     // of 8 waves per CU
     int cus = device_cus();
@@ -525,7 +556,7 @@ hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
                        stream, w, rows, cols, x, y);
     return hipGetLastError();
   }
-  return launch_mfma(w, rows, cols, x, y, m, stream);
+  return launch_mfma(g, cols, x, m, stream);
 }
 
 }  // namespace qd

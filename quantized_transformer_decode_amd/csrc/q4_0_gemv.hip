@@ -35,11 +35,34 @@ struct QGroup {
 };
 
 struct QShape {
-  const QD_GLOBAL uint8_t *w;
-  int rows, bpr;
+  int bpr;
   int rg0, stride;      // the wave's first row group and the stride
   int sa, sb;           // the wave's step range
 };
+
+// One matrix of a launch, resolved from a row-group index: the row groups of
+// the launch's matrices are numbered back to back (matrix k owns
+// [tile0[k], tile0[k+1])).
+struct QItem {
+  const QD_GLOBAL uint8_t *w;
+  QD_GLOBAL float *y;
+  int rows;
+  int trow;             // first row of the row group in its matrix
+};
+
+template <int R>
+__device__ __forceinline__ QItem q_item(const Q40Group &grp, int rg) {
+  int k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < grp.n && rg >= grp.tile0[i]) k = i;
+  QItem it;
+  it.w = gp(grp.w[k]);
+  it.y = gp(grp.y[k]);
+  it.rows = grp.rows[k];
+  it.trow = (rg - grp.tile0[k]) * 8 * R;
+  return it;
+}
 
 struct QCursor {
   int j, s;             // j-th row group of the wave, step s
@@ -56,18 +79,19 @@ __device__ __forceinline__ void qc_next(QCursor &c, const QShape &S, int &left) 
 
 // Row r of a lane's R rows in row group g: 8R*g + 8r + lane/8.
 template <int R>
-__device__ __forceinline__ void qg_issue(QGroup<R> &G, QCursor &c, const QShape &S, int lane,
-                                         int &left) {
+__device__ __forceinline__ void qg_issue(QGroup<R> &G, QCursor &c, const QShape &S,
+                                         const Q40Group &grp, int lane, int &left) {
 #pragma unroll
   for (int u = 0; u < kQU; ++u) {
-    const int base = (S.rg0 + c.j * S.stride) * 8 * R + (lane >> 3);
+    const QItem it = q_item<R>(grp, S.rg0 + c.j * S.stride);
+    const int base = it.trow + (lane >> 3);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = min(base + 8 * r, S.rows - 1);
+      const int n = min(base + 8 * r, it.rows - 1);
       const size_t flat = (size_t)n * S.bpr + 8 * c.s + (lane & 7);
       const uint32_t odd = (uint32_t)(flat & 1);
       const QD_GLOBAL uint32_t *p =
-          (const QD_GLOBAL uint32_t *)(S.w + 18 * flat - 2 * odd);
+          (const QD_GLOBAL uint32_t *)(it.w + 18 * flat - 2 * odd);
       const u32x4 v = __builtin_nontemporal_load((const QD_GLOBAL u32x4 *)p);
       G.w[u][r][0] = v.x;
       G.w[u][r][1] = v.y;
@@ -109,9 +133,9 @@ __device__ __forceinline__ void block_dot(const uint32_t (&nib)[R][4], const flo
 // Items past the end of the walk are computed with d = 0.
 template <int MT, int R, bool STORE>
 __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][R], QCursor &c,
-                                           const QShape &S, int &left, int lane, const float *xs,
-                                           const float *xsum, int cols, int t0, int m,
-                                           QD_GLOBAL float *y) {
+                                           const QShape &S, const Q40Group &grp, int &left,
+                                           int lane, const float *xs, const float *xsum,
+                                           int cols, int t0, int m) {
 #pragma unroll
   for (int u = 0; u < kQU; ++u) {
     const int valid = left > 0;  // wave-uniform
@@ -137,15 +161,16 @@ __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][
       for (int r = 0; r < R; ++r) acc[t][r] = fmaf(d[r], dot[r] + corr, acc[t][r]);
     }
     if (STORE && valid && c.s == S.sb - 1) {
-      const int base = (S.rg0 + c.j * S.stride) * 8 * R + (lane >> 3);
+      const QItem it = q_item<R>(grp, S.rg0 + c.j * S.stride);
+      const int base = it.trow + (lane >> 3);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float v = group_sum<8>(acc[t][r]);
           const int n = base + 8 * r;
-          if ((lane & 7) == 0 && n < S.rows && t0 + t < m)
-            y[(size_t)(t0 + t) * S.rows + n] = v;
+          if ((lane & 7) == 0 && n < it.rows && t0 + t < m)
+            it.y[(size_t)(t0 + t) * it.rows + n] = v;
           acc[t][r] = 0.f;
         }
     }
@@ -159,8 +184,7 @@ __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][
 
 template <int MT, int R, int KS>
 __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
-    const uint8_t *__restrict__ w_, int rows, int cols, const float *__restrict__ x_,
-    float *__restrict__ y_, int t0, int m) {
+    const Q40Group grp, int cols, const float *__restrict__ x_, int t0, int m) {
   constexpr int SLOTS = kQW / KS;
   __shared__ float red[KS > 1 ? kQW * MT * R * 8 : 1];
   extern __shared__ __attribute__((aligned(16))) float qsh[];
@@ -168,20 +192,17 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   const int bpr = cols >> 5;
   float *xsum = qsh + MT * cols;      // [MT][bpr]
   const QD_GLOBAL float *x = gp(x_);
-  QD_GLOBAL float *y = gp(y_);
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int slot = wave / KS, split = wave % KS;
   const int steps = bpr >> 3;
   QShape S;
-  S.w = gp(w_);
-  S.rows = rows;
   S.bpr = bpr;
   S.sa = uni(steps * split / KS);
   S.sb = uni(steps * (split + 1) / KS);
   S.rg0 = blockIdx.x * SLOTS + slot;
   S.stride = gridDim.x * SLOTS;
-  const int ngroups = (rows + 8 * R - 1) / (8 * R);
+  const int ngroups = grp.tile0[grp.n];
   int mine = 0;
   if (S.rg0 < ngroups) mine = KS == 1 ? (ngroups - 1 - S.rg0) / S.stride + 1 : 1;
   const int n = uni(mine * (S.sb - S.sa));
@@ -202,7 +223,7 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   floatx4 xv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) xv[k] = xp[k];
-  if (n > 0) qg_issue<R>(A, ci, S, lane, li);
+  if (n > 0) qg_issue<R>(A, ci, S, grp, lane, li);
   if ((int)threadIdx.x < nblk) {
     const bool live = t0 + bt < m;
     float sum = 0.f;
@@ -227,17 +248,17 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
     // register group is issued before the current one is consumed.
     for (;;) {
       if (lc <= kQU) {
-        qg_compute<MT, R, KS == 1>(A, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+        qg_compute<MT, R, KS == 1>(A, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
         break;
       }
-      qg_issue<R>(B, ci, S, lane, li);
-      qg_compute<MT, R, KS == 1>(A, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+      qg_issue<R>(B, ci, S, grp, lane, li);
+      qg_compute<MT, R, KS == 1>(A, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
       if (lc <= kQU) {
-        qg_compute<MT, R, KS == 1>(B, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+        qg_compute<MT, R, KS == 1>(B, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
         break;
       }
-      qg_issue<R>(A, ci, S, lane, li);
-      qg_compute<MT, R, KS == 1>(B, acc, cc, S, lc, lane, xs, xsum, cols, t0, m, y);
+      qg_issue<R>(A, ci, S, grp, lane, li);
+      qg_compute<MT, R, KS == 1>(B, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
     }
   }
   if constexpr (KS > 1) {
@@ -257,15 +278,18 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
       float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < KS; ++k) sum += red[((sl * KS + k) * MT + t) * 8 * R + rr];
-      const int nn = (blockIdx.x * SLOTS + sl) * 8 * R + rr;
-      if (nn < rows && t0 + t < m) y[(size_t)(t0 + t) * rows + nn] = sum;
+      const int rg = blockIdx.x * SLOTS + sl;
+      if (rg >= ngroups) continue;
+      const QItem it = q_item<R>(grp, rg);
+      const int nn = it.trow + rr;
+      if (nn < it.rows && t0 + t < m) it.y[(size_t)(t0 + t) * it.rows + nn] = sum;
     }
   }
 }
 
 template <int MT, int R, int KS>
-hipError_t launch_q_ks(const uint8_t *w, int rows, int cols, const float *x, float *y, int t0,
-                       int m, int grid, hipStream_t stream) {
+hipError_t launch_q_ks(const Q40Group &g, int cols, const float *x, int t0, int m, int grid,
+                       hipStream_t stream) {
   const size_t lds = (size_t)MT * cols * 4 + (size_t)MT * (cols / 32) * 4;
   if (lds > 48 * 1024) {  // above the default dynamic-LDS limit: raise it once
     static bool raised = false;
@@ -278,24 +302,25 @@ hipError_t launch_q_ks(const uint8_t *w, int rows, int cols, const float *x, flo
     }
   }
   hipLaunchKernelGGL((q4_0_gemv_kernel<MT, R, KS>), dim3(grid), dim3(kQThreads), lds, stream,
-                     w, rows, cols, x, y, t0, m);
+                     g, cols, x, t0, m);
   return hipGetLastError();
 }
 
-// KS: split a row's steps over up to 8 waves until the matrix gives about
+// KS: split a row's steps over up to 8 waves until the launch gives about
 // kQTargetWaves waves (each wave keeping at least one register group);
 // KS = 1 walks row groups grid-stride with kQStreamWgsPerCu workgroups per CU.
 constexpr int kQTargetWaves = 4096;
 constexpr int kQStreamWgsPerCu = 2;
 
-// R rows per lane share each read of x: one for a single token (the loads
-// then dominate), more as tokens multiply the x reads.
 template <int MT>
-hipError_t launch_q_mt(const uint8_t *w, int rows, int cols, const float *x, float *y, int t0,
-                       int m, hipStream_t stream) {
-  constexpr int R = 1;
+hipError_t launch_q_mt(Q40Group g, int cols, const float *x, int t0, int m,
+                       hipStream_t stream) {
+  constexpr int R = 1;  // rows per lane
+  g.tile0[0] = 0;
+  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + 8 * R - 1) / (8 * R);
+  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
   const int steps = cols / 256;
-  const long ngroups = (rows + 8 * R - 1) / (8 * R);
+  const long ngroups = g.tile0[g.n];
   int ks = 1;
   while (ks < 8 && ngroups * ks < kQTargetWaves && steps / (2 * ks) >= kQU) ks *= 2;
   if (ks == 1) {
@@ -303,20 +328,19 @@ hipError_t launch_q_mt(const uint8_t *w, int rows, int cols, const float *x, flo
     if (cus < 1) cus = 256;
     long grid = (ngroups + kQW - 1) / kQW;
     if (grid > (long)kQStreamWgsPerCu * cus) grid = (long)kQStreamWgsPerCu * cus;
-    return launch_q_ks<MT, R, 1>(w, rows, cols, x, y, t0, m, (int)grid, stream);
+    return launch_q_ks<MT, R, 1>(g, cols, x, t0, m, (int)grid, stream);
   }
   const int grid = (int)((ngroups * ks + kQW - 1) / kQW);
   switch (ks) {
-    case 2: return launch_q_ks<MT, R, 2>(w, rows, cols, x, y, t0, m, grid, stream);
-    case 4: return launch_q_ks<MT, R, 4>(w, rows, cols, x, y, t0, m, grid, stream);
-    default: return launch_q_ks<MT, R, 8>(w, rows, cols, x, y, t0, m, grid, stream);
+    case 2: return launch_q_ks<MT, R, 2>(g, cols, x, t0, m, grid, stream);
+    case 4: return launch_q_ks<MT, R, 4>(g, cols, x, t0, m, grid, stream);
+    default: return launch_q_ks<MT, R, 8>(g, cols, x, t0, m, grid, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_q4_0_gemv(const uint8_t *w, int rows, int cols,
-                            const float *x, float *y, int m,
+hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
                             hipStream_t stream) {
   // tokens per pass limited by the LDS copy of x (fp32 plus block sums) and
   // by one x block per thread for the staging
@@ -328,9 +352,9 @@ hipError_t launch_q4_0_gemv(const uint8_t *w, int rows, int cols,
     const int lim = left < cap ? left : cap;
     hipError_t e;
     int mt;
-    if (lim >= 4) { mt = 4; e = launch_q_mt<4>(w, rows, cols, x, y, t0, m, stream); }
-    else if (lim >= 2) { mt = 2; e = launch_q_mt<2>(w, rows, cols, x, y, t0, m, stream); }
-    else { mt = 1; e = launch_q_mt<1>(w, rows, cols, x, y, t0, m, stream); }
+    if (lim >= 4) { mt = 4; e = launch_q_mt<4>(g, cols, x, t0, m, stream); }
+    else if (lim >= 2) { mt = 2; e = launch_q_mt<2>(g, cols, x, t0, m, stream); }
+    else { mt = 1; e = launch_q_mt<1>(g, cols, x, t0, m, stream); }
     if (e != hipSuccess) return e;
     t0 += mt;
   }

@@ -248,39 +248,86 @@ qd_status affine_i8_g64_pack(const void *codes_u32, const void *scales_bf16,
 qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
                               const void *x_bf16, void *y_bf16, int64_t m,
                               void *stream) {
-  if (!w_packed || !x_bf16 || !y_bf16) return QD_EINVAL;
-  if (rows < 1 || rows > kMaxRows || m < 1 || m > 16 || cols < 1) return QD_EINVAL;
+  const qd_affine_gemv_item item = {w_packed, y_bf16, rows};
+  return qgemv_affine_i8_g64_group(&item, 1, cols, x_bf16, m, stream);
+}
+
+qd_status qgemv_affine_i8_g64_group(const qd_affine_gemv_item *items, int64_t n_items,
+                                    int64_t cols, const void *x_bf16, int64_t m,
+                                    void *stream) {
+  if (!items || !x_bf16 || n_items < 1 || n_items > qd::kMaxGroup) return QD_EINVAL;
+  if (m < 1 || m > 16 || cols < 1) return QD_EINVAL;
   if (cols % 64 != 0 || cols > kMaxGemvCols) return QD_ESHAPE;
-  if (!aligned(w_packed, 16) || !aligned(x_bf16, 16) || !aligned(y_bf16, 2))
-    return QD_EALIGN;
-  const size_t ny = (size_t)m * rows * 2;
-  if (overlap(y_bf16, ny, w_packed, affine_bytes(rows, cols)) ||
-      overlap(y_bf16, ny, x_bf16, (size_t)m * cols * 2))
-    return QD_EINVAL;
+  if (!aligned(x_bf16, 16)) return QD_EALIGN;
+  for (int64_t k = 0; k < n_items; ++k) {
+    const qd_affine_gemv_item &it = items[k];
+    if (!it.w_packed || !it.y_bf16) return QD_EINVAL;
+    if (it.rows < 1 || it.rows > kMaxRows) return QD_EINVAL;
+    if (!aligned(it.w_packed, 16) || !aligned(it.y_bf16, 2)) return QD_EALIGN;
+  }
+  // an output may overlap neither the input, nor any weights, nor another output
+  for (int64_t k = 0; k < n_items; ++k) {
+    const size_t ny = (size_t)m * items[k].rows * 2;
+    if (overlap(items[k].y_bf16, ny, x_bf16, (size_t)m * cols * 2)) return QD_EINVAL;
+    for (int64_t j = 0; j < n_items; ++j) {
+      if (overlap(items[k].y_bf16, ny, items[j].w_packed, affine_bytes(items[j].rows, cols)))
+        return QD_EINVAL;
+      if (j > k && overlap(items[k].y_bf16, ny, items[j].y_bf16, (size_t)m * items[j].rows * 2))
+        return QD_EINVAL;
+    }
+  }
   qd_status st = check_device();
   if (st != QD_OK) return st;
-  hipError_t e = qd::launch_affine_gemv((const uint8_t *)w_packed, (int)rows,
-                                        (int)cols, (const uint16_t *)x_bf16,
-                                        (uint16_t *)y_bf16, (int)m,
+  qd::AffineGroup g = {};
+  g.n = (int)n_items;
+  for (int64_t k = 0; k < n_items; ++k) {
+    g.w[k] = (const uint8_t *)items[k].w_packed;
+    g.y[k] = (uint16_t *)items[k].y_bf16;
+    g.rows[k] = (int)items[k].rows;
+  }
+  hipError_t e = qd::launch_affine_gemv(g, (int)cols, (const uint16_t *)x_bf16, (int)m,
                                         (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 
 qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
                      const float *x, float *y, int64_t m, void *stream) {
-  if (!w_q4_0 || !x || !y) return QD_EINVAL;
-  if (rows < 1 || rows > kMaxRows || m < 1 || m > 16 || cols < 1) return QD_EINVAL;
+  const qd_q4_0_gemv_item item = {w_q4_0, y, rows};
+  return qgemv_q4_0_group(&item, 1, cols, x, m, stream);
+}
+
+qd_status qgemv_q4_0_group(const qd_q4_0_gemv_item *items, int64_t n_items, int64_t cols,
+                           const float *x, int64_t m, void *stream) {
+  if (!items || !x || n_items < 1 || n_items > qd::kMaxGroup) return QD_EINVAL;
+  if (m < 1 || m > 16 || cols < 1) return QD_EINVAL;
   if (cols % 256 != 0 || cols > kMaxGemvCols) return QD_ESHAPE;
-  if (!aligned(w_q4_0, 16) || !aligned(x, 16) || !aligned(y, 4)) return QD_EALIGN;
-  const size_t ny = (size_t)m * rows * 4;
-  if (overlap(y, ny, w_q4_0, q40_bytes(rows, cols)) ||
-      overlap(y, ny, x, (size_t)m * cols * 4))
-    return QD_EINVAL;
+  if (!aligned(x, 16)) return QD_EALIGN;
+  for (int64_t k = 0; k < n_items; ++k) {
+    const qd_q4_0_gemv_item &it = items[k];
+    if (!it.w_q4_0 || !it.y) return QD_EINVAL;
+    if (it.rows < 1 || it.rows > kMaxRows) return QD_EINVAL;
+    if (!aligned(it.w_q4_0, 16) || !aligned(it.y, 4)) return QD_EALIGN;
+  }
+  for (int64_t k = 0; k < n_items; ++k) {
+    const size_t ny = (size_t)m * items[k].rows * 4;
+    if (overlap(items[k].y, ny, x, (size_t)m * cols * 4)) return QD_EINVAL;
+    for (int64_t j = 0; j < n_items; ++j) {
+      if (overlap(items[k].y, ny, items[j].w_q4_0, q40_bytes(items[j].rows, cols)))
+        return QD_EINVAL;
+      if (j > k && overlap(items[k].y, ny, items[j].y, (size_t)m * items[j].rows * 4))
+        return QD_EINVAL;
+    }
+  }
   qd_status st = check_device();
   if (st != QD_OK) return st;
-  hipError_t e = qd::launch_q4_0_gemv((const uint8_t *)w_q4_0, (int)rows,
-                                      (int)cols, x, y, (int)m,
-                                      (hipStream_t)stream);
+  qd::Q40Group g = {};
+  g.n = (int)n_items;
+  for (int64_t k = 0; k < n_items; ++k) {
+    g.w[k] = (const uint8_t *)items[k].w_q4_0;
+    g.y[k] = items[k].y;
+    g.rows[k] = (int)items[k].rows;
+  }
+  hipError_t e = qd::launch_q4_0_gemv(g, (int)cols, x, (int)m, (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 

@@ -11,12 +11,29 @@ namespace qd {
 // Compute units of the current device, cached per device (0 if unknown).
 int device_cus();
 
-hipError_t launch_affine_gemv(const uint8_t *w, int rows, int cols,
-                              const uint16_t *x, uint16_t *y, int m,
+// GEMVs of one launch that share their input x (and so `cols`): matrix k
+// has rows[k] rows and owns the row tiles [tile0[k], tile0[k+1]) of the
+// launch (tiles of the kernel's own height; the launcher fills tile0).
+constexpr int kMaxGroup = 4;
+struct AffineGroup {
+  const uint8_t *w[kMaxGroup];
+  uint16_t *y[kMaxGroup];
+  int rows[kMaxGroup];
+  int tile0[kMaxGroup + 1];
+  int n;
+};
+struct Q40Group {
+  const uint8_t *w[kMaxGroup];
+  float *y[kMaxGroup];
+  int rows[kMaxGroup];
+  int tile0[kMaxGroup + 1];
+  int n;
+};
+
+hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
                               hipStream_t stream);
 
-hipError_t launch_q4_0_gemv(const uint8_t *w, int rows, int cols,
-                            const float *x, float *y, int m,
+hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
                             hipStream_t stream);
 
 hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,

@@ -105,6 +105,58 @@ def test_errors_q4_0_gemv_and_gemm():
     assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, (1 << 22) + 1, None) == qd.QD_EINVAL
 
 
+D = 0x7f3000000000
+E = 0x7f4000000000
+
+
+def _affine_items(*items):
+    arr = (qd.AffineGemvItem * max(1, len(items)))()
+    for i, (w, y, rows) in enumerate(items):
+        arr[i] = qd.AffineGemvItem(w, y, rows)
+    return arr
+
+
+def _q4_items(*items):
+    arr = (qd.Q40GemvItem * max(1, len(items)))()
+    for i, (w, y, rows) in enumerate(items):
+        arr[i] = qd.Q40GemvItem(w, y, rows)
+    return arr
+
+
+def test_errors_affine_gemv_group():
+    f = "qgemv_affine_i8_g64_group"
+    two = _affine_items((A, C, 64), (D, E, 32))
+    assert _call(f, None, 1, 1024, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, two, 0, 1024, B, 1, None) == qd.QD_EINVAL
+    five = _affine_items(*[(A + (i << 32), C + (i << 32), 16) for i in range(5)])
+    assert _call(f, five, 5, 1024, B, 1, None) == qd.QD_EINVAL      # at most 4
+    assert _call(f, two, 2, 1024, None, 1, None) == qd.QD_EINVAL
+    assert _call(f, two, 2, 1024, B, 17, None) == qd.QD_EINVAL
+    assert _call(f, two, 2, 1000, B, 1, None) == qd.QD_ESHAPE
+    assert _call(f, _affine_items((A, C, 64), (None, E, 32)), 2, 1024, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, _affine_items((A, C, 64), (D, E, 0)), 2, 1024, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, _affine_items((A, C, 64), (D + 8, E, 32)), 2, 1024, B, 1, None) == qd.QD_EALIGN
+    assert _call(f, two, 2, 1024, B + 2, 1, None) == qd.QD_EALIGN
+    # an output over another item's weights, over another output, over x
+    assert _call(f, _affine_items((A, C, 64), (D, A + 64, 32)), 2, 1024, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, _affine_items((A, C, 64), (D, C + 64, 32)), 2, 1024, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, _affine_items((A, B + 2, 64), (D, E, 32)), 2, 1024, B, 1, None) == qd.QD_EINVAL
+
+
+def test_errors_q4_0_gemv_group():
+    f = "qgemv_q4_0_group"
+    two = _q4_items((A, C, 64), (D, E, 32))
+    assert _call(f, None, 1, 512, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, two, 0, 512, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, two, 5, 512, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, two, 2, 512, B, 0, None) == qd.QD_EINVAL
+    assert _call(f, two, 2, 480, B, 1, None) == qd.QD_ESHAPE
+    assert _call(f, _q4_items((A, C, 64), (D, E + 2, 32)), 2, 512, B, 1, None) == qd.QD_EALIGN
+    assert _call(f, two, 2, 512, B + 4, 1, None) == qd.QD_EALIGN
+    assert _call(f, _q4_items((A, C, 64), (D, A + 64, 32)), 2, 512, B, 1, None) == qd.QD_EINVAL
+    assert _call(f, _q4_items((A, C, 64), (D, C + 128, 32)), 2, 512, B, 1, None) == qd.QD_EINVAL
+
+
 def test_errors_quantize_and_pack():
     f = "q4_0_quantize"
     assert _call(f, None, 4, 64, C, None) == qd.QD_EINVAL
@@ -138,4 +190,8 @@ def test_valid_args_reach_device_check():
     assert _call("qgemv_q4_0", A, 64, 512, B, C, 4, None) == qd.QD_EDEVICE
     assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, 1500, None) == qd.QD_EDEVICE
     assert _call("q4_0_quantize", A, 3, 32, C, None) == qd.QD_EDEVICE
+    assert _call("qgemv_affine_i8_g64_group", _affine_items((A, C, 64), (D, E, 32)), 2, 1024,
+                 B, 4, None) == qd.QD_EDEVICE
+    assert _call("qgemv_q4_0_group", _q4_items((A, C, 64), (D, E, 32)), 2, 512,
+                 B, 4, None) == qd.QD_EDEVICE
     assert _call("affine_i8_g64_pack", A, B, C, 4, 64, A + (1 << 20), None) == qd.QD_EDEVICE

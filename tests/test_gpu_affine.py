@@ -89,6 +89,38 @@ def test_large_sampled(rows, cols, m):
     del blob
 
 
+# Same-input groups in one launch: the decode step's q/k/v and gate/up, ragged
+# row counts, the per-group scale path (cols % 256 != 0), four matrices, and a
+# group large enough for the streaming walk to cross matrix boundaries
+# (checked on sampled rows).
+GROUPS = [
+    ((2048, 1024, 1024), 1024, 1), ((6144, 6144), 2048, 16), ((17, 130, 64, 5), 192, 3),
+    ((1000, 33), 2048, 10), ((40000, 30016), 1024, 4),
+]
+
+
+@pytest.mark.parametrize("rows_list,cols,m", GROUPS)
+def test_group_parity(rows_list, cols, m):
+    print(f"affine group rows={rows_list} cols={cols} m={m}", flush=True)
+    trs = [synth.affine_triplet(r, cols, key=(7, k, r)) for k, r in enumerate(rows_list)]
+    blobs = [pack_on_device(tr) for tr in trs]
+    x = synth.x_bf16(m, cols, key=(7, cols, m))
+    ys = [torch.full((m, r), float("nan"), dtype=torch.bfloat16, device=DEV) for r in rows_list]
+    qd.qgemv_affine_i8_g64_group([(b, y, r) for b, y, r in zip(blobs, ys, rows_list)],
+                                 cols, dev_bf16(x), m)
+    torch.cuda.synchronize()
+    for k, (r, b, y) in enumerate(zip(rows_list, blobs, ys)):
+        got = host_bf16_f64(y)
+        if r > 4096:
+            sel = np.unique(np.concatenate([np.random.default_rng(k).integers(0, r, 512),
+                                            np.arange(16), np.arange(r - 24, r)]))
+            ref = oracle.affine_gemv(b.cpu().numpy(), r, cols, x, row_sel=sel)
+            check_bf16_output(got[:, sel], ref, f"group item {k} ({r}x{cols}) sampled")
+        else:
+            ref = oracle.affine_gemv(b.cpu().numpy(), r, cols, x)
+            check_bf16_output(got, ref, f"group item {k} ({r}x{cols})")
+
+
 def test_closed_forms_on_device():
     # zero scales: y = sum_g bias_g * X_g; constant codes q0: y = sum_g
     # (s_g q0 + b_g) X_g -- compared with the oracle, which is pinned to

@@ -81,6 +81,35 @@ def test_gemv_parity(rows, cols, m):
     check_f32_output(y.cpu().numpy(), ref, f"{rows}x{cols} m={m}")
 
 
+# Same-input Q4_0 groups in one launch: a Whisper decoder layer's q/k/v,
+# ragged rows, tokens 1..16, and a group long enough for the streaming walk
+# to cross matrix boundaries (sampled rows).
+GROUPS = [((1280, 1280, 1280), 1280, 1), ((512, 512), 2048, 4), ((5, 130, 64, 9), 256, 2),
+          ((300, 77), 512, 16), ((20000, 30000), 1280, 1)]
+
+
+@pytest.mark.parametrize("rows_list,cols,m", GROUPS)
+def test_gemv_group_parity(rows_list, cols, m):
+    print(f"q4_0 gemv group rows={rows_list} cols={cols} m={m}", flush=True)
+    wqs = [oracle.q4_0_quantize(synth.w_f32(r, cols, key=(8, k, r)), r, cols)
+           for k, r in enumerate(rows_list)]
+    x = synth.x_f32(m, cols, key=(8, cols, m))
+    ws = [dev_u8(wq) for wq in wqs]
+    ys = [torch.full((m, r), float("nan"), device=DEV) for r in rows_list]
+    qd.qgemv_q4_0_group([(w, y, r) for w, y, r in zip(ws, ys, rows_list)], cols, dev_f32(x), m)
+    torch.cuda.synchronize()
+    for k, (r, wq, y) in enumerate(zip(rows_list, wqs, ys)):
+        got = y.cpu().numpy()
+        if r > 4096:
+            sel = np.unique(np.concatenate([np.random.default_rng(k).integers(0, r, 512),
+                                            np.arange(16), np.arange(r - 24, r)]))
+            ref = oracle.q4_0_gemm(wq, r, cols, x, row_sel=sel)
+            check_f32_output(got[:, sel], ref, f"group item {k} ({r}x{cols}) sampled")
+        else:
+            ref = oracle.q4_0_gemm(wq, r, cols, x)
+            check_f32_output(got, ref, f"group item {k} ({r}x{cols})")
+
+
 def test_gemv_zero_blocks_exact():
     # nibbles 8 (or d = 0) contribute exactly 0
     rows, cols = 64, 512
