@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rows", default="all",
                    help="comma-separated extra rows to measure, 'all' or 'none'")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the order-free sweep (profiling runs that average the "
+                        "headline kernel's launches)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (the "
                         "reference dispatch for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
@@ -534,10 +537,12 @@ def main():
         ms = event_time(lambda: step.run_step(cur), args.steps, args.warmup, cur)
         wall = time.perf_counter() - t0
         assert qd.qgemv_affine_i8_g64_step_check(step.plan) == 0
-        n_sweep = step.plan_sweep()
-        ms_sweep = event_time(lambda: qd.qgemv_affine_i8_g64_step_run(step.sweep_plan, cur),
-                              max(10, args.steps // 4), max(2, args.warmup // 4), cur)
-        assert qd.qgemv_affine_i8_g64_step_check(step.sweep_plan) == 0
+        ms_sweep, n_sweep = None, None
+        if not args.no_sweep:
+            n_sweep = step.plan_sweep()
+            ms_sweep = event_time(lambda: qd.qgemv_affine_i8_g64_step_run(step.sweep_plan, cur),
+                                  max(10, args.steps // 4), max(2, args.warmup // 4), cur)
+            assert qd.qgemv_affine_i8_g64_step_check(step.sweep_plan) == 0
         variant = ("one persistent launch per step (one workgroup per CU); stage s+1 "
                    "reads its inputs only after every workgroup finished stage s")
         kernel, launches = "affine_step_kernel", 1
