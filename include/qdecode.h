@@ -166,9 +166,11 @@ size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
  * _step_workspace_bytes) and fills *plan.  Synchronises `stream` before
  * returning.  Requirements beyond those of each op: m == 1; ops[0].stage ==
  * 0 and each op's stage equals its predecessor's or one more; ops of one
- * stage share cols; per stage sum(m*ceil(cols/1024)*1024) <= 16384; no op's output overlaps
- * any op's weights or input, or the workspace (QD_EINVAL / QD_ESHAPE /
- * QD_EALIGN as for the single GEMV).  The workspace, weights and inputs must
+ * stage share cols; per stage sum(m*ceil(cols/1024)*1024) <= 16384 and
+ * sum(m*cols) <= 64 * (compute units of the device) (QD_ESHAPE; the second
+ * bound only binds on parts with fewer than 256 CUs); no op's output
+ * overlaps any op's weights or input, or the workspace (QD_EINVAL /
+ * QD_ESHAPE / QD_EALIGN as for the single GEMV).  The workspace, weights and inputs must
  * stay valid while runs are in flight. */
 qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
                                         int64_t n_ops, int64_t m,

@@ -36,7 +36,11 @@ namespace {
 
 constexpr int NCW = 8;             // compute waves per workgroup
 constexpr int kThreads = (NCW + 1) * kWave;
-constexpr int G = 8;               // items (1 KiB row chunks) per register group
+// Items (1 KiB row chunks) per register group; two groups are in flight per
+// wave.  Three covers a wave's share of a layer stage of 0.6B-1.7B decoders
+// (1-3 items); larger groups mostly re-read past-the-end items, which delays
+// the stage hand-off more than the deeper stream helps the LM-head stage.
+constexpr int G = 3;
 constexpr unsigned kPollLimit = 1u << 18;   // global polls (~1 us each)
 constexpr unsigned kLdsSpinLimit = 1u << 27;
 

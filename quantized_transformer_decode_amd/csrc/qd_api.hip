@@ -166,6 +166,19 @@ qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
 // Staging bytes for a grid of nwg workgroups: per stage and replica, room for
 // one 256-byte line per slice of 2^lg words (the words themselves are
 // stored densely at the start of that room).
+// Each workgroup publishes at most 64 words of a stage's input (one per
+// lane), so a stage input may hold at most 64 words per workgroup.
+bool step_fits_grid(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
+  int64_t i = 0;
+  while (i < n_ops) {
+    int64_t j = i, words = 0;
+    while (j < n_ops && ops[j].stage == ops[i].stage) words += m * ops[j++].cols;
+    if (words > (int64_t)64 * nwg) return false;
+    i = j;
+  }
+  return true;
+}
+
 size_t step_staging_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
   size_t bytes = 0;
   int64_t i = 0;
@@ -381,7 +394,7 @@ size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
   // current device
   if (check_device() != QD_OK) return 0;
   const int nwg = current_cus();
-  if (nwg < kMinStepWgs) return 0;
+  if (nwg < kMinStepWgs || !step_fits_grid(ops, n_ops, m, nwg)) return 0;
   return bytes + step_staging_bytes(ops, n_ops, m, nwg);
 }
 
@@ -407,6 +420,7 @@ qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
   if (st != QD_OK) return st;
   const int nwg = current_cus();
   if (nwg < kMinStepWgs) return QD_EDEVICE;
+  if (!step_fits_grid(ops, n_ops, m, nwg)) return QD_ESHAPE;
   need += step_staging_bytes(ops, n_ops, m, nwg);
   if (workspace_bytes < need) return QD_EINVAL;
 
