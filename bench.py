@@ -11,9 +11,11 @@ Qwen3AsrMetalEngine::step runs this GEMV sequence once per generated token).
 Prints one JSON line.  `value` is decoder tokens/s at batch 1 (1000 /
 ms_per_step).  The line also carries weight GB/s and the fraction of the
 8 TB/s HBM peak, the roofline of the dominant kernel (HIP events on its
-stream), the CPU oracle timed on the host (it also re-checks the outputs of
-the timed buffers), and under "rows" a measurement of every other part of
-the path on its own workload:
+stream; also against a measured practical read ceiling, the library's
+streaming read probe over 2 GiB), p10/p50/p90 of single-step times, the ROCm
+version and clocks, the CPU oracle timed on the host (it also re-checks the
+outputs of the timed buffers), and under "rows" a measurement of every other
+part of the path on its own workload:
   affine_gemv_1024       single 1024x1024 affine GEMV, batch 1
   affine_lm_head         the tied LM heads (151936 x 1024 / x 2048) at M = 1, 4, 16:
                          single large GEMVs, weights streamed past the 256 MB MALL
@@ -502,6 +504,55 @@ def run_rows(qd, names):
     return out
 
 
+def step_distribution(fn, n, stream):
+    """Per-step HIP-event times (ms) of n back-to-back calls: p10 / p50 / p90."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"n": n, "p10": t[n // 10], "p50": t[n // 2], "p90": t[(9 * n) // 10],
+            "min": t[0], "max": t[-1]}
+
+
+def hbm_read_ceiling(qd, nbytes=2 << 30, iters=10):
+    """GB/s of the library's streaming read probe over nbytes of HBM: the
+    practical ceiling the GEMV rooflines are also set against."""
+    import torch
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ms = event_time(lambda: qd.stream_read(buf, nbytes, sink), iters, 2)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def environment():
+    """ROCm version, device and clocks (rocm-smi; None where unavailable)."""
+    import subprocess
+    import torch
+    env = {"device": torch.cuda.get_device_name(0),
+           "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+           "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:  # the clocks are context only
+        env["clocks"] = None
+    return env
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -536,6 +587,7 @@ def main():
         t0 = time.perf_counter()
         ms = event_time(lambda: step.run_step(cur), args.steps, args.warmup, cur)
         wall = time.perf_counter() - t0
+        dist = step_distribution(lambda: step.run_step(cur), min(args.steps, 200), cur)
         assert qd.qgemv_affine_i8_g64_step_check(step.plan) == 0
         ms_sweep, n_sweep = None, None
         if not args.no_sweep:
@@ -548,6 +600,7 @@ def main():
         kernel, launches = "affine_step_kernel", 1
     else:
         ms, wall = ms_graph, None
+        dist = step_distribution(g.replay, min(args.steps, 200), cur)
         ms_sweep, n_sweep = None, None
         variant = "hipgraph: 197 GEMV launches in decoder order"
         kernel, launches = "affine_gemv_mfma_kernel", len(step.mats)
@@ -578,6 +631,7 @@ def main():
         },
         "weight_GBps": gbps,
         "hbm_peak_frac": gbps / HBM_PEAK_GBPS,
+        "step_ms_distribution": dist,
         "graph_of_197_launches_ms_per_step": ms_graph,
         "graph_of_113_stage_launches_ms_per_step": ms_grouped,
         "independent_sweep": None if ms_sweep is None else {
@@ -598,6 +652,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(step)
     step.free()
     torch.cuda.empty_cache()
+    ceiling = hbm_read_ceiling(qd)
+    out["hbm_read_ceiling_GBps"] = ceiling
+    out["roofline"]["practical_peak"] = ceiling
+    out["roofline"]["frac_of_practical"] = achieved / ceiling
+    out["env"] = environment()
     names = ROWS if args.rows == "all" else [] if args.rows == "none" else args.rows.split(",")
     if names:
         out["rows"] = run_rows(qd, names)

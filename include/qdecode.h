@@ -256,6 +256,19 @@ qd_status qgemm_q4_0_prefill(const void *w_q4_0, int64_t rows, int64_t cols,
 qd_status q4_0_quantize(const float *w, int64_t rows, int64_t cols, void *out,
                         void *stream);
 
+/* ---- measurement aid (not a step of the decode path) ---------------------- */
+
+/* Reads `bytes` bytes of device memory at `buf` once, with the access pattern
+ * of the GEMV weight streams (every wave reads contiguous 1 KiB chunks with
+ * 16-byte non-temporal loads, many chunks in flight), so that bytes / time
+ * is a practical HBM read ceiling to set the GEMV rooflines against (the
+ * 8 TB/s figure is the interface's peak).  buf: device, 16-byte aligned;
+ * bytes: a positive multiple of 1024; sink: device, one uint32 that keeps
+ * the loads live (its value afterwards is unspecified).  QD_EINVAL (null
+ * pointer, bytes 0), QD_ESHAPE (bytes % 1024), QD_EALIGN; asynchronous on
+ * `stream`. */
+qd_status qd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

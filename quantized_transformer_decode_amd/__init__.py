@@ -31,6 +31,7 @@ EXPORTS = (
     "qgemv_q4_0", "qgemv_q4_0_group", "qgemm_q4_0_prefill", "q4_0_quantize",
     "qgemv_affine_i8_g64_step_workspace_bytes", "qgemv_affine_i8_g64_step_plan",
     "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
+    "qd_stream_read",
 )
 
 
@@ -109,10 +110,12 @@ def lib() -> ctypes.CDLL:
         L.qgemv_affine_i8_g64_step_plan.argtypes = [OPS, I64, I64, P, SZ, PLAN, P]
         L.qgemv_affine_i8_g64_step_run.argtypes = [PLAN, P]
         L.qgemv_affine_i8_g64_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
+        L.qd_stream_read.argtypes = [P, SZ, P, P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
                   "qgemv_affine_i8_g64_group", "qgemv_q4_0_group",
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
-                  "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check"):
+                  "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
+                  "qd_stream_read"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -201,6 +204,13 @@ def qgemm_q4_0_prefill(w_q4_0, rows: int, cols: int, x_bf16, y, m: int,
 def q4_0_quantize(w, rows: int, cols: int, out, stream=None) -> None:
     _check("q4_0_quantize", lib().q4_0_quantize(
         _ptr(w), rows, cols, _ptr(out), _stream(stream)))
+
+
+def stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    """Read nbytes of device memory once (a practical HBM read ceiling; not a
+    step of the decode path)."""
+    _check("qd_stream_read", lib().qd_stream_read(_ptr(buf), nbytes, _ptr(sink),
+                                                  _stream(stream)))
 
 
 # ---- decode step in one launch -------------------------------------------------

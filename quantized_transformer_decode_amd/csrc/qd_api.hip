@@ -381,6 +381,16 @@ qd_status q4_0_quantize(const float *w, int64_t rows, int64_t cols, void *out,
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 
+qd_status qd_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+  if (!buf || !sink || bytes == 0) return QD_EINVAL;
+  if (bytes % 1024 != 0) return QD_ESHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QD_EALIGN;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_stream_read(buf, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
 }  // extern "C"
 
 extern "C" {

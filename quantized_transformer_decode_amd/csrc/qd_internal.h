@@ -43,6 +43,11 @@ hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,
 hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
                                 hipStream_t stream);
 
+// Practical HBM read ceiling (hbm_probe.hip): reads `bytes` (a multiple of
+// 1024) once.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink,
+                              hipStream_t stream);
+
 // Persistent decode-step kernel (decode_step.hip): one workgroup per CU.
 struct StepOp;
 struct StepStage;

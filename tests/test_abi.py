@@ -173,6 +173,16 @@ def test_errors_quantize_and_pack():
     assert _call(g, A, B, C, 4, 64, A + 128, None) == qd.QD_EINVAL  # overlaps codes
 
 
+def test_errors_stream_read():
+    f = "qd_stream_read"
+    assert _call(f, None, 1024, B, None) == qd.QD_EINVAL
+    assert _call(f, A, 1024, None, None) == qd.QD_EINVAL
+    assert _call(f, A, 0, B, None) == qd.QD_EINVAL
+    assert _call(f, A, 1000, B, None) == qd.QD_ESHAPE
+    assert _call(f, A + 8, 1024, B, None) == qd.QD_EALIGN
+    assert _call(f, A, 1024, B + 2, None) == qd.QD_EALIGN
+
+
 def _gpu_visible():
     try:
         hip = ctypes.CDLL("libamdhip64.so")
@@ -188,6 +198,7 @@ def test_valid_args_reach_device_check():
     # GPU is the device check -- proving validation passed and nothing launched
     assert _call("qgemv_affine_i8_g64", A, 64, 1024, B, C, 1, None) == qd.QD_EDEVICE
     assert _call("qgemv_q4_0", A, 64, 512, B, C, 4, None) == qd.QD_EDEVICE
+    assert _call("qd_stream_read", A, 1 << 20, B, None) == qd.QD_EDEVICE
     assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, 1500, None) == qd.QD_EDEVICE
     assert _call("q4_0_quantize", A, 3, 32, C, None) == qd.QD_EDEVICE
     assert _call("qgemv_affine_i8_g64_group", _affine_items((A, C, 64), (D, E, 32)), 2, 1024,
