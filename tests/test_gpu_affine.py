@@ -40,6 +40,8 @@ CASES = [
     (1, 64, 1), (5, 128, 3), (17, 64, 16), (130, 192, 2), (1024, 1024, 1),
     (2048, 1024, 1), (1024, 2048, 1), (3072, 1024, 1), (1024, 3072, 1),
     (1000, 2048, 4), (6144, 2048, 10), (2048, 6144, 16), (333, 320, 7),
+    # the widest input the GEMV takes (8192 columns) at 1 and 16 tokens
+    (64, 8192, 1), (257, 8192, 16),
 ]
 
 

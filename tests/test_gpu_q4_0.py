@@ -68,6 +68,8 @@ def test_quantize_special_values():
     (2048, 512, 1), (512, 2048, 1), (2048, 512, 4), (512, 2048, 4),
     (1280, 1280, 1), (5120, 1280, 1), (1280, 5120, 1),
     (1, 256, 1), (9, 256, 3), (100, 768, 16), (37, 2816, 5),
+    # the widest input the GEMV takes (8192 columns)
+    (97, 8192, 4), (33, 8192, 16),
 ])
 def test_gemv_parity(rows, cols, m):
     print(f"q4_0 gemv rows={rows} cols={cols} m={m}", flush=True)
@@ -131,6 +133,8 @@ def _gemm(wq, rows, cols, x_bits, m):
 @pytest.mark.parametrize("rows,cols,m", [
     (64, 256, 1), (80, 512, 15), (130, 768, 17), (320, 512, 130), (1, 256, 64),
     (1280, 1280, 65),
+    # long K: the widest input the GEMM takes (65536 columns), and 16384
+    (96, 65536, 3), (70, 16384, 130),
 ])
 def test_gemm_parity_full(rows, cols, m):
     print(f"q4_0 gemm rows={rows} cols={cols} m={m}", flush=True)
