@@ -74,7 +74,10 @@ def lib() -> ctypes.CDLL:
         L.qdo_affine_pack.restype = None
         L.qdo_affine_weight.argtypes = [P, I64, I64, I64, I64]
         L.qdo_affine_weight.restype = D
-        L.qdo_affine_gemv.argtypes = [P, I64, I64, P, I64, P, I64, P, I64, P]
+        L.qdo_affine_gemv.argtypes = [P, I64, I64, P, ctypes.c_int, I64, P, I64, P, I64, P]
+        L.qdo_affine_embed_row.argtypes = [P, I64, I64, I64, ctypes.c_int, P]
+        L.qdo_f32_to_bf16_rne.argtypes = [ctypes.c_float]
+        L.qdo_f32_to_bf16_rne.restype = ctypes.c_uint16
         L.qdo_affine_gemv.restype = None
         L.qdo_q4_0_weight.argtypes = [P, I64, I64, I64]
         L.qdo_q4_0_weight.restype = D
@@ -145,8 +148,9 @@ def affine_weight(blob: np.ndarray, rows: int, cols: int, r: int, c: int) -> flo
 
 
 def affine_gemv(blob: np.ndarray, rows: int, cols: int, x_bf16: np.ndarray,
-                m_sel=None, row_sel=None) -> np.ndarray:
-    """f64 y[len(m_sel), len(row_sel)] for x BF16 bits [m, cols]."""
+                m_sel=None, row_sel=None, x_f16: bool = False) -> np.ndarray:
+    """f64 y[len(m_sel), len(row_sel)] for x [m, cols] given as BF16 bits (or
+    f16 bits with x_f16)."""
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, cols)
     m = x.shape[0]
@@ -157,9 +161,23 @@ def affine_gemv(blob: np.ndarray, rows: int, cols: int, x_bf16: np.ndarray,
     if rs is not None:
         assert rs.min(initial=0) >= 0 and rs.max(initial=0) < max(rows, 1)
     y = np.zeros((n_m, n_r), dtype=np.float64)
-    lib().qdo_affine_gemv(_ptr(blob), rows, cols, _ptr(x), m, _ptr(ms), n_m,
-                          _ptr(rs), n_r, _ptr(y))
+    lib().qdo_affine_gemv(_ptr(blob), rows, cols, _ptr(x), int(bool(x_f16)), m, _ptr(ms),
+                          n_m, _ptr(rs), n_r, _ptr(y))
     return y
+
+
+def affine_embed_row(blob: np.ndarray, rows: int, cols: int, token: int,
+                     out_f16: bool = True) -> np.ndarray:
+    """The tied-embedding row of `token` as uint16 bits (f16, or BF16)."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    assert 0 <= token < rows
+    out = np.zeros(cols, dtype=np.uint16)
+    lib().qdo_affine_embed_row(_ptr(blob), rows, cols, token, int(bool(out_f16)), _ptr(out))
+    return out
+
+
+def f32_to_bf16_rne(x: float) -> int:
+    return int(lib().qdo_f32_to_bf16_rne(x))
 
 
 # ---- ggml Q4_0 -------------------------------------------------------------

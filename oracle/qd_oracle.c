@@ -19,7 +19,10 @@
  *        -- load_packed_linear (dtype, shape and byte-count contract; blob
  *           order weight | scales | biases),
  *        -- embed_row_bytes (the scalar dequantisation q*scale + bias with
- *           the group index row*groups + col/64, little-endian BF16).
+ *           the group index row*groups + col/64, little-endian BF16; the
+ *           tied-embedding row it returns is computed in f32 and stored as
+ *           f16),
+ *        -- the f16 activations of the Metal GEMV (x and y are f16 there).
  *   [P4] fuel-transformers 0.19.1, src/models/lazy_quantized_whisper.rs
  *        -- module documentation (Q4_0 is ggml's BlockQ4_0 / from_float),
  *        -- quantize_in_out_to_q4_0 (row-major block stream, 18-byte
@@ -106,6 +109,19 @@ uint16_t qdo_f32_to_f16_rne(float x) {
   return (uint16_t)(sign | ((uint32_t)biased << 10) | (q - 1024u));
 }
 
+/* binary32 -> bfloat16, round to nearest, ties to even: keep the upper 16
+ * bits of the binary32 pattern, rounding on the lower 16 (NaN made quiet). */
+uint16_t qdo_f32_to_bf16_rne(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
+    return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t low = u & 0xffffu, keep = u >> 16;
+  if (low > 0x8000u || (low == 0x8000u && (keep & 1u)))
+    keep += 1u; /* a carry into the exponent is the correct rounding */
+  return (uint16_t)keep;
+}
+
 /* ---- affine-INT8 g64 ---------------------------------------------------- */
 
 /* Byte sizes and offsets of the single resident buffer
@@ -144,11 +160,11 @@ double qdo_affine_weight(const uint8_t *blob, int64_t rows, int64_t cols,
   return q * s + b;
 }
 
-/* y[i, j] = sum_c w[row_sel[j], c] * x[m_sel[i], c], x BF16 [m, cols]
- * row-major.  Selections let large shapes be checked on sampled outputs;
- * pass NULL for "all". */
+/* y[i, j] = sum_c w[row_sel[j], c] * x[m_sel[i], c], x [m, cols] row-major,
+ * BF16 bits (x_f16 == 0) or f16 bits (x_f16 != 0).  Selections let large
+ * shapes be checked on sampled outputs; pass NULL for "all". */
 void qdo_affine_gemv(const uint8_t *blob, int64_t rows, int64_t cols,
-                     const uint16_t *x_bf16, int64_t m, const int64_t *m_sel,
+                     const uint16_t *x_bits, int x_f16, int64_t m, const int64_t *m_sel,
                      int64_t n_m, const int64_t *row_sel, int64_t n_rows,
                      double *y) {
   if (!m_sel) n_m = m;
@@ -161,9 +177,30 @@ void qdo_affine_gemv(const uint8_t *blob, int64_t rows, int64_t cols,
       double acc = 0.0;
       for (int64_t c = 0; c < cols; ++c)
         acc += qdo_affine_weight(blob, rows, cols, r, c) *
-               qdo_bf16_to_f64(x_bf16[t * cols + c]);
+               (x_f16 ? qdo_f16_to_f64(x_bits[t * cols + c])
+                      : qdo_bf16_to_f64(x_bits[t * cols + c]));
       y[i * n_rows + j] = acc;
     }
+  }
+}
+
+/* [P3] embed_row_bytes: the tied-embedding row of `token` as 16-bit values,
+ * each q*scale + bias evaluated in binary32 (q*scale is exact there: at most
+ * 8 + 8 significant bits, so only the addition rounds) and then rounded to
+ * f16 (out_f16 != 0, the page's store) or to BF16 -- two roundings, as the
+ * page has them. */
+void qdo_affine_embed_row(const uint8_t *blob, int64_t rows, int64_t cols,
+                          int64_t token, int out_f16, uint16_t *out) {
+  int64_t groups = cols / QDO_GROUP;
+  const uint8_t *scales = blob + qdo_affine_scales_offset(rows, cols);
+  const uint8_t *biases = blob + qdo_affine_biases_offset(rows, cols);
+  for (int64_t c = 0; c < cols; ++c) {
+    int64_t g = token * groups + c / QDO_GROUP;
+    float q = (float)blob[token * cols + c];
+    float s = (float)qdo_bf16_to_f64(le16(scales + 2 * g));
+    float b = (float)qdo_bf16_to_f64(le16(biases + 2 * g));
+    float v = q * s + b; /* -ffp-contract=off: a product, then a rounded sum */
+    out[c] = out_f16 ? qdo_f32_to_f16_rne(v) : qdo_f32_to_bf16_rne(v);
   }
 }
 

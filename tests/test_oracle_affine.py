@@ -146,3 +146,89 @@ def test_matches_numpy_restatement():
     y = oracle.affine_gemv(blob, rows, cols, x)
     ref = reference_np.bf16_bits_to_f64(x) @ reference_np.affine_dense(blob, rows, cols).T
     assert oracle.normwise_error(y, ref) < 1e-13
+
+
+# ---- f16 activations and the tied-embedding row ---------------------------
+
+def _f16_bits(a):
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+def test_brute_force_k64_f16_input():
+    # the same exact case with x given as f16 ones (0x3C00)
+    codes = np.arange(64, dtype=np.uint8).reshape(1, 64)
+    tr = synth.affine_triplet_custom(codes, np.array([[2.0 ** -8]]), np.array([[-0.5]]))
+    x = np.full((1, 64), 0x3C00, dtype=np.uint16)
+    assert oracle.affine_gemv(_blob(tr), 1, 64, x, x_f16=True)[0, 0] == -24.125
+
+
+def test_gemv_f16_input_decodes_like_numpy():
+    # f16 x decoded by the oracle equals numpy's float16 values (normal,
+    # subnormal and signed zero inputs), through a one-hot weight row
+    rows, cols = 1, 64
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    vals = np.array([1.5, -2.0 ** -20, 65504.0, -0.0, 2.0 ** -24, 0.333], dtype=np.float16)
+    for k, v in enumerate(vals):
+        codes[:] = 0
+        codes[0, k] = 1
+        tr = synth.affine_triplet_custom(codes, np.array([[1.0]]), np.array([[0.0]]))
+        x = np.zeros((1, cols), dtype=np.uint16)
+        x[0, k] = vals.view(np.uint16)[k]
+        assert oracle.affine_gemv(_blob(tr), rows, cols, x, x_f16=True)[0, 0] == float(v)
+
+
+def test_embed_row_double_rounding_pin():
+    # embed_row_bytes rounds q*scale + bias to f32 first, then to f16.
+    # q = 226, scale = 145 * 2^-26 (BF16 0x3611), bias = 1.0: the exact value
+    # 1 + 2^-11 + 2^-25 becomes the f16 midpoint 1 + 2^-11 in f32, which ties
+    # to even (0x3C00); rounding the exact value straight to f16 would give
+    # 0x3C01.  In BF16 (ulp 2^-7 at 1) both readings give 1.0 (0x3F80).
+    cols = 64
+    codes = np.full((1, cols), 226, dtype=np.uint8)
+    tr = synth.affine_triplet_custom(codes, np.array([[145 * 2.0 ** -26]]), np.array([[1.0]]))
+    assert int(tr.scales[0, 0]) == 0x3611 and int(tr.biases[0, 0]) == 0x3F80
+    blob = _blob(tr)
+    assert np.all(oracle.affine_embed_row(blob, 1, cols, 0, out_f16=True) == 0x3C00)
+    assert np.all(oracle.affine_embed_row(blob, 1, cols, 0, out_f16=False) == 0x3F80)
+
+
+def test_embed_row_closed_forms():
+    # q = 0 -> the bias itself; q = 255, s = 2^-8, b = -0.5 -> 127/256 (0x37F0)
+    cols = 128
+    codes = np.zeros((2, cols), dtype=np.uint8)
+    codes[1, :] = 255
+    sc = np.array([[1e-3, 5e-3], [2.0 ** -8, 2.0 ** -8]])
+    bi = np.array([[-0.5, 0.25], [-0.5, -0.5]])
+    blob = _blob(synth.affine_triplet_custom(codes, sc, bi))
+    r0 = oracle.affine_embed_row(blob, 2, cols, 0)
+    assert np.all(r0[:64] == 0xB800) and np.all(r0[64:] == 0x3400)
+    assert np.all(oracle.affine_embed_row(blob, 2, cols, 1) == 0x37F0)
+    assert np.all(oracle.affine_embed_row(blob, 2, cols, 1, out_f16=False) == 0x3EFE)
+
+
+def test_embed_row_matches_numpy_f32_arithmetic():
+    # numpy's float32 arithmetic and float16 / torch's bfloat16 conversions
+    # (independent implementations) agree with the oracle bit for bit
+    rows, cols = 40, 256
+    tr = synth.affine_triplet(rows, cols, key=(81, 0, 0))
+    blob = _blob(tr)
+    q = tr.codes.view(np.uint8).reshape(rows, cols).astype(np.float32)
+    s = np.repeat(_bf16(tr.scales), 64, axis=1).astype(np.float32)
+    b = np.repeat(_bf16(tr.biases), 64, axis=1).astype(np.float32)
+    v = q * s + b  # float32 product, then float32 sum
+    want16 = v.astype(np.float16).view(np.uint16)
+    wantb = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for r in (0, 1, 17, rows - 1):
+        assert np.array_equal(oracle.affine_embed_row(blob, rows, cols, r), want16[r])
+        assert np.array_equal(oracle.affine_embed_row(blob, rows, cols, r, out_f16=False),
+                              wantb[r])
+
+
+def test_bf16_encoder_matches_torch():
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 4000),
+                           np.array([0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8,
+                                     3.3895314e38, np.inf, -np.inf, 1e-40], dtype=np.float32)])
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16_rne(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, want)
