@@ -19,6 +19,8 @@ part of the path on its own workload:
   affine_gemv_1024       single 1024x1024 affine GEMV, batch 1
   affine_lm_head         the tied LM heads (151936 x 1024 / x 2048) at M = 1, 4, 16:
                          single large GEMVs, weights streamed past the 256 MB MALL
+  affine_f16             the same 151936 x 1024 GEMV with f16 activations (the
+                         page's Metal dtype) and the device tied-embedding lookup
   q4_0_ffn_pair          Whisper-base FFN pair (fc1 2048x512, fc2 512x2048), M = 1, 4
   qwen3_1_7b_step        Qwen3-1.7B-shaped decode step at M = 1, 4, 10, 16
                          (graphs of one launch per stage: same-input GEMVs grouped)
@@ -277,6 +279,36 @@ def row_affine_lm_head(qd):
     return out
 
 
+def row_affine_f16(qd):
+    """The f16-activation GEMV (the page's Metal dtype) on the 151936 x 1024
+    LM head at M = 1, 4, 16 (two alternating copies, as for BF16), and the
+    device lookup of 16 tied-embedding rows of that table as f16."""
+    import numpy as np
+    import torch
+    import synth
+    rows, cols = 151936, 1024
+    nbytes = qd.affine_i8_g64_bytes(rows, cols)
+    blobs = [affine_blob(qd, rows, cols, (3, 28, 7 + k)) for k in range(2)]
+    res = {"weight_bytes": nbytes}
+    for m in (1, 4, 16):
+        bits = synth.x_f16(m, cols, key=(3, 30, m))
+        x = torch.from_numpy(bits.view(np.int16).copy()).to(DEV).view(torch.float16)
+        y = torch.empty((m, rows), dtype=torch.float16, device=DEV)
+        g = capture(lambda: [qd.qgemv_affine_i8_g64_f16(blobs[i % 2], rows, cols, x, y, m)
+                             for i in range(8)])
+        ms = event_time(g.replay, 5, 2) / 8
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[f"M{m}"] = {"us": ms * 1e3, "GBps": gbps, "hbm_peak_frac": gbps / HBM_PEAK_GBPS}
+    ids = [int(t) for t in np.linspace(0, rows - 1, 16)]
+    emb = torch.empty((16, cols), dtype=torch.float16, device=DEV)
+    g = capture(lambda: [qd.affine_i8_g64_embed_rows(blobs[0], rows, cols, ids, emb)
+                         for _ in range(8)])
+    res["embed_rows_16_tokens_us"] = event_time(g.replay, 20, 2) / 8 * 1e3
+    del blobs
+    torch.cuda.empty_cache()
+    return res
+
+
 def q4_0_from_f32(qd, w_host, rows, cols):
     import torch
     wq = torch.empty(qd.q4_0_bytes(rows, cols), dtype=torch.uint8, device=DEV)
@@ -444,7 +476,7 @@ def row_q4_0_bake(qd):
             "hbm_peak_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
-ROWS = ("affine_gemv_1024", "affine_lm_head", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
+ROWS = ("affine_gemv_1024", "affine_lm_head", "affine_f16", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
         "whisper_large_decoder", "q4_0_bake")
 
 

@@ -131,6 +131,30 @@ qd_status qgemv_affine_i8_g64_group(const qd_affine_gemv_item *items, int64_t n_
                                     int64_t cols, const void *x_bf16, int64_t m,
                                     void *stream);
 
+/* The same GEMV with f16 activations, the dtype of the page's Metal GEMV
+ * (turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::gemv
+ * reads and writes f16 buffers): x f16 [m, cols], y f16 [m, rows] rounded to
+ * nearest even from the fp32 accumulator (f16 subnormals kept, overflow to
+ * infinity); scales and biases stay BF16 in the blob.  Arguments, alignment
+ * and status codes as qgemv_affine_i8_g64. */
+qd_status qgemv_affine_i8_g64_f16(const void *w_packed, int64_t rows, int64_t cols,
+                                  const void *x_f16, void *y_f16, int64_t m, void *stream);
+
+/* Tied-embedding rows on the device (turbospark-runtime 0.3.0,
+ * qwen3_asr_metal.rs -- embed_row_bytes): out[i, c] = q*scale + bias of row
+ * token_ids[i] of the packed matrix, evaluated in f32 (the product is exact,
+ * the sum rounds once) and rounded to f16 (out_f16 = 1, the page's store) or
+ * BF16 (out_f16 = 0), nearest even -- bit-exact.
+ *   w_packed   device, the affine blob for [rows, cols], 16-byte aligned
+ *   token_ids  host, n ids, each 0 <= id < rows (QD_EINVAL otherwise)
+ *   n          1 <= n <= 16
+ *   out        device, 16-bit [n, cols], 8-byte aligned; must not overlap
+ *              the blob
+ * Requires cols % 64 == 0 and cols <= 8192 (QD_ESHAPE). */
+qd_status affine_i8_g64_embed_rows(const void *w_packed, int64_t rows, int64_t cols,
+                                   const int64_t *token_ids, int64_t n, void *out,
+                                   int32_t out_f16, void *stream);
+
 /* ---- one decode step of affine GEMVs in a single launch ------------------ */
 
 /* One GEMV of a decode step: y[m, rows] = x[m, cols] W^T (same operation,

@@ -31,7 +31,7 @@ EXPORTS = (
     "qgemv_q4_0", "qgemv_q4_0_group", "qgemm_q4_0_prefill", "q4_0_quantize",
     "qgemv_affine_i8_g64_step_workspace_bytes", "qgemv_affine_i8_g64_step_plan",
     "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
-    "qd_stream_read",
+    "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
 )
 
 
@@ -111,11 +111,14 @@ def lib() -> ctypes.CDLL:
         L.qgemv_affine_i8_g64_step_run.argtypes = [PLAN, P]
         L.qgemv_affine_i8_g64_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
         L.qd_stream_read.argtypes = [P, SZ, P, P]
+        L.qgemv_affine_i8_g64_f16.argtypes = [P, I64, I64, P, P, I64, P]
+        L.affine_i8_g64_embed_rows.argtypes = [P, I64, I64, ctypes.POINTER(ctypes.c_int64), I64,
+                                               P, ctypes.c_int32, P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
                   "qgemv_affine_i8_g64_group", "qgemv_q4_0_group",
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
                   "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
-                  "qd_stream_read"):
+                  "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -168,6 +171,21 @@ def qgemv_affine_i8_g64(w_packed, rows: int, cols: int, x_bf16, y_bf16, m: int,
                         stream=None) -> None:
     _check("qgemv_affine_i8_g64", lib().qgemv_affine_i8_g64(
         _ptr(w_packed), rows, cols, _ptr(x_bf16), _ptr(y_bf16), m, _stream(stream)))
+
+
+def qgemv_affine_i8_g64_f16(w_packed, rows: int, cols: int, x_f16, y_f16, m: int,
+                            stream=None) -> None:
+    _check("qgemv_affine_i8_g64_f16", lib().qgemv_affine_i8_g64_f16(
+        _ptr(w_packed), rows, cols, _ptr(x_f16), _ptr(y_f16), m, _stream(stream)))
+
+
+def affine_i8_g64_embed_rows(w_packed, rows: int, cols: int, token_ids, out,
+                             out_f16: bool = True, stream=None) -> None:
+    """token_ids: host sequence of ints (1..16 of them)."""
+    ids = (ctypes.c_int64 * len(token_ids))(*[int(t) for t in token_ids])
+    _check("affine_i8_g64_embed_rows", lib().affine_i8_g64_embed_rows(
+        _ptr(w_packed), rows, cols, ids, len(token_ids), _ptr(out), 1 if out_f16 else 0,
+        _stream(stream)))
 
 
 def qgemv_q4_0(w_q4_0, rows: int, cols: int, x, y, m: int, stream=None) -> None:

@@ -5,8 +5,10 @@
 // dequantisation, Qwen3AsrMetalEngine::gemv for the GEMV), regrouped per
 // 64-column group g as
 //   y[t, r] = sum_g s[r,g] * (sum_{c in g} q*x) + b[r,g] * (sum_{c in g} x)
-// Codes are exact in fp32 and in BF16, accumulation is fp32, the output is
-// rounded once to BF16 (nearest even).
+// Codes are exact in fp32, BF16 and f16, accumulation is fp32, the output is
+// rounded once (nearest even) to the activation type: BF16, or f16 as in the
+// page's Metal GEMV.  Also here: the tied-embedding row lookup
+// (embed_row_bytes) on the device.
 //
 // Two kernels: the matrix-core kernel serves every batch size (one MFMA pair
 // per group covers all 16 token rows; the VALU only converts codes and
@@ -46,15 +48,36 @@ namespace {
 constexpr int kMW = 8;
 constexpr int kMThreads = kMW * kWave;
 
+// Activation type of the matrix-core kernel: x and y BF16 (the configs) or
+// f16 (the page's Metal GEMV); scales and biases are BF16 in both.
+struct ActBf16 {
+  typedef bf16x8 vec;
+  static constexpr uint32_t kOnes = 0x3F803F80u;  // two 1.0
+  static __device__ __forceinline__ vec codes(uint32_t a, uint32_t b) { return codes8_bf16(a, b); }
+  static __device__ __forceinline__ floatx4 mfma(vec a, vec b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t store(float v) { return f32_to_bf16(v); }
+};
+struct ActF16 {
+  typedef halfx8 vec;
+  static constexpr uint32_t kOnes = 0x3C003C00u;
+  static __device__ __forceinline__ vec codes(uint32_t a, uint32_t b) { return codes8_f16(a, b); }
+  static __device__ __forceinline__ floatx4 mfma(vec a, vec b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t store(float v) { return f32_to_f16(v); }
+};
+
 // Scales and biases: with CH (the group count a multiple of 4) each buffer
 // of U = 4 groups also loads, per 16-row block, one 8-byte piece per lane --
 // lanes n and 32+n the scales of row n for the buffer's four groups, lanes
 // 16+n and 48+n its biases -- and ds_bpermute hands each lane the pair it
 // needs; without CH every lane loads its row's scale and bias per group.
-template <int R, int U, bool CH>
+template <int R, int U, bool CH, class A>
 struct MGroup {
   u32x4 q[U][R];
-  bf16x8 xa[U], xb[U];
+  typename A::vec xa[U], xb[U];
   uint16_t sc[CH ? 1 : U][R], bi[CH ? 1 : U][R];
   u32x2 sbv[R];
 };
@@ -113,8 +136,8 @@ __device__ __forceinline__ void mc_next(MCursor &c, const MShape &S, int &left) 
 // Addresses are a wave-uniform base (the tile's first row, the group) plus a
 // 32-bit per-lane offset, so the loads take the scalar-base form.  Rows past
 // the end of the matrix are clamped to its last row.
-template <int R, int U, bool CH, bool XL>
-__device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const MShape &S,
+template <int R, int U, bool CH, bool XL, class A>
+__device__ __forceinline__ void mg_issue(MGroup<R, U, CH, A> &G, MCursor &c, const MShape &S,
                                          const AffineGroup &grp,
                                          const QD_GLOBAL uint16_t *x, uint32_t xoff,
                                          const uint8_t *xl, uint32_t xloff, int lane,
@@ -123,12 +146,12 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const 
   for (int u = 0; u < U; ++u) {
     if constexpr (XL) {
       const uint8_t *xp = xl + xloff + 128 * c.g;
-      G.xa[u] = *(const bf16x8 *)(xp);
-      G.xb[u] = *(const bf16x8 *)(xp + 16);
+      G.xa[u] = *(const typename A::vec *)(xp);
+      G.xb[u] = *(const typename A::vec *)(xp + 16);
     } else {
       const QD_GLOBAL uint8_t *xg = (const QD_GLOBAL uint8_t *)(x + 64 * c.g);
-      G.xa[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff));
-      G.xb[u] = __builtin_bit_cast(bf16x8, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
+      G.xa[u] = __builtin_bit_cast(typename A::vec, *(const QD_GLOBAL u32x4 *)(xg + xoff));
+      G.xb[u] = __builtin_bit_cast(typename A::vec, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
     }
     const MItem it = item_of_tile<R>(grp, S.cols, S.groups, S.ts0 + c.j * S.stride);
     const int trow = it.trow;
@@ -159,7 +182,7 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH> &G, MCursor &c, const 
 
 // Output of one finished tile (KS = 1): lane holds tokens 4*(lane/16)+v of
 // weight row lane%16 of each 16-row block.
-template <int R>
+template <int R, class A>
 __device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S,
                                          const AffineGroup &grp, int j, int m, int lane) {
   const MItem it = item_of_tile<R>(grp, S.cols, S.groups, S.ts0 + j * S.stride);
@@ -170,7 +193,7 @@ __device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S,
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = 4 * (lane >> 4) + v;
-      if (t < m && n < it.rows) it.y[(size_t)t * it.rows + n] = f32_to_bf16(acc[r][v]);
+      if (t < m && n < it.rows) it.y[(size_t)t * it.rows + n] = A::store(acc[r][v]);
       acc[r][v] = 0.f;
     }
   }
@@ -178,10 +201,10 @@ __device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S,
 
 // Items past the end of the walk (padding up to a whole buffer) are
 // computed with zero scale and bias.
-template <int R, int U, bool CH, bool STORE>
-__device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&acc)[R],
+template <int R, int U, bool CH, bool STORE, class A>
+__device__ __forceinline__ void mg_compute(const MGroup<R, U, CH, A> &G, floatx4 (&acc)[R],
                                            MCursor &c, const MShape &S, const AffineGroup &grp,
-                                           int &left, int m, int lane, bf16x8 ones) {
+                                           int &left, int m, int lane, typename A::vec ones) {
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   const int src4 = (4 * (lane & 15) + (lane >> 4)) * 4;
   const int srcs = (lane & 15) * 4, srcb = srcs + 64;
@@ -189,8 +212,8 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int valid = left > 0;  // wave-uniform
-    floatx4 Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xa[u], ones, z, 0, 0, 0);
-    Sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xb[u], ones, Sx, 0, 0, 0);
+    floatx4 Sx = A::mfma(G.xa[u], ones, z);
+    Sx = A::mfma(G.xb[u], ones, Sx);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // lane 16*g4 + n takes row n's quarter g4 from lane 4*n + g4
@@ -199,9 +222,8 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&
                        (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.y),
                        (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.z),
                        (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.w)};
-      floatx4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xa[u], codes8_bf16(q.x, q.y), z,
-                                                          0, 0, 0);
-      P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(G.xb[u], codes8_bf16(q.z, q.w), P, 0, 0, 0);
+      floatx4 P = A::mfma(G.xa[u], A::codes(q.x, q.y), z);
+      P = A::mfma(G.xb[u], A::codes(q.z, q.w), P);
       float s, b;
       if constexpr (CH) {
         if ((u & 1) == 0) {
@@ -220,7 +242,7 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[r][v] = fmaf(s, P[v], fmaf(b, Sx[v], acc[r][v]));
     }
-    if (STORE && valid && c.g == S.gb - 1) mg_store(acc, S, grp, c.j, m, lane);
+    if (STORE && valid && c.g == S.gb - 1) mg_store<R, A>(acc, S, grp, c.j, m, lane);
     left -= valid;
     const int g = c.g + valid;
     const int wrap = g == S.gb;
@@ -229,7 +251,7 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH> &G, floatx4 (&
   }
 }
 
-// x [m][cols] BF16 into LDS, rows padded to 2*cols + 16 bytes (the 16
+// x [m][cols] (16-bit values) into LDS, rows padded to 2*cols + 16 bytes (the 16
 // token rows of a fragment read then start in different banks).
 __device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x, int m,
                                         int cols) {
@@ -255,7 +277,7 @@ __device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x
   }
 }
 
-template <int R, int U, int KS, bool CH, bool XL>
+template <int R, int U, int KS, bool CH, bool XL, class Act>
 __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     const AffineGroup grp, int cols, const uint16_t *__restrict__ x_, int m) {
   constexpr int SLOTS = kMW / KS;
@@ -287,15 +309,15 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   floatx4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bf16x8 ones = __builtin_bit_cast(
-      bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const typename Act::vec ones = __builtin_bit_cast(
+      typename Act::vec, u32x4{Act::kOnes, Act::kOnes, Act::kOnes, Act::kOnes});
   MCursor ci, cc;  // issue and compute cursors
   ci.j = cc.j = 0;
   ci.g = cc.g = S.ga;
   int li = n, lc = n;
-  MGroup<R, U, CH> A, B;
+  MGroup<R, U, CH, Act> A, B;
   // the first buffer's codes and scales are in flight while x is staged
-  if (n > 0) mg_issue<R, U, CH, false>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+  if (n > 0) mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
   if constexpr (XL) {
     stage_x(xl, x, m, cols);
     // LDS writes done, then the barrier (global loads stay in flight)
@@ -307,17 +329,17 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     // is issued before the current one is consumed.
     for (;;) {
       if (lc <= U) {
-        mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, grp, lc, m, lane, ones);
+        mg_compute<R, U, CH, KS == 1, Act>(A, acc, cc, S, grp, lc, m, lane, ones);
         break;
       }
-      mg_issue<R, U, CH, XL>(B, ci, S, grp, x, xoff, xl, xloff, lane, li);
-      mg_compute<R, U, CH, KS == 1>(A, acc, cc, S, grp, lc, m, lane, ones);
+      mg_issue<R, U, CH, XL, Act>(B, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_compute<R, U, CH, KS == 1, Act>(A, acc, cc, S, grp, lc, m, lane, ones);
       if (lc <= U) {
-        mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, grp, lc, m, lane, ones);
+        mg_compute<R, U, CH, KS == 1, Act>(B, acc, cc, S, grp, lc, m, lane, ones);
         break;
       }
-      mg_issue<R, U, CH, XL>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
-      mg_compute<R, U, CH, KS == 1>(B, acc, cc, S, grp, lc, m, lane, ones);
+      mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_compute<R, U, CH, KS == 1, Act>(B, acc, cc, S, grp, lc, m, lane, ones);
     }
   }
   if constexpr (KS > 1) {
@@ -337,7 +359,7 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
       const MItem it = item_of_tile<R>(grp, cols, S.groups, tile);
       const int tt = 4 * (l >> 4) + v;
       const int nn = it.trow + 16 * r + (l & 15);
-      if (tt < m && nn < it.rows) it.y[(size_t)tt * it.rows + nn] = f32_to_bf16(sum);
+      if (tt < m && nn < it.rows) it.y[(size_t)tt * it.rows + nn] = Act::store(sum);
     }
   }
 }
@@ -354,7 +376,7 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
 // CU then still fit the 160 KiB of LDS).
 constexpr int kXlBudget = 72 * 1024;
 
-template <int KS, bool CH, bool XL>
+template <int KS, bool CH, bool XL, class Act>
 hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
                           hipStream_t stream) {
   constexpr int R = QD_AFFINE_MFMA_R;
@@ -364,28 +386,28 @@ hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int
     static bool raised = false;
     if (!raised) {
       hipError_t e = hipFuncSetAttribute(
-          (const void *)affine_gemv_mfma_kernel<R, U, KS, CH, XL>,
+          (const void *)affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act>,
           hipFuncAttributeMaxDynamicSharedMemorySize, kXlBudget);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
-  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL>), dim3(grid), dim3(kMThreads),
+  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act>), dim3(grid), dim3(kMThreads),
                      lds, stream, g, cols, x, m);
   return hipGetLastError();
 }
 
 // Only the streaming walk (KS = 1) stages x: there a workgroup reuses it over
 // many tiles, while a split workgroup reads each element of x once anyway.
-template <int KS, bool CH>
+template <int KS, bool CH, class Act>
 hipError_t launch_mfma_xl(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
                           hipStream_t stream) {
   if (KS == 1 && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
-    return launch_mfma_ks<KS, CH, true>(g, cols, x, m, grid, stream);
-  return launch_mfma_ks<KS, CH, false>(g, cols, x, m, grid, stream);
+    return launch_mfma_ks<KS, CH, true, Act>(g, cols, x, m, grid, stream);
+  return launch_mfma_ks<KS, CH, false, Act>(g, cols, x, m, grid, stream);
 }
 
-template <bool CH>
+template <bool CH, class Act>
 hipError_t launch_mfma_ch(AffineGroup g, int cols, const uint16_t *x, int m,
                           hipStream_t stream) {
   // KS: split K over up to 8 waves until the launch gives about
@@ -406,20 +428,21 @@ hipError_t launch_mfma_ch(AffineGroup g, int cols, const uint16_t *x, int m,
     if (cus < 1) cus = 256;
     long grid = (ntiles + kMW - 1) / kMW;
     if (grid > (long)kStreamWgsPerCu * cus) grid = (long)kStreamWgsPerCu * cus;
-    return launch_mfma_xl<1, CH>(g, cols, x, m, (int)grid, stream);
+    return launch_mfma_xl<1, CH, Act>(g, cols, x, m, (int)grid, stream);
   }
   const int grid = (int)((ntiles * ks + kMW - 1) / kMW);
   switch (ks) {
-    case 2: return launch_mfma_xl<2, CH>(g, cols, x, m, grid, stream);
-    case 4: return launch_mfma_xl<4, CH>(g, cols, x, m, grid, stream);
-    default: return launch_mfma_xl<8, CH>(g, cols, x, m, grid, stream);
+    case 2: return launch_mfma_xl<2, CH, Act>(g, cols, x, m, grid, stream);
+    case 4: return launch_mfma_xl<4, CH, Act>(g, cols, x, m, grid, stream);
+    default: return launch_mfma_xl<8, CH, Act>(g, cols, x, m, grid, stream);
   }
 }
 
+template <class Act>
 hipError_t launch_mfma(const AffineGroup &g, int cols, const uint16_t *x, int m,
                        hipStream_t stream) {
-  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true>(g, cols, x, m, stream);
-  return launch_mfma_ch<false>(g, cols, x, m, stream);
+  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true, Act>(g, cols, x, m, stream);
+  return launch_mfma_ch<false, Act>(g, cols, x, m, stream);
 }
 
 // ---- batch 1: streaming kernel ---------------------------------------------
@@ -532,10 +555,57 @@ __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
   }
 }
 
+// ---- tied-embedding rows ------------------------------------------------------
+//
+// out[i, c] = round16(fl32(q[t_i, c] * s + b)) (embed_row_bytes): q*s is
+// exact in fp32, so one fused multiply-add gives the page's f32 value; it is
+// then rounded to f16 or BF16.  Each thread handles four columns of one
+// group; blockIdx.y is the token.
+constexpr int kEmbedThreads = 256;
+
+__global__ __launch_bounds__(kEmbedThreads) void affine_embed_rows_kernel(
+    const uint8_t *__restrict__ w_, int rows, int cols, const EmbedTokens tk,
+    uint16_t *__restrict__ out_, int f16) {
+  const int c = (blockIdx.x * kEmbedThreads + threadIdx.x) * 4;
+  if (c >= cols) return;
+  const int i = blockIdx.y;
+  const size_t tok = (size_t)tk.t[i];
+  const QD_GLOBAL uint8_t *w = gp(w_);
+  const int groups = cols >> 6;
+  const uint32_t q = *(const QD_GLOBAL uint32_t *)(w + tok * cols + c);
+  const QD_GLOBAL uint16_t *sc = (const QD_GLOBAL uint16_t *)(w + (size_t)rows * cols);
+  const size_t gi = tok * groups + (c >> 6);
+  const float s = bf16_to_f32(sc[gi]);
+  const float b = bf16_to_f32(sc[(size_t)rows * groups + gi]);
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float v = fmaf((float)((q >> (8 * k)) & 0xffu), s, b);
+    // Two roundings, as the page has them: the f32 value, then the 16-bit
+    // store.  The empty asm makes v opaque: the compiler would otherwise
+    // fuse the multiply-add and the f16 conversion into one
+    // v_fma_mixlo_f16, which rounds the exact value to f16 once and can
+    // differ in the last bit.
+    __asm__("" : "+v"(v));
+    o[k] = f16 ? f32_to_f16(v) : f32_to_bf16(v);
+  }
+  *(QD_GLOBAL u32x2 *)(gp(out_) + (size_t)i * cols + c) =
+      u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+}
+
 }  // namespace
 
-hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
+hipError_t launch_affine_embed_rows(const uint8_t *w, int rows, int cols, const EmbedTokens &tk,
+                                    uint16_t *out, bool f16, hipStream_t stream) {
+  dim3 grid((cols / 4 + kEmbedThreads - 1) / kEmbedThreads, tk.n);
+  hipLaunchKernelGGL(affine_embed_rows_kernel, grid, dim3(kEmbedThreads), 0, stream, w, rows,
+                     cols, tk, out, f16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m, bool f16,
                               hipStream_t stream) {
+  if (f16) return launch_mfma<ActF16>(g, cols, x, m, stream);
   // Batch 1 takes the VALU streaming kernel only for a single very large
   // matrix (LM heads), where its 1 KiB-per-row loads keep the most bytes in
   // flight; below that the matrix-core kernel's K split gives more waves.
@@ -556,7 +626,7 @@ hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
                        stream, w, rows, cols, x, y);
     return hipGetLastError();
   }
-  return launch_mfma(g, cols, x, m, stream);
+  return launch_mfma<ActBf16>(g, cols, x, m, stream);
 }
 
 }  // namespace qd

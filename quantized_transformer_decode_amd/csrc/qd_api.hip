@@ -258,16 +258,11 @@ qd_status affine_i8_g64_pack(const void *codes_u32, const void *scales_bf16,
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 
-qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
-                              const void *x_bf16, void *y_bf16, int64_t m,
-                              void *stream) {
-  const qd_affine_gemv_item item = {w_packed, y_bf16, rows};
-  return qgemv_affine_i8_g64_group(&item, 1, cols, x_bf16, m, stream);
-}
+}  // extern "C"
 
-qd_status qgemv_affine_i8_g64_group(const qd_affine_gemv_item *items, int64_t n_items,
-                                    int64_t cols, const void *x_bf16, int64_t m,
-                                    void *stream) {
+// The affine GEMVs of one launch (shared input x), activations BF16 or f16.
+static qd_status affine_group(const qd_affine_gemv_item *items, int64_t n_items, int64_t cols,
+                              const void *x_bf16, int64_t m, bool f16, void *stream) {
   if (!items || !x_bf16 || n_items < 1 || n_items > qd::kMaxGroup) return QD_EINVAL;
   if (m < 1 || m > 16 || cols < 1) return QD_EINVAL;
   if (cols % 64 != 0 || cols > kMaxGemvCols) return QD_ESHAPE;
@@ -298,8 +293,52 @@ qd_status qgemv_affine_i8_g64_group(const qd_affine_gemv_item *items, int64_t n_
     g.y[k] = (uint16_t *)items[k].y_bf16;
     g.rows[k] = (int)items[k].rows;
   }
-  hipError_t e = qd::launch_affine_gemv(g, (int)cols, (const uint16_t *)x_bf16, (int)m,
+  hipError_t e = qd::launch_affine_gemv(g, (int)cols, (const uint16_t *)x_bf16, (int)m, f16,
                                         (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+extern "C" {
+
+qd_status qgemv_affine_i8_g64(const void *w_packed, int64_t rows, int64_t cols,
+                              const void *x_bf16, void *y_bf16, int64_t m,
+                              void *stream) {
+  const qd_affine_gemv_item item = {w_packed, y_bf16, rows};
+  return affine_group(&item, 1, cols, x_bf16, m, false, stream);
+}
+
+qd_status qgemv_affine_i8_g64_group(const qd_affine_gemv_item *items, int64_t n_items,
+                                    int64_t cols, const void *x_bf16, int64_t m,
+                                    void *stream) {
+  return affine_group(items, n_items, cols, x_bf16, m, false, stream);
+}
+
+qd_status qgemv_affine_i8_g64_f16(const void *w_packed, int64_t rows, int64_t cols,
+                                  const void *x_f16, void *y_f16, int64_t m, void *stream) {
+  const qd_affine_gemv_item item = {w_packed, y_f16, rows};
+  return affine_group(&item, 1, cols, x_f16, m, true, stream);
+}
+
+qd_status affine_i8_g64_embed_rows(const void *w_packed, int64_t rows, int64_t cols,
+                                   const int64_t *token_ids, int64_t n, void *out,
+                                   int32_t out_f16, void *stream) {
+  if (!w_packed || !token_ids || !out) return QD_EINVAL;
+  if (n < 1 || n > qd::kMaxEmbedTokens || (out_f16 != 0 && out_f16 != 1)) return QD_EINVAL;
+  if (rows < 1 || rows > kMaxRows || cols < 1) return QD_EINVAL;
+  if (cols % 64 != 0 || cols > kMaxGemvCols) return QD_ESHAPE;
+  if (!aligned(w_packed, 16) || !aligned(out, 8)) return QD_EALIGN;
+  qd::EmbedTokens tk = {};
+  tk.n = (int)n;
+  for (int64_t i = 0; i < n; ++i) {
+    if (token_ids[i] < 0 || token_ids[i] >= rows) return QD_EINVAL;
+    tk.t[i] = (int)token_ids[i];
+  }
+  if (overlap(out, (size_t)n * cols * 2, w_packed, affine_bytes(rows, cols))) return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_affine_embed_rows((const uint8_t *)w_packed, (int)rows, (int)cols,
+                                              tk, (uint16_t *)out, out_f16 == 1,
+                                              (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 

@@ -23,6 +23,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// binary32 -> binary16, round to nearest even (v_cvt_f16_f32; f16
+// subnormals are kept).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
   return (float)h;
@@ -102,6 +108,14 @@ __device__ __forceinline__ bf16x8 codes8_bf16(uint32_t a, uint32_t b) {
   const floatx8 f = {ubyte<0>(a), ubyte<1>(a), ubyte<2>(a), ubyte<3>(a),
                      ubyte<0>(b), ubyte<1>(b), ubyte<2>(b), ubyte<3>(b)};
   return __builtin_convertvector(f, bf16x8);
+}
+
+// The same as f16 (0..255 are exact in f16 too).
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ halfx8 codes8_f16(uint32_t a, uint32_t b) {
+  const floatx8 f = {ubyte<0>(a), ubyte<1>(a), ubyte<2>(a), ubyte<3>(a),
+                     ubyte<0>(b), ubyte<1>(b), ubyte<2>(b), ubyte<3>(b)};
+  return __builtin_convertvector(f, halfx8);
 }
 
 // LDS layout of an activation vector for the wave-per-1KiB-chunk GEMVs:

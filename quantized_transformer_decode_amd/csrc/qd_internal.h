@@ -30,8 +30,18 @@ struct Q40Group {
   int n;
 };
 
-hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
+// x and y BF16, or f16 with f16 = true (scales and biases BF16 in both).
+hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m, bool f16,
                               hipStream_t stream);
+
+// Tied-embedding rows: token ids t[0..n) (already checked to be < rows).
+constexpr int kMaxEmbedTokens = 16;
+struct EmbedTokens {
+  int t[kMaxEmbedTokens];
+  int n;
+};
+hipError_t launch_affine_embed_rows(const uint8_t *w, int rows, int cols, const EmbedTokens &tk,
+                                    uint16_t *out, bool f16, hipStream_t stream);
 
 hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
                             hipStream_t stream);

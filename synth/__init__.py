@@ -101,6 +101,14 @@ def x_bf16(m: int, cols: int, key=(0, 0, 0)) -> np.ndarray:
     return to_bf16_bits(rng(c, l, mm, K_X).standard_normal((m, cols)).astype(np.float32))
 
 
+def x_f16(m: int, cols: int, key=(0, 0, 0)) -> np.ndarray:
+    """Activations f16(N(0, 1)) as uint16 bits [m, cols] (numpy's rounding
+    to nearest even)."""
+    c, l, mm = key
+    return rng(c, l, mm, K_X).standard_normal((m, cols)).astype(np.float32).astype(
+        np.float16).view(np.uint16)
+
+
 def x_f32(m: int, cols: int, key=(0, 0, 0)) -> np.ndarray:
     """Activations f32 N(0, 1) [m, cols]."""
     c, l, mm = key

@@ -93,6 +93,48 @@ def check_bf16_output(got_f64: np.ndarray, ref_f64: np.ndarray, what: str = "",
     return pre
 
 
+def dev_f16(bits: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.float16)
+
+
+def f16_rounding_interval(got: np.ndarray):
+    """[lo, hi] of the reals that round (nearest even) to each f16 value
+    (finite values; subnormal spacing 2^-24)."""
+    g = np.asarray(got, dtype=np.float64)
+    a = np.abs(g)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    u = 2.0 ** (e - 10)                                   # spacing in |g|'s binade
+    pow2 = (a >= 2.0 ** -13) & (a == 2.0 ** np.floor(np.log2(np.maximum(a, 1e-300))))
+    toward0 = np.where(pow2, u / 4, u / 2)                # the binade below is twice as fine
+    away = u / 2
+    lo = np.where(g >= 0, g - toward0, g - away)
+    hi = np.where(g >= 0, g + away, g + toward0)
+    return lo, hi
+
+
+def check_f16_output(got_f64: np.ndarray, ref_f64: np.ndarray, what: str = "",
+                     noise: float = 1e-5) -> float:
+    """f16 outputs: as check_bf16_output with f16's rounding (11 significant
+    bits): each stored value is the nearest-even rounding of the exact value
+    up to `noise` (fp32 accumulation), and the stored values are within 2^-11
+    (+ noise) normwise."""
+    got = np.asarray(got_f64, dtype=np.float64)
+    ref = np.asarray(ref_f64, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite outputs"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    lo, hi = f16_rounding_interval(got)
+    dist = np.maximum(0.0, np.maximum(lo - ref, ref - hi))
+    pre = float(dist.max()) / scale if scale > 0 else float(dist.max())
+    assert pre <= TOL_BF16, f"{what}: pre-rounding normwise {pre:.3e} > {TOL_BF16}"
+    bad = dist > noise * scale
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs are not the rounding of " \
+        f"the exact value, e.g. got {got[bad][:3]} ref {ref[bad][:3]}"
+    stored = oracle.normwise_error(got, ref)
+    assert stored <= 2.0 ** -11 + noise, f"{what}: stored normwise {stored:.3e}"
+    return pre
+
+
 def check_f32_output(got: np.ndarray, ref_f64: np.ndarray, what: str = "") -> float:
     err = oracle.normwise_error(got, ref_f64)
     assert err <= TOL_F32, f"{what}: normwise {err:.3e} > {TOL_F32}"

@@ -87,6 +87,37 @@ def test_errors_affine_gemv():
     assert ok  # the valid form is exercised by test_valid_args_reach_device_check
 
 
+def test_errors_affine_gemv_f16():
+    # the f16 variant validates exactly like the BF16 one
+    f = "qgemv_affine_i8_g64_f16"
+    assert _call(f, None, 64, 1024, B, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, B, C, 17, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1000, B, C, 1, None) == qd.QD_ESHAPE
+    assert _call(f, A, 64, 1024, B + 2, C, 1, None) == qd.QD_EALIGN
+    assert _call(f, A, 64, 1024, B, A + 64, 1, None) == qd.QD_EINVAL
+
+
+def _ids(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_errors_embed_rows():
+    f = "affine_i8_g64_embed_rows"
+    ids = _ids(0, 5, 63)
+    assert _call(f, None, 64, 1024, ids, 3, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, None, 3, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, ids, 3, None, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, ids, 0, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, _ids(*range(17)), 17, C, 1, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, ids, 3, C, 2, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1024, _ids(0, 64), 2, C, 1, None) == qd.QD_EINVAL  # id >= rows
+    assert _call(f, A, 64, 1024, _ids(-1), 1, C, 0, None) == qd.QD_EINVAL
+    assert _call(f, A, 64, 1000, ids, 3, C, 1, None) == qd.QD_ESHAPE
+    assert _call(f, A + 8, 64, 1024, ids, 3, C, 1, None) == qd.QD_EALIGN
+    assert _call(f, A, 64, 1024, ids, 3, C + 4, 1, None) == qd.QD_EALIGN
+    assert _call(f, A, 64, 1024, ids, 3, A + 128, 1, None) == qd.QD_EINVAL  # overlaps the blob
+
+
 def test_errors_q4_0_gemv_and_gemm():
     for f in ("qgemv_q4_0", "qgemm_q4_0_prefill"):
         assert _call(f, None, 64, 512, B, C, 1, None) == qd.QD_EINVAL
@@ -199,6 +230,9 @@ def test_valid_args_reach_device_check():
     assert _call("qgemv_affine_i8_g64", A, 64, 1024, B, C, 1, None) == qd.QD_EDEVICE
     assert _call("qgemv_q4_0", A, 64, 512, B, C, 4, None) == qd.QD_EDEVICE
     assert _call("qd_stream_read", A, 1 << 20, B, None) == qd.QD_EDEVICE
+    assert _call("qgemv_affine_i8_g64_f16", A, 64, 1024, B, C, 1, None) == qd.QD_EDEVICE
+    assert _call("affine_i8_g64_embed_rows", A, 64, 1024, _ids(0, 63), 2, C, 0,
+                 None) == qd.QD_EDEVICE
     assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, 1500, None) == qd.QD_EDEVICE
     assert _call("q4_0_quantize", A, 3, 32, C, None) == qd.QD_EDEVICE
     assert _call("qgemv_affine_i8_g64_group", _affine_items((A, C, 64), (D, E, 32)), 2, 1024,

@@ -30,3 +30,17 @@ def test_check_accepts_correct_rounding_and_rejects_offsets():
     except AssertionError:
         return
     raise AssertionError("an output one BF16 step off was accepted")
+
+
+def test_f16_rounding_interval_matches_numpy():
+    # every double lies in the interval of its own f16 rounding, and the next
+    # double above the interval rounds elsewhere
+    from helpers import f16_rounding_interval
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(100000) * 10.0 ** rng.integers(-7, 4, 100000)
+    g = v.astype(np.float16).astype(np.float64)
+    ok = np.isfinite(g)
+    lo, hi = f16_rounding_interval(g[ok])
+    assert np.all((v[ok] >= lo) & (v[ok] <= hi))
+    assert np.all(np.nextafter(hi, np.inf).astype(np.float16).astype(np.float64) != g[ok])
+    assert np.all(np.nextafter(lo, -np.inf).astype(np.float16).astype(np.float64) != g[ok])
