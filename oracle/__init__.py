@@ -232,6 +232,27 @@ def q4_0_gemm(wq: np.ndarray, rows: int, cols: int, x: np.ndarray,
     return y
 
 
+def gelu_tanh(v: np.ndarray) -> np.ndarray:
+    """The tanh form of GELU, 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))),
+    in f64 (the Whisper page applies `gelu_tanh` after fc1 without defining
+    it; this is the standard tanh approximation of Hendrycks & Gimpel)."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+
+
+def q_linear(wq: np.ndarray, rows: int, cols: int, x: np.ndarray, bias=None,
+             gelu: bool = False, m_sel=None, row_sel=None) -> np.ndarray:
+    """fuel-transformers 0.19.1, lazy_quantized_whisper.rs -- q_linear: the
+    Q4_0 product, then the optional f32 bias [rows] broadcast over the token
+    rows; then, for fc1 in encoder_layer / decoder_layer, gelu_tanh.  f64."""
+    y = q4_0_gemm(wq, rows, cols, x, m_sel=m_sel, row_sel=row_sel)
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float32).astype(np.float64).reshape(-1)
+        assert b.size == rows
+        y = y + (b if row_sel is None else b[np.asarray(row_sel)])[None, :]
+    return gelu_tanh(y) if gelu else y
+
+
 # ---- tolerance metric -------------------------------------------------------
 
 def normwise_error(got: np.ndarray, ref: np.ndarray) -> float:

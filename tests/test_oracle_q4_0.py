@@ -192,3 +192,43 @@ def test_gemm_matches_numpy_and_selection():
     assert oracle.normwise_error(y, ref) < 1e-12
     ys = oracle.q4_0_gemm(s, rows, cols, x, m_sel=[3, 0], row_sel=[39, 7, 7])
     assert np.array_equal(ys, y[[3, 0]][:, [39, 7, 7]])
+
+
+# ---- q_linear: bias and gelu_tanh -------------------------------------------
+
+def test_gelu_tanh_matches_torch_and_known_values():
+    # torch's tanh-approximate GELU (an independent implementation) in f64,
+    # and values fixed by the formula: gelu(0) = 0, gelu(1) = 0.84119199...,
+    # gelu(v) -> v for large v, -> 0 for very negative v
+    v = np.concatenate([np.linspace(-12, 12, 2001), [0.0, 1.0, -1.0, 40.0, -40.0]])
+    want = torch.nn.functional.gelu(torch.from_numpy(v), approximate="tanh").numpy()
+    got = oracle.gelu_tanh(v)
+    assert np.max(np.abs(got - want)) <= 1e-15 * np.max(np.abs(want))
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.gelu_tanh(np.array([1.0]))[0] - 0.8411919906082768) < 1e-15
+    assert oracle.gelu_tanh(np.array([40.0]))[0] == 40.0
+    assert abs(oracle.gelu_tanh(np.array([-40.0]))[0]) < 1e-300
+
+
+def test_q_linear_bias_closed_form():
+    # all-zero weights (d = 0): the output is the bias, broadcast over tokens
+    rows, cols, m = 48, 256, 5
+    wq = oracle.q4_0_quantize(np.zeros((rows, cols), np.float32), rows, cols)
+    bias = synth.w_f32(1, rows, std=1.0, key=(84, 0, 0)).reshape(-1)
+    x = synth.x_f32(m, cols, key=(84, 0, 1))
+    y = oracle.q_linear(wq, rows, cols, x, bias)
+    assert np.array_equal(y, np.broadcast_to(bias.astype(np.float64), (m, rows)))
+    g = oracle.q_linear(wq, rows, cols, x, bias, gelu=True)
+    assert np.array_equal(g, oracle.gelu_tanh(np.broadcast_to(bias.astype(np.float64), (m, rows))))
+
+
+def test_q_linear_is_gemm_plus_bias_on_selections():
+    rows, cols, m = 40, 512, 6
+    wq = oracle.q4_0_quantize(synth.w_f32(rows, cols, key=(85, 0, 0)), rows, cols)
+    x = synth.x_f32(m, cols, key=(85, 0, 1))
+    bias = synth.w_f32(1, rows, std=0.5, key=(85, 0, 2)).reshape(-1)
+    full = oracle.q_linear(wq, rows, cols, x, bias, gelu=True)
+    part = oracle.q_linear(wq, rows, cols, x, bias, gelu=True, m_sel=[5, 0], row_sel=[39, 2, 7])
+    assert np.array_equal(part, full[np.ix_([5, 0], [39, 2, 7])])
+    plain = oracle.q4_0_gemm(wq, rows, cols, x)
+    assert np.array_equal(oracle.q_linear(wq, rows, cols, x), plain)
