@@ -418,9 +418,38 @@ def row_whisper_large_prefill(qd, layers):
         per[name] = {"us": mk * 1e3, "TFLOPs": 2 * m * r * c / (mk * 1e-3) / 1e12,
                      "mfma_frac": 2 * m * r * c / (mk * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     tf = flops / (ms * 1e-3) / 1e12
+    # the layer as the page runs it (q_linear): q, k, v in one launch (k has
+    # no bias), o, fc1 with gelu_tanh, fc2 -- biases and GELU in the epilogue
+    byname = {name: (r, c, wq) for name, r, c, wq in lay}
+    bias = {name: torch.full((r,), 0.01, device=DEV) for name, r, _, _ in lay}
+    yl = {name: torch.empty((m, r), device=DEV) for name, r, _, _ in lay}
+
+    def linear_layer():
+        qd.qlinear_q4_0_gemm([(byname[n][2], None if n == "k" else bias[n], yl[n], byname[n][0])
+                              for n in ("q", "k", "v")], 1280, xs[1280], m)
+        qd.qlinear_q4_0_gemm([(byname["o"][2], bias["o"], yl["o"], byname["o"][0])], 1280,
+                             xs[1280], m)
+        qd.qlinear_q4_0_gemm([(byname["fc1"][2], bias["fc1"], yl["fc1"], byname["fc1"][0])],
+                             1280, xs[1280], m, gelu=True)
+        qd.qlinear_q4_0_gemm([(byname["fc2"][2], bias["fc2"], yl["fc2"], byname["fc2"][0])],
+                             5120, xs[5120], m)
+    gl = capture(linear_layer)
+    ms_lin = event_time(gl.replay, 10, 3)
+    gq = capture(lambda: qd.qlinear_q4_0_gemm(
+        [(byname[n][2], None if n == "k" else bias[n], yl[n], byname[n][0]) for n in ("q", "k", "v")],
+        1280, xs[1280], m))
+    ms_qkv = event_time(gq.replay, 20, 3)
+    f_qkv = 3 * 2 * m * 1280 * 1280
     return {"frames": m, "flops_per_layer": flops, "ms_per_layer": ms,
             "ms_32_layers": 32 * ms, "TFLOPs": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
-            "per_matrix": per}
+            "per_matrix": per,
+            "q_linear_layer": {
+                "note": "q, k, v as one grouped launch (3 x 1280 columns), biases and "
+                        "gelu_tanh (fc1) in the epilogue",
+                "ms": ms_lin, "TFLOPs": flops / (ms_lin * 1e-3) / 1e12,
+                "mfma_frac": flops / (ms_lin * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                "qkv_grouped_us": ms_qkv * 1e3,
+                "qkv_grouped_TFLOPs": f_qkv / (ms_qkv * 1e-3) / 1e12}}
 
 
 def row_whisper_large_decoder(qd, layers):
@@ -453,11 +482,31 @@ def row_whisper_large_decoder(qd, layers):
     ms = event_time(g.replay, 20, 3)
     g192 = capture(lambda: [qd.qgemv_q4_0(w, r, c, x, y, 1) for _, w, r, c, x, y in ops])
     ms192 = event_time(g192.replay, 20, 3)
+    # the same step as the page's q_linear calls: biases (none for k) and
+    # gelu_tanh after fc1 in the epilogue
+    biases = {id(y): torch.full((r,), 0.01, device=DEV) for name, _, r, _, _, y in ops
+              if name != "k"}
+
+    def linear():
+        i = 0
+        while i < len(ops):
+            if ops[i][0] == "q":
+                qd.qlinear_q4_0_gemv([(w, biases.get(id(y)), y, r)
+                                      for _, w, r, _, _, y in ops[i:i + 3]],
+                                     ops[i][3], ops[i][4], 1)
+                i += 3
+            else:
+                name, w, r, c, x, y = ops[i]
+                qd.qlinear_q4_0_gemv([(w, biases[id(y)], y, r)], c, x, 1, gelu=name == "fc1")
+                i += 1
+    gl = capture(linear)
+    ms_lin = event_time(gl.replay, 20, 3)
     return {"gemvs": len(ops), "weight_bytes": wb, "ms_per_step": ms,
             "tokens_per_s": 1000.0 / ms, "weight_GBps": wb / (ms * 1e-3) / 1e9,
             "hbm_peak_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "variant": "128 launches (q, k, v grouped) in a HIP graph",
-            "ms_per_step_192_launches": ms192}
+            "ms_per_step_192_launches": ms192,
+            "ms_per_step_q_linear": ms_lin}
 
 
 def row_q4_0_bake(qd):

@@ -264,6 +264,35 @@ qd_status qgemm_q4_0_prefill(const void *w_q4_0, int64_t rows, int64_t cols,
                              const void *x_bf16, float *y, int64_t m,
                              void *stream);
 
+/* q_linear: the Q4_0 product, then an optional f32 bias [rows] broadcast
+ * over the token rows, then optionally gelu_tanh, the tanh form of GELU
+ * 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ * (fuel-transformers 0.19.1, lazy_quantized_whisper.rs -- q_linear, and
+ * encoder_layer / decoder_layer, which apply gelu_tanh after fc1).  Up to
+ * four products that read the same x share one launch (a layer's q, k, v:
+ * 3 x 1280 output columns).
+ *   w_q4_0  device, Q4_0 stream [rows, cols], 16-byte aligned
+ *   bias    device, f32 [rows], 4-byte aligned, or NULL (k has none)
+ *   y       device, f32 [m, rows] (GEMV: 4-byte, GEMM: 16-byte aligned)
+ *   rows    1 <= rows < 2^31 */
+typedef struct qd_q4_0_linear_item {
+  const void *w_q4_0;
+  const float *bias;
+  float *y;
+  int64_t rows;
+} qd_q4_0_linear_item;
+
+/* GEMV form: x f32 [m, cols], 1 <= m <= 16, cols % 256 == 0, cols <= 8192;
+ * gelu 0 or 1.  No output may overlap x, any weights, any bias or another
+ * output (QD_EINVAL).  Status codes as qgemv_q4_0_group. */
+qd_status qlinear_q4_0_gemv(const qd_q4_0_linear_item *items, int64_t n_items, int64_t cols,
+                            const float *x, int64_t m, int32_t gelu, void *stream);
+
+/* GEMM (prefill) form on the matrix cores: x BF16 [m, cols], any m >= 1,
+ * cols % 256 == 0, cols <= 65536; otherwise as qlinear_q4_0_gemv. */
+qd_status qlinear_q4_0_gemm(const qd_q4_0_linear_item *items, int64_t n_items, int64_t cols,
+                            const void *x_bf16, int64_t m, int32_t gelu, void *stream);
+
 /* f32 -> Q4_0 bake (fuel-transformers 0.19.1, lazy_quantized_whisper.rs --
  * quantize_in_out_to_q4_0 with ggml's BlockQ4_0::from_float): per block of
  * 32, d = (element of largest magnitude, first index on ties) / -8 in f32,

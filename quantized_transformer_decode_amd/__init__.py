@@ -32,7 +32,14 @@ EXPORTS = (
     "qgemv_affine_i8_g64_step_workspace_bytes", "qgemv_affine_i8_g64_step_plan",
     "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
     "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
+    "qlinear_q4_0_gemv", "qlinear_q4_0_gemm",
 )
+
+
+class Q40LinearItem(ctypes.Structure):
+    """qd_q4_0_linear_item"""
+    _fields_ = [("w_q4_0", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("rows", ctypes.c_int64)]
 
 
 class AffineGemvOp(ctypes.Structure):
@@ -112,13 +119,17 @@ def lib() -> ctypes.CDLL:
         L.qgemv_affine_i8_g64_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
         L.qd_stream_read.argtypes = [P, SZ, P, P]
         L.qgemv_affine_i8_g64_f16.argtypes = [P, I64, I64, P, P, I64, P]
+        LIN = ctypes.POINTER(Q40LinearItem)
+        L.qlinear_q4_0_gemv.argtypes = [LIN, I64, I64, P, I64, ctypes.c_int32, P]
+        L.qlinear_q4_0_gemm.argtypes = [LIN, I64, I64, P, I64, ctypes.c_int32, P]
         L.affine_i8_g64_embed_rows.argtypes = [P, I64, I64, ctypes.POINTER(ctypes.c_int64), I64,
                                                P, ctypes.c_int32, P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
                   "qgemv_affine_i8_g64_group", "qgemv_q4_0_group",
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
                   "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
-                  "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows"):
+                  "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
+                  "qlinear_q4_0_gemv", "qlinear_q4_0_gemm"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -186,6 +197,29 @@ def affine_i8_g64_embed_rows(w_packed, rows: int, cols: int, token_ids, out,
     _check("affine_i8_g64_embed_rows", lib().affine_i8_g64_embed_rows(
         _ptr(w_packed), rows, cols, ids, len(token_ids), _ptr(out), 1 if out_f16 else 0,
         _stream(stream)))
+
+
+def _linear_items(items):
+    """items: iterable of (w_q4_0, bias or None, y, rows)."""
+    items = list(items)
+    arr = (Q40LinearItem * len(items))()
+    for k, (w, b, y, rows) in enumerate(items):
+        arr[k] = Q40LinearItem(_ptr(w), None if b is None else _ptr(b), _ptr(y), rows)
+    return arr, len(items)
+
+
+def qlinear_q4_0_gemv(items, cols: int, x, m: int, gelu: bool = False, stream=None) -> None:
+    """items: (w_q4_0, bias or None, y, rows) for each product sharing x."""
+    arr, n = _linear_items(items)
+    _check("qlinear_q4_0_gemv", lib().qlinear_q4_0_gemv(arr, n, cols, _ptr(x), m,
+                                                         1 if gelu else 0, _stream(stream)))
+
+
+def qlinear_q4_0_gemm(items, cols: int, x_bf16, m: int, gelu: bool = False,
+                      stream=None) -> None:
+    arr, n = _linear_items(items)
+    _check("qlinear_q4_0_gemm", lib().qlinear_q4_0_gemm(arr, n, cols, _ptr(x_bf16), m,
+                                                         1 if gelu else 0, _stream(stream)))
 
 
 def qgemv_q4_0(w_q4_0, rows: int, cols: int, x, y, m: int, stream=None) -> None:

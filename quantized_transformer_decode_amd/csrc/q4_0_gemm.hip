@@ -11,6 +11,11 @@
 // kernel interleaves the MFMAs of block b with the delta scaling of block
 // b-1's partial products.
 //
+// Up to four products that share x go in one launch (the q/k/v of a layer,
+// 3 x 1280 output columns instead of 1280): their column tiles are numbered
+// back to back and each workgroup looks up its matrix.  The q_linear
+// epilogue (f32 bias, gelu_tanh for fc1) is applied at the store.
+//
 // Tiling: a 256-thread workgroup owns a BM (frames) x BN (weight rows)
 // output tile, 64 x 64 by default; its four waves are 2 x 2, each
 // BM/2 x BN/2.  Each LDS stage covers 128 columns of K (four Q4_0 blocks):
@@ -136,20 +141,31 @@ __device__ __forceinline__ void stage_store(const Stage<BM, BN> &st, uint16_t *A
   Ds[r * NB + b] = dead ? 0.f : f16_to_f32(dbits);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool MULTI, bool EPI>
 __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
-    const uint8_t *__restrict__ w_, int rows, int cols, const uint16_t *__restrict__ x_,
-    float *__restrict__ y_, int m) {
+    const Q40Group grp, int cols, const uint16_t *__restrict__ x_, int m) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const QD_GLOBAL uint8_t *w = gp(w_);
+  // this workgroup's matrix: column tiles are numbered back to back (a
+  // single matrix takes its descriptor at fixed offsets)
+  const int bx = blockIdx.x;
+  int k = 0;
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i)
+      if (i < grp.n && bx >= grp.tile0[i]) k = i;
+    k = uni(k);
+  }
+  const QD_GLOBAL uint8_t *w = gp(grp.w[k]);
+  const int rows = grp.rows[k];
+  QD_GLOBAL float *y = gp(grp.y[k]);
+  const float *bias = grp.bias[k];
   const QD_GLOBAL uint16_t *x = gp(x_);
-  QD_GLOBAL float *y = gp((float *)y_);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uni(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int n0 = (bx - grp.tile0[k]) * BN;
   const int nstages = cols / BK;
 
   using T = Tile<BM, BN>;
@@ -169,6 +185,13 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
   const int kq = (lane >> 4) * 8;  // this lane's 8 K indices within a block
   const int arow = wm * (BM / 2) + (lane & 15);
   const int bcol = wn * (BN / 2) + (lane & 15);
+  // the bias of this lane's output columns, loaded before the K loop
+  float bj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + bcol + j * 16;
+    bj[j] = (EPI && bias && n < rows) ? ((const QD_GLOBAL float *)bias)[n] : 0.f;
+  }
 
   // One stage from LDS buffer `buf`: per block, TM x TN MFMAs of the exact
   // codes, then the previous block's partial products scaled by its deltas.
@@ -225,42 +248,57 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
 
   // C layout of a 16x16 f32 MFMA tile: lane holds rows 4*(lane/16)+v of
   // column lane%16.
+  auto store = [&](auto act) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + bcol + j * 16;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + v;
-        if (t < m && n < rows) y[(size_t)t * rows + n] = acc[i][j][v];
+        for (int v = 0; v < 4; ++v) {
+          const int t = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + v;
+          if (t < m && n < rows)
+            y[(size_t)t * rows + n] = EPI ? act(acc[i][j][v] + bj[j]) : acc[i][j][v];
+        }
       }
-    }
+  };
+  if (EPI && grp.gelu)
+    store([](float v) { return linear_epilogue(v, nullptr, 0, 1); });
+  else
+    store([](float v) { return v; });
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(const uint8_t *w, int rows, int cols, const uint16_t *x, float *y,
-                       int m, hipStream_t stream) {
+template <int BM, int BN, bool MULTI, bool EPI>
+hipError_t launch_tile(Q40Group g, int cols, const uint16_t *x, int m, hipStream_t stream) {
   const size_t lds = 2 * (size_t)Tile<BM, BN>::STAGE_BYTES;
   static bool attr_set = false;  // the limit is per function; setting it twice is harmless
   if (!attr_set && lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemm_kernel<BM, BN>,
+    hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemm_kernel<BM, BN, MULTI, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((rows + BN - 1) / BN, (m + BM - 1) / BM);
-  hipLaunchKernelGGL((q4_0_gemm_kernel<BM, BN>), grid, dim3(kThreads), lds, stream, w, rows,
-                     cols, x, y, m);
+  g.tile0[0] = 0;
+  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + BN - 1) / BN;
+  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
+  dim3 grid(g.tile0[g.n], (m + BM - 1) / BM);
+  hipLaunchKernelGGL((q4_0_gemm_kernel<BM, BN, MULTI, EPI>), grid, dim3(kThreads), lds, stream, g,
+                     cols, x, m);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,
-                            const uint16_t *x, float *y, int m,
+hipError_t launch_q4_0_gemm(Q40Group g, int cols, const uint16_t *x, int m,
                             hipStream_t stream) {
-  return launch_tile<QD_GEMM_BM, QD_GEMM_BN>(w, rows, cols, x, y, m, stream);
+  // kernels specialised for one matrix and for a plain product
+  bool epi = g.gelu != 0;
+  for (int k = 0; k < g.n; ++k) epi = epi || g.bias[k] != nullptr;
+  if (g.n > 1)
+    return epi ? launch_tile<QD_GEMM_BM, QD_GEMM_BN, true, true>(g, cols, x, m, stream)
+               : launch_tile<QD_GEMM_BM, QD_GEMM_BN, true, false>(g, cols, x, m, stream);
+  return epi ? launch_tile<QD_GEMM_BM, QD_GEMM_BN, false, true>(g, cols, x, m, stream)
+             : launch_tile<QD_GEMM_BM, QD_GEMM_BN, false, false>(g, cols, x, m, stream);
 }
 
 }  // namespace qd

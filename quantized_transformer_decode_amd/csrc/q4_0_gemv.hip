@@ -46,6 +46,7 @@ struct QShape {
 struct QItem {
   const QD_GLOBAL uint8_t *w;
   QD_GLOBAL float *y;
+  const float *bias;    // f32 [rows] or null
   int rows;
   int trow;             // first row of the row group in its matrix
 };
@@ -59,6 +60,7 @@ __device__ __forceinline__ QItem q_item(const Q40Group &grp, int rg) {
   QItem it;
   it.w = gp(grp.w[k]);
   it.y = gp(grp.y[k]);
+  it.bias = grp.bias[k];
   it.rows = grp.rows[k];
   it.trow = (rg - grp.tile0[k]) * 8 * R;
   return it;
@@ -131,7 +133,7 @@ __device__ __forceinline__ void block_dot(const uint32_t (&nib)[R][4], const flo
 }
 
 // Items past the end of the walk are computed with d = 0.
-template <int MT, int R, bool STORE>
+template <int MT, int R, bool STORE, bool EPI>
 __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][R], QCursor &c,
                                            const QShape &S, const Q40Group &grp, int &left,
                                            int lane, const float *xs, const float *xsum,
@@ -170,7 +172,8 @@ __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][
           const float v = group_sum<8>(acc[t][r]);
           const int n = base + 8 * r;
           if ((lane & 7) == 0 && n < it.rows && t0 + t < m)
-            it.y[(size_t)(t0 + t) * it.rows + n] = v;
+            it.y[(size_t)(t0 + t) * it.rows + n] =
+                EPI ? linear_epilogue(v, it.bias, n, grp.gelu) : v;
           acc[t][r] = 0.f;
         }
     }
@@ -182,7 +185,7 @@ __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][
   }
 }
 
-template <int MT, int R, int KS>
+template <int MT, int R, int KS, bool EPI>
 __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
     const Q40Group grp, int cols, const float *__restrict__ x_, int t0, int m) {
   constexpr int SLOTS = kQW / KS;
@@ -248,17 +251,17 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
     // register group is issued before the current one is consumed.
     for (;;) {
       if (lc <= kQU) {
-        qg_compute<MT, R, KS == 1>(A, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
+        qg_compute<MT, R, KS == 1, EPI>(A, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
         break;
       }
       qg_issue<R>(B, ci, S, grp, lane, li);
-      qg_compute<MT, R, KS == 1>(A, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
+      qg_compute<MT, R, KS == 1, EPI>(A, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
       if (lc <= kQU) {
-        qg_compute<MT, R, KS == 1>(B, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
+        qg_compute<MT, R, KS == 1, EPI>(B, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
         break;
       }
       qg_issue<R>(A, ci, S, grp, lane, li);
-      qg_compute<MT, R, KS == 1>(B, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
+      qg_compute<MT, R, KS == 1, EPI>(B, acc, cc, S, grp, lc, lane, xs, xsum, cols, t0, m);
     }
   }
   if constexpr (KS > 1) {
@@ -282,26 +285,28 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
       if (rg >= ngroups) continue;
       const QItem it = q_item<R>(grp, rg);
       const int nn = it.trow + rr;
-      if (nn < it.rows && t0 + t < m) it.y[(size_t)(t0 + t) * it.rows + nn] = sum;
+      if (nn < it.rows && t0 + t < m)
+        it.y[(size_t)(t0 + t) * it.rows + nn] =
+            EPI ? linear_epilogue(sum, it.bias, nn, grp.gelu) : sum;
     }
   }
 }
 
-template <int MT, int R, int KS>
+template <int MT, int R, int KS, bool EPI>
 hipError_t launch_q_ks(const Q40Group &g, int cols, const float *x, int t0, int m, int grid,
                        hipStream_t stream) {
   const size_t lds = (size_t)MT * cols * 4 + (size_t)MT * (cols / 32) * 4;
   if (lds > 48 * 1024) {  // above the default dynamic-LDS limit: raise it once
     static bool raised = false;
     if (!raised) {
-      hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemv_kernel<MT, R, KS>,
+      hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemv_kernel<MT, R, KS, EPI>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                          kQLdsBudget + 4096);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
-  hipLaunchKernelGGL((q4_0_gemv_kernel<MT, R, KS>), dim3(grid), dim3(kQThreads), lds, stream,
+  hipLaunchKernelGGL((q4_0_gemv_kernel<MT, R, KS, EPI>), dim3(grid), dim3(kQThreads), lds, stream,
                      g, cols, x, t0, m);
   return hipGetLastError();
 }
@@ -312,7 +317,7 @@ hipError_t launch_q_ks(const Q40Group &g, int cols, const float *x, int t0, int 
 constexpr int kQTargetWaves = 4096;
 constexpr int kQStreamWgsPerCu = 2;
 
-template <int MT>
+template <int MT, bool EPI>
 hipError_t launch_q_mt(Q40Group g, int cols, const float *x, int t0, int m,
                        hipStream_t stream) {
   constexpr int R = 1;  // rows per lane
@@ -328,13 +333,13 @@ hipError_t launch_q_mt(Q40Group g, int cols, const float *x, int t0, int m,
     if (cus < 1) cus = 256;
     long grid = (ngroups + kQW - 1) / kQW;
     if (grid > (long)kQStreamWgsPerCu * cus) grid = (long)kQStreamWgsPerCu * cus;
-    return launch_q_ks<MT, R, 1>(g, cols, x, t0, m, (int)grid, stream);
+    return launch_q_ks<MT, R, 1, EPI>(g, cols, x, t0, m, (int)grid, stream);
   }
   const int grid = (int)((ngroups * ks + kQW - 1) / kQW);
   switch (ks) {
-    case 2: return launch_q_ks<MT, R, 2>(g, cols, x, t0, m, grid, stream);
-    case 4: return launch_q_ks<MT, R, 4>(g, cols, x, t0, m, grid, stream);
-    default: return launch_q_ks<MT, R, 8>(g, cols, x, t0, m, grid, stream);
+    case 2: return launch_q_ks<MT, R, 2, EPI>(g, cols, x, t0, m, grid, stream);
+    case 4: return launch_q_ks<MT, R, 4, EPI>(g, cols, x, t0, m, grid, stream);
+    default: return launch_q_ks<MT, R, 8, EPI>(g, cols, x, t0, m, grid, stream);
   }
 }
 
@@ -346,15 +351,28 @@ hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
   // by one x block per thread for the staging
   int cap = kQLdsBudget / (cols * 4 + cols / 8);
   if (cap * (cols / 32) > kQThreads) cap = kQThreads / (cols / 32);
+  // kernels specialised for a plain product (no bias, no GELU)
+  bool epi = g.gelu != 0;
+  for (int k = 0; k < g.n; ++k) epi = epi || g.bias[k] != nullptr;
   int t0 = 0;
   while (t0 < m) {
     const int left = m - t0;
     const int lim = left < cap ? left : cap;
     hipError_t e;
     int mt;
-    if (lim >= 4) { mt = 4; e = launch_q_mt<4>(g, cols, x, t0, m, stream); }
-    else if (lim >= 2) { mt = 2; e = launch_q_mt<2>(g, cols, x, t0, m, stream); }
-    else { mt = 1; e = launch_q_mt<1>(g, cols, x, t0, m, stream); }
+    if (lim >= 4) {
+      mt = 4;
+      e = epi ? launch_q_mt<4, true>(g, cols, x, t0, m, stream)
+              : launch_q_mt<4, false>(g, cols, x, t0, m, stream);
+    } else if (lim >= 2) {
+      mt = 2;
+      e = epi ? launch_q_mt<2, true>(g, cols, x, t0, m, stream)
+              : launch_q_mt<2, false>(g, cols, x, t0, m, stream);
+    } else {
+      mt = 1;
+      e = epi ? launch_q_mt<1, true>(g, cols, x, t0, m, stream)
+              : launch_q_mt<1, false>(g, cols, x, t0, m, stream);
+    }
     if (e != hipSuccess) return e;
     t0 += mt;
   }

@@ -342,65 +342,100 @@ qd_status affine_i8_g64_embed_rows(const void *w_packed, int64_t rows, int64_t c
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 
-qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
-                     const float *x, float *y, int64_t m, void *stream) {
-  const qd_q4_0_gemv_item item = {w_q4_0, y, rows};
-  return qgemv_q4_0_group(&item, 1, cols, x, m, stream);
-}
+}  // extern "C"
 
-qd_status qgemv_q4_0_group(const qd_q4_0_gemv_item *items, int64_t n_items, int64_t cols,
-                           const float *x, int64_t m, void *stream) {
+// q_linear products of one launch (shared input): validation shared by the
+// GEMV (f32 x, m <= 16) and the GEMM (BF16 x, any m) forms.
+static qd_status q40_linear_check(const qd_q4_0_linear_item *items, int64_t n_items,
+                                  int64_t cols, const void *x, size_t xbytes, int64_t m,
+                                  int32_t gelu, size_t y_align) {
   if (!items || !x || n_items < 1 || n_items > qd::kMaxGroup) return QD_EINVAL;
-  if (m < 1 || m > 16 || cols < 1) return QD_EINVAL;
-  if (cols % 256 != 0 || cols > kMaxGemvCols) return QD_ESHAPE;
+  if (gelu != 0 && gelu != 1) return QD_EINVAL;
   if (!aligned(x, 16)) return QD_EALIGN;
   for (int64_t k = 0; k < n_items; ++k) {
-    const qd_q4_0_gemv_item &it = items[k];
+    const qd_q4_0_linear_item &it = items[k];
     if (!it.w_q4_0 || !it.y) return QD_EINVAL;
     if (it.rows < 1 || it.rows > kMaxRows) return QD_EINVAL;
-    if (!aligned(it.w_q4_0, 16) || !aligned(it.y, 4)) return QD_EALIGN;
+    if (!aligned(it.w_q4_0, 16) || !aligned(it.y, y_align) || !aligned(it.bias, 4))
+      return QD_EALIGN;
   }
+  // an output may overlap neither the input, nor any weights or bias, nor
+  // another output
   for (int64_t k = 0; k < n_items; ++k) {
     const size_t ny = (size_t)m * items[k].rows * 4;
-    if (overlap(items[k].y, ny, x, (size_t)m * cols * 4)) return QD_EINVAL;
+    if (overlap(items[k].y, ny, x, xbytes)) return QD_EINVAL;
     for (int64_t j = 0; j < n_items; ++j) {
-      if (overlap(items[k].y, ny, items[j].w_q4_0, q40_bytes(items[j].rows, cols)))
+      if (overlap(items[k].y, ny, items[j].w_q4_0, q40_bytes(items[j].rows, cols)) ||
+          (items[j].bias && overlap(items[k].y, ny, items[j].bias, (size_t)items[j].rows * 4)))
         return QD_EINVAL;
       if (j > k && overlap(items[k].y, ny, items[j].y, (size_t)m * items[j].rows * 4))
         return QD_EINVAL;
     }
   }
-  qd_status st = check_device();
-  if (st != QD_OK) return st;
+  return QD_OK;
+}
+
+static qd::Q40Group q40_group(const qd_q4_0_linear_item *items, int64_t n_items, int32_t gelu) {
   qd::Q40Group g = {};
   g.n = (int)n_items;
+  g.gelu = gelu;
   for (int64_t k = 0; k < n_items; ++k) {
     g.w[k] = (const uint8_t *)items[k].w_q4_0;
     g.y[k] = items[k].y;
+    g.bias[k] = items[k].bias;
     g.rows[k] = (int)items[k].rows;
   }
-  hipError_t e = qd::launch_q4_0_gemv(g, (int)cols, x, (int)m, (hipStream_t)stream);
+  return g;
+}
+
+extern "C" {
+
+qd_status qlinear_q4_0_gemv(const qd_q4_0_linear_item *items, int64_t n_items, int64_t cols,
+                            const float *x, int64_t m, int32_t gelu, void *stream) {
+  if (m < 1 || m > 16 || cols < 1) return QD_EINVAL;
+  if (cols % 256 != 0 || cols > kMaxGemvCols) return QD_ESHAPE;
+  qd_status st = q40_linear_check(items, n_items, cols, x, (size_t)m * cols * 4, m, gelu, 4);
+  if (st != QD_OK) return st;
+  st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_q4_0_gemv(q40_group(items, n_items, gelu), (int)cols, x, (int)m,
+                                      (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status qlinear_q4_0_gemm(const qd_q4_0_linear_item *items, int64_t n_items, int64_t cols,
+                            const void *x_bf16, int64_t m, int32_t gelu, void *stream) {
+  if (m < 1 || m > kMaxGemmM || cols < 1) return QD_EINVAL;
+  if (cols % 256 != 0 || cols > kMaxGemmCols) return QD_ESHAPE;
+  qd_status st = q40_linear_check(items, n_items, cols, x_bf16, (size_t)m * cols * 2, m, gelu,
+                                  16);
+  if (st != QD_OK) return st;
+  st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_q4_0_gemm(q40_group(items, n_items, gelu), (int)cols,
+                                      (const uint16_t *)x_bf16, (int)m, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status qgemv_q4_0(const void *w_q4_0, int64_t rows, int64_t cols,
+                     const float *x, float *y, int64_t m, void *stream) {
+  const qd_q4_0_linear_item item = {w_q4_0, nullptr, y, rows};
+  return qlinear_q4_0_gemv(&item, 1, cols, x, m, 0, stream);
+}
+
+qd_status qgemv_q4_0_group(const qd_q4_0_gemv_item *items, int64_t n_items, int64_t cols,
+                           const float *x, int64_t m, void *stream) {
+  if (!items || n_items < 1 || n_items > qd::kMaxGroup) return QD_EINVAL;
+  qd_q4_0_linear_item li[qd::kMaxGroup];
+  for (int64_t k = 0; k < n_items; ++k) li[k] = {items[k].w_q4_0, nullptr, items[k].y, items[k].rows};
+  return qlinear_q4_0_gemv(li, n_items, cols, x, m, 0, stream);
 }
 
 qd_status qgemm_q4_0_prefill(const void *w_q4_0, int64_t rows, int64_t cols,
                              const void *x_bf16, float *y, int64_t m,
                              void *stream) {
-  if (!w_q4_0 || !x_bf16 || !y) return QD_EINVAL;
-  if (rows < 1 || rows > kMaxRows || m < 1 || m > kMaxGemmM || cols < 1) return QD_EINVAL;
-  if (cols % 256 != 0 || cols > kMaxGemmCols) return QD_ESHAPE;
-  if (!aligned(w_q4_0, 16) || !aligned(x_bf16, 16) || !aligned(y, 16))
-    return QD_EALIGN;
-  const size_t ny = (size_t)m * rows * 4;
-  if (overlap(y, ny, w_q4_0, q40_bytes(rows, cols)) ||
-      overlap(y, ny, x_bf16, (size_t)m * cols * 2))
-    return QD_EINVAL;
-  qd_status st = check_device();
-  if (st != QD_OK) return st;
-  hipError_t e = qd::launch_q4_0_gemm((const uint8_t *)w_q4_0, (int)rows,
-                                      (int)cols, (const uint16_t *)x_bf16, y,
-                                      (int)m, (hipStream_t)stream);
-  return e == hipSuccess ? QD_OK : hip_fail(e);
+  const qd_q4_0_linear_item item = {w_q4_0, nullptr, y, rows};
+  return qlinear_q4_0_gemm(&item, 1, cols, x_bf16, m, 0, stream);
 }
 
 qd_status q4_0_quantize(const float *w, int64_t rows, int64_t cols, void *out,

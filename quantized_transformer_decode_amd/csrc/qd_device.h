@@ -34,6 +34,14 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)h;
 }
 
+// The q_linear epilogue: + bias[n] (when given), then the tanh form of GELU,
+// 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), with gelu.
+__device__ __forceinline__ float linear_epilogue(float v, const float *bias, int n, int gelu) {
+  if (bias) v += ((const __attribute__((address_space(1))) float *)bias)[n];
+  if (gelu) v = 0.5f * v * (1.f + tanhf(0.7978845608028654f * fmaf(0.044715f * v, v * v, v)));
+  return v;
+}
+
 // Byte n (0..3) of a dword as float (v_cvt_f32_ubyteN).
 template <int N>
 __device__ __forceinline__ float ubyte(uint32_t v) {

@@ -22,12 +22,16 @@ struct AffineGroup {
   int tile0[kMaxGroup + 1];
   int n;
 };
+// Q4_0 products of one launch, each with an optional f32 bias [rows] added
+// to its outputs and, with gelu, gelu_tanh applied after it (q_linear).
 struct Q40Group {
   const uint8_t *w[kMaxGroup];
   float *y[kMaxGroup];
+  const float *bias[kMaxGroup];
   int rows[kMaxGroup];
   int tile0[kMaxGroup + 1];
   int n;
+  int gelu;
 };
 
 // x and y BF16, or f16 with f16 = true (scales and biases BF16 in both).
@@ -46,8 +50,7 @@ hipError_t launch_affine_embed_rows(const uint8_t *w, int rows, int cols, const 
 hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
                             hipStream_t stream);
 
-hipError_t launch_q4_0_gemm(const uint8_t *w, int rows, int cols,
-                            const uint16_t *x, float *y, int m,
+hipError_t launch_q4_0_gemm(Q40Group g, int cols, const uint16_t *x, int m,
                             hipStream_t stream);
 
 hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,

@@ -118,6 +118,32 @@ def test_errors_embed_rows():
     assert _call(f, A, 64, 1024, ids, 3, A + 128, 1, None) == qd.QD_EINVAL  # overlaps the blob
 
 
+def _lin(*items):
+    arr = (qd.Q40LinearItem * len(items))()
+    for k, (w, b, y, r) in enumerate(items):
+        arr[k] = qd.Q40LinearItem(w, b, y, r)
+    return arr
+
+
+def test_errors_qlinear():
+    for f, y_al in (("qlinear_q4_0_gemv", 4), ("qlinear_q4_0_gemm", 16)):
+        D = 0x7f3000000000
+        ok = _lin((A, D, C, 64))
+        assert _call(f, None, 1, 512, B, 4, 0, None) == qd.QD_EINVAL
+        assert _call(f, ok, 0, 512, B, 4, 0, None) == qd.QD_EINVAL
+        assert _call(f, ok, 1, 512, B, 4, 2, None) == qd.QD_EINVAL        # gelu not 0/1
+        assert _call(f, ok, 1, 500, B, 4, 0, None) == qd.QD_ESHAPE
+        assert _call(f, _lin((A, D + 2, C, 64)), 1, 512, B, 4, 0, None) == qd.QD_EALIGN
+        assert _call(f, _lin((A, D, C + y_al // 2, 64)), 1, 512, B, 4, 0, None) == qd.QD_EALIGN
+        # output overlapping a bias, weights or another output
+        assert _call(f, _lin((A, D, D + 16, 64)), 1, 512, B, 4, 0, None) == qd.QD_EINVAL
+        assert _call(f, _lin((A, None, A + 64, 64)), 1, 512, B, 4, 0, None) == qd.QD_EINVAL
+        assert _call(f, _lin((A, None, C, 64), (A, None, C + 256, 64)), 2, 512, B, 4, 0,
+                     None) == qd.QD_EINVAL
+    assert _call("qlinear_q4_0_gemv", _lin((A, None, C, 64)), 1, 512, B, 17, 0,
+                 None) == qd.QD_EINVAL
+
+
 def test_errors_q4_0_gemv_and_gemm():
     for f in ("qgemv_q4_0", "qgemm_q4_0_prefill"):
         assert _call(f, None, 64, 512, B, C, 1, None) == qd.QD_EINVAL
@@ -231,6 +257,9 @@ def test_valid_args_reach_device_check():
     assert _call("qgemv_q4_0", A, 64, 512, B, C, 4, None) == qd.QD_EDEVICE
     assert _call("qd_stream_read", A, 1 << 20, B, None) == qd.QD_EDEVICE
     assert _call("qgemv_affine_i8_g64_f16", A, 64, 1024, B, C, 1, None) == qd.QD_EDEVICE
+    lin = _lin((A, 0x7f3000000000, C, 64), (B, None, C + (1 << 20), 64))
+    assert _call("qlinear_q4_0_gemv", lin, 2, 512, 0x7f4000000000, 4, 1, None) == qd.QD_EDEVICE
+    assert _call("qlinear_q4_0_gemm", lin, 2, 512, 0x7f4000000000, 99, 0, None) == qd.QD_EDEVICE
     assert _call("affine_i8_g64_embed_rows", A, 64, 1024, _ids(0, 63), 2, C, 0,
                  None) == qd.QD_EDEVICE
     assert _call("qgemm_q4_0_prefill", A, 64, 512, B, C, 1500, None) == qd.QD_EDEVICE

@@ -176,3 +176,77 @@ def test_gemm_rows_match_gemv():
         qd.qgemv_q4_0(dev_u8(wq), rows, cols, dev_f32(xf[t0:t0 + mm]), yv[t0:t0 + mm], mm)
     torch.cuda.synchronize()
     assert oracle.normwise_error(yg, yv.cpu().numpy().astype(np.float64)) < 1e-5
+
+
+# ---- q_linear: bias and gelu_tanh in the epilogue, grouped products --------
+
+def _bias(rows, key):
+    return synth.w_f32(1, rows, std=0.5, key=(11, rows, key)).reshape(-1)
+
+
+@pytest.mark.parametrize("shapes,cols,m,gelu", [
+    ((1280, 1280, 1280), 1280, 1, False),   # a decoder layer's q, k, v (k without bias)
+    ((5120,), 1280, 1, True),               # fc1 + gelu_tanh
+    ((1280,), 5120, 4, False),              # fc2
+    ((33, 300), 512, 16, True),             # ragged rows, 16 tokens
+])
+def test_qlinear_gemv_parity(shapes, cols, m, gelu):
+    print(f"qlinear gemv {shapes} cols={cols} m={m} gelu={gelu}", flush=True)
+    wqs = [oracle.q4_0_quantize(synth.w_f32(r, cols, key=(12, k, r)), r, cols)
+           for k, r in enumerate(shapes)]
+    biases = [None if k == 1 else _bias(r, k) for k, r in enumerate(shapes)]
+    x = synth.x_f32(m, cols, key=(12, cols, m))
+    ys = [torch.full((m, r), float("nan"), device=DEV) for r in shapes]
+    qd.qlinear_q4_0_gemv([(dev_u8(wq), None if b is None else dev_f32(b), y, r)
+                          for wq, b, y, r in zip(wqs, biases, ys, shapes)],
+                         cols, dev_f32(x), m, gelu=gelu)
+    torch.cuda.synchronize()
+    for k, (wq, b, y, r) in enumerate(zip(wqs, biases, ys, shapes)):
+        ref = oracle.q_linear(wq, r, cols, x, b, gelu=gelu)
+        check_f32_output(y.cpu().numpy(), ref, f"item {k} ({r}x{cols})")
+
+
+@pytest.mark.parametrize("shapes,cols,m,gelu", [
+    ((80, 130, 64), 512, 70, False),
+    ((320,), 768, 130, True),
+])
+def test_qlinear_gemm_parity_full(shapes, cols, m, gelu):
+    print(f"qlinear gemm {shapes} cols={cols} m={m} gelu={gelu}", flush=True)
+    wqs = [oracle.q4_0_quantize(synth.w_f32(r, cols, key=(13, k, r)), r, cols)
+           for k, r in enumerate(shapes)]
+    biases = [None if k == 1 else _bias(r, 10 + k) for k, r in enumerate(shapes)]
+    x = synth.x_bf16(m, cols, key=(13, cols, m))
+    ys = [torch.full((m, r), float("nan"), device=DEV) for r in shapes]
+    qd.qlinear_q4_0_gemm([(dev_u8(wq), None if b is None else dev_f32(b), y, r)
+                          for wq, b, y, r in zip(wqs, biases, ys, shapes)],
+                         cols, dev_bf16(x), m, gelu=gelu)
+    torch.cuda.synchronize()
+    for k, (wq, b, y, r) in enumerate(zip(wqs, biases, ys, shapes)):
+        check_f32_output(y.cpu().numpy(), oracle.q_linear(wq, r, cols, x, b, gelu=gelu),
+                         f"item {k} ({r}x{cols})")
+
+
+def test_qlinear_gemm_whisper_qkv_and_fc1_1500_sampled():
+    # the encoder's fused q/k/v (3 x 1280 columns, k without bias) and fc1 +
+    # gelu_tanh at 1500 frames, checked on sampled outputs
+    m, d = 1500, 1280
+    x = synth.x_bf16(m, d, key=(14, 0, 0))
+    for shapes, gelu in (((d, d, d), False), ((5120,), True)):
+        print(f"qlinear gemm 1500 {shapes} gelu={gelu}", flush=True)
+        wqs = [oracle.q4_0_quantize(synth.w_f32(r, d, key=(14, k, r)), r, d)
+               for k, r in enumerate(shapes)]
+        biases = [None if (k == 1 and len(shapes) == 3) else _bias(r, 20 + k)
+                  for k, r in enumerate(shapes)]
+        ys = [torch.full((m, r), float("nan"), device=DEV) for r in shapes]
+        qd.qlinear_q4_0_gemm([(dev_u8(wq), None if b is None else dev_f32(b), y, r)
+                              for wq, b, y, r in zip(wqs, biases, ys, shapes)],
+                             d, dev_bf16(x), m, gelu=gelu)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(len(shapes))
+        ms = np.unique(np.concatenate([rng.integers(0, m, 32), [0, 63, 64, 1499]]))
+        for k, (wq, b, y, r) in enumerate(zip(wqs, biases, ys, shapes)):
+            rs = np.unique(np.concatenate([rng.integers(0, r, 96), [0, 63, 64, r - 1]]))
+            got = y.cpu().numpy()
+            ref = oracle.q_linear(wq, r, d, x, b, gelu=gelu, m_sel=ms, row_sel=rs)
+            check_f32_output(got[np.ix_(ms, rs)], ref, f"item {k} ({r}x{d}) sampled")
+            assert np.isfinite(got).all()
