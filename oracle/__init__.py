@@ -253,6 +253,34 @@ def q_linear(wq: np.ndarray, rows: int, cols: int, x: np.ndarray, bias=None,
     return gelu_tanh(y) if gelu else y
 
 
+# ---- decode attention --------------------------------------------------------
+
+def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, length: int,
+                     scale: float, kv_start: int = 0) -> np.ndarray:
+    """turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step
+    (encode_attention_decode): one query row per head against the cached
+    rows [kv_start, length) of its K/V head, softmax(scale * q.k) v, in f64.
+    q [heads, d]; k_cache, v_cache [rows, kv_heads, d] (the cache row of
+    position t holds every K/V head); q head h reads K/V head
+    h // (heads // kv_heads) (grouped-query attention).  Inputs are float
+    arrays (decode stored bits before calling)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k_cache, dtype=np.float64)
+    v = np.asarray(v_cache, dtype=np.float64)
+    heads, d = q.shape
+    kv_heads = k.shape[1]
+    assert heads % kv_heads == 0 and k.shape[2] == d and 0 <= kv_start < length <= k.shape[0]
+    group = heads // kv_heads
+    out = np.zeros((heads, d), dtype=np.float64)
+    for h in range(heads):
+        j = h // group
+        s = scale * (k[kv_start:length, j, :] @ q[h])  # scores of the window
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[h] = p @ v[kv_start:length, j, :]
+    return out
+
+
 # ---- tolerance metric -------------------------------------------------------
 
 def normwise_error(got: np.ndarray, ref: np.ndarray) -> float:
