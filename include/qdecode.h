@@ -309,6 +309,48 @@ qd_status qlinear_q4_0_gemm(const qd_q4_0_linear_item *items, int64_t n_items, i
 qd_status q4_0_quantize(const float *w, int64_t rows, int64_t cols, void *out,
                         void *stream);
 
+/* ---- decode attention over the K/V cache ---------------------------------- */
+
+/* Bytes of the attention_decode workspace for this head shape (0 if the
+ * shape is not supported): a bound over every window length. */
+int64_t attention_decode_workspace_bytes(int64_t heads, int64_t kv_heads, int64_t head_dim);
+
+/* Grouped-query decode attention for one token (turbospark-runtime 0.3.0,
+ * qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step, encode_attention_decode
+ * with its split-softmax scratch): for every query head h, with K/V head
+ * j = h / (heads / kv_heads),
+ *   out[h] = sum_t softmax_t(scale * q[h] . k[t, j]) v[t, j],
+ *   t in [kv_start, length)
+ * (the page attends the causal prefix: kv_start 0, length position + 1,
+ * scale 1/sqrt(head_dim)).  Scores, exponentials and sums in fp32, the
+ * output rounded once (nearest even) to the 16-bit type.  Workgroups take
+ * chunks of the window (split softmax) and a second launch merges the
+ * chunks of each head; a window of up to 32 rows (head_dim 128) or 64 rows
+ * (head_dim 64) is one chunk and takes one launch.
+ *   q          device, [heads, head_dim] 16-bit, 16-byte aligned
+ *   k_cache,   device, [>= length rows, kv_heads, head_dim] 16-bit (the
+ *   v_cache    cache row of position t holds every K/V head), 16-byte aligned
+ *   heads, kv_heads  heads % kv_heads == 0 with heads / kv_heads in
+ *              {1, 2, 4, 8} and 1 <= kv_heads <= 65535 (QD_ESHAPE)
+ *   head_dim   64 or 128 (QD_ESHAPE)
+ *   length, kv_start  0 <= kv_start < length <= 2^30 (QD_EINVAL)
+ *   scale      finite (QD_EINVAL)
+ *   f16        1: q, caches and out are f16 (the page's type); 0: BF16
+ *   out        device, [heads, head_dim] 16-bit, 16-byte aligned
+ *   workspace  device, f32 scratch for the chunk partials, 16-byte
+ *              aligned, at least attention_decode_workspace_bytes(heads,
+ *              kv_heads, head_dim) bytes (QD_EINVAL otherwise; the size does
+ *              not depend on the window, so one workspace serves every call
+ *              of a head shape); its contents on entry do not matter and are
+ *              unspecified afterwards
+ * out may overlap neither the inputs nor the workspace, nor the workspace
+ * the inputs (QD_EINVAL).  Asynchronous on `stream`; calls sharing one
+ * workspace must be ordered on one stream. */
+qd_status attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                           int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t length,
+                           int64_t kv_start, float scale, int32_t f16, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- measurement aid (not a step of the decode path) ---------------------- */
 
 /* Reads `bytes` bytes of device memory at `buf` once, with the access pattern

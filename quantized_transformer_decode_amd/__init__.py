@@ -33,6 +33,7 @@ EXPORTS = (
     "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
     "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
     "qlinear_q4_0_gemv", "qlinear_q4_0_gemm",
+    "attention_decode_workspace_bytes", "attention_decode",
 )
 
 
@@ -124,12 +125,16 @@ def lib() -> ctypes.CDLL:
         L.qlinear_q4_0_gemm.argtypes = [LIN, I64, I64, P, I64, ctypes.c_int32, P]
         L.affine_i8_g64_embed_rows.argtypes = [P, I64, I64, ctypes.POINTER(ctypes.c_int64), I64,
                                                P, ctypes.c_int32, P]
+        L.attention_decode_workspace_bytes.argtypes = [I64, I64, I64]
+        L.attention_decode_workspace_bytes.restype = I64
+        L.attention_decode.argtypes = [P, P, P, I64, I64, I64, I64, I64, ctypes.c_float,
+                                       ctypes.c_int32, P, P, SZ, P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
                   "qgemv_affine_i8_g64_group", "qgemv_q4_0_group",
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
                   "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
                   "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
-                  "qlinear_q4_0_gemv", "qlinear_q4_0_gemm"):
+                  "qlinear_q4_0_gemv", "qlinear_q4_0_gemm", "attention_decode"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -256,6 +261,24 @@ def qgemm_q4_0_prefill(w_q4_0, rows: int, cols: int, x_bf16, y, m: int,
 def q4_0_quantize(w, rows: int, cols: int, out, stream=None) -> None:
     _check("q4_0_quantize", lib().q4_0_quantize(
         _ptr(w), rows, cols, _ptr(out), _stream(stream)))
+
+
+def attention_decode_workspace_bytes(heads: int, kv_heads: int, head_dim: int) -> int:
+    return int(lib().attention_decode_workspace_bytes(heads, kv_heads, head_dim))
+
+
+def attention_decode(q, k_cache, v_cache, heads: int, kv_heads: int, head_dim: int,
+                     length: int, kv_start: int, scale: float, out, workspace,
+                     workspace_bytes: int, f16: bool = True, stream=None) -> None:
+    """Grouped-query decode attention of one token over the cache rows
+    [kv_start, length); q/out [heads, head_dim], caches [rows, kv_heads,
+    head_dim], all f16 (f16=True) or BF16.  workspace: device, 16-byte
+    aligned, attention_decode_workspace_bytes(heads, kv_heads, head_dim)
+    bytes for any window."""
+    _check("attention_decode", lib().attention_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), heads, kv_heads, head_dim, length, kv_start,
+        float(scale), 1 if f16 else 0, _ptr(out), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
 
 
 def stream_read(buf, nbytes: int, sink, stream=None) -> None:

@@ -1,0 +1,356 @@
+// attention.hip -- decode attention over the K/V cache (grouped-query), one
+// query row per head, split softmax.
+//
+// turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step
+// runs encode_attention_decode after the K/V projections have written the
+// current position's row into the cache: every query head h attends the rows
+// [kv_start, length) of K/V head h / (heads / kv_heads),
+//   out[h] = softmax_t(scale * q[h] . k[t]) v[t].
+// The cache row of position t holds all K/V heads ([rows][kv_heads][d]).
+//
+// Split softmax (the page keeps a split-softmax scratch for this): the
+// positions are cut into chunks; a workgroup takes one K/V head and one
+// chunk, for every query head of the group, so each cached row is read once
+// per group.  Inside a wave, d/8 lanes share a row (8 dimensions, 16 bytes
+// each) and the wave covers 64 / (d/8) rows per load; every lane keeps an
+// online softmax (running max m, sum l, output o) of the rows it has seen,
+// merged across lanes with shuffles and across waves in LDS.  A second
+// kernel, one workgroup per query head, combines the chunks' (m, l, o):
+// M = max m, out = sum o e^(m-M) / sum l e^(m-M); a window that fits one
+// chunk is normalised and stored by the first kernel.  Scores, exponentials
+// and sums are fp32; the output is rounded once to the 16-bit activation
+// type.  (Folding the combine into the first kernel -- the last workgroup
+// of a K/V head merging it -- measured slower at every window size: that
+// one workgroup's chain of memory round trips costs more than the second
+// launch.)
+#include "qd_device.h"
+#include "qd_internal.h"
+
+namespace qd {
+namespace {
+
+constexpr int kAttThreads = 256;
+constexpr int kAttWaves = kAttThreads / kWave;
+constexpr int kAttUnroll = 2;      // row loads in flight per lane (K and V each)
+constexpr int kAttTargetWgs = 512; // about two workgroups per CU of a 256-CU device
+
+template <bool F16>
+__device__ __forceinline__ float to_f32(uint32_t bits) {
+  return F16 ? f16_to_f32(bits) : bf16_to_f32(bits);
+}
+
+template <bool F16>
+__device__ __forceinline__ void unpack8(const u32x4 w, float (&f)[8]) {
+  const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = to_f32<F16>(e[i] & 0xffffu);
+    f[2 * i + 1] = to_f32<F16>(e[i] >> 16);
+  }
+}
+
+// Merge (m2, l2, o2) into (m, l, o); m = -inf marks an empty state.
+template <int G>
+__device__ __forceinline__ void merge(float (&m)[G], float (&l)[G], float (&o)[G][8],
+                                      const float (&m2)[G], const float (&l2)[G],
+                                      const float (&o2)[G][8]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mm = fmaxf(m[h], m2[h]);
+    const float a = m[h] == -INFINITY ? 0.f : __expf(m[h] - mm);
+    const float b = m2[h] == -INFINITY ? 0.f : __expf(m2[h] - mm);
+    l[h] = l[h] * a + l2[h] * b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[h][i] = o[h][i] * a + o2[h][i] * b;
+    m[h] = mm;
+  }
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t store16(float v) {
+  return F16 ? f32_to_f16(v) : f32_to_bf16(v);
+}
+
+// The G * D outputs of G query heads from their nchunks partials (layout of
+// attention_partial_kernel), by one workgroup: thread t
+// takes output t (and t + 256, ...); when there are fewer outputs than
+// threads, S slices of the chunks run side by side and merge in LDS.  Chunks
+// are read kCombBatch at a time with independent loads, and each batch is
+// folded in against its own maximum, so a head costs about
+// nchunks / (S * kCombBatch) memory round trips.
+constexpr int kCombBatch = 16;
+template <int D, int G, bool F16>
+__device__ __forceinline__ void combine_chunks(const QD_GLOBAL float *part, int nchunks,
+                                               QD_GLOBAL uint16_t *out) {
+  constexpr int OUTS = G * D;
+  constexpr int S = OUTS >= kAttThreads ? 1 : kAttThreads / OUTS;
+  constexpr int PER = OUTS >= kAttThreads ? OUTS / kAttThreads : 1;
+  constexpr int W = kAttThreads / S;  // outputs per pass
+  __shared__ float sm[S][W], sl[S][W], so[S][W];
+  const int t = threadIdx.x;
+  const int slice = t / W, k = t % W;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = r * kAttThreads + k;
+    const int h = idx / D, i = idx % D;
+    const QD_GLOBAL float *ph = part + (size_t)h * nchunks * (D + 2);
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int c0 = slice; c0 < nchunks; c0 += kCombBatch * S) {
+      float mc[kCombBatch], lc[kCombBatch], oc[kCombBatch];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const int c = min(c0 + u * S, nchunks - 1);
+        const QD_GLOBAL float *pc = ph + (size_t)c * (D + 2);
+        mc[u] = pc[0];
+        lc[u] = pc[1];
+        oc[u] = pc[2 + i];
+      }
+      float mb = m;
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u)
+        if (c0 + u * S < nchunks) mb = fmaxf(mb, mc[u]);
+      const float a = m == -INFINITY ? 0.f : __expf(m - mb);
+      l *= a;
+      o *= a;
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const float w =
+            (c0 + u * S < nchunks && mc[u] != -INFINITY) ? __expf(mc[u] - mb) : 0.f;
+        l = fmaf(lc[u], w, l);
+        o = fmaf(oc[u], w, o);
+      }
+      m = mb;
+    }
+    if (S > 1) {
+      sm[slice][k] = m;
+      sl[slice][k] = l;
+      so[slice][k] = o;
+      __syncthreads();
+      if (slice == 0) {
+        for (int q = 1; q < S; ++q) {
+          const float m2 = sm[q][k], l2 = sl[q][k], o2 = so[q][k];
+          const float mm = fmaxf(m, m2);
+          const float a = m == -INFINITY ? 0.f : __expf(m - mm);
+          const float b = m2 == -INFINITY ? 0.f : __expf(m2 - mm);
+          l = l * a + l2 * b;
+          o = o * a + o2 * b;
+          m = mm;
+        }
+        out[idx] = store16<F16>(o / l);
+      }
+    } else {
+      out[idx] = store16<F16>(o / l);
+    }
+  }
+}
+
+// Chunk c of K/V head j for its G query heads.  With FINAL (a single chunk)
+// the normalised output is stored; otherwise the partial (m, l, o[d]) goes to
+// part[((j * G + h) * nchunks + c) * (d + 2) + {0: m, 1: l, 2..: o}].
+template <int D, int G, bool F16, bool FINAL>
+__global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
+    const uint16_t *__restrict__ q_, const uint16_t *__restrict__ k_,
+    const uint16_t *__restrict__ v_, int kv_heads, int kv_start, int length, int rows_per_wave,
+    float scale, float *__restrict__ part, uint16_t *__restrict__ out_) {
+  constexpr int LPP = D / 8;         // lanes per cached row
+  constexpr int PPS = kWave / LPP;   // rows per wave load
+  __shared__ float red[kAttWaves][G][10][LPP];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = blockIdx.y;          // K/V head
+  const int c = blockIdx.x;          // chunk
+  const int nchunks = gridDim.x;
+  const int sub = lane % LPP, grp = lane / LPP;
+  const QD_GLOBAL uint16_t *q = gp(q_);
+  const QD_GLOBAL uint16_t *kc = gp(k_);
+  const QD_GLOBAL uint16_t *vc = gp(v_);
+  const size_t row = (size_t)kv_heads * D;  // elements per cache row
+
+  // this lane's 8 dimensions of each query head, fp32, pre-scaled
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    unpack8<F16>(*(const QD_GLOBAL u32x4 *)(q + (size_t)(j * G + h) * D + 8 * sub), qf[h]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[h][i] *= scale;
+  }
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
+  }
+  const int t0 = kv_start + (c * kAttWaves + wave) * rows_per_wave;
+  const int t1 = min(t0 + rows_per_wave, length);
+  for (int tb = t0; tb < t1; tb += PPS * kAttUnroll) {
+    u32x4 kw[kAttUnroll], vw[kAttUnroll];
+    bool valid[kAttUnroll];
+#pragma unroll
+    for (int u = 0; u < kAttUnroll; ++u) {
+      const int t = tb + u * PPS + grp;
+      valid[u] = t < t1;
+      const int tr = valid[u] ? t : t1 - 1;  // rows past the range re-read its last row
+      const size_t off = (size_t)tr * row + (size_t)j * D + 8 * sub;
+      kw[u] = *(const QD_GLOBAL u32x4 *)(kc + off);
+      vw[u] = *(const QD_GLOBAL u32x4 *)(vc + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kAttUnroll; ++u) {
+      float kf[8], vf[8];
+      unpack8<F16>(kw[u], kf);
+      unpack8<F16>(vw[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(qf[h][i], kf[i], s);
+        // the row's score: sum over its LPP lanes
+#pragma unroll
+        for (int w = 1; w < LPP; w <<= 1) s += __shfl_xor(s, w, kWave);
+        if (!valid[u]) s = -INFINITY;
+        const float mm = fmaxf(m[h], s);
+        const float a = m[h] == -INFINITY ? 0.f : __expf(m[h] - mm);
+        const float p = s == -INFINITY ? 0.f : __expf(s - mm);
+        l[h] = l[h] * a + p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[h][i] = fmaf(p, vf[i], o[h][i] * a);
+        m[h] = mm;
+      }
+    }
+  }
+  // merge the row slots of the wave (lanes with the same sub)
+#pragma unroll
+  for (int w = LPP; w < kWave; w <<= 1) {
+    float m2[G], l2[G], o2[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m2[h] = __shfl_xor(m[h], w, kWave);
+      l2[h] = __shfl_xor(l[h], w, kWave);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o2[h][i] = __shfl_xor(o[h][i], w, kWave);
+    }
+    merge<G>(m, l, o, m2, l2, o2);
+  }
+  // merge the waves in LDS; the first row slot of wave 0 finishes the chunk
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      red[wave][h][0][sub] = m[h];
+      red[wave][h][1][sub] = l[h];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave][h][2 + i][sub] = o[h][i];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    if (grp == 0) {
+      for (int w = 1; w < kAttWaves; ++w) {
+        float m2[G], l2[G], o2[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          m2[h] = red[w][h][0][sub];
+          l2[h] = red[w][h][1][sub];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o2[h][i] = red[w][h][2 + i][sub];
+        }
+        merge<G>(m, l, o, m2, l2, o2);
+      }
+      if (FINAL) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          uint32_t e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            e[i] = (uint32_t)store16<F16>(o[h][2 * i] / l[h]) |
+                   ((uint32_t)store16<F16>(o[h][2 * i + 1] / l[h]) << 16);
+          u32x4 st;
+          st.x = e[0];
+          st.y = e[1];
+          st.z = e[2];
+          st.w = e[3];
+          *(QD_GLOBAL u32x4 *)(gp(out_) + (size_t)(j * G + h) * D + 8 * sub) = st;
+        }
+      } else {
+        QD_GLOBAL float *pp = gp(part);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          QD_GLOBAL float *dst = pp + ((size_t)(j * G + h) * nchunks + c) * (D + 2);
+          if (sub == 0) {
+            dst[0] = m[h];
+            dst[1] = l[h];
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dst[2 + 8 * sub + i] = o[h][i];
+        }
+      }
+    }
+  }
+}
+
+// out[h] from the nchunks partials of query head h, one workgroup per head.
+template <int D, bool F16>
+__global__ __launch_bounds__(kAttThreads) void attention_combine_kernel(
+    const float *__restrict__ part, int nchunks, uint16_t *__restrict__ out) {
+  const int h = blockIdx.x;
+  combine_chunks<D, 1, F16>(gp(part) + (size_t)h * nchunks * (D + 2), nchunks,
+                            gp(out) + (size_t)h * D);
+}
+
+template <int D, int G, bool F16>
+hipError_t launch_att(const AttentionArgs &a, hipStream_t stream) {
+  const AttentionPlan p = attention_plan(a.kv_heads, a.length - a.kv_start, D);
+  if (p.nchunks < 1 || p.nchunks > attention_max_chunks(a.kv_heads)) return hipErrorInvalidValue;
+  if (p.nchunks == 1) {
+    hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, true>), dim3(1, a.kv_heads),
+                       dim3(kAttThreads), 0, stream, a.q, a.k, a.v, a.kv_heads, a.kv_start,
+                       a.length, p.rows_per_wave, a.scale, a.part, a.out);
+  } else {
+    hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, false>),
+                       dim3(p.nchunks, a.kv_heads), dim3(kAttThreads), 0, stream, a.q, a.k, a.v,
+                       a.kv_heads, a.kv_start, a.length, p.rows_per_wave, a.scale, a.part,
+                       a.out);
+    hipLaunchKernelGGL((attention_combine_kernel<D, F16>), dim3(a.kv_heads * G),
+                       dim3(kAttThreads), 0, stream, a.part, p.nchunks, a.out);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool F16>
+hipError_t launch_att_g(const AttentionArgs &a, hipStream_t stream) {
+  switch (a.heads / a.kv_heads) {
+    case 1: return launch_att<D, 1, F16>(a, stream);
+    case 2: return launch_att<D, 2, F16>(a, stream);
+    case 4: return launch_att<D, 4, F16>(a, stream);
+    default: return launch_att<D, 8, F16>(a, stream);
+  }
+}
+
+}  // namespace
+
+AttentionPlan attention_plan(int64_t kv_heads, int64_t window, int head_dim) {
+  // whole loads of rows per wave, about kAttTargetWgs workgroups in all
+  const int64_t step = (int64_t)(kWave / (head_dim / 8)) * kAttUnroll;
+  const int64_t want = (kAttTargetWgs + kv_heads - 1) / kv_heads;
+  int64_t rpw = (window + want * kAttWaves - 1) / (want * kAttWaves);
+  rpw = (rpw + step - 1) / step * step;
+  if (rpw < step) rpw = step;
+  AttentionPlan p;
+  p.rows_per_wave = (int)rpw;
+  p.nchunks = (int)((window + rpw * kAttWaves - 1) / (rpw * kAttWaves));
+  return p;
+}
+
+int64_t attention_max_chunks(int64_t kv_heads) {
+  // nchunks = ceil(window / (kAttWaves * rpw)) with kAttWaves * rpw >= window / want
+  return (kAttTargetWgs + kv_heads - 1) / kv_heads;
+}
+
+hipError_t launch_attention_decode(const AttentionArgs &a, hipStream_t stream) {
+  if (a.head_dim == 64)
+    return a.f16 ? launch_att_g<64, true>(a, stream) : launch_att_g<64, false>(a, stream);
+  return a.f16 ? launch_att_g<128, true>(a, stream) : launch_att_g<128, false>(a, stream);
+}
+
+}  // namespace qd

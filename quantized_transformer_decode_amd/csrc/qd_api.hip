@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 
 #include "../../include/qdecode.h"
 #include "qd_internal.h"
@@ -608,6 +609,63 @@ qd_status qgemv_affine_i8_g64_step_check(const qd_step_plan *plan,
   if (e != hipSuccess) return hip_fail(e);
   *error_bits = v;
   return v ? QD_ESTEP : QD_OK;
+}
+
+}  // extern "C"
+
+static bool attention_shape_ok(int64_t heads, int64_t kv_heads, int64_t head_dim) {
+  if (kv_heads < 1 || kv_heads > 65535 || heads < 1 || heads % kv_heads != 0) return false;
+  const int64_t g = heads / kv_heads;
+  return (g == 1 || g == 2 || g == 4 || g == 8) && (head_dim == 64 || head_dim == 128);
+}
+
+extern "C" {
+
+int64_t attention_decode_workspace_bytes(int64_t heads, int64_t kv_heads, int64_t head_dim) {
+  if (!attention_shape_ok(heads, kv_heads, head_dim)) return 0;
+  return heads * qd::attention_max_chunks(kv_heads) * (head_dim + 2) * 4;
+}
+
+qd_status attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                           int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t length,
+                           int64_t kv_start, float scale, int32_t f16, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k_cache || !v_cache || !out || !workspace) return QD_EINVAL;
+  if (f16 != 0 && f16 != 1) return QD_EINVAL;
+  if (!attention_shape_ok(heads, kv_heads, head_dim)) return QD_ESHAPE;
+  if (kv_start < 0 || kv_start >= length || length > (int64_t(1) << 30)) return QD_EINVAL;
+  if (!std::isfinite(scale)) return QD_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16))
+    return QD_EALIGN;
+  const int64_t need = attention_decode_workspace_bytes(heads, kv_heads, head_dim);
+  if ((int64_t)workspace_bytes < need) return QD_EINVAL;
+  const size_t qb = (size_t)heads * head_dim * 2;
+  const size_t cb = (size_t)length * kv_heads * head_dim * 2;
+  const void *ins[3] = {q, k_cache, v_cache};
+  const size_t insz[3] = {qb, cb, cb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(out, qb, ins[i], insz[i])) return QD_EINVAL;
+    if (overlap(workspace, (size_t)need, ins[i], insz[i])) return QD_EINVAL;
+  }
+  if (overlap(out, qb, workspace, (size_t)need)) return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  qd::AttentionArgs a;
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k_cache;
+  a.v = (const uint16_t *)v_cache;
+  a.out = (uint16_t *)out;
+  a.part = (float *)workspace;
+  a.heads = (int)heads;
+  a.kv_heads = (int)kv_heads;
+  a.head_dim = (int)head_dim;
+  a.kv_start = (int)kv_start;
+  a.length = (int)length;
+  a.scale = scale;
+  a.f16 = f16 == 1;
+  hipError_t e = qd::launch_attention_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 
 }  // extern "C"

@@ -56,6 +56,26 @@ hipError_t launch_q4_0_gemm(Q40Group g, int cols, const uint16_t *x, int m,
 hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
                                 hipStream_t stream);
 
+// Decode attention over the K/V cache (attention.hip).  q, k, v and out are
+// 16-bit (f16, else BF16); the cache rows are [rows][kv_heads][head_dim];
+// part holds heads * nchunks * (head_dim + 2) floats of chunk partials.
+struct AttentionArgs {
+  const uint16_t *q, *k, *v;
+  uint16_t *out;
+  float *part;
+  int heads, kv_heads, head_dim, kv_start, length;
+  float scale;
+  bool f16;
+};
+// Rows per wave and chunks of the window [kv_start, length) (host only).
+struct AttentionPlan {
+  int rows_per_wave, nchunks;
+};
+AttentionPlan attention_plan(int64_t kv_heads, int64_t window, int head_dim);
+// Upper bound of nchunks over every window (host only).
+int64_t attention_max_chunks(int64_t kv_heads);
+hipError_t launch_attention_decode(const AttentionArgs &a, hipStream_t stream);
+
 // Practical HBM read ceiling (hbm_probe.hip): reads `bytes` (a multiple of
 // 1024) once.
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink,

@@ -109,6 +109,21 @@ def x_f16(m: int, cols: int, key=(0, 0, 0)) -> np.ndarray:
         np.float16).view(np.uint16)
 
 
+def attention_inputs(heads: int, kv_heads: int, head_dim: int, rows: int, key=(0, 0, 0),
+                     f16: bool = True):
+    """Decode-attention operands as 16-bit bits (f16, else BF16): q [heads,
+    head_dim] and K, V caches [rows, kv_heads, head_dim], entries N(0, 1)
+    (the scale of per-head RMS-normed q and k)."""
+    c, l, mm = key
+    g = rng(c, l, mm, K_X)
+    a = [g.standard_normal(shape).astype(np.float32)
+         for shape in ((heads, head_dim), (rows, kv_heads, head_dim),
+                       (rows, kv_heads, head_dim))]
+    if f16:
+        return tuple(x.astype(np.float16).view(np.uint16) for x in a)
+    return tuple(to_bf16_bits(x) for x in a)
+
+
 def x_f32(m: int, cols: int, key=(0, 0, 0)) -> np.ndarray:
     """Activations f32 N(0, 1) [m, cols]."""
     c, l, mm = key

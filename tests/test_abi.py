@@ -240,6 +240,56 @@ def test_errors_stream_read():
     assert _call(f, A, 1024, B + 2, None) == qd.QD_EALIGN
 
 
+OUT = 0x7f3000000000
+WS = 0x7f4000000000
+
+
+def test_attention_workspace_bytes():
+    f = qd.attention_decode_workspace_bytes
+    # one float per (head, chunk, d + 2) for at most ceil(512 / kv_heads) chunks
+    assert f(16, 8, 128) == 16 * 64 * 130 * 4
+    assert f(8, 8, 64) == 8 * 64 * 66 * 4
+    assert f(65, 65, 128) == 65 * 8 * 130 * 4
+    assert f(8, 1, 128) == 8 * 512 * 130 * 4
+    assert f(16, 8, 96) == 0          # head_dim
+    assert f(24, 8, 128) == 0         # group of 3
+    assert f(16, 0, 128) == 0
+    assert f(16, 16, 128) > 0 and f(128, 16, 128) > 0 and f(256, 16, 128) == 0
+
+
+def test_errors_attention_decode():
+    f = "attention_decode"
+    ws = qd.attention_decode_workspace_bytes(16, 8, 128)
+
+    def call(q=A, k=B, v=C, heads=16, kvh=8, d=128, n=100, s=0, scale=0.088, f16=1, out=OUT,
+             w=WS, wb=ws):
+        return _call(f, q, k, v, heads, kvh, d, n, s, ctypes.c_float(scale), f16, out, w, wb,
+                     None)
+
+    for bad in ({"q": None}, {"k": None}, {"v": None}, {"out": None}, {"w": None}):
+        assert call(**bad) == qd.QD_EINVAL
+    assert call(f16=2) == qd.QD_EINVAL
+    assert call(heads=24) == qd.QD_ESHAPE             # group of 3
+    assert call(heads=12) == qd.QD_ESHAPE             # not a multiple of kv_heads
+    assert call(heads=256, kvh=16) == qd.QD_ESHAPE    # group of 16
+    assert call(d=96) == qd.QD_ESHAPE
+    assert call(kvh=0) == qd.QD_ESHAPE
+    assert call(n=0) == qd.QD_EINVAL                  # empty window
+    assert call(s=100) == qd.QD_EINVAL
+    assert call(s=-1) == qd.QD_EINVAL
+    assert call(n=(1 << 30) + 1, wb=1 << 40) == qd.QD_EINVAL
+    assert call(scale=float("nan")) == qd.QD_EINVAL
+    assert call(scale=float("inf")) == qd.QD_EINVAL
+    assert call(q=A + 8) == qd.QD_EALIGN
+    assert call(k=B + 2) == qd.QD_EALIGN
+    assert call(out=OUT + 8) == qd.QD_EALIGN
+    assert call(w=WS + 4) == qd.QD_EALIGN
+    assert call(wb=ws - 1) == qd.QD_EINVAL            # workspace too small
+    assert call(out=B + 4096) == qd.QD_EINVAL         # output inside the K cache
+    assert call(w=C + 4096) == qd.QD_EINVAL           # workspace inside the V cache
+    assert call(out=WS + 256) == qd.QD_EINVAL         # output inside the workspace
+
+
 def _gpu_visible():
     try:
         hip = ctypes.CDLL("libamdhip64.so")
@@ -269,3 +319,6 @@ def test_valid_args_reach_device_check():
     assert _call("qgemv_q4_0_group", _q4_items((A, C, 64), (D, E, 32)), 2, 512,
                  B, 4, None) == qd.QD_EDEVICE
     assert _call("affine_i8_g64_pack", A, B, C, 4, 64, A + (1 << 20), None) == qd.QD_EDEVICE
+    ws = qd.attention_decode_workspace_bytes(16, 8, 128)
+    assert _call("attention_decode", A, B, C, 16, 8, 128, 4096, 0, ctypes.c_float(0.088), 1,
+                 OUT, WS, ws, None) == qd.QD_EDEVICE
