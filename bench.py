@@ -525,8 +525,46 @@ def row_q4_0_bake(qd):
             "hbm_peak_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
+def row_attention_decode(qd):
+    """Grouped-query decode attention, f16 (the page's Metal dtype), as a
+    decode step runs it: one call per layer over 28 layers' own caches
+    (Qwen3-0.6B/1.7B heads: 16 query / 8 K/V heads of 128) at windows of
+    128 .. 32768 rows, and the 32-head (Qwen3-4B) shape at 4096.  Bytes are
+    the K and V rows of the window (+ q and out), read once per call."""
+    import math
+    import numpy as np
+    import torch
+    import synth
+    layers = 28
+    out = {"layers": layers, "dtype": "f16"}
+    for heads, kv, d, n in ((16, 8, 128, 128), (16, 8, 128, 1024), (16, 8, 128, 4096),
+                            (16, 8, 128, 32768), (32, 8, 128, 4096)):
+        qb, kb, vb = synth.attention_inputs(heads, kv, d, n, key=(12, heads, n))
+        def dev(bits):
+            return torch.from_numpy(bits.view(np.int16).copy()).to(DEV).view(torch.float16)
+        q, k0, v0 = dev(qb), dev(kb), dev(vb)
+        ks = [k0.clone() for _ in range(layers)]
+        vs = [v0.clone() for _ in range(layers)]
+        del k0, v0
+        o = torch.empty((heads, d), dtype=torch.float16, device=DEV)
+        wsb = qd.attention_decode_workspace_bytes(heads, kv, d)
+        ws = torch.empty(wsb // 4, dtype=torch.float32, device=DEV)
+        scale = 1.0 / math.sqrt(d)
+        g = capture(lambda: [qd.attention_decode(q, ks[i], vs[i], heads, kv, d, n, 0, scale, o,
+                                                 ws, wsb) for i in range(layers)])
+        ms = event_time(g.replay, 10, 2) / layers
+        nbytes = 2 * n * kv * d * 2 + 2 * heads * d * 2
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[f"h{heads}_kv{kv}_d{d}_n{n}"] = {
+            "us_per_layer": ms * 1e3, "bytes_per_call": nbytes, "GBps": gbps,
+            "hbm_peak_frac": gbps / HBM_PEAK_GBPS, "us_per_token_all_layers": ms * 1e3 * layers}
+        del ks, vs
+        torch.cuda.empty_cache()
+    return out
+
+
 ROWS = ("affine_gemv_1024", "affine_lm_head", "affine_f16", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
-        "whisper_large_decoder", "q4_0_bake")
+        "whisper_large_decoder", "q4_0_bake", "attention_decode")
 
 
 # HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs

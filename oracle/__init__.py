@@ -17,6 +17,8 @@ Sources (page title -- section):
   fuel-transformers 0.19.1, src/models/lazy_quantized_whisper.rs -- module
       documentation, quantize_in_out_to_q4_0, q_linear (Q4_0 format, bake and
       matmul).
+  turbospark-runtime 0.3.0, src/qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step
+      (the decoder step: norms, RoPE, decode attention, SiLU-mul, residuals).
 """
 from __future__ import annotations
 
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.qdo_affine_weight.restype = D
         L.qdo_affine_gemv.argtypes = [P, I64, I64, P, ctypes.c_int, I64, P, I64, P, I64, P]
         L.qdo_affine_embed_row.argtypes = [P, I64, I64, I64, ctypes.c_int, P]
+        L.qdo_affine_gemv_f64.argtypes = [P, I64, I64, P, P, I64, P]
+        L.qdo_affine_gemv_f64.restype = None
         L.qdo_f32_to_bf16_rne.argtypes = [ctypes.c_float]
         L.qdo_f32_to_bf16_rne.restype = ctypes.c_uint16
         L.qdo_affine_gemv.restype = None
@@ -279,6 +283,121 @@ def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, le
         p /= p.sum()
         out[h] = p @ v[kv_start:length, j, :]
     return out
+
+
+# ---- the decoder step around the GEMVs ---------------------------------------
+#
+# turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step:
+# every buffer of the step (the residual row x, normed, q, the K/V cache
+# rows, attn, delta, gate, up, logits) holds f16; the norm weights are BF16.
+# The kernels' internal precision is not on the page: each op here is
+# evaluated exactly (f64, exact weights) and its result rounded to f16 once,
+# where the page stores it.
+
+def round_f16(v) -> np.ndarray:
+    """Nearest-even f16 rounding of f64 values, taken directly from f64
+    (numpy's double -> half conversion), returned as f64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def f16_bits(v) -> np.ndarray:
+    """uint16 bits of values that are already f16 numbers."""
+    a = np.asarray(v, dtype=np.float64)
+    h = a.astype(np.float16)
+    assert np.array_equal(h.astype(np.float64), a, equal_nan=True), "not f16 values"
+    return h.view(np.uint16)
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """encode_rms_norm_bf16w / _perhead: over the last axis,
+    y = x / sqrt(mean(x^2) + eps) * w (per head for a [heads, d] input)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+
+def rope_neox(x: np.ndarray, position: int, theta: float) -> np.ndarray:
+    """encode_rope_neox_subdim with the rotary width equal to head_dim:
+    rotate-half RoPE on [..., d]; pair (i, i + d/2) turns by the angle
+    position * theta^(-2i/d)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    ang = position * np.power(float(theta), -2.0 * np.arange(half, dtype=np.float64) / d)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """encode_silu_mul: silu(gate) * up, silu(g) = g / (1 + e^-g)."""
+    g = np.asarray(gate, dtype=np.float64)
+    return g / (1.0 + np.exp(-g)) * np.asarray(up, dtype=np.float64)
+
+
+def affine_gemv_f64(blob: np.ndarray, rows: int, cols: int, x: np.ndarray,
+                    row_sel=None) -> np.ndarray:
+    """y = W x for one f64 vector (exact weights, f64 sum)."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64).reshape(cols))
+    rs, n_r = _sel(row_sel, rows)
+    y = np.zeros(n_r, dtype=np.float64)
+    lib().qdo_affine_gemv_f64(_ptr(blob), rows, cols, _ptr(x), _ptr(rs), n_r, _ptr(y))
+    return y
+
+
+def qwen3_step(x_row, position: int, model: dict, k_caches, v_caches, f16: bool = True,
+               logit_rows=None):
+    """Qwen3AsrMetalEngine::step for one input row at `position`, in the
+    page's op order; appends the rotated K and the V row of every layer at
+    cache row `position` (caches [rows, kv_heads, head_dim] f64 arrays,
+    modified in place) and returns (x after the last layer, logits of
+    `logit_rows` (all rows if None) or None when model["embed"] is None).
+
+    model: hidden, heads, kv_heads, head_dim, inter, eps, theta (the page's
+    f32 config values), layers: list of dicts with affine blobs q, k, v, o,
+    gate, up, down and norm weights in_norm, q_norm, k_norm, post_norm (f64
+    values of BF16 weights); final_norm; embed (the tied table's blob) and
+    vocab.  With f16, every stored buffer is rounded to f16 (the page's
+    buffers) and the GEMVs read their f16 inputs; without, nothing is
+    rounded (the same maths in f64)."""
+    hid, heads, kvh, d = model["hidden"], model["heads"], model["kv_heads"], model["head_dim"]
+    inter, eps, theta = model["inter"], model["eps"], model["theta"]
+    r = round_f16 if f16 else (lambda v: np.asarray(v, dtype=np.float64))
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(d)))  # the page's f32 1/sqrt(d)
+
+    def gemv(blob, rows, cols, v, row_sel=None):
+        if f16:
+            return affine_gemv(blob, rows, cols, f16_bits(v).reshape(1, cols), row_sel=row_sel,
+                               x_f16=True)[0]
+        return affine_gemv_f64(blob, rows, cols, v, row_sel=row_sel)
+
+    x = r(x_row)
+    for L, kc, vc in zip(model["layers"], k_caches, v_caches):
+        normed = r(rms_norm(x, L["in_norm"], eps))
+        q = r(gemv(L["q"], heads * d, hid, normed)).reshape(heads, d)
+        k = r(gemv(L["k"], kvh * d, hid, normed)).reshape(kvh, d)
+        v = r(gemv(L["v"], kvh * d, hid, normed)).reshape(kvh, d)
+        q = r(rms_norm(q, L["q_norm"], eps))
+        k = r(rms_norm(k, L["k_norm"], eps))
+        q = r(rope_neox(q, position, theta))
+        k = r(rope_neox(k, position, theta))
+        kc[position] = k
+        vc[position] = v
+        attn = r(attention_decode(q, kc, vc, position + 1, scale))
+        delta = r(gemv(L["o"], hid, heads * d, attn.reshape(-1)))
+        x = r(x + delta)
+        normed = r(rms_norm(x, L["post_norm"], eps))
+        gate = r(gemv(L["gate"], inter, hid, normed))
+        up = r(gemv(L["up"], inter, hid, normed))
+        act = r(silu_mul(gate, up))
+        delta = r(gemv(L["down"], hid, inter, act))
+        x = r(x + delta)
+    if model.get("embed") is None:
+        return x, None
+    normed = r(rms_norm(x, model["final_norm"], eps))
+    logits = r(gemv(model["embed"], model["vocab"], hid, normed, row_sel=logit_rows))
+    return x, logits
 
 
 # ---- tolerance metric -------------------------------------------------------

@@ -184,6 +184,21 @@ void qdo_affine_gemv(const uint8_t *blob, int64_t rows, int64_t cols,
   }
 }
 
+/* y[j] = sum_c w(r, c) x[c] for one f64 input vector (rows row_sel[j], or
+ * all rows): the same exact-weight dot product as qdo_affine_gemv for inputs
+ * that are not 16-bit values (the unrounded decoder-step reference). */
+void qdo_affine_gemv_f64(const uint8_t *blob, int64_t rows, int64_t cols, const double *x,
+                         const int64_t *row_sel, int64_t n_rows, double *y) {
+  if (!row_sel) n_rows = rows;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t j = 0; j < n_rows; ++j) {
+    int64_t r = row_sel ? row_sel[j] : j;
+    double acc = 0.0;
+    for (int64_t c = 0; c < cols; ++c) acc += qdo_affine_weight(blob, rows, cols, r, c) * x[c];
+    y[j] = acc;
+  }
+}
+
 /* [P3] embed_row_bytes: the tied-embedding row of `token` as 16-bit values,
  * each q*scale + bias evaluated in binary32 (q*scale is exact there: at most
  * 8 + 8 significant bits, so only the addition rounds) and then rounded to

@@ -70,13 +70,13 @@ class AffineTriplet:
     biases: np.ndarray  # uint16 [rows, cols//64]
 
 
-def affine_triplet(rows: int, cols: int, key=(0, 0, 0)) -> AffineTriplet:
-    """codes uniform u8 0..255; scales uniform [1e-3, 1e-2] -> BF16;
+def affine_triplet(rows: int, cols: int, key=(0, 0, 0), scale_range=(1e-3, 1e-2)) -> AffineTriplet:
+    """codes uniform u8 0..255; scales uniform in scale_range -> BF16;
     biases BF16(-128 * scale_bf16 + N(0, 1e-4))."""
     c, l, m = key
     g = cols // 64
     codes = rng(c, l, m, K_CODES).integers(0, 256, size=rows * cols, dtype=np.uint8)
-    s = rng(c, l, m, K_SCALES).uniform(1e-3, 1e-2, size=(rows, g))
+    s = rng(c, l, m, K_SCALES).uniform(scale_range[0], scale_range[1], size=(rows, g))
     s_bits = to_bf16_bits(s.astype(np.float32))
     s_val = bf16_bits_to_f32(s_bits).astype(np.float64)
     b = -128.0 * s_val + rng(c, l, m, K_BIASES).normal(0.0, 1e-4, size=(rows, g))
@@ -173,6 +173,52 @@ def decode_step_matrices(spec: DecoderSpec):
         stage += 1
     out.append((spec.layers, "lm_head", spec.vocab, spec.hidden, stage))
     return out
+
+
+@dataclass(frozen=True)
+class Qwen3Spec:
+    """Decoder shape and config values of a Qwen3 text model (eps and theta
+    as the page's f32 config values)."""
+    name: str
+    hidden: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    inter: int
+    vocab: int
+    layers: int
+    eps: float = 1e-6
+    theta: float = 1e6
+
+
+QWEN3_0_6B_STEP = Qwen3Spec("qwen3-0.6b", 1024, 16, 8, 128, 3072, 151936, 28)
+QWEN3_TINY_STEP = Qwen3Spec("qwen3-tiny", 256, 4, 2, 64, 512, 1000, 2)
+
+
+def qwen3_model(spec: Qwen3Spec, key: int = 0, layers=None):
+    """Random-init weights of a Qwen3 decoder in the page's storage forms:
+    per layer the affine triplets q, k, v, o, gate, up, down (scales uniform
+    in [1e-4, 1e-3]: weights of about 0.04 rms, as trained int8 layers) and
+    BF16 norm weights in_norm, q_norm, k_norm, post_norm ~ N(1, 0.1); the
+    final norm; the tied embedding table as a triplet [vocab, hidden]."""
+    sr = (1e-4, 1e-3)
+    hid, d = spec.hidden, spec.head_dim
+    shapes = (("q", spec.heads * d, hid), ("k", spec.kv_heads * d, hid),
+              ("v", spec.kv_heads * d, hid), ("o", hid, spec.heads * d),
+              ("gate", spec.inter, hid), ("up", spec.inter, hid), ("down", hid, spec.inter))
+    norms = (("in_norm", hid), ("q_norm", d), ("k_norm", d), ("post_norm", hid))
+    out = []
+    for li in range(spec.layers if layers is None else layers):
+        L = {}
+        for j, (name, rows, cols) in enumerate(shapes):
+            L[name] = affine_triplet(rows, cols, key=(20 + key, li, j), scale_range=sr)
+        for j, (name, n) in enumerate(norms):
+            w = rng(20 + key, li, 16 + j, K_WF32).normal(1.0, 0.1, size=n).astype(np.float32)
+            L[name] = to_bf16_bits(w)
+        out.append(L)
+    fw = rng(20 + key, 9999, 0, K_WF32).normal(1.0, 0.1, size=hid).astype(np.float32)
+    embed = affine_triplet(spec.vocab, hid, key=(20 + key, 9999, 1), scale_range=sr)
+    return {"layers": out, "final_norm": to_bf16_bits(fw), "embed": embed}
 
 
 WHISPER_BASE_FFN = [("fc1", 2048, 512), ("fc2", 512, 2048)]
