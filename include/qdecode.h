@@ -351,6 +351,105 @@ qd_status attention_decode(const void *q, const void *k_cache, const void *v_cac
                            int64_t kv_start, float scale, int32_t f16, void *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- the decoder step around the GEMVs ------------------------------------ */
+
+/* turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step
+ * and the ops it encodes.  Every activation buffer is f16 (the page's
+ * buffers), norm weights are BF16; each op computes in fp32 and rounds its
+ * result to f16 once, where the page stores it. */
+
+/* encode_residual_add + encode_rms_norm_bf16w: when delta is not NULL,
+ * x <- f16(x + delta) (written back; the page's residual add); then
+ * out = f16(x / sqrt(mean(x^2) + eps) * w).
+ *   x      device, f16 [n], 8-byte aligned (in/out)
+ *   delta  device, f16 [n], 8-byte aligned, or NULL
+ *   w      device, BF16 [n], 8-byte aligned
+ *   out    device, f16 [n], 8-byte aligned; may not overlap x, delta or w
+ * Requires n % 64 == 0 and 64 <= n <= 8192 (QD_ESHAPE), eps finite and
+ * >= 0 (QD_EINVAL).  One workgroup; asynchronous on `stream`. */
+qd_status rmsnorm_f16(void *x, const void *delta, const void *w, int64_t n, float eps,
+                      void *out, void *stream);
+
+/* encode_rms_norm_bf16w_perhead + encode_rope_neox_subdim (rotary width =
+ * head_dim) on q and on the new K row, which then lands in the cache, and
+ * the V row copied into the cache: with p = *position (device int32),
+ *   q[h]           <- f16(rope(f16(rmsnorm(q[h]) * q_norm), p))   (in place)
+ *   k_cache[p, j]  <- f16(rope(f16(rmsnorm(k_src[j]) * k_norm), p))
+ *   v_cache[p, j]  <- v_src[j]
+ * where rope turns the pair (i, i + d/2) by p * theta^(-2i/d) (angle and its
+ * sine and cosine in fp64, the rotation in fp32).
+ *   q, k_src, v_src  device, f16 [heads * d] / [kv_heads * d] / [kv_heads * d]
+ *   q_norm, k_norm   device, BF16 [head_dim]
+ *   position         device, one int32; a value outside [0, capacity) writes
+ *                    nothing and sets bit 1 of *error_word
+ *   k_cache, v_cache device, f16 [capacity, kv_heads, head_dim]
+ *   error_word       device, one uint32 (bits are only ever set)
+ * Requires head_dim 64 or 128 and heads, kv_heads >= 1 (QD_ESHAPE),
+ * 1 <= capacity <= 2^30, eps >= 0 and theta > 0 finite (QD_EINVAL), every
+ * pointer non-NULL (QD_EINVAL) and 2-byte aligned (QD_EALIGN). */
+qd_status qk_norm_rope_f16(void *q, const void *k_src, const void *v_src, const void *q_norm,
+                           const void *k_norm, int64_t heads, int64_t kv_heads, int64_t head_dim,
+                           float eps, float theta, const int32_t *position, int64_t capacity,
+                           void *k_cache, void *v_cache, uint32_t *error_word, void *stream);
+
+/* encode_silu_mul: out = f16(silu(gate) * up), silu(g) = g / (1 + e^-g).
+ * gate, up, out: device f16 [n], 8-byte aligned; out may be gate (the page
+ * writes gate in place) but may not overlap up otherwise.  n % 4 == 0,
+ * n >= 4 (QD_ESHAPE). */
+qd_status silu_mul_f16(const void *gate, const void *up, void *out, int64_t n, void *stream);
+
+/* One decoder layer's weights (device pointers). */
+typedef struct {
+  const void *q, *k, *v, *o, *gate, *up, *down; /* affine blobs, 16-byte aligned */
+  const void *in_norm, *q_norm, *k_norm, *post_norm; /* BF16 vectors, 8-byte aligned */
+  void *k_cache, *v_cache; /* f16 [capacity, kv_heads, head_dim], 16-byte aligned */
+} qd_qwen3_layer;
+
+/* A Qwen3 text decoder in the page's storage forms (host struct; `layers`
+ * is a host array of n_layers entries). */
+typedef struct {
+  int64_t hidden, heads, kv_heads, head_dim, inter, vocab, n_layers, capacity;
+  float eps, theta;            /* rms_norm_eps, rope_theta */
+  const qd_qwen3_layer *layers;
+  const void *final_norm;      /* BF16 [hidden], 8-byte aligned */
+  const void *embed;           /* affine blob [vocab, hidden]: the tied LM head */
+} qd_qwen3_model;
+
+/* Bytes of the step workspace for this model (0 if the model is not
+ * supported): one error word, the f16 scratch rows and the attention
+ * partials. */
+size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model);
+
+/* Qwen3AsrMetalEngine::step for one row: x (device, f16 [hidden], 16-byte
+ * aligned) goes through every layer at p = *position (device int32) --
+ * rmsnorm, the q/k/v GEMVs (one launch), per-head q/k norms and RoPE with
+ * the K/V rows appended at cache row p, decode attention over rows [0, p],
+ * the o GEMV, residual add, rmsnorm, the gate/up GEMVs (one launch),
+ * silu*mul, the down GEMV, residual add -- leaving the new residual row in
+ * x.  When logits (device, f16 [vocab], 2-byte aligned) is not NULL, the
+ * final norm and the tied LM-head GEMV write the next-token logits.  With
+ * advance = 1, *position is incremented at the end of the step.  The
+ * kernels read p from device memory, allocate nothing and launch no memset,
+ * so the caller may capture one call in a HIP graph and replay it token
+ * after token (with advance = 1).  A position outside [0, capacity) makes
+ * the step write nothing to the caches and sets bit 1 of the workspace's
+ * error word (qwen3_step_check).
+ *   workspace  device, 256-byte aligned, >= qwen3_step_workspace_bytes;
+ *              zero-filled before its first use (the error word)
+ * Model requirements (QD_ESHAPE): hidden, inter and heads * head_dim
+ * multiples of 64 and <= 8192; head_dim 64 or 128; heads / kv_heads in
+ * {1, 2, 4, 8}; vocab, n_layers >= 1; 1 <= capacity <= 2^30.  Null or
+ * misaligned pointers: QD_EINVAL / QD_EALIGN.  Calls sharing a workspace
+ * must be ordered on one stream. */
+qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t workspace_bytes,
+                         void *x, int32_t *position, void *logits, int32_t advance,
+                         void *stream);
+
+/* Synchronises `stream`, returns the workspace's error word in *error_bits
+ * and clears it; QD_ESTEP if it was non-zero (bit 1: a position outside
+ * [0, capacity)). */
+qd_status qwen3_step_check(void *workspace, uint32_t *error_bits, void *stream);
+
 /* ---- measurement aid (not a step of the decode path) ---------------------- */
 
 /* Reads `bytes` bytes of device memory at `buf` once, with the access pattern

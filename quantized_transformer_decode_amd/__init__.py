@@ -34,7 +34,27 @@ EXPORTS = (
     "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
     "qlinear_q4_0_gemv", "qlinear_q4_0_gemm",
     "attention_decode_workspace_bytes", "attention_decode",
+    "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16",
+    "qwen3_step_workspace_bytes", "qwen3_step_run", "qwen3_step_check",
 )
+
+
+class Qwen3Layer(ctypes.Structure):
+    """qd_qwen3_layer"""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "k", "v", "o", "gate", "up", "down", "in_norm", "q_norm", "k_norm",
+                 "post_norm", "k_cache", "v_cache")]
+
+
+class Qwen3Model(ctypes.Structure):
+    """qd_qwen3_model"""
+    _fields_ = [("hidden", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("inter", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("n_layers", ctypes.c_int64), ("capacity", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("theta", ctypes.c_float),
+                ("layers", ctypes.POINTER(Qwen3Layer)), ("final_norm", ctypes.c_void_p),
+                ("embed", ctypes.c_void_p)]
 
 
 class Q40LinearItem(ctypes.Structure):
@@ -126,6 +146,16 @@ def lib() -> ctypes.CDLL:
         L.affine_i8_g64_embed_rows.argtypes = [P, I64, I64, ctypes.POINTER(ctypes.c_int64), I64,
                                                P, ctypes.c_int32, P]
         L.attention_decode_workspace_bytes.argtypes = [I64, I64, I64]
+        F32 = ctypes.c_float
+        L.rmsnorm_f16.argtypes = [P, P, P, I64, F32, P, P]
+        L.qk_norm_rope_f16.argtypes = [P, P, P, P, P, I64, I64, I64, F32, F32, P, I64, P, P, P,
+                                       P]
+        L.silu_mul_f16.argtypes = [P, P, P, I64, P]
+        MP = ctypes.POINTER(Qwen3Model)
+        L.qwen3_step_workspace_bytes.argtypes = [MP]
+        L.qwen3_step_workspace_bytes.restype = SZ
+        L.qwen3_step_run.argtypes = [MP, P, SZ, P, P, P, ctypes.c_int32, P]
+        L.qwen3_step_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
         L.attention_decode_workspace_bytes.restype = I64
         L.attention_decode.argtypes = [P, P, P, I64, I64, I64, I64, I64, ctypes.c_float,
                                        ctypes.c_int32, P, P, SZ, P]
@@ -134,7 +164,9 @@ def lib() -> ctypes.CDLL:
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
                   "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check",
                   "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
-                  "qlinear_q4_0_gemv", "qlinear_q4_0_gemm", "attention_decode"):
+                  "qlinear_q4_0_gemv", "qlinear_q4_0_gemm", "attention_decode",
+                  "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16", "qwen3_step_run",
+                  "qwen3_step_check"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -279,6 +311,66 @@ def attention_decode(q, k_cache, v_cache, heads: int, kv_heads: int, head_dim: i
         _ptr(q), _ptr(k_cache), _ptr(v_cache), heads, kv_heads, head_dim, length, kv_start,
         float(scale), 1 if f16 else 0, _ptr(out), _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def rmsnorm_f16(x, delta, w, n: int, eps: float, out, stream=None) -> None:
+    """x <- f16(x + delta) when delta is given, then out = f16(rmsnorm(x) * w)."""
+    _check("rmsnorm_f16", lib().rmsnorm_f16(
+        _ptr(x), None if delta is None else _ptr(delta), _ptr(w), n, float(eps), _ptr(out),
+        _stream(stream)))
+
+
+def qk_norm_rope_f16(q, k_src, v_src, q_norm, k_norm, heads: int, kv_heads: int,
+                     head_dim: int, eps: float, theta: float, position, capacity: int, k_cache,
+                     v_cache, error_word, stream=None) -> None:
+    """Per-head RMSNorm + NeoX RoPE at *position (device int32) of q (in
+    place) and of k_src into K cache row *position; V row copied."""
+    _check("qk_norm_rope_f16", lib().qk_norm_rope_f16(
+        _ptr(q), _ptr(k_src), _ptr(v_src), _ptr(q_norm), _ptr(k_norm), heads, kv_heads,
+        head_dim, float(eps), float(theta), _ptr(position), capacity, _ptr(k_cache),
+        _ptr(v_cache), _ptr(error_word), _stream(stream)))
+
+
+def silu_mul_f16(gate, up, out, n: int, stream=None) -> None:
+    _check("silu_mul_f16", lib().silu_mul_f16(_ptr(gate), _ptr(up), _ptr(out), n,
+                                              _stream(stream)))
+
+
+def qwen3_model(hidden, heads, kv_heads, head_dim, inter, vocab, capacity, eps, theta,
+                layers, final_norm, embed):
+    """Build the qd_qwen3_model struct.  layers: list of dicts with the
+    device tensors (or addresses) of Qwen3Layer's fields.  The returned
+    object keeps the layer array alive."""
+    arr = (Qwen3Layer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = Qwen3Layer(*[_ptr(L[n]) for n, _ in Qwen3Layer._fields_])
+    m = Qwen3Model(hidden, heads, kv_heads, head_dim, inter, vocab, len(layers), capacity,
+                   eps, theta, arr, _ptr(final_norm), _ptr(embed))
+    m._layers = arr
+    return m
+
+
+def qwen3_step_workspace_bytes(model) -> int:
+    return int(lib().qwen3_step_workspace_bytes(ctypes.byref(model)))
+
+
+def qwen3_step_run(model, workspace, workspace_bytes: int, x, position, logits=None,
+                   advance: bool = False, stream=None) -> None:
+    """One decoder step of the row x at *position (device int32)."""
+    _check("qwen3_step_run", lib().qwen3_step_run(
+        ctypes.byref(model), _ptr(workspace), workspace_bytes, _ptr(x), _ptr(position),
+        None if logits is None else _ptr(logits), 1 if advance else 0, _stream(stream)))
+
+
+def qwen3_step_check(workspace, stream=None) -> int:
+    """Synchronise, then return and clear the step's error word (0: no error;
+    bit 1: a position outside the cache)."""
+    bits = ctypes.c_uint32(0)
+    st = lib().qwen3_step_check(_ptr(workspace), ctypes.byref(bits), _stream(stream))
+    if st == QD_ESTEP:
+        return int(bits.value)
+    _check("qwen3_step_check", st)
+    return 0
 
 
 def stream_read(buf, nbytes: int, sink, stream=None) -> None:

@@ -71,87 +71,74 @@ __device__ __forceinline__ uint16_t store16(float v) {
   return F16 ? f32_to_f16(v) : f32_to_bf16(v);
 }
 
-// The G * D outputs of G query heads from their nchunks partials (layout of
-// attention_partial_kernel), by one workgroup: thread t
-// takes output t (and t + 256, ...); when there are fewer outputs than
-// threads, S slices of the chunks run side by side and merge in LDS.  Chunks
-// are read kCombBatch at a time with independent loads, and each batch is
-// folded in against its own maximum, so a head costs about
-// nchunks / (S * kCombBatch) memory round trips.
+// The d outputs of one query head from its nchunks partials (layout of
+// attention_partial_kernel), by one workgroup: S = 256 / d slices of the
+// chunks run side by side, thread t taking dimension t % d of slice t / d,
+// and merge in LDS.  Chunks are read kCombBatch at a time with independent
+// loads, and each batch is folded in against its own maximum, so a head
+// costs about nchunks / (S * kCombBatch) memory round trips.
 constexpr int kCombBatch = 16;
-template <int D, int G, bool F16>
+template <int D, bool F16>
 __device__ __forceinline__ void combine_chunks(const QD_GLOBAL float *part, int nchunks,
                                                QD_GLOBAL uint16_t *out) {
-  constexpr int OUTS = G * D;
-  constexpr int S = OUTS >= kAttThreads ? 1 : kAttThreads / OUTS;
-  constexpr int PER = OUTS >= kAttThreads ? OUTS / kAttThreads : 1;
-  constexpr int W = kAttThreads / S;  // outputs per pass
-  __shared__ float sm[S][W], sl[S][W], so[S][W];
+  constexpr int S = kAttThreads / D;
+  __shared__ float sm[S][D], sl[S][D], so[S][D];
   const int t = threadIdx.x;
-  const int slice = t / W, k = t % W;
+  const int slice = t / D, i = t % D;
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int c0 = slice; c0 < nchunks; c0 += kCombBatch * S) {
+    float mc[kCombBatch], lc[kCombBatch], oc[kCombBatch];
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int idx = r * kAttThreads + k;
-    const int h = idx / D, i = idx % D;
-    const QD_GLOBAL float *ph = part + (size_t)h * nchunks * (D + 2);
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int c0 = slice; c0 < nchunks; c0 += kCombBatch * S) {
-      float mc[kCombBatch], lc[kCombBatch], oc[kCombBatch];
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        const int c = min(c0 + u * S, nchunks - 1);
-        const QD_GLOBAL float *pc = ph + (size_t)c * (D + 2);
-        mc[u] = pc[0];
-        lc[u] = pc[1];
-        oc[u] = pc[2 + i];
-      }
-      float mb = m;
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u)
-        if (c0 + u * S < nchunks) mb = fmaxf(mb, mc[u]);
-      const float a = m == -INFINITY ? 0.f : __expf(m - mb);
-      l *= a;
-      o *= a;
-#pragma unroll
-      for (int u = 0; u < kCombBatch; ++u) {
-        const float w =
-            (c0 + u * S < nchunks && mc[u] != -INFINITY) ? __expf(mc[u] - mb) : 0.f;
-        l = fmaf(lc[u], w, l);
-        o = fmaf(oc[u], w, o);
-      }
-      m = mb;
+    for (int u = 0; u < kCombBatch; ++u) {
+      const int c = min(c0 + u * S, nchunks - 1);
+      const QD_GLOBAL float *pc = part + (size_t)c * (D + 2);
+      mc[u] = pc[0];
+      lc[u] = pc[1];
+      oc[u] = pc[2 + i];
     }
-    if (S > 1) {
-      sm[slice][k] = m;
-      sl[slice][k] = l;
-      so[slice][k] = o;
-      __syncthreads();
-      if (slice == 0) {
-        for (int q = 1; q < S; ++q) {
-          const float m2 = sm[q][k], l2 = sl[q][k], o2 = so[q][k];
-          const float mm = fmaxf(m, m2);
-          const float a = m == -INFINITY ? 0.f : __expf(m - mm);
-          const float b = m2 == -INFINITY ? 0.f : __expf(m2 - mm);
-          l = l * a + l2 * b;
-          o = o * a + o2 * b;
-          m = mm;
-        }
-        out[idx] = store16<F16>(o / l);
-      }
-    } else {
-      out[idx] = store16<F16>(o / l);
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u)
+      if (c0 + u * S < nchunks) mb = fmaxf(mb, mc[u]);
+    const float a = m == -INFINITY ? 0.f : __expf(m - mb);
+    l *= a;
+    o *= a;
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) {
+      const float w = (c0 + u * S < nchunks && mc[u] != -INFINITY) ? __expf(mc[u] - mb) : 0.f;
+      l = fmaf(lc[u], w, l);
+      o = fmaf(oc[u], w, o);
     }
+    m = mb;
   }
+  sm[slice][i] = m;
+  sl[slice][i] = l;
+  so[slice][i] = o;
+  __syncthreads();
+  if (slice != 0) return;
+  for (int q = 1; q < S; ++q) {
+    const float m2 = sm[q][i], l2 = sl[q][i], o2 = so[q][i];
+    const float mm = fmaxf(m, m2);
+    const float a = m == -INFINITY ? 0.f : __expf(m - mm);
+    const float b = m2 == -INFINITY ? 0.f : __expf(m2 - mm);
+    l = l * a + l2 * b;
+    o = o * a + o2 * b;
+    m = mm;
+  }
+  out[i] = store16<F16>(o / l);
 }
 
 // Chunk c of K/V head j for its G query heads.  With FINAL (a single chunk)
 // the normalised output is stored; otherwise the partial (m, l, o[d]) goes to
-// part[((j * G + h) * nchunks + c) * (d + 2) + {0: m, 1: l, 2..: o}].
+// part[((j * G + h) * nchunks + c) * (d + 2) + {0: m, 1: l, 2..: o}]
+// (nchunks = the grid's chunk count).  With pos_dev, the window is
+// [0, *pos_dev + 1) and kv_start, length are ignored.
 template <int D, int G, bool F16, bool FINAL>
 __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
     const uint16_t *__restrict__ q_, const uint16_t *__restrict__ k_,
     const uint16_t *__restrict__ v_, int kv_heads, int kv_start, int length, int rows_per_wave,
-    float scale, float *__restrict__ part, uint16_t *__restrict__ out_) {
+    float scale, const int *__restrict__ pos_dev, int capacity, float *__restrict__ part,
+    uint16_t *__restrict__ out_) {
   constexpr int LPP = D / 8;         // lanes per cached row
   constexpr int PPS = kWave / LPP;   // rows per wave load
   __shared__ float red[kAttWaves][G][10][LPP];
@@ -159,8 +146,17 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
   const int wave = threadIdx.x >> 6;
   const int j = blockIdx.y;          // K/V head
   const int c = blockIdx.x;          // chunk
-  const int nchunks = gridDim.x;
+  const int nchunks = gridDim.x;  // the partials' chunk stride
   const int sub = lane % LPP, grp = lane / LPP;
+  if (pos_dev) {
+    // window [0, position + 1) read from device memory; the grid covers the
+    // whole cache and the chunks past the window exit
+    const int pos = gp(pos_dev)[0];
+    if (pos < 0 || pos >= capacity) return;
+    kv_start = 0;
+    length = pos + 1;
+    if (c * kAttWaves * rows_per_wave >= length) return;
+  }
   const QD_GLOBAL uint16_t *q = gp(q_);
   const QD_GLOBAL uint16_t *kc = gp(k_);
   const QD_GLOBAL uint16_t *vc = gp(v_);
@@ -289,30 +285,41 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
   }
 }
 
-// out[h] from the nchunks partials of query head h, one workgroup per head.
+// out[h] from the nchunks partials of query head h (chunk stride `stride`),
+// one workgroup per head; with pos_dev, nchunks follows from the window
+// [0, *pos_dev + 1) and rows_per_wave.
 template <int D, bool F16>
 __global__ __launch_bounds__(kAttThreads) void attention_combine_kernel(
-    const float *__restrict__ part, int nchunks, uint16_t *__restrict__ out) {
+    const float *__restrict__ part, int stride, int nchunks, const int *__restrict__ pos_dev,
+    int capacity, int rows_per_wave, uint16_t *__restrict__ out) {
   const int h = blockIdx.x;
-  combine_chunks<D, 1, F16>(gp(part) + (size_t)h * nchunks * (D + 2), nchunks,
+  if (pos_dev) {
+    const int pos = gp(pos_dev)[0];
+    if (pos < 0 || pos >= capacity) return;
+    nchunks = (pos + kAttWaves * rows_per_wave) / (kAttWaves * rows_per_wave);
+  }
+  combine_chunks<D, F16>(gp(part) + (size_t)h * stride * (D + 2), nchunks,
                             gp(out) + (size_t)h * D);
 }
 
 template <int D, int G, bool F16>
 hipError_t launch_att(const AttentionArgs &a, hipStream_t stream) {
-  const AttentionPlan p = attention_plan(a.kv_heads, a.length - a.kv_start, D);
+  // with a device position the chunk grid covers the whole cache
+  const int window = a.pos_dev ? a.capacity : a.length - a.kv_start;
+  const AttentionPlan p = attention_plan(a.kv_heads, window, D);
   if (p.nchunks < 1 || p.nchunks > attention_max_chunks(a.kv_heads)) return hipErrorInvalidValue;
-  if (p.nchunks == 1) {
+  if (p.nchunks == 1 && !a.pos_dev) {
     hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, true>), dim3(1, a.kv_heads),
                        dim3(kAttThreads), 0, stream, a.q, a.k, a.v, a.kv_heads, a.kv_start,
-                       a.length, p.rows_per_wave, a.scale, a.part, a.out);
+                       a.length, p.rows_per_wave, a.scale, a.pos_dev, a.capacity, a.part, a.out);
   } else {
     hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, false>),
                        dim3(p.nchunks, a.kv_heads), dim3(kAttThreads), 0, stream, a.q, a.k, a.v,
-                       a.kv_heads, a.kv_start, a.length, p.rows_per_wave, a.scale, a.part,
-                       a.out);
+                       a.kv_heads, a.kv_start, a.length, p.rows_per_wave, a.scale, a.pos_dev,
+                       a.capacity, a.part, a.out);
     hipLaunchKernelGGL((attention_combine_kernel<D, F16>), dim3(a.kv_heads * G),
-                       dim3(kAttThreads), 0, stream, a.part, p.nchunks, a.out);
+                       dim3(kAttThreads), 0, stream, a.part, p.nchunks, p.nchunks, a.pos_dev,
+                       a.capacity, p.rows_per_wave, a.out);
   }
   return hipGetLastError();
 }

@@ -664,8 +664,281 @@ qd_status attention_decode(const void *q, const void *k_cache, const void *v_cac
   a.length = (int)length;
   a.scale = scale;
   a.f16 = f16 == 1;
+  a.pos_dev = nullptr;
+  a.capacity = 0;
   hipError_t e = qd::launch_attention_decode(a, (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+}  // extern "C"
+
+// ---- the decoder step around the GEMVs --------------------------------------
+
+static bool finite_nonneg(float v) { return std::isfinite(v) && v >= 0.f; }
+
+extern "C" {
+
+qd_status rmsnorm_f16(void *x, const void *delta, const void *w, int64_t n, float eps,
+                      void *out, void *stream) {
+  if (!x || !w || !out || !finite_nonneg(eps)) return QD_EINVAL;
+  if (n < 64 || n > 8192 || n % 64 != 0) return QD_ESHAPE;
+  if (!aligned(x, 8) || !aligned(w, 8) || !aligned(out, 8) || (delta && !aligned(delta, 8)))
+    return QD_EALIGN;
+  const size_t nb = (size_t)n * 2;
+  if (overlap(out, nb, x, nb) || overlap(out, nb, w, nb) || (delta && overlap(out, nb, delta, nb)))
+    return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_add_rmsnorm((uint16_t *)x, (const uint16_t *)delta,
+                                        (const uint16_t *)w, (int)n, eps, (uint16_t *)out,
+                                        nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status qk_norm_rope_f16(void *q, const void *k_src, const void *v_src, const void *q_norm,
+                           const void *k_norm, int64_t heads, int64_t kv_heads, int64_t head_dim,
+                           float eps, float theta, const int32_t *position, int64_t capacity,
+                           void *k_cache, void *v_cache, uint32_t *error_word, void *stream) {
+  if (!q || !k_src || !v_src || !q_norm || !k_norm || !position || !k_cache || !v_cache ||
+      !error_word)
+    return QD_EINVAL;
+  if (heads < 1 || kv_heads < 1 || heads > 65535 || kv_heads > 65535 ||
+      (head_dim != 64 && head_dim != 128))
+    return QD_ESHAPE;
+  if (capacity < 1 || capacity > (int64_t(1) << 30) || !finite_nonneg(eps) ||
+      !std::isfinite(theta) || theta <= 0.f)
+    return QD_EINVAL;
+  const void *p2[] = {q, k_src, v_src, q_norm, k_norm, k_cache, v_cache};
+  for (const void *p : p2)
+    if (!aligned(p, 2)) return QD_EALIGN;
+  if (!aligned(position, 4) || !aligned(error_word, 4)) return QD_EALIGN;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_qk_norm_rope(
+      (uint16_t *)q, (const uint16_t *)k_src, (const uint16_t *)v_src, (const uint16_t *)q_norm,
+      (const uint16_t *)k_norm, (int)heads, (int)kv_heads, (int)head_dim, eps, theta, position,
+      (int)capacity, (uint16_t *)k_cache, (uint16_t *)v_cache, error_word, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status silu_mul_f16(const void *gate, const void *up, void *out, int64_t n, void *stream) {
+  if (!gate || !up || !out) return QD_EINVAL;
+  if (n < 4 || n % 4 != 0 || n > (int64_t(1) << 30)) return QD_ESHAPE;
+  if (!aligned(gate, 8) || !aligned(up, 8) || !aligned(out, 8)) return QD_EALIGN;
+  const size_t nb = (size_t)n * 2;
+  if (overlap(out, nb, up, nb) || (out != gate && overlap(out, nb, gate, nb))) return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = qd::launch_silu_mul((const uint16_t *)gate, (const uint16_t *)up,
+                                     (uint16_t *)out, (int)n, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the step workspace's parts (each 256-byte aligned).
+struct StepLayout {
+  size_t err, normed, q, kbuf, vbuf, attn, delta, gate, up, part, total;
+};
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+bool qwen3_shape_ok(const qd_qwen3_model &m) {
+  const int64_t qw = m.heads * m.head_dim;
+  auto w64 = [](int64_t v) { return v >= 64 && v <= kMaxGemvCols && v % 64 == 0; };
+  return w64(m.hidden) && w64(m.inter) && w64(qw) && attention_shape_ok(m.heads, m.kv_heads,
+                                                                       m.head_dim) &&
+         m.vocab >= 1 && m.vocab <= kMaxRows && m.n_layers >= 1 && m.capacity >= 1 &&
+         m.capacity <= (int64_t(1) << 30);
+}
+
+StepLayout qwen3_layout(const qd_qwen3_model &m) {
+  StepLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round256(bytes);
+    return at;
+  };
+  const size_t qw = (size_t)m.heads * m.head_dim, kw = (size_t)m.kv_heads * m.head_dim;
+  L.err = take(4);
+  L.normed = take(m.hidden * 2);
+  L.q = take(qw * 2);
+  L.kbuf = take(kw * 2);
+  L.vbuf = take(kw * 2);
+  L.attn = take(qw * 2);
+  L.delta = take(m.hidden * 2);
+  L.gate = take(m.inter * 2);
+  L.up = take(m.inter * 2);
+  L.part = take((size_t)attention_decode_workspace_bytes(m.heads, m.kv_heads, m.head_dim));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model) {
+  if (!model || !qwen3_shape_ok(*model)) return 0;
+  return qwen3_layout(*model).total;
+}
+
+qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t workspace_bytes,
+                         void *x, int32_t *position, void *logits, int32_t advance,
+                         void *stream) {
+  if (!model || !workspace || !x || !position || !model->layers || !model->final_norm ||
+      !model->embed)
+    return QD_EINVAL;
+  if (advance != 0 && advance != 1) return QD_EINVAL;
+  const qd_qwen3_model &m = *model;
+  if (!qwen3_shape_ok(m)) return QD_ESHAPE;
+  if (!finite_nonneg(m.eps) || !std::isfinite(m.theta) || m.theta <= 0.f) return QD_EINVAL;
+  const StepLayout L = qwen3_layout(m);
+  if (workspace_bytes < L.total) return QD_EINVAL;
+  if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(position, 4) ||
+      (logits && !aligned(logits, 2)) || !aligned(m.final_norm, 8) || !aligned(m.embed, 16))
+    return QD_EALIGN;
+  for (int64_t l = 0; l < m.n_layers; ++l) {
+    const qd_qwen3_layer &ly = m.layers[l];
+    const void *blobs[] = {ly.q, ly.k, ly.v, ly.o, ly.gate, ly.up, ly.down};
+    const void *norms[] = {ly.in_norm, ly.q_norm, ly.k_norm, ly.post_norm};
+    for (const void *p : blobs)
+      if (!p) return QD_EINVAL;
+    for (const void *p : norms)
+      if (!p) return QD_EINVAL;
+    if (!ly.k_cache || !ly.v_cache) return QD_EINVAL;
+    for (const void *p : blobs)
+      if (!aligned(p, 16)) return QD_EALIGN;
+    for (const void *p : norms)
+      if (!aligned(p, 8)) return QD_EALIGN;
+    if (!aligned(ly.k_cache, 16) || !aligned(ly.v_cache, 16)) return QD_EALIGN;
+  }
+  const size_t hb = (size_t)m.hidden * 2;
+  if (overlap(x, hb, workspace, L.total) ||
+      (logits && (overlap(logits, (size_t)m.vocab * 2, workspace, L.total) ||
+                  overlap(logits, (size_t)m.vocab * 2, x, hb))))
+    return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  unsigned *err = (unsigned *)(ws + L.err);
+  uint16_t *normed = (uint16_t *)(ws + L.normed), *q = (uint16_t *)(ws + L.q);
+  uint16_t *kbuf = (uint16_t *)(ws + L.kbuf), *vbuf = (uint16_t *)(ws + L.vbuf);
+  uint16_t *attn = (uint16_t *)(ws + L.attn), *delta = (uint16_t *)(ws + L.delta);
+  uint16_t *gate = (uint16_t *)(ws + L.gate), *up = (uint16_t *)(ws + L.up);
+  uint16_t *xr = (uint16_t *)x;
+  const int hid = (int)m.hidden, d = (int)m.head_dim, H = (int)m.heads, KV = (int)m.kv_heads;
+  const int qw = H * d, kw = KV * d, inter = (int)m.inter;
+  const float scale = 1.0f / sqrtf((float)d);  // the page's f32 1/sqrt(head_dim)
+  int *pos = (int *)position;
+  hipError_t e = hipSuccess;
+#define QD_TRY(call)               \
+  do {                             \
+    e = (call);                    \
+    if (e != hipSuccess) return hip_fail(e); \
+  } while (0)
+
+  QD_TRY(qd::launch_add_rmsnorm(xr, nullptr, (const uint16_t *)m.layers[0].in_norm, hid, m.eps,
+                                normed, nullptr, s));
+  for (int64_t l = 0; l < m.n_layers; ++l) {
+    const qd_qwen3_layer &ly = m.layers[l];
+    qd::AffineGroup g = {};
+    g.n = 3;
+    g.w[0] = (const uint8_t *)ly.q;
+    g.y[0] = q;
+    g.rows[0] = qw;
+    g.w[1] = (const uint8_t *)ly.k;
+    g.y[1] = kbuf;
+    g.rows[1] = kw;
+    g.w[2] = (const uint8_t *)ly.v;
+    g.y[2] = vbuf;
+    g.rows[2] = kw;
+    QD_TRY(qd::launch_affine_gemv(g, hid, normed, 1, true, s));
+    QD_TRY(qd::launch_qk_norm_rope(q, kbuf, vbuf, (const uint16_t *)ly.q_norm,
+                                   (const uint16_t *)ly.k_norm, H, KV, d, m.eps, m.theta, pos,
+                                   (int)m.capacity, (uint16_t *)ly.k_cache,
+                                   (uint16_t *)ly.v_cache, err, s));
+    qd::AttentionArgs a;
+    a.q = q;
+    a.k = (const uint16_t *)ly.k_cache;
+    a.v = (const uint16_t *)ly.v_cache;
+    a.out = attn;
+    a.part = (float *)(ws + L.part);
+    a.heads = H;
+    a.kv_heads = KV;
+    a.head_dim = d;
+    a.kv_start = 0;
+    a.length = 1;
+    a.scale = scale;
+    a.f16 = true;
+    a.pos_dev = pos;
+    a.capacity = (int)m.capacity;
+    QD_TRY(qd::launch_attention_decode(a, s));
+    qd::AffineGroup go = {};
+    go.n = 1;
+    go.w[0] = (const uint8_t *)ly.o;
+    go.y[0] = delta;
+    go.rows[0] = hid;
+    QD_TRY(qd::launch_affine_gemv(go, qw, attn, 1, true, s));
+    QD_TRY(qd::launch_add_rmsnorm(xr, delta, (const uint16_t *)ly.post_norm, hid, m.eps, normed,
+                                  nullptr, s));
+    qd::AffineGroup gu = {};
+    gu.n = 2;
+    gu.w[0] = (const uint8_t *)ly.gate;
+    gu.y[0] = gate;
+    gu.rows[0] = inter;
+    gu.w[1] = (const uint8_t *)ly.up;
+    gu.y[1] = up;
+    gu.rows[1] = inter;
+    QD_TRY(qd::launch_affine_gemv(gu, hid, normed, 1, true, s));
+    QD_TRY(qd::launch_silu_mul(gate, up, gate, inter, s));
+    qd::AffineGroup gd = {};
+    gd.n = 1;
+    gd.w[0] = (const uint8_t *)ly.down;
+    gd.y[0] = delta;
+    gd.rows[0] = hid;
+    QD_TRY(qd::launch_affine_gemv(gd, inter, gate, 1, true, s));
+    const bool last = l + 1 == m.n_layers;
+    // residual add, then the next layer's input norm (or the final norm)
+    const void *next_w = last ? (logits ? m.final_norm : nullptr) : m.layers[l + 1].in_norm;
+    QD_TRY(qd::launch_add_rmsnorm(xr, delta, (const uint16_t *)next_w, hid, m.eps, normed,
+                                  last && advance ? pos : nullptr, s));
+  }
+  if (logits) {
+    qd::AffineGroup gl = {};
+    gl.n = 1;
+    gl.w[0] = (const uint8_t *)m.embed;
+    gl.y[0] = (uint16_t *)logits;
+    gl.rows[0] = (int)m.vocab;
+    QD_TRY(qd::launch_affine_gemv(gl, hid, normed, 1, true, s));
+  }
+#undef QD_TRY
+  return QD_OK;
+}
+
+qd_status qwen3_step_check(void *workspace, uint32_t *error_bits, void *stream) {
+  if (!workspace || !error_bits) return QD_EINVAL;
+  if (!aligned(workspace, 256)) return QD_EALIGN;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  uint32_t bits = 0;
+  e = hipMemcpy(&bits, workspace, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  *error_bits = bits;
+  if (bits) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(workspace, &zero, 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e);
+    return QD_ESTEP;
+  }
+  return QD_OK;
 }
 
 }  // extern "C"

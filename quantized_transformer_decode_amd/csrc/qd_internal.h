@@ -59,6 +59,9 @@ hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
 // Decode attention over the K/V cache (attention.hip).  q, k, v and out are
 // 16-bit (f16, else BF16); the cache rows are [rows][kv_heads][head_dim];
 // part holds heads * nchunks * (head_dim + 2) floats of chunk partials.
+// With pos_dev (device int32), the window is [0, *pos_dev + 1) of a cache of
+// `capacity` rows (nothing is computed when the position is outside it) and
+// kv_start / length are ignored.
 struct AttentionArgs {
   const uint16_t *q, *k, *v;
   uint16_t *out;
@@ -66,6 +69,8 @@ struct AttentionArgs {
   int heads, kv_heads, head_dim, kv_start, length;
   float scale;
   bool f16;
+  const int *pos_dev;
+  int capacity;
 };
 // Rows per wave and chunks of the window [kv_start, length) (host only).
 struct AttentionPlan {
@@ -75,6 +80,23 @@ AttentionPlan attention_plan(int64_t kv_heads, int64_t window, int head_dim);
 // Upper bound of nchunks over every window (host only).
 int64_t attention_max_chunks(int64_t kv_heads);
 hipError_t launch_attention_decode(const AttentionArgs &a, hipStream_t stream);
+
+// Small ops of the decoder step (decoder_ops.hip), f16 buffers, BF16 norm
+// weights.  add_rmsnorm: x <- f16(x + delta) (delta optional), then
+// out = f16(rmsnorm(x) * w) (w optional), then *advance += 1 (optional);
+// n % 4 == 0, n <= 8192.  qk_norm_rope: per-head RMSNorm + NeoX RoPE at
+// *pos_dev of q (in place) and of k_src into K cache row *pos_dev, V row
+// copied into the V cache; a position outside [0, capacity) sets bit 1 of
+// *err and writes nothing.  silu_mul: out = f16(silu(gate) * up), n % 4 == 0.
+hipError_t launch_add_rmsnorm(uint16_t *x, const uint16_t *delta, const uint16_t *w, int n,
+                              float eps, uint16_t *out, int *advance, hipStream_t stream);
+hipError_t launch_qk_norm_rope(uint16_t *q, const uint16_t *k_src, const uint16_t *v_src,
+                               const uint16_t *q_w, const uint16_t *k_w, int heads, int kv_heads,
+                               int d, float eps, float theta, const int *pos_dev, int capacity,
+                               uint16_t *k_cache, uint16_t *v_cache, unsigned *err,
+                               hipStream_t stream);
+hipError_t launch_silu_mul(const uint16_t *gate, const uint16_t *up, uint16_t *out, int n,
+                           hipStream_t stream);
 
 // Practical HBM read ceiling (hbm_probe.hip): reads `bytes` (a multiple of
 // 1024) once.

@@ -290,6 +290,92 @@ def test_errors_attention_decode():
     assert call(out=WS + 256) == qd.QD_EINVAL         # output inside the workspace
 
 
+def test_errors_decoder_ops():
+    f = "rmsnorm_f16"
+    F = ctypes.c_float
+    assert _call(f, None, None, B, 1024, F(1e-6), C, None) == qd.QD_EINVAL
+    assert _call(f, A, None, None, 1024, F(1e-6), C, None) == qd.QD_EINVAL
+    assert _call(f, A, None, B, 1024, F(-1.0), C, None) == qd.QD_EINVAL
+    assert _call(f, A, None, B, 1024, F(float("nan")), C, None) == qd.QD_EINVAL
+    assert _call(f, A, None, B, 1000, F(1e-6), C, None) == qd.QD_ESHAPE
+    assert _call(f, A, None, B, 16384, F(1e-6), C, None) == qd.QD_ESHAPE
+    assert _call(f, A + 4, None, B, 1024, F(1e-6), C, None) == qd.QD_EALIGN
+    assert _call(f, A, OUT + 2, B, 1024, F(1e-6), C, None) == qd.QD_EALIGN
+    assert _call(f, A, None, B, 1024, F(1e-6), A + 64, None) == qd.QD_EINVAL  # out overlaps x
+
+    f = "qk_norm_rope_f16"
+
+    def qk(q=A, ks=B, vs=C, qn=OUT, kn=OUT + 256, h=16, kv=8, d=128, eps=1e-6, th=1e6,
+           pos=WS, cap=4096, kc=0x7f5000000000, vc=0x7f6000000000, err=WS + 64):
+        return _call(f, q, ks, vs, qn, kn, h, kv, d, F(eps), F(th), pos, cap, kc, vc, err, None)
+
+    for bad in ({"q": None}, {"ks": None}, {"pos": None}, {"vc": None}, {"err": None}):
+        assert qk(**bad) == qd.QD_EINVAL
+    assert qk(d=96) == qd.QD_ESHAPE
+    assert qk(kv=0) == qd.QD_ESHAPE
+    assert qk(cap=0) == qd.QD_EINVAL
+    assert qk(th=0.0) == qd.QD_EINVAL
+    assert qk(eps=float("inf")) == qd.QD_EINVAL
+    assert qk(q=A + 1) == qd.QD_EALIGN
+    assert qk(pos=WS + 2) == qd.QD_EALIGN
+
+    f = "silu_mul_f16"
+    assert _call(f, None, B, C, 3072, None) == qd.QD_EINVAL
+    assert _call(f, A, B, C, 3070, None) == qd.QD_ESHAPE
+    assert _call(f, A, B, C, 0, None) == qd.QD_ESHAPE
+    assert _call(f, A + 2, B, C, 3072, None) == qd.QD_EALIGN
+    assert _call(f, A, B, B + 8, 3072, None) == qd.QD_EINVAL     # out overlaps up
+    assert _call(f, A, B, A + 8, 3072, None) == qd.QD_EINVAL     # partly over gate
+
+
+def _qwen3(**kw):
+    layer = qd.Qwen3Layer(*[0x7f7000000000 + (i << 32) for i in range(13)])
+    arr = (qd.Qwen3Layer * 2)(layer, layer)
+    d = dict(hidden=1024, heads=16, kv_heads=8, head_dim=128, inter=3072, vocab=151936,
+             n_layers=2, capacity=4096, eps=1e-6, theta=1e6, layers=arr,
+             final_norm=0x7f8000000000, embed=0x7f9000000000)
+    d.update(kw)
+    m = qd.Qwen3Model(**d)
+    m._keep = arr
+    return m
+
+
+def test_qwen3_step_workspace_and_errors():
+    wb = qd.qwen3_step_workspace_bytes
+    m = _qwen3()
+    n = wb(m)
+    # error word, normed, q, k, v, attn, delta, gate, up (each 256-padded), partials
+    rows = 256 + 2048 + 4096 + 2048 + 2048 + 4096 + 2048 + 6144 + 6144
+    assert n == rows + qd.attention_decode_workspace_bytes(16, 8, 128)
+    for bad in (dict(hidden=1000), dict(head_dim=96), dict(heads=24), dict(inter=16384),
+                dict(capacity=0), dict(vocab=0), dict(n_layers=0)):
+        assert wb(_qwen3(**bad)) == 0, bad
+    f = "qwen3_step_run"
+    X, POS, LOG = 0x7fa000000000, 0x7fb000000000, 0x7fc000000000
+    ref = ctypes.byref
+
+    def run(model=m, ws=WS, nb=n, x=X, pos=POS, logits=LOG, adv=1):
+        return _call(f, ref(model), ws, nb, x, pos, logits, adv, None)
+
+    assert run(ws=None) == qd.QD_EINVAL
+    assert run(x=None) == qd.QD_EINVAL
+    assert run(pos=None) == qd.QD_EINVAL
+    assert run(adv=2) == qd.QD_EINVAL
+    assert run(nb=n - 1) == qd.QD_EINVAL
+    assert run(model=_qwen3(embed=None)) == qd.QD_EINVAL
+    assert run(model=_qwen3(theta=-1.0)) == qd.QD_EINVAL
+    assert run(model=_qwen3(hidden=1000)) == qd.QD_ESHAPE
+    assert run(ws=WS + 16) == qd.QD_EALIGN
+    assert run(x=X + 8) == qd.QD_EALIGN
+    assert run(x=WS + 1024) == qd.QD_EINVAL      # x inside the workspace
+    layer = qd.Qwen3Layer(*[0x7f7000000000 + (i << 32) for i in range(13)])
+    layer.k_cache = None
+    assert run(model=_qwen3(layers=(qd.Qwen3Layer * 2)(layer, layer))) == qd.QD_EINVAL
+    layer.k_cache = 0x7fd000000000 + 8
+    assert run(model=_qwen3(layers=(qd.Qwen3Layer * 2)(layer, layer))) == qd.QD_EALIGN
+    assert _call("qwen3_step_check", None, ctypes.byref(ctypes.c_uint32()), None) == qd.QD_EINVAL
+
+
 def _gpu_visible():
     try:
         hip = ctypes.CDLL("libamdhip64.so")
@@ -322,3 +408,11 @@ def test_valid_args_reach_device_check():
     ws = qd.attention_decode_workspace_bytes(16, 8, 128)
     assert _call("attention_decode", A, B, C, 16, 8, 128, 4096, 0, ctypes.c_float(0.088), 1,
                  OUT, WS, ws, None) == qd.QD_EDEVICE
+    F = ctypes.c_float
+    assert _call("rmsnorm_f16", A, B, C, 1024, F(1e-6), OUT, None) == qd.QD_EDEVICE
+    assert _call("silu_mul_f16", A, B, A, 3072, None) == qd.QD_EDEVICE
+    assert _call("qk_norm_rope_f16", A, B, C, OUT, OUT + 256, 16, 8, 128, F(1e-6), F(1e6), WS,
+                 4096, 0x7f5000000000, 0x7f6000000000, WS + 64, None) == qd.QD_EDEVICE
+    m = _qwen3()
+    assert _call("qwen3_step_run", ctypes.byref(m), WS, qd.qwen3_step_workspace_bytes(m),
+                 0x7fa000000000, 0x7fb000000000, None, 1, None) == qd.QD_EDEVICE
