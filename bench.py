@@ -563,8 +563,75 @@ def row_attention_decode(qd):
     return out
 
 
+def row_qwen3_decoder_step(qd):
+    """The whole Qwen3-0.6B decoder step (28 layers: norms, q/k/v, per-head
+    norms + RoPE with the cache append, attention over the cache, o,
+    residuals, gate/up, SiLU-mul, down; final norm and the tied LM head),
+    f16 buffers, captured once in a HIP graph and replayed token after token
+    (the position advances on the device), at cache contexts of 128, 1024
+    and 4096 rows (random f16 K/V rows before the first position).  Bytes
+    per token: every weight blob once + the K/V rows attended."""
+    import numpy as np
+    import torch
+    import synth
+    spec = synth.QWEN3_0_6B_STEP
+    m = synth.qwen3_model(spec)
+
+    def u16dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to(DEV)
+
+    def blob(tr):
+        b = torch.empty(qd.affine_i8_g64_bytes(tr.rows, tr.cols), dtype=torch.uint8, device=DEV)
+        qd.affine_i8_g64_pack(u8dev(tr.codes), u8dev(tr.scales), u8dev(tr.biases), tr.rows,
+                              tr.cols, b)
+        return b
+
+    steps, ctxs = 64, (128, 1024, 4096)
+    cap = max(ctxs) + steps
+    layers, wbytes = [], 0
+    for L in m["layers"]:
+        d = {n: blob(L[n]) for n in ("q", "k", "v", "o", "gate", "up", "down")}
+        wbytes += sum(t.numel() for t in d.values())
+        d.update({n: u16dev(L[n]) for n in ("in_norm", "q_norm", "k_norm", "post_norm")})
+        shape = (cap, spec.kv_heads, spec.head_dim)
+        d["k_cache"] = (torch.randn(shape, device=DEV) * 0.5).half()
+        d["v_cache"] = torch.randn(shape, device=DEV).half()
+        layers.append(d)
+    embed = blob(m["embed"])
+    final_norm = u16dev(m["final_norm"])
+    wbytes += embed.numel()
+    del m
+    model = qd.qwen3_model(spec.hidden, spec.heads, spec.kv_heads, spec.head_dim, spec.inter,
+                           spec.vocab, cap, float(np.float32(spec.eps)),
+                           float(np.float32(spec.theta)), layers, final_norm, embed)
+    wsb = qd.qwen3_step_workspace_bytes(model)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    x = torch.randn(spec.hidden, device=DEV).half()
+    logits = torch.empty(spec.vocab, dtype=torch.float16, device=DEV)
+    g = capture(lambda: qd.qwen3_step_run(model, ws, wsb, x, pos, logits, advance=True))
+    out = {"model": spec.name, "layers": spec.layers, "weight_bytes": wbytes,
+           "launches_per_token": spec.layers * 10 + 2}
+    for ctx in ctxs:
+        pos.fill_(ctx)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        pos.fill_(ctx)
+        ms = event_time(g.replay, steps, 0)
+        assert int(pos.item()) == ctx + steps
+        kv_bytes = spec.layers * 2 * (ctx + steps // 2) * spec.kv_heads * spec.head_dim * 2
+        gbps = (wbytes + kv_bytes) / (ms * 1e-3) / 1e9
+        out[f"ctx{ctx}"] = {"ms_per_token": ms, "tokens_per_s": 1e3 / ms,
+                            "GBps_weights_plus_kv": gbps, "hbm_peak_frac": gbps / HBM_PEAK_GBPS}
+    assert qd.qwen3_step_check(ws) == 0
+    del layers, embed, g
+    torch.cuda.empty_cache()
+    return out
+
+
 ROWS = ("affine_gemv_1024", "affine_lm_head", "affine_f16", "q4_0_ffn_pair", "qwen3_1_7b_step", "whisper_large_prefill",
-        "whisper_large_decoder", "q4_0_bake", "attention_decode")
+        "whisper_large_decoder", "q4_0_bake", "attention_decode", "qwen3_decoder_step")
 
 
 # HBM traffic of the headline kernel per launch, from two rocprofv3 --pmc runs
