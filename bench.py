@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (the "
                         "reference dispatch for rocprofv3 FETCH_SIZE/WRITE_SIZE scaling)")
+    p.add_argument("--no-env", action="store_true",
+                   help="skip the rocm-smi clock query (profiled runs: under rocprofv3 --pmc "
+                        "a child process would start with the GPU already initialised)")
     p.add_argument("--variant", default="step", choices=["step", "graph"],
                    help="step: the whole step as one persistent launch (default); "
                         "graph: 197 GEMV launches captured in a HIP graph")
@@ -842,7 +845,7 @@ def main():
     out["hbm_read_ceiling_GBps"] = ceiling
     out["roofline"]["practical_peak"] = ceiling
     out["roofline"]["frac_of_practical"] = achieved / ceiling
-    out["env"] = environment()
+    out["env"] = None if args.no_env else environment()
     names = ROWS if args.rows == "all" else [] if args.rows == "none" else args.rows.split(",")
     if names:
         out["rows"] = run_rows(qd, names)

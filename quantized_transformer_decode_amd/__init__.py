@@ -339,8 +339,9 @@ def silu_mul_f16(gate, up, out, n: int, stream=None) -> None:
 def qwen3_model(hidden, heads, kv_heads, head_dim, inter, vocab, capacity, eps, theta,
                 layers, final_norm, embed):
     """Build the qd_qwen3_model struct.  layers: list of dicts with the
-    device tensors (or addresses) of Qwen3Layer's fields.  The returned
-    object keeps the layer array alive."""
+    device tensors (or addresses) of Qwen3Layer's fields.  The struct holds
+    device addresses only: the caller keeps every tensor alive while the
+    model is in use (the returned object keeps only the host layer array)."""
     arr = (Qwen3Layer * len(layers))()
     for i, L in enumerate(layers):
         arr[i] = Qwen3Layer(*[_ptr(L[n]) for n, _ in Qwen3Layer._fields_])
