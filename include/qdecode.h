@@ -401,7 +401,7 @@ qd_status silu_mul_f16(const void *gate, const void *up, void *out, int64_t n, v
 /* One decoder layer's weights (device pointers). */
 typedef struct {
   const void *q, *k, *v, *o, *gate, *up, *down; /* affine blobs, 16-byte aligned */
-  const void *in_norm, *q_norm, *k_norm, *post_norm; /* BF16 vectors, 8-byte aligned */
+  const void *in_norm, *q_norm, *k_norm, *post_norm; /* BF16 vectors, 16-byte aligned */
   void *k_cache, *v_cache; /* f16 [capacity, kv_heads, head_dim], 16-byte aligned */
 } qd_qwen3_layer;
 
@@ -411,7 +411,7 @@ typedef struct {
   int64_t hidden, heads, kv_heads, head_dim, inter, vocab, n_layers, capacity;
   float eps, theta;            /* rms_norm_eps, rope_theta */
   const qd_qwen3_layer *layers;
-  const void *final_norm;      /* BF16 [hidden], 8-byte aligned */
+  const void *final_norm;      /* BF16 [hidden], 16-byte aligned */
   const void *embed;           /* affine blob [vocab, hidden]: the tied LM head */
 } qd_qwen3_model;
 

@@ -180,6 +180,20 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH, A> &G, MCursor &c, con
   }
 }
 
+// The x part of a buffer issued before x was staged, again from LDS (a
+// prologue's row exists only there): the same walk as mg_issue's.
+template <int R, int U, bool CH, class A>
+__device__ __forceinline__ void mg_reload_x(MGroup<R, U, CH, A> &G, MCursor c, const MShape &S,
+                                            const uint8_t *xl, uint32_t xloff, int left) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint8_t *xp = xl + xloff + 128 * c.g;
+    G.xa[u] = *(const typename A::vec *)(xp);
+    G.xb[u] = *(const typename A::vec *)(xp + 16);
+    mc_next(c, S, left);
+  }
+}
+
 // Output of one finished tile (KS = 1): lane holds tokens 4*(lane/16)+v of
 // weight row lane%16 of each 16-row block.
 template <int R, class A>
@@ -277,9 +291,96 @@ __device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x
   }
 }
 
-template <int R, int U, int KS, bool CH, bool XL, class Act>
+__device__ __forceinline__ float round_f16(float v) { return f16_to_f32(f32_to_f16(v)); }
+
+__device__ __forceinline__ float half_of(const u32x4 &w, int e) {
+  const uint32_t d = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+  return f16_to_f32((d >> (16 * (e & 1))) & 0xffffu);
+}
+
+__device__ __forceinline__ u32x4 pack_halves(const float (&v)[8]) {
+  u32x4 r;
+  r.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+  r.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+  r.z = (uint32_t)f32_to_f16(v[4]) | ((uint32_t)f32_to_f16(v[5]) << 16);
+  r.w = (uint32_t)f32_to_f16(v[6]) | ((uint32_t)f32_to_f16(v[7]) << 16);
+  return r;
+}
+
+// The transformed input row (m = 1, f16) into LDS, in stage_x's layout
+// (GemvPrologue): kind 1 the residual add and RMSNorm, kind 2 SiLU-mul.
+// cols <= 8192: at most two 8-value chunks per thread.
+template <int PRO>
+__device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_t *x, int cols,
+                                            const GemvPrologue &pro) {
+  constexpr int CPT = 2;
+  const int chunks = cols >> 3;
+  const int t = threadIdx.x;
+  float a[CPT][8];
+  if constexpr (PRO == 1) {
+    __shared__ float red[kMW];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int i = t + k * kMThreads;
+      if (i < chunks) {
+        const u32x4 xv = *(const QD_GLOBAL u32x4 *)(x + 8 * i);
+        u32x4 dv = {0u, 0u, 0u, 0u};
+        if (pro.delta) dv = *(const QD_GLOBAL u32x4 *)(gp(pro.delta) + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[k][e] = pro.delta ? round_f16(half_of(xv, e) + half_of(dv, e)) : half_of(xv, e);
+          ss = fmaf(a[k][e], a[k][e], ss);
+        }
+        if (pro.delta && pro.x_out && blockIdx.x == 0)
+          *(QD_GLOBAL u32x4 *)(gp(pro.x_out) + 8 * i) = pack_halves(a[k]);
+      }
+    }
+    ss = wave_sum(ss);
+    if ((t & 63) == 0) red[t >> 6] = ss;
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMW; ++w) tot += red[w];
+    const float inv = 1.f / sqrtf(tot / (float)cols + pro.eps);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int i = t + k * kMThreads;
+      if (i < chunks) {
+        const u32x4 wv = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
+        const uint32_t we[4] = {wv.x, wv.y, wv.z, wv.w};
+        float n[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          n[e] = a[k][e] * inv * bf16_to_f32((we[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        *(u32x4 *)(xl + 16 * i) = pack_halves(n);
+      }
+    }
+    if (pro.advance && blockIdx.x == 0 && t == 0) gp(pro.advance)[0] += 1;
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int i = t + k * kMThreads;
+      if (i < chunks) {
+        const u32x4 gv = *(const QD_GLOBAL u32x4 *)(x + 8 * i);
+        const u32x4 uv = *(const QD_GLOBAL u32x4 *)(gp(pro.up) + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float g = half_of(gv, e);
+          a[k][e] = g / (1.f + expf(-g)) * half_of(uv, e);
+        }
+        *(u32x4 *)(xl + 16 * i) = pack_halves(a[k]);
+      }
+    }
+  }
+}
+
+// PRO != 0: a step GEMV (m = 1, f16, XL) reading the row that stage_x_pro
+// builds.
+template <int R, int U, int KS, bool CH, bool XL, class Act, int PRO>
 __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
-    const AffineGroup grp, int cols, const uint16_t *__restrict__ x_, int m) {
+    const AffineGroup grp, int cols, const uint16_t *__restrict__ x_, int m,
+    const GemvPrologue pro) {
   constexpr int SLOTS = kMW / KS;
   __shared__ float red[KS > 1 ? kMW * R * kWave * 4 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t xsh[];  // x (XL)
@@ -316,12 +417,20 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   ci.g = cc.g = S.ga;
   int li = n, lc = n;
   MGroup<R, U, CH, Act> A, B;
+  const MCursor c0 = ci;
+  const int l0 = li;
   // the first buffer's codes and scales are in flight while x is staged
   if (n > 0) mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
   if constexpr (XL) {
-    stage_x(xl, x, m, cols);
+    if constexpr (PRO == 0)
+      stage_x(xl, x, m, cols);
+    else
+      stage_x_pro<PRO>(xl, x, cols, pro);
     // LDS writes done, then the barrier (global loads stay in flight)
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the first buffer read the untransformed x from memory
+    if constexpr (PRO != 0)
+      if (n > 0) mg_reload_x<R, U, CH, Act>(A, c0, S, xl, xloff, l0);
   }
   if (n > 0) {
     // Loads are never conditional (the compiler then waits for exactly the
@@ -376,9 +485,9 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
 // CU then still fit the 160 KiB of LDS).
 constexpr int kXlBudget = 72 * 1024;
 
-template <int KS, bool CH, bool XL, class Act>
+template <int KS, bool CH, bool XL, class Act, int PRO>
 hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
-                          hipStream_t stream) {
+                          const GemvPrologue &pro, hipStream_t stream) {
   constexpr int R = QD_AFFINE_MFMA_R;
   constexpr int U = CH ? 4 : 2;
   const size_t lds = XL ? (size_t)m * (2 * cols + 16) : 0;
@@ -386,30 +495,35 @@ hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int
     static bool raised = false;
     if (!raised) {
       hipError_t e = hipFuncSetAttribute(
-          (const void *)affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act>,
+          (const void *)affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act, PRO>,
           hipFuncAttributeMaxDynamicSharedMemorySize, kXlBudget);
       if (e != hipSuccess) return e;
       raised = true;
     }
   }
-  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act>), dim3(grid), dim3(kMThreads),
-                     lds, stream, g, cols, x, m);
+  hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act, PRO>), dim3(grid),
+                     dim3(kMThreads), lds, stream, g, cols, x, m, pro);
   return hipGetLastError();
 }
 
 // Only the streaming walk (KS = 1) stages x: there a workgroup reuses it over
 // many tiles, while a split workgroup reads each element of x once anyway.
-template <int KS, bool CH, class Act>
+// A prologue always stages (the transformed row exists only in LDS).
+template <int KS, bool CH, class Act, int PRO>
 hipError_t launch_mfma_xl(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
-                          hipStream_t stream) {
-  if (KS == 1 && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
-    return launch_mfma_ks<KS, CH, true, Act>(g, cols, x, m, grid, stream);
-  return launch_mfma_ks<KS, CH, false, Act>(g, cols, x, m, grid, stream);
+                          const GemvPrologue &pro, hipStream_t stream) {
+  if constexpr (PRO != 0) {
+    return launch_mfma_ks<KS, CH, true, Act, PRO>(g, cols, x, m, grid, pro, stream);
+  } else {
+    if (KS == 1 && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
+      return launch_mfma_ks<KS, CH, true, Act, PRO>(g, cols, x, m, grid, pro, stream);
+    return launch_mfma_ks<KS, CH, false, Act, PRO>(g, cols, x, m, grid, pro, stream);
+  }
 }
 
-template <bool CH, class Act>
+template <bool CH, class Act, int PRO>
 hipError_t launch_mfma_ch(AffineGroup g, int cols, const uint16_t *x, int m,
-                          hipStream_t stream) {
+                          const GemvPrologue &pro, hipStream_t stream) {
   // KS: split K over up to 8 waves until the launch gives about
   // kTargetWaves waves (each wave keeping at least one buffer of groups);
   // KS = 1 walks tiles grid-stride with kStreamWgsPerCu workgroups per CU.
@@ -428,21 +542,21 @@ hipError_t launch_mfma_ch(AffineGroup g, int cols, const uint16_t *x, int m,
     if (cus < 1) cus = 256;
     long grid = (ntiles + kMW - 1) / kMW;
     if (grid > (long)kStreamWgsPerCu * cus) grid = (long)kStreamWgsPerCu * cus;
-    return launch_mfma_xl<1, CH, Act>(g, cols, x, m, (int)grid, stream);
+    return launch_mfma_xl<1, CH, Act, PRO>(g, cols, x, m, (int)grid, pro, stream);
   }
   const int grid = (int)((ntiles * ks + kMW - 1) / kMW);
   switch (ks) {
-    case 2: return launch_mfma_xl<2, CH, Act>(g, cols, x, m, grid, stream);
-    case 4: return launch_mfma_xl<4, CH, Act>(g, cols, x, m, grid, stream);
-    default: return launch_mfma_xl<8, CH, Act>(g, cols, x, m, grid, stream);
+    case 2: return launch_mfma_xl<2, CH, Act, PRO>(g, cols, x, m, grid, pro, stream);
+    case 4: return launch_mfma_xl<4, CH, Act, PRO>(g, cols, x, m, grid, pro, stream);
+    default: return launch_mfma_xl<8, CH, Act, PRO>(g, cols, x, m, grid, pro, stream);
   }
 }
 
-template <class Act>
+template <class Act, int PRO = 0>
 hipError_t launch_mfma(const AffineGroup &g, int cols, const uint16_t *x, int m,
-                       hipStream_t stream) {
-  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true, Act>(g, cols, x, m, stream);
-  return launch_mfma_ch<false, Act>(g, cols, x, m, stream);
+                       const GemvPrologue &pro, hipStream_t stream) {
+  if ((cols / 64) % 4 == 0) return launch_mfma_ch<true, Act, PRO>(g, cols, x, m, pro, stream);
+  return launch_mfma_ch<false, Act, PRO>(g, cols, x, m, pro, stream);
 }
 
 // ---- batch 1: streaming kernel ---------------------------------------------
@@ -605,7 +719,8 @@ hipError_t launch_affine_embed_rows(const uint8_t *w, int rows, int cols, const 
 
 hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m, bool f16,
                               hipStream_t stream) {
-  if (f16) return launch_mfma<ActF16>(g, cols, x, m, stream);
+  const GemvPrologue none = {};
+  if (f16) return launch_mfma<ActF16>(g, cols, x, m, none, stream);
   // Batch 1 takes the VALU streaming kernel only for a single very large
   // matrix (LM heads), where its 1 KiB-per-row loads keep the most bytes in
   // flight; below that the matrix-core kernel's K split gives more waves.
@@ -626,7 +741,14 @@ hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
                        stream, w, rows, cols, x, y);
     return hipGetLastError();
   }
-  return launch_mfma<ActBf16>(g, cols, x, m, stream);
+  return launch_mfma<ActBf16>(g, cols, x, m, none, stream);
+}
+
+hipError_t launch_affine_gemv_pro(AffineGroup g, int cols, const uint16_t *x,
+                                  const GemvPrologue &pro, hipStream_t stream) {
+  if (pro.kind == 1) return launch_mfma<ActF16, 1>(g, cols, x, 1, pro, stream);
+  if (pro.kind == 2) return launch_mfma<ActF16, 2>(g, cols, x, 1, pro, stream);
+  return launch_mfma<ActF16>(g, cols, x, 1, pro, stream);
 }
 
 }  // namespace qd

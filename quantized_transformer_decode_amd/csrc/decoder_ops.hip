@@ -37,14 +37,15 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   return s;
 }
 
-// x <- f16(x + delta) when delta is given (written back), then
-// out = f16(x / sqrt(mean(x^2) + eps) * w) when w is given; one workgroup.
+// a = x, or f16(x + delta) stored to x_out when delta is given (x_out may be
+// x: each element is read and written by the same thread); then
+// out = f16(a / sqrt(mean(a^2) + eps) * w) when w is given; one workgroup.
 // advance (optional): *advance += 1 once everything else is issued.
 __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
-    uint16_t *__restrict__ x_, const uint16_t *__restrict__ delta_, const uint16_t *__restrict__ w_,
-    int n, float eps, uint16_t *__restrict__ out_, int *__restrict__ advance) {
+    const uint16_t *x_, const uint16_t *__restrict__ delta_, const uint16_t *__restrict__ w_,
+    int n, float eps, uint16_t *__restrict__ out_, uint16_t *x_out, int *__restrict__ advance) {
   __shared__ float red[kNormThreads / kWave];
-  QD_GLOBAL uint16_t *x = gp(x_);
+  const QD_GLOBAL uint16_t *x = gp(x_);
   const int t = threadIdx.x;
   const int chunks = n / 4;
   float v[kNormMaxChunks][4];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
         u32x2 st;
         st.x = (uint32_t)f32_to_f16(v[k][0]) | ((uint32_t)f32_to_f16(v[k][1]) << 16);
         st.y = (uint32_t)f32_to_f16(v[k][2]) | ((uint32_t)f32_to_f16(v[k][3]) << 16);
-        *(QD_GLOBAL u32x2 *)(x + 4 * c) = st;
+        *(QD_GLOBAL u32x2 *)(gp(x_out) + 4 * c) = st;
       }
     }
   }
@@ -166,10 +167,11 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t *__restric
 
 }  // namespace
 
-hipError_t launch_add_rmsnorm(uint16_t *x, const uint16_t *delta, const uint16_t *w, int n,
-                              float eps, uint16_t *out, int *advance, hipStream_t stream) {
+hipError_t launch_add_rmsnorm(const uint16_t *x, const uint16_t *delta, const uint16_t *w, int n,
+                              float eps, uint16_t *out, uint16_t *x_out, int *advance,
+                              hipStream_t stream) {
   hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(1), dim3(kNormThreads), 0, stream, x, delta, w, n,
-                     eps, out, advance);
+                     eps, out, x_out, advance);
   return hipGetLastError();
 }
 

@@ -689,9 +689,9 @@ qd_status rmsnorm_f16(void *x, const void *delta, const void *w, int64_t n, floa
     return QD_EINVAL;
   qd_status st = check_device();
   if (st != QD_OK) return st;
-  hipError_t e = qd::launch_add_rmsnorm((uint16_t *)x, (const uint16_t *)delta,
+  hipError_t e = qd::launch_add_rmsnorm((const uint16_t *)x, (const uint16_t *)delta,
                                         (const uint16_t *)w, (int)n, eps, (uint16_t *)out,
-                                        nullptr, (hipStream_t)stream);
+                                        (uint16_t *)x, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 
@@ -740,7 +740,7 @@ namespace {
 
 // Byte offsets of the step workspace's parts (each 256-byte aligned).
 struct StepLayout {
-  size_t err, normed, q, kbuf, vbuf, attn, delta, gate, up, part, total;
+  size_t err, xalt, q, kbuf, vbuf, attn, delta, gate, up, part, total;
 };
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
@@ -764,7 +764,7 @@ StepLayout qwen3_layout(const qd_qwen3_model &m) {
   };
   const size_t qw = (size_t)m.heads * m.head_dim, kw = (size_t)m.kv_heads * m.head_dim;
   L.err = take(4);
-  L.normed = take(m.hidden * 2);
+  L.xalt = take(m.hidden * 2);
   L.q = take(qw * 2);
   L.kbuf = take(kw * 2);
   L.vbuf = take(kw * 2);
@@ -799,7 +799,7 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
   const StepLayout L = qwen3_layout(m);
   if (workspace_bytes < L.total) return QD_EINVAL;
   if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(position, 4) ||
-      (logits && !aligned(logits, 2)) || !aligned(m.final_norm, 8) || !aligned(m.embed, 16))
+      (logits && !aligned(logits, 2)) || !aligned(m.final_norm, 16) || !aligned(m.embed, 16))
     return QD_EALIGN;
   for (int64_t l = 0; l < m.n_layers; ++l) {
     const qd_qwen3_layer &ly = m.layers[l];
@@ -813,7 +813,7 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     for (const void *p : blobs)
       if (!aligned(p, 16)) return QD_EALIGN;
     for (const void *p : norms)
-      if (!aligned(p, 8)) return QD_EALIGN;
+      if (!aligned(p, 16)) return QD_EALIGN;
     if (!aligned(ly.k_cache, 16) || !aligned(ly.v_cache, 16)) return QD_EALIGN;
   }
   const size_t hb = (size_t)m.hidden * 2;
@@ -827,26 +827,38 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
   unsigned *err = (unsigned *)(ws + L.err);
-  uint16_t *normed = (uint16_t *)(ws + L.normed), *q = (uint16_t *)(ws + L.q);
+  uint16_t *q = (uint16_t *)(ws + L.q);
   uint16_t *kbuf = (uint16_t *)(ws + L.kbuf), *vbuf = (uint16_t *)(ws + L.vbuf);
   uint16_t *attn = (uint16_t *)(ws + L.attn), *delta = (uint16_t *)(ws + L.delta);
   uint16_t *gate = (uint16_t *)(ws + L.gate), *up = (uint16_t *)(ws + L.up);
-  uint16_t *xr = (uint16_t *)x;
+  // The residual row alternates between the caller's x and a scratch row:
+  // a fused residual add reads one and writes the other, so no workgroup
+  // reads a row that another is rewriting.  A step has 2 * n_layers adds,
+  // so the final row lands in x again.
+  uint16_t *res[2] = {(uint16_t *)x, (uint16_t *)(ws + L.xalt)};
+  int cur = 0;
   const int hid = (int)m.hidden, d = (int)m.head_dim, H = (int)m.heads, KV = (int)m.kv_heads;
   const int qw = H * d, kw = KV * d, inter = (int)m.inter;
   const float scale = 1.0f / sqrtf((float)d);  // the page's f32 1/sqrt(head_dim)
   int *pos = (int *)position;
   hipError_t e = hipSuccess;
-#define QD_TRY(call)               \
-  do {                             \
-    e = (call);                    \
+#define QD_TRY(call)                         \
+  do {                                       \
+    e = (call);                              \
     if (e != hipSuccess) return hip_fail(e); \
   } while (0)
 
-  QD_TRY(qd::launch_add_rmsnorm(xr, nullptr, (const uint16_t *)m.layers[0].in_norm, hid, m.eps,
-                                normed, nullptr, s));
   for (int64_t l = 0; l < m.n_layers; ++l) {
     const qd_qwen3_layer &ly = m.layers[l];
+    // [residual add +] input RMSNorm, fused into the q/k/v GEMVs (one launch)
+    qd::GemvPrologue pn = {};
+    pn.kind = 1;
+    pn.w = (const uint16_t *)ly.in_norm;
+    pn.eps = m.eps;
+    if (l > 0) {
+      pn.delta = delta;
+      pn.x_out = res[cur ^ 1];
+    }
     qd::AffineGroup g = {};
     g.n = 3;
     g.w[0] = (const uint8_t *)ly.q;
@@ -858,7 +870,8 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     g.w[2] = (const uint8_t *)ly.v;
     g.y[2] = vbuf;
     g.rows[2] = kw;
-    QD_TRY(qd::launch_affine_gemv(g, hid, normed, 1, true, s));
+    QD_TRY(qd::launch_affine_gemv_pro(g, hid, res[cur], pn, s));
+    if (l > 0) cur ^= 1;
     QD_TRY(qd::launch_qk_norm_rope(q, kbuf, vbuf, (const uint16_t *)ly.q_norm,
                                    (const uint16_t *)ly.k_norm, H, KV, d, m.eps, m.theta, pos,
                                    (int)m.capacity, (uint16_t *)ly.k_cache,
@@ -885,8 +898,13 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     go.y[0] = delta;
     go.rows[0] = hid;
     QD_TRY(qd::launch_affine_gemv(go, qw, attn, 1, true, s));
-    QD_TRY(qd::launch_add_rmsnorm(xr, delta, (const uint16_t *)ly.post_norm, hid, m.eps, normed,
-                                  nullptr, s));
+    // residual add + post-attention RMSNorm, fused into the gate/up GEMVs
+    qd::GemvPrologue pp = {};
+    pp.kind = 1;
+    pp.delta = delta;
+    pp.w = (const uint16_t *)ly.post_norm;
+    pp.x_out = res[cur ^ 1];
+    pp.eps = m.eps;
     qd::AffineGroup gu = {};
     gu.n = 2;
     gu.w[0] = (const uint8_t *)ly.gate;
@@ -895,27 +913,38 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     gu.w[1] = (const uint8_t *)ly.up;
     gu.y[1] = up;
     gu.rows[1] = inter;
-    QD_TRY(qd::launch_affine_gemv(gu, hid, normed, 1, true, s));
-    QD_TRY(qd::launch_silu_mul(gate, up, gate, inter, s));
+    QD_TRY(qd::launch_affine_gemv_pro(gu, hid, res[cur], pp, s));
+    cur ^= 1;
+    // SiLU-mul, fused into the down GEMV
+    qd::GemvPrologue ps = {};
+    ps.kind = 2;
+    ps.up = up;
     qd::AffineGroup gd = {};
     gd.n = 1;
     gd.w[0] = (const uint8_t *)ly.down;
     gd.y[0] = delta;
     gd.rows[0] = hid;
-    QD_TRY(qd::launch_affine_gemv(gd, inter, gate, 1, true, s));
-    const bool last = l + 1 == m.n_layers;
-    // residual add, then the next layer's input norm (or the final norm)
-    const void *next_w = last ? (logits ? m.final_norm : nullptr) : m.layers[l + 1].in_norm;
-    QD_TRY(qd::launch_add_rmsnorm(xr, delta, (const uint16_t *)next_w, hid, m.eps, normed,
-                                  last && advance ? pos : nullptr, s));
+    QD_TRY(qd::launch_affine_gemv_pro(gd, inter, gate, ps, s));
   }
+  // the last residual add; with logits, fused with the final norm into the
+  // tied LM head
   if (logits) {
+    qd::GemvPrologue pf = {};
+    pf.kind = 1;
+    pf.delta = delta;
+    pf.w = (const uint16_t *)m.final_norm;
+    pf.x_out = res[cur ^ 1];
+    pf.advance = advance ? pos : nullptr;
+    pf.eps = m.eps;
     qd::AffineGroup gl = {};
     gl.n = 1;
     gl.w[0] = (const uint8_t *)m.embed;
     gl.y[0] = (uint16_t *)logits;
     gl.rows[0] = (int)m.vocab;
-    QD_TRY(qd::launch_affine_gemv(gl, hid, normed, 1, true, s));
+    QD_TRY(qd::launch_affine_gemv_pro(gl, hid, res[cur], pf, s));
+  } else {
+    QD_TRY(qd::launch_add_rmsnorm(res[cur], delta, nullptr, hid, m.eps, nullptr, res[cur ^ 1],
+                                  advance ? pos : nullptr, s));
   }
 #undef QD_TRY
   return QD_OK;

@@ -38,6 +38,23 @@ struct Q40Group {
 hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m, bool f16,
                               hipStream_t stream);
 
+// An input transform fused into an f16 GEMV at m = 1 (the decoder step): the
+// workgroups stage the transformed row in LDS instead of x itself.
+//   kind 1, residual add + RMSNorm: a = x, or f16(x + delta) with delta;
+//           the GEMV reads f16(a / sqrt(mean(a^2) + eps) * w) (w BF16);
+//           workgroup 0 stores a to x_out (which must not be x) when delta
+//           is given, and adds 1 to *advance when advance is given.
+//   kind 2, SiLU-mul: the GEMV reads f16(silu(x) * up).
+struct GemvPrologue {
+  int kind;
+  const uint16_t *delta, *w, *up;
+  uint16_t *x_out;
+  int *advance;
+  float eps;
+};
+hipError_t launch_affine_gemv_pro(AffineGroup g, int cols, const uint16_t *x,
+                                  const GemvPrologue &pro, hipStream_t stream);
+
 // Tied-embedding rows: token ids t[0..n) (already checked to be < rows).
 constexpr int kMaxEmbedTokens = 16;
 struct EmbedTokens {
@@ -82,14 +99,15 @@ int64_t attention_max_chunks(int64_t kv_heads);
 hipError_t launch_attention_decode(const AttentionArgs &a, hipStream_t stream);
 
 // Small ops of the decoder step (decoder_ops.hip), f16 buffers, BF16 norm
-// weights.  add_rmsnorm: x <- f16(x + delta) (delta optional), then
-// out = f16(rmsnorm(x) * w) (w optional), then *advance += 1 (optional);
-// n % 4 == 0, n <= 8192.  qk_norm_rope: per-head RMSNorm + NeoX RoPE at
+// weights.  add_rmsnorm: a = x, or f16(x + delta) stored to x_out (which may
+// be x) when delta is given; then out = f16(rmsnorm(a) * w) (w optional),
+// then *advance += 1 (optional); n % 4 == 0, n <= 8192.  qk_norm_rope: per-head RMSNorm + NeoX RoPE at
 // *pos_dev of q (in place) and of k_src into K cache row *pos_dev, V row
 // copied into the V cache; a position outside [0, capacity) sets bit 1 of
 // *err and writes nothing.  silu_mul: out = f16(silu(gate) * up), n % 4 == 0.
-hipError_t launch_add_rmsnorm(uint16_t *x, const uint16_t *delta, const uint16_t *w, int n,
-                              float eps, uint16_t *out, int *advance, hipStream_t stream);
+hipError_t launch_add_rmsnorm(const uint16_t *x, const uint16_t *delta, const uint16_t *w, int n,
+                              float eps, uint16_t *out, uint16_t *x_out, int *advance,
+                              hipStream_t stream);
 hipError_t launch_qk_norm_rope(uint16_t *q, const uint16_t *k_src, const uint16_t *v_src,
                                const uint16_t *q_w, const uint16_t *k_w, int heads, int kv_heads,
                                int d, float eps, float theta, const int *pos_dev, int capacity,
