@@ -128,17 +128,58 @@ __device__ __forceinline__ void combine_chunks(const QD_GLOBAL float *part, int 
   out[i] = store16<F16>(o / l);
 }
 
+// The page's per-head RMSNorm (rounded to f16) and RoPE (rounded to f16) of
+// this lane's 8 dimensions 8 * sub .. 8 * sub + 7 of one head; the head's
+// other dimensions sit in the other lanes of the row slot (LPP lanes), the
+// RoPE partner of dimension i (i +- d/2) in lane sub ^ LPP/2.  cs holds the
+// cosine and sine of each pair's angle.
+template <int D>
+__device__ __forceinline__ void norm_rope8(float (&x)[8], const u32x4 wv, int sub, float eps,
+                                           const float (*cs)[D / 2]) {
+  constexpr int LPP = D / 8, HALF = D / 2;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+  for (int o = 1; o < LPP; o <<= 1) ss += __shfl_xor(ss, o, kWave);
+  const float inv = 1.f / sqrtf(ss / (float)D + eps);
+  const uint32_t we[4] = {wv.x, wv.y, wv.z, wv.w};
+  float n[8], other[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    n[e] = f16_to_f32(f32_to_f16(x[e] * inv * bf16_to_f32((we[e >> 1] >> (16 * (e & 1))) & 0xffffu)));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) other[e] = __shfl_xor(n[e], LPP / 2, kWave);
+  const bool first = sub < LPP / 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int p = (8 * sub + e) % HALF;
+    const float c = cs[0][p], s = cs[1][p];
+    x[e] = f16_to_f32(f32_to_f16(first ? n[e] * c - other[e] * s : n[e] * c + other[e] * s));
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8_f16(const float (&v)[8]) {
+  u32x4 r;
+  r.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+  r.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+  r.z = (uint32_t)f32_to_f16(v[4]) | ((uint32_t)f32_to_f16(v[5]) << 16);
+  r.w = (uint32_t)f32_to_f16(v[6]) | ((uint32_t)f32_to_f16(v[7]) << 16);
+  return r;
+}
+
 // Chunk c of K/V head j for its G query heads.  With FINAL (a single chunk)
 // the normalised output is stored; otherwise the partial (m, l, o[d]) goes to
 // part[((j * G + h) * nchunks + c) * (d + 2) + {0: m, 1: l, 2..: o}]
 // (nchunks = the grid's chunk count).  With pos_dev, the window is
-// [0, *pos_dev + 1) and kv_start, length are ignored.
-template <int D, int G, bool F16, bool FINAL>
+// [0, *pos_dev + 1) and kv_start, length are ignored.  With QKR (device
+// position, f16), q is raw: see AttentionQkRope.
+template <int D, int G, bool F16, bool FINAL, bool QKR>
 __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
-    const uint16_t *__restrict__ q_, const uint16_t *__restrict__ k_,
-    const uint16_t *__restrict__ v_, int kv_heads, int kv_start, int length, int rows_per_wave,
-    float scale, const int *__restrict__ pos_dev, int capacity, float *__restrict__ part,
-    uint16_t *__restrict__ out_) {
+    const uint16_t *__restrict__ q_, const uint16_t *k_, const uint16_t *v_, int kv_heads,
+    int kv_start, int length, int rows_per_wave, float scale, const int *__restrict__ pos_dev,
+    int capacity, float *__restrict__ part, uint16_t *__restrict__ out_,
+    const AttentionQkRope qkr) {
   constexpr int LPP = D / 8;         // lanes per cached row
   constexpr int PPS = kWave / LPP;   // rows per wave load
   __shared__ float red[kAttWaves][G][10][LPP];
@@ -152,7 +193,10 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
     // window [0, position + 1) read from device memory; the grid covers the
     // whole cache and the chunks past the window exit
     const int pos = gp(pos_dev)[0];
-    if (pos < 0 || pos >= capacity) return;
+    if (pos < 0 || pos >= capacity) {
+      if (QKR && c == 0 && j == 0 && threadIdx.x == 0) atomicOr(qkr.err, 1u);
+      return;
+    }
     kv_start = 0;
     length = pos + 1;
     if (c * kAttWaves * rows_per_wave >= length) return;
@@ -162,27 +206,13 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
   const QD_GLOBAL uint16_t *vc = gp(v_);
   const size_t row = (size_t)kv_heads * D;  // elements per cache row
 
-  // this lane's 8 dimensions of each query head, fp32, pre-scaled
-  float qf[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    unpack8<F16>(*(const QD_GLOBAL u32x4 *)(q + (size_t)(j * G + h) * D + 8 * sub), qf[h]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qf[h][i] *= scale;
-  }
-  float m[G], l[G], o[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
-  }
+  // The rows of this wave: loads of the next rows are issued before the
+  // current ones are computed (the first ones before q is prepared).
   const int t0 = kv_start + (c * kAttWaves + wave) * rows_per_wave;
   const int t1 = min(t0 + rows_per_wave, length);
-  for (int tb = t0; tb < t1; tb += PPS * kAttUnroll) {
-    u32x4 kw[kAttUnroll], vw[kAttUnroll];
-    bool valid[kAttUnroll];
+  u32x4 kw[kAttUnroll], vw[kAttUnroll];
+  bool valid[kAttUnroll];
+  auto issue = [&](int tb) {
 #pragma unroll
     for (int u = 0; u < kAttUnroll; ++u) {
       const int t = tb + u * PPS + grp;
@@ -192,26 +222,110 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
       kw[u] = *(const QD_GLOBAL u32x4 *)(kc + off);
       vw[u] = *(const QD_GLOBAL u32x4 *)(vc + off);
     }
+  };
+  if (t0 < t1) issue(t0);
+
+  // this lane's 8 dimensions of each query head, fp32, pre-scaled
+  float qf[G][8];
+  // QKR: the new K/V row of head j, for the chunk that holds it
+  __shared__ __attribute__((aligned(16))) uint16_t knew[QKR ? D : 8], vnew[QKR ? D : 8];
+  const int pos = length - 1;
+  const bool mine = QKR && (pos - kv_start) / (kAttWaves * rows_per_wave) == c;
+  if constexpr (QKR) {
+    __shared__ float cs[2][D / 2];
+    u32x4 qraw[G], kraw, vraw;
+    const u32x4 wq = *(const QD_GLOBAL u32x4 *)(gp(qkr.q_w) + 8 * sub);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      qraw[h] = *(const QD_GLOBAL u32x4 *)(q + (size_t)(j * G + h) * D + 8 * sub);
+    const bool kwave = mine && wave == 0 && grp == 0;
+    u32x4 wk = {0u, 0u, 0u, 0u};
+    if (kwave) {
+      kraw = *(const QD_GLOBAL u32x4 *)(gp(qkr.k_src) + (size_t)j * D + 8 * sub);
+      vraw = *(const QD_GLOBAL u32x4 *)(gp(qkr.v_src) + (size_t)j * D + 8 * sub);
+      wk = *(const QD_GLOBAL u32x4 *)(gp(qkr.k_w) + 8 * sub);
+    }
+    if (threadIdx.x < D / 2) {
+      const double ang = (double)pos * pow((double)qkr.theta, -2.0 * threadIdx.x / (double)D);
+      cs[0][threadIdx.x] = (float)cos(ang);
+      cs[1][threadIdx.x] = (float)sin(ang);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      unpack8<true>(qraw[h], qf[h]);
+      norm_rope8<D>(qf[h], wq, sub, qkr.eps, cs);
+    }
+    if (kwave) {
+      float kx[8];
+      unpack8<true>(kraw, kx);
+      norm_rope8<D>(kx, wk, sub, qkr.eps, cs);
+      const u32x4 kp = pack8_f16(kx);
+      const size_t off = (size_t)pos * kv_heads * D + (size_t)j * D + 8 * sub;
+      *(QD_GLOBAL u32x4 *)(gp((uint16_t *)k_) + off) = kp;
+      *(QD_GLOBAL u32x4 *)(gp((uint16_t *)v_) + off) = vraw;
+      *(u32x4 *)(knew + 8 * sub) = kp;
+      *(u32x4 *)(vnew + 8 * sub) = vraw;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[h][i] *= scale;
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      unpack8<F16>(*(const QD_GLOBAL u32x4 *)(q + (size_t)(j * G + h) * D + 8 * sub), qf[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[h][i] *= scale;
+    }
+  }
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
+  }
+  for (int tb = t0; tb < t1; tb += PPS * kAttUnroll) {
+    if constexpr (QKR) {
+      // the row this step appends: from LDS, not the cache being written
+      if (mine) {
+#pragma unroll
+        for (int u = 0; u < kAttUnroll; ++u)
+          if (tb + u * PPS + grp == pos) {
+            kw[u] = *(const u32x4 *)(knew + 8 * sub);
+            vw[u] = *(const u32x4 *)(vnew + 8 * sub);
+          }
+      }
+    }
+    float kf[kAttUnroll][8], vf[kAttUnroll][8];
+    bool cv[kAttUnroll];
 #pragma unroll
     for (int u = 0; u < kAttUnroll; ++u) {
-      float kf[8], vf[8];
-      unpack8<F16>(kw[u], kf);
-      unpack8<F16>(vw[u], vf);
+      unpack8<F16>(kw[u], kf[u]);
+      unpack8<F16>(vw[u], vf[u]);
+      cv[u] = valid[u];
+    }
+    if (tb + PPS * kAttUnroll < t1) issue(tb + PPS * kAttUnroll);
+#pragma unroll
+    for (int u = 0; u < kAttUnroll; ++u) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s = fmaf(qf[h][i], kf[i], s);
+        for (int i = 0; i < 8; ++i) s = fmaf(qf[h][i], kf[u][i], s);
         // the row's score: sum over its LPP lanes
 #pragma unroll
         for (int w = 1; w < LPP; w <<= 1) s += __shfl_xor(s, w, kWave);
-        if (!valid[u]) s = -INFINITY;
+        if (!cv[u]) s = -INFINITY;
         const float mm = fmaxf(m[h], s);
         const float a = m[h] == -INFINITY ? 0.f : __expf(m[h] - mm);
         const float p = s == -INFINITY ? 0.f : __expf(s - mm);
         l[h] = l[h] * a + p;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[h][i] = fmaf(p, vf[i], o[h][i] * a);
+        for (int i = 0; i < 8; ++i) o[h][i] = fmaf(p, vf[u][i], o[h][i] * a);
         m[h] = mm;
       }
     }
@@ -308,19 +422,33 @@ hipError_t launch_att(const AttentionArgs &a, hipStream_t stream) {
   const int window = a.pos_dev ? a.capacity : a.length - a.kv_start;
   const AttentionPlan p = attention_plan(a.kv_heads, window, D);
   if (p.nchunks < 1 || p.nchunks > attention_max_chunks(a.kv_heads)) return hipErrorInvalidValue;
+  const AttentionQkRope none = {};
   if (p.nchunks == 1 && !a.pos_dev) {
-    hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, true>), dim3(1, a.kv_heads),
+    hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, true, false>), dim3(1, a.kv_heads),
                        dim3(kAttThreads), 0, stream, a.q, a.k, a.v, a.kv_heads, a.kv_start,
-                       a.length, p.rows_per_wave, a.scale, a.pos_dev, a.capacity, a.part, a.out);
-  } else {
-    hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, false>),
+                       a.length, p.rows_per_wave, a.scale, a.pos_dev, a.capacity, a.part, a.out,
+                       none);
+    return hipGetLastError();
+  }
+  if constexpr (F16) {
+    if (a.qkr) {
+      if (!a.pos_dev) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attention_partial_kernel<D, G, true, false, true>),
+                         dim3(p.nchunks, a.kv_heads), dim3(kAttThreads), 0, stream, a.q, a.k,
+                         a.v, a.kv_heads, a.kv_start, a.length, p.rows_per_wave, a.scale,
+                         a.pos_dev, a.capacity, a.part, a.out, *a.qkr);
+    }
+  }
+  if (!a.qkr)
+    hipLaunchKernelGGL((attention_partial_kernel<D, G, F16, false, false>),
                        dim3(p.nchunks, a.kv_heads), dim3(kAttThreads), 0, stream, a.q, a.k, a.v,
                        a.kv_heads, a.kv_start, a.length, p.rows_per_wave, a.scale, a.pos_dev,
-                       a.capacity, a.part, a.out);
-    hipLaunchKernelGGL((attention_combine_kernel<D, F16>), dim3(a.kv_heads * G),
-                       dim3(kAttThreads), 0, stream, a.part, p.nchunks, p.nchunks, a.pos_dev,
-                       a.capacity, p.rows_per_wave, a.out);
-  }
+                       a.capacity, a.part, a.out, none);
+  else if (!F16)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attention_combine_kernel<D, F16>), dim3(a.kv_heads * G),
+                     dim3(kAttThreads), 0, stream, a.part, p.nchunks, p.nchunks, a.pos_dev,
+                     a.capacity, p.rows_per_wave, a.out);
   return hipGetLastError();
 }
 

@@ -666,6 +666,7 @@ qd_status attention_decode(const void *q, const void *k_cache, const void *v_cac
   a.f16 = f16 == 1;
   a.pos_dev = nullptr;
   a.capacity = 0;
+  a.qkr = nullptr;
   hipError_t e = qd::launch_attention_decode(a, (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
@@ -872,10 +873,16 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     g.rows[2] = kw;
     QD_TRY(qd::launch_affine_gemv_pro(g, hid, res[cur], pn, s));
     if (l > 0) cur ^= 1;
-    QD_TRY(qd::launch_qk_norm_rope(q, kbuf, vbuf, (const uint16_t *)ly.q_norm,
-                                   (const uint16_t *)ly.k_norm, H, KV, d, m.eps, m.theta, pos,
-                                   (int)m.capacity, (uint16_t *)ly.k_cache,
-                                   (uint16_t *)ly.v_cache, err, s));
+    // per-head norms + RoPE of q and the new K row, and the K/V append at
+    // row p, fused into the attention's first kernel
+    qd::AttentionQkRope qr;
+    qr.k_src = kbuf;
+    qr.v_src = vbuf;
+    qr.q_w = (const uint16_t *)ly.q_norm;
+    qr.k_w = (const uint16_t *)ly.k_norm;
+    qr.eps = m.eps;
+    qr.theta = m.theta;
+    qr.err = err;
     qd::AttentionArgs a;
     a.q = q;
     a.k = (const uint16_t *)ly.k_cache;
@@ -891,6 +898,7 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     a.f16 = true;
     a.pos_dev = pos;
     a.capacity = (int)m.capacity;
+    a.qkr = &qr;
     QD_TRY(qd::launch_attention_decode(a, s));
     qd::AffineGroup go = {};
     go.n = 1;

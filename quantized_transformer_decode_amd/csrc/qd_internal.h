@@ -79,6 +79,16 @@ hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
 // With pos_dev (device int32), the window is [0, *pos_dev + 1) of a cache of
 // `capacity` rows (nothing is computed when the position is outside it) and
 // kv_start / length are ignored.
+// With qkr (device position and f16 only), q is the raw q/k/v GEMV output:
+// the first kernel applies the per-head RMSNorm and NeoX RoPE of
+// launch_qk_norm_rope to q (in registers) and to the new K row of k_src,
+// which it appends, with the V row of v_src, at cache row *pos_dev; a
+// position outside the cache sets bit 1 of *err.
+struct AttentionQkRope {
+  const uint16_t *k_src, *v_src, *q_w, *k_w;
+  float eps, theta;
+  unsigned *err;
+};
 struct AttentionArgs {
   const uint16_t *q, *k, *v;
   uint16_t *out;
@@ -88,6 +98,7 @@ struct AttentionArgs {
   bool f16;
   const int *pos_dev;
   int capacity;
+  const AttentionQkRope *qkr;
 };
 // Rows per wave and chunks of the window [kv_start, length) (host only).
 struct AttentionPlan {
