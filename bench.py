@@ -32,6 +32,7 @@ All inputs are seeded synthetic data of the pages' shapes (see synth/).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -115,10 +116,14 @@ def capture(fn):
     return g
 
 
-def affine_blob(qd, rows, cols, key):
+def affine_blob(qd, rows, cols, key, digests=None):
+    """The packed blob of one synthetic matrix; with `digests` (a list), the
+    sha256 of its codes, scales and biases are appended in that order."""
     import torch
     import synth
     tr = synth.affine_triplet(rows, cols, key=key)
+    if digests is not None:
+        digests += [synth.sha256(tr.codes), synth.sha256(tr.scales), synth.sha256(tr.biases)]
     blob = torch.empty(qd.affine_i8_g64_bytes(rows, cols), dtype=torch.uint8, device=DEV)
     qd.affine_i8_g64_pack(u8dev(tr.codes), u8dev(tr.scales), u8dev(tr.biases), rows, cols, blob)
     return blob
@@ -138,11 +143,13 @@ class DecodeStep:
         self.m = m
         self.mats = synth.decode_step_matrices(spec)
         self.blobs, self.xs, self.ys, self.x_host = [], [], [], []
+        self.digests = []  # sha256 of every generated tensor, in generation order
         self.weight_bytes = 0
         for i, (layer, name, rows, cols, stage) in enumerate(self.mats):
-            self.blobs.append(affine_blob(qd, rows, cols, (cfg, layer, i)))
+            self.blobs.append(affine_blob(qd, rows, cols, (cfg, layer, i), self.digests))
             xb = synth.x_bf16(m, cols, key=(cfg, layer, 1000 + i))
             self.x_host.append(xb)
+            self.digests.append(synth.sha256(xb))
             self.xs.append(bf16dev(xb))
             self.ys.append(torch.empty((m, rows), dtype=torch.bfloat16, device=DEV))
             self.weight_bytes += qd.affine_i8_g64_bytes(rows, cols)
@@ -817,6 +824,12 @@ def main():
             "batch": 1, "weight_bytes": step.weight_bytes,
             "activations": "bf16 in/out, u8 codes, fp32 accumulate",
             "variant": variant,
+            "inputs_sha256": {
+                "tensors": len(step.digests),
+                "order": "per GEMV in decoder order: codes, scales, biases, x",
+                "sha256_of_digests": hashlib.sha256(
+                    "".join(step.digests).encode()).hexdigest(),
+            },
         },
         "weight_GBps": gbps,
         "hbm_peak_frac": gbps / HBM_PEAK_GBPS,
