@@ -421,10 +421,13 @@ def row_whisper_large_prefill(qd, layers):
     g = capture(lambda: [qd.qgemm_q4_0_prefill(wq, r, c, xs[c], ys[k], m)
                          for k, (_, r, c, wq) in enumerate(lay)])
     ms = event_time(g.replay, 10, 3)
+    # per matrix: ten back-to-back launches per graph (a graph of one ~20 us
+    # launch leaves the GPU idle between replays, and the timing turns bimodal)
     per = {}
     for k, (name, r, c, wq) in enumerate(lay):
-        gk = capture(lambda k=k, r=r, c=c, wq=wq: qd.qgemm_q4_0_prefill(wq, r, c, xs[c], ys[k], m))
-        mk = event_time(gk.replay, 20, 3)
+        gk = capture(lambda k=k, r=r, c=c, wq=wq: [
+            qd.qgemm_q4_0_prefill(wq, r, c, xs[c], ys[k], m) for _ in range(10)])
+        mk = event_time(gk.replay, 5, 2) / 10
         per[name] = {"us": mk * 1e3, "TFLOPs": 2 * m * r * c / (mk * 1e-3) / 1e12,
                      "mfma_frac": 2 * m * r * c / (mk * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     tf = flops / (ms * 1e-3) / 1e12
@@ -445,10 +448,10 @@ def row_whisper_large_prefill(qd, layers):
                              5120, xs[5120], m)
     gl = capture(linear_layer)
     ms_lin = event_time(gl.replay, 10, 3)
-    gq = capture(lambda: qd.qlinear_q4_0_gemm(
+    gq = capture(lambda: [qd.qlinear_q4_0_gemm(
         [(byname[n][2], None if n == "k" else bias[n], yl[n], byname[n][0]) for n in ("q", "k", "v")],
-        1280, xs[1280], m))
-    ms_qkv = event_time(gq.replay, 20, 3)
+        1280, xs[1280], m) for _ in range(10)])
+    ms_qkv = event_time(gq.replay, 5, 2) / 10
     f_qkv = 3 * 2 * m * 1280 * 1280
     return {"frames": m, "flops_per_layer": flops, "ms_per_layer": ms,
             "ms_32_layers": 32 * ms, "TFLOPs": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,

@@ -352,3 +352,32 @@ def test_step_qwen3_0_6b_shape_two_layers():
         qd.qwen3_step_run(gm.model, gm.ws, gm.wsb, x, pos, logits, advance=True)
         torch.cuda.synchronize()
         _check_step(gm, p, _h(x), _h(logits), *ref[p], logit_rows=rows)
+
+
+def test_step_without_logits_odd_layers_advancing():
+    # three layers (an odd count), no LM head: the last residual add runs as
+    # its own kernel, which also advances the position
+    spec = synth.QWEN3_TINY_STEP
+    gm = GpuModel(spec, capacity=8, layers=3)
+    xs_bits = synth.x_f16(4, spec.hidden, key=(38, 0, 0))
+    k16, v16 = empty_caches(spec, gm.cap, gm.nl)
+    k64, v64 = empty_caches(spec, gm.cap, gm.nl)
+    om = dict(gm.om, embed=None)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    x = torch.empty(spec.hidden, dtype=torch.float16, device=DEV)
+    for p in range(4):
+        x.copy_(dev_f16(xs_bits[p]))
+        qd.qwen3_step_run(gm.model, gm.ws, gm.wsb, x, pos, None, advance=True)
+        torch.cuda.synchronize()
+        assert int(pos.item()) == p + 1
+        xr = _bits_f64(xs_bits[p])
+        x16, _ = oracle.qwen3_step(xr, p, om, k16, v16, f16=True)
+        x64, _ = oracle.qwen3_step(xr, p, om, k64, v64, f16=False)
+        got = _h(x)
+        e = oracle.normwise_error(got, x16)
+        assert e <= _bound(got, x16, x64), f"pos={p}: x {e:.3e}"
+        for li in range(3):
+            got_k = _h(gm.layers[li]["k_cache"][p])
+            assert oracle.normwise_error(got_k, k16[li][p]) <= _bound(got_k, k16[li][p],
+                                                                      k64[li][p])
+    assert qd.qwen3_step_check(gm.ws) == 0
