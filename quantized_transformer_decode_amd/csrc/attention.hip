@@ -22,7 +22,8 @@
 // type.  (Folding the combine into the first kernel -- the last workgroup
 // of a K/V head merging it -- measured slower at every window size: that
 // one workgroup's chain of memory round trips costs more than the second
-// launch.)
+// launch.)  Inside the decoder step, the first kernel also takes over the
+// per-head q/k RMSNorm + RoPE and the K/V cache append (QKR).
 #include "qd_device.h"
 #include "qd_internal.h"
 

@@ -13,8 +13,11 @@
 //     and the norm reads that f16 value);
 //   * per-head RMSNorm + RoPE (the normed head is rounded to f16 before the
 //     rotation) + the copy of the V row into the cache.
-// The step reads `position` from device memory, so a captured graph of the
-// step can be replayed token after token.
+// These kernels serve the standalone entry points (and the last residual
+// add of a step without logits); inside qwen3_step_run the same arithmetic
+// runs as prologues of the GEMVs (affine_gemv.hip) and of the attention
+// (attention.hip).  `position` is read from device memory, so a captured
+// graph can be replayed token after token.
 #include "qd_device.h"
 #include "qd_internal.h"
 

@@ -381,3 +381,28 @@ def test_step_without_logits_odd_layers_advancing():
             assert oracle.normwise_error(got_k, k16[li][p]) <= _bound(got_k, k16[li][p],
                                                                       k64[li][p])
     assert qd.qwen3_step_check(gm.ws) == 0
+
+
+@pytest.mark.parametrize("heads,kv_heads,head_dim", [(4, 4, 64), (8, 2, 64), (16, 2, 128),
+                                                     (8, 1, 128)])
+def test_step_head_groupings(heads, kv_heads, head_dim):
+    # 1, 4 and 8 query heads per K/V head (the fused attention prologue's
+    # other instances), one layer, positions 0..69: with a 4096-row cache the
+    # attention chunks hold 32 (d 128) or 64 (d 64) rows, so the window
+    # crosses chunk boundaries and the appended row moves between chunks
+    spec = synth.Qwen3Spec(f"qwen3-g{heads // kv_heads}-d{head_dim}", 256, heads, kv_heads,
+                           head_dim, 512, 1000, 1)
+    print(f"step heads={heads} kv={kv_heads} d={head_dim}", flush=True)
+    gm = GpuModel(spec, capacity=4096)
+    positions = list(range(70))
+    xs_bits = synth.x_f16(len(positions), spec.hidden, key=(39, heads, head_dim))
+    ref = _oracle_runs(gm, [_bits_f64(b) for b in xs_bits])
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    x = torch.empty(spec.hidden, dtype=torch.float16, device=DEV)
+    logits = torch.empty(spec.vocab, dtype=torch.float16, device=DEV)
+    for p in positions:
+        x.copy_(dev_f16(xs_bits[p]))
+        qd.qwen3_step_run(gm.model, gm.ws, gm.wsb, x, pos, logits, advance=True)
+        torch.cuda.synchronize()
+        _check_step(gm, p, _h(x), _h(logits), *ref[p])
+    assert qd.qwen3_step_check(gm.ws) == 0
