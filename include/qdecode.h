@@ -439,8 +439,9 @@ size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model);
  * Model requirements (QD_ESHAPE): hidden, inter and heads * head_dim
  * multiples of 64 and <= 8192; head_dim 64 or 128; heads / kv_heads in
  * {1, 2, 4, 8}; vocab, n_layers >= 1; 1 <= capacity <= 2^30.  Null or
- * misaligned pointers: QD_EINVAL / QD_EALIGN.  Calls sharing a workspace
- * must be ordered on one stream. */
+ * misaligned pointers: QD_EINVAL / QD_EALIGN; x, logits, the workspace and
+ * a layer's K and V caches must not overlap one another (QD_EINVAL).  Calls
+ * sharing a workspace must be ordered on one stream. */
 qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t workspace_bytes,
                          void *x, int32_t *position, void *logits, int32_t advance,
                          void *stream);

@@ -822,6 +822,16 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
       (logits && (overlap(logits, (size_t)m.vocab * 2, workspace, L.total) ||
                   overlap(logits, (size_t)m.vocab * 2, x, hb))))
     return QD_EINVAL;
+  // the caches (written by the step) clear of the workspace, x and logits
+  const size_t cb = (size_t)m.capacity * m.kv_heads * m.head_dim * 2;
+  for (int64_t l = 0; l < m.n_layers; ++l) {
+    const void *caches[2] = {m.layers[l].k_cache, m.layers[l].v_cache};
+    for (const void *c : caches)
+      if (overlap(c, cb, workspace, L.total) || overlap(c, cb, x, hb) ||
+          (logits && overlap(c, cb, logits, (size_t)m.vocab * 2)))
+        return QD_EINVAL;
+    if (overlap(caches[0], cb, caches[1], cb)) return QD_EINVAL;
+  }
   qd_status st = check_device();
   if (st != QD_OK) return st;
 

@@ -373,6 +373,10 @@ def test_qwen3_step_workspace_and_errors():
     assert run(model=_qwen3(layers=(qd.Qwen3Layer * 2)(layer, layer))) == qd.QD_EINVAL
     layer.k_cache = 0x7fd000000000 + 8
     assert run(model=_qwen3(layers=(qd.Qwen3Layer * 2)(layer, layer))) == qd.QD_EALIGN
+    layer.k_cache = WS + 4096                    # a cache inside the workspace
+    assert run(model=_qwen3(layers=(qd.Qwen3Layer * 2)(layer, layer))) == qd.QD_EINVAL
+    layer.k_cache = layer.v_cache + 1024         # K and V caches overlapping
+    assert run(model=_qwen3(layers=(qd.Qwen3Layer * 2)(layer, layer))) == qd.QD_EINVAL
     assert _call("qwen3_step_check", None, ctypes.byref(ctypes.c_uint32()), None) == qd.QD_EINVAL
 
 
