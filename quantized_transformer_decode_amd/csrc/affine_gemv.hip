@@ -319,6 +319,13 @@ __device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_
   float a[CPT][8];
   if constexpr (PRO == 1) {
     __shared__ float red[kMW];
+    // the norm weights are loaded with x and delta (one memory round trip)
+    u32x4 wv[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int i = min(t + k * kMThreads, chunks - 1);
+      wv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
+    }
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
@@ -347,8 +354,7 @@ __device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_
     for (int k = 0; k < CPT; ++k) {
       const int i = t + k * kMThreads;
       if (i < chunks) {
-        const u32x4 wv = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
-        const uint32_t we[4] = {wv.x, wv.y, wv.z, wv.w};
+        const uint32_t we[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
         float n[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)

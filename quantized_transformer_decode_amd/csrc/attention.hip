@@ -247,9 +247,16 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
       wk = *(const QD_GLOBAL u32x4 *)(gp(qkr.k_w) + 8 * sub);
     }
     if (threadIdx.x < D / 2) {
-      const double ang = (double)pos * pow((double)qkr.theta, -2.0 * threadIdx.x / (double)D);
-      cs[0][threadIdx.x] = (float)cos(ang);
-      cs[1][threadIdx.x] = (float)sin(ang);
+      // angle pos * theta^(-2i/d) and its reduction to [-pi, pi] in fp64
+      // (a position of tens of thousands times the frequency needs it), the
+      // sine and cosine of the reduced angle in fp32
+      constexpr double kTwoPi = 6.283185307179586;
+      const double ang = (double)pos * exp2(-2.0 * threadIdx.x / (double)D * log2((double)qkr.theta));
+      const float r = (float)(ang - kTwoPi * rint(ang / kTwoPi));
+      float sn, cn;
+      sincosf(r, &sn, &cn);
+      cs[0][threadIdx.x] = cn;
+      cs[1][threadIdx.x] = sn;
     }
     __syncthreads();
 #pragma unroll
