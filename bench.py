@@ -236,6 +236,85 @@ def cpu_baseline(step: DecodeStep):
     }
 
 
+def cpu_baseline_rows():
+    """The oracle (f64, all host cores) on a bounded sample of every other
+    config's workload, with the extrapolation to the whole workload stated
+    in each entry.  Inputs are the same shapes and distributions as the GPU
+    rows (seeded host tensors)."""
+    import oracle
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def affine(rows, cols, key):
+        tr = synth.affine_triplet(rows, cols, key=key)
+        return oracle.affine_pack(tr.codes, tr.scales, tr.biases, rows, cols)
+
+    # config 1: one 1024 x 1024 affine GEMV, batch 1
+    blob = affine(1024, 1024, (1, 0, 0))
+    x = synth.x_bf16(1, 1024, key=(1, 0, 1))
+    dt = min(timed(lambda: oracle.affine_gemv(blob, 1024, 1024, x)) for _ in range(3))
+    nb = oracle.affine_bytes(1024, 1024)
+    out["affine_gemv_1024"] = {"us_per_gemv": dt * 1e6, "weight_GBps": nb / dt / 1e9,
+                               "sample": "the whole GEMV (best of 3)"}
+    # config 2: Whisper-base FFN pair, Q4_0 bake and GEMV at M = 1, 4
+    pair = []
+    t_bake = 0.0
+    for name, rows, cols in synth.WHISPER_BASE_FFN:
+        w = synth.w_f32(rows, cols, key=(2, 0, rows))
+        t0 = time.perf_counter()
+        pair.append((rows, cols, oracle.q4_0_quantize(w, rows, cols)))
+        t_bake += time.perf_counter() - t0
+    pb = sum(oracle.q4_0_bytes(r, c) for r, c, _ in pair)
+    ffn = {"bake_us_per_pair": t_bake * 1e6}
+    for m in (1, 4):
+        xs = [synth.x_f32(m, c, key=(2, m, c)) for _, c, _ in pair]
+        dt = min(timed(lambda: [oracle.q4_0_gemm(wq, r, c, xx) for (r, c, wq), xx in
+                                zip(pair, xs)]) for _ in range(3))
+        ffn[f"M{m}"] = {"us_per_pair": dt * 1e6, "weight_GBps": pb / dt / 1e9}
+    ffn["sample"] = "the whole pair (best of 3)"
+    out["q4_0_ffn_pair"] = ffn
+    # config 4: Qwen3-1.7B step at batch 1 -- one layer's seven GEMVs timed,
+    # the step is that per-weight time over all 1.83 GB of weights
+    spec = synth.QWEN3_1_7B
+    mats = [m_ for m_ in synth.decode_step_matrices(spec) if m_[0] == 0]
+    blobs = [affine(r, c, (4, 0, i)) for i, (_, _, r, c, _) in enumerate(mats)]
+    xs = [synth.x_bf16(1, c, key=(4, 0, 100 + i)) for i, (_, _, r, c, _) in enumerate(mats)]
+    dt = timed(lambda: [oracle.affine_gemv(b, r, c, xx) for b, (_, _, r, c, _), xx in
+                        zip(blobs, mats, xs)])
+    lb = sum(oracle.affine_bytes(r, c) for _, _, r, c, _ in mats)
+    step_s = dt * 1827979264 / lb
+    out["qwen3_1_7b_step"] = {"tokens_per_s": 1.0 / step_s, "weight_GBps": lb / dt / 1e9,
+                              "sample": "layer 0's 7 GEMVs (%d bytes) in %.3f s, scaled by "
+                                        "weight bytes to the 1,827,979,264-byte step, M = 1"
+                                        % (lb, dt)}
+    # configs 5a / 5b: one Whisper-large layer, baked by the oracle
+    lay = [(name, r, c, oracle.q4_0_quantize(synth.w_f32(r, c, key=(5, 0, k)), r, c))
+           for k, (name, r, c) in enumerate(synth.WHISPER_LARGE_LAYER)]
+    frames = 64
+    xb = {c: synth.x_bf16(frames, c, key=(5, 99, c)) for c in (1280, 5120)}
+    dt = timed(lambda: [oracle.q4_0_gemm(wq, r, c, xb[c]) for _, r, c, wq in lay])
+    flops = sum(2 * frames * r * c for _, r, c, _ in lay)
+    layer_s = dt * synth.WHISPER_LARGE_FRAMES / frames
+    out["whisper_large_prefill"] = {
+        "TFLOPs": flops / dt / 1e12, "ms_per_layer": layer_s * 1e3,
+        "ms_32_layers": 32 * layer_s * 1e3,
+        "sample": "one encoder layer's six GEMMs on %d of the 1500 frames (%.3f s), scaled "
+                  "by frames" % (frames, dt)}
+    x1 = {c: synth.x_f32(1, c, key=(5, 98, c)) for c in (1280, 5120)}
+    dt = timed(lambda: [oracle.q4_0_gemm(wq, r, c, x1[c]) for _, r, c, wq in lay])
+    db = sum(oracle.q4_0_bytes(r, c) for _, r, c, _ in lay)
+    out["whisper_large_decoder"] = {
+        "tokens_per_s": 1.0 / (32 * dt), "weight_GBps": db / dt / 1e9,
+        "sample": "one decoder layer's six GEMVs at M = 1 (%.3f s), times 32 layers" % dt}
+    return {"cores": cores, "kind": "oracle", "configs": out}
+
+
 # ---- rows ------------------------------------------------------------------------
 
 def row_affine_gemv_1024(qd):
@@ -855,6 +934,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(step)
+        out["cpu_baseline_rows"] = cpu_baseline_rows()
     step.free()
     torch.cuda.empty_cache()
     ceiling = hbm_read_ceiling(qd)
