@@ -325,8 +325,8 @@ int64_t attention_decode_workspace_bytes(int64_t heads, int64_t kv_heads, int64_
  * scale 1/sqrt(head_dim)).  Scores, exponentials and sums in fp32, the
  * output rounded once (nearest even) to the 16-bit type.  Workgroups take
  * chunks of the window (split softmax) and a second launch merges the
- * chunks of each head; a window of up to 32 rows (head_dim 128) or 64 rows
- * (head_dim 64) is one chunk and takes one launch.
+ * chunks of each head; a window of up to 128 rows is one chunk and takes
+ * one launch.
  *   q          device, [heads, head_dim] 16-bit, 16-byte aligned
  *   k_cache,   device, [>= length rows, kv_heads, head_dim] 16-bit (the
  *   v_cache    cache row of position t holds every K/V head), 16-byte aligned

@@ -34,6 +34,7 @@ constexpr int kAttThreads = 256;
 constexpr int kAttWaves = kAttThreads / kWave;
 constexpr int kAttUnroll = 2;      // row loads in flight per lane (K and V each)
 constexpr int kAttTargetWgs = 512; // about two workgroups per CU of a 256-CU device
+constexpr int kAttSingleRowsPerWave = 32;  // windows up to 4 * 32 rows: a single chunk
 
 template <bool F16>
 __device__ __forceinline__ float to_f32(uint32_t bits) {
@@ -477,6 +478,8 @@ AttentionPlan attention_plan(int64_t kv_heads, int64_t window, int head_dim) {
   const int64_t step = (int64_t)(kWave / (head_dim / 8)) * kAttUnroll;
   const int64_t want = (kAttTargetWgs + kv_heads - 1) / kv_heads;
   int64_t rpw = (window + want * kAttWaves - 1) / (want * kAttWaves);
+  // a short window is one chunk: one launch beats a second one for the merge
+  if (window <= kAttWaves * kAttSingleRowsPerWave) rpw = (window + kAttWaves - 1) / kAttWaves;
   rpw = (rpw + step - 1) / step * step;
   if (rpw < step) rpw = step;
   AttentionPlan p;

@@ -63,10 +63,11 @@ def _case(heads, kv_heads, d, rows, length, kv_start, f16, scale=None, key=0):
 
 
 # Qwen3 0.6B/1.7B (16/8 heads), 4B (32/8), 8 query heads per K/V head, plain
-# multi-head at d 64; windows of one row, within one chunk (<= 32 rows at 8
-# K/V heads), one past it, ragged multi-chunk lengths and long contexts
+# multi-head at d 64; windows of one row, within the single-chunk range
+# (<= 128 rows), one past it, ragged multi-chunk lengths and long contexts
 CASES = [
-    (16, 8, 128, 1, 0), (16, 8, 128, 7, 0), (16, 8, 128, 32, 0), (16, 8, 128, 33, 0),
+    (16, 8, 128, 1, 0), (16, 8, 128, 7, 0), (16, 8, 128, 128, 0), (16, 8, 128, 129, 0),
+    (16, 8, 128, 33, 0),
     (16, 8, 128, 1000, 0), (16, 8, 128, 4097, 0), (32, 8, 128, 1500, 3),
     (64, 8, 128, 257, 0), (8, 8, 64, 333, 10), (4, 2, 64, 70000, 0), (16, 8, 128, 32768, 0),
 ]
