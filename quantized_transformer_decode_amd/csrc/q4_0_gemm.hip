@@ -38,9 +38,13 @@ namespace qd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BK = 128;                 // K columns per stage (4 blocks)
+#ifndef QD_GEMM_BK
+#define QD_GEMM_BK 128
+#endif
+constexpr int BK = QD_GEMM_BK;          // K columns per stage
 constexpr int NB = BK / 32;             // Q4_0 blocks per stage
-constexpr int LDA = BK + 8;             // LDS row stride in bf16 (272 bytes)
+constexpr int CPR = BK / 8;             // 16-byte x chunks per tile row per stage
+constexpr int LDA = BK + 8;             // LDS row stride in bf16
 
 template <int BM, int BN>
 struct Tile {
@@ -49,7 +53,7 @@ struct Tile {
   static constexpr int STAGE_BYTES = (A_ELEMS + B_ELEMS) * 2 + BN * NB * 4;
   static constexpr int TM = BM / 32;    // 16x16 MFMA tiles per wave along M
   static constexpr int TN = BN / 32;    // ... along N (waves are 2 x 2)
-  static constexpr int XCH = BM * 16 / kThreads;  // x 16-byte chunks per thread
+  static constexpr int XCH = BM * CPR / kThreads;  // x 16-byte chunks per thread
   static constexpr int WB = BN * NB / kThreads;   // weight blocks per thread (<= 1)
 };
 
@@ -73,15 +77,15 @@ struct Stage {
 };
 
 // Global loads of one stage: x rows m0.., columns k0..k0+127; the weight
-// block (row n0 + tid/4, block kb0 + tid%4).
+// block (row n0 + tid/NB, block kb0 + tid%NB).
 template <int BM, int BN>
 __device__ __forceinline__ void stage_load(Stage<BM, BN> &st, const QD_GLOBAL uint16_t *x,
                                            const QD_GLOBAL uint8_t *w, int m, int rows,
                                            int cols, int m0, int n0, int kb0, int tid) {
 #pragma unroll
   for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
-    const int c = tid + i * kThreads;  // 16-byte chunk of the 128 x 256-byte tile
-    const int r = c >> 4, ch = c & 15;
+    const int c = tid + i * kThreads;  // 16-byte chunk of the BM x 2*BK-byte tile
+    const int r = c / CPR, ch = c % CPR;
     // frames past m read frame m-1: they only feed output rows that are
     // never stored
     const int row = min(m0 + r, m - 1);
@@ -89,7 +93,7 @@ __device__ __forceinline__ void stage_load(Stage<BM, BN> &st, const QD_GLOBAL ui
     st.xa[i] = make_uint4(v.x, v.y, v.z, v.w);
   }
   st.has_w = tid < BN * NB;
-  const int r = (tid >> 2) % BN, b = tid & 3;
+  const int r = (tid / NB) % BN, b = tid % NB;
   int n = n0 + r;
   if (n >= rows) n = rows - 1;  // clamped rows are zeroed at the store
   const size_t flat = (size_t)n * (cols >> 5) + kb0 + b;
@@ -110,11 +114,11 @@ __device__ __forceinline__ void stage_store(const Stage<BM, BN> &st, uint16_t *A
 #pragma unroll
   for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
     const int c = tid + i * kThreads;
-    const int r = c >> 4, ch = c & 15;
+    const int r = c / CPR, ch = c % CPR;
     *(uint4 *)(As + r * LDA + ch * 8) = st.xa[i];
   }
   if (!st.has_w) return;
-  const int r = tid >> 2, b = tid & 3;
+  const int r = tid / NB, b = tid % NB;
   const bool odd = st.fb & 1, dead = st.fb & 2;
   // d: bytes 0-1 of the block; nibble bytes 2..17
   const uint32_t dbits = odd ? (st.w[0] >> 16) : (st.w[0] & 0xffffu);
