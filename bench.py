@@ -834,7 +834,7 @@ def environment():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the decode path runs on one GPU; --gpus must be 1 "
                           "(the path runs on a single MI355X; sharding is described in the "
                           "design notes, not launched)"}))
         return 2
