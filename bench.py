@@ -359,7 +359,8 @@ def row_affine_lm_head(qd):
             y = torch.empty((m, rows), dtype=torch.bfloat16, device=DEV)
             g = capture(lambda: [qd.qgemv_affine_i8_g64(blobs[i % 2], rows, cols, x, y, m)
                                  for i in range(8)])
-            ms = event_time(g.replay, 5, 2) / 8
+            # the clocks settle over the first ~100 launches of a row
+            ms = event_time(g.replay, 10, 12) / 8
             gbps = nbytes / (ms * 1e-3) / 1e9
             res[f"M{m}"] = {"us": ms * 1e3, "GBps": gbps, "hbm_peak_frac": gbps / HBM_PEAK_GBPS}
         out[f"{rows}x{cols}"] = res
@@ -385,7 +386,7 @@ def row_affine_f16(qd):
         y = torch.empty((m, rows), dtype=torch.float16, device=DEV)
         g = capture(lambda: [qd.qgemv_affine_i8_g64_f16(blobs[i % 2], rows, cols, x, y, m)
                              for i in range(8)])
-        ms = event_time(g.replay, 5, 2) / 8
+        ms = event_time(g.replay, 10, 12) / 8
         gbps = nbytes / (ms * 1e-3) / 1e9
         res[f"M{m}"] = {"us": ms * 1e3, "GBps": gbps, "hbm_peak_frac": gbps / HBM_PEAK_GBPS}
     ids = [int(t) for t in np.linspace(0, rows - 1, 16)]

@@ -572,9 +572,11 @@ hipError_t launch_mfma(const AffineGroup &g, int cols, const uint16_t *x, int m,
 // register groups of kG items, double-buffered: the next group's loads are
 // issued (always the same number, so the compiler waits for exactly the
 // group being consumed) before the current group is computed.  x sits in LDS
-// in the xswz layout, fp32.
+// in the xswz layout, fp32.  Groups of two items with up to four
+// workgroups per CU measured fastest on the LM heads (8 items: ~10-30 %
+// slower; 8 workgroups per CU: no better).
 
-constexpr int kG = 8;
+constexpr int kG = 2;
 constexpr int kM1Threads = 512;
 constexpr int kM1Waves = kM1Threads / kWave;
 
@@ -728,9 +730,11 @@ hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
   const GemvPrologue none = {};
   if (f16) return launch_mfma<ActF16>(g, cols, x, m, none, stream);
   // Batch 1 takes the VALU streaming kernel only for a single very large
-  // matrix (LM heads), where its 1 KiB-per-row loads keep the most bytes in
-  // flight; below that the matrix-core kernel's K split gives more waves.
-  if (g.n == 1 && m == 1 && (int64_t)g.rows[0] * cols >= ((int64_t)1 << 28)) {
+  // matrix (LM heads, >= 2^27 weights), where its 1 KiB-per-row loads keep
+  // the most bytes in flight (151936 x 1024: 5.2-5.4 TB/s against ~4.0 for
+  // the matrix-core kernel); below that the matrix-core kernel's K split
+  // gives more waves.
+  if (g.n == 1 && m == 1 && (int64_t)g.rows[0] * cols >= ((int64_t)1 << 27)) {
     const uint8_t *w = g.w[0];
     uint16_t *y = g.y[0];
     const int rows = g.rows[0];
