@@ -610,6 +610,7 @@ __device__ __forceinline__ void m1_issue(M1Group &g, const QD_GLOBAL uint8_t *w,
   }
 }
 
+template <bool F16>
 __device__ __forceinline__ void m1_compute(const M1Group &g, int cols, int chunks, int lo, int n,
                                            int i0, int lane, const float *xl,
                                            QD_GLOBAL uint16_t *y, float &rowsum) {
@@ -638,7 +639,7 @@ __device__ __forceinline__ void m1_compute(const M1Group &g, int cols, int chunk
       if (!valid) p = 0.f;
       rowsum += wave_sum_dpp(p);
       if (ch == chunks - 1) {
-        if (lane == 0) y[row] = f32_to_bf16(rowsum);
+        if (lane == 0) y[row] = F16 ? f32_to_f16(rowsum) : f32_to_bf16(rowsum);
         rowsum = 0.f;
       }
       if (++ch == chunks) {
@@ -649,12 +650,41 @@ __device__ __forceinline__ void m1_compute(const M1Group &g, int cols, int chunk
   }
 }
 
+// x and y BF16, or f16 with F16.  PRO = 1 (f16 only): the staged row is the
+// residual add + RMSNorm of GemvPrologue kind 1 (the decoder step's final
+// norm before the tied LM head).
+template <bool F16, int PRO>
 __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
     const uint8_t *__restrict__ w_, int rows, int cols, const uint16_t *__restrict__ x,
-    uint16_t *__restrict__ y_) {
+    uint16_t *__restrict__ y_, const GemvPrologue pro) {
   extern __shared__ __attribute__((aligned(16))) float xl[];  // chunks*1024, xswz layout
   const int chunks = (cols + 1023) >> 10;
-  for (int e = threadIdx.x; e < cols; e += kM1Threads) xl[xswz(e)] = bf16_to_f32(x[e]);
+  if constexpr (PRO == 1) {
+    __shared__ float red[kM1Waves];
+    float ss = 0.f;
+    for (int e = threadIdx.x; e < cols; e += kM1Threads) {
+      float a = f16_to_f32(x[e]);
+      if (pro.delta) {
+        a = round_f16(a + f16_to_f32(gp(pro.delta)[e]));
+        if (pro.x_out && blockIdx.x == 0) gp(pro.x_out)[e] = f32_to_f16(a);
+      }
+      xl[xswz(e)] = a;
+      ss = fmaf(a, a, ss);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kM1Waves; ++w) tot += red[w];
+    const float inv = 1.f / sqrtf(tot / (float)cols + pro.eps);
+    for (int e = threadIdx.x; e < cols; e += kM1Threads)
+      xl[xswz(e)] = round_f16(xl[xswz(e)] * inv * bf16_to_f32(gp(pro.w)[e]));
+    if (pro.advance && blockIdx.x == 0 && threadIdx.x == 0) gp(pro.advance)[0] += 1;
+  } else {
+    for (int e = threadIdx.x; e < cols; e += kM1Threads)
+      xl[xswz(e)] = F16 ? f16_to_f32(x[e]) : bf16_to_f32(x[e]);
+  }
   __syncthreads();
   const QD_GLOBAL uint8_t *w = gp(w_);
   QD_GLOBAL uint16_t *y = gp(y_);
@@ -670,10 +700,10 @@ __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
   m1_issue(A, w, rows, cols, chunks, lo, n, 0, lane);
   for (int i = 0; i < n; i += 2 * kG) {
     m1_issue(B, w, rows, cols, chunks, lo, n, i + kG < n ? i + kG : i, lane);
-    m1_compute(A, cols, chunks, lo, n, i, lane, xl, y, rowsum);
+    m1_compute<F16>(A, cols, chunks, lo, n, i, lane, xl, y, rowsum);
     if (i + kG >= n) break;
     m1_issue(A, w, rows, cols, chunks, lo, n, i + 2 * kG < n ? i + 2 * kG : i + kG, lane);
-    m1_compute(B, cols, chunks, lo, n, i + kG, lane, xl, y, rowsum);
+    m1_compute<F16>(B, cols, chunks, lo, n, i + kG, lane, xl, y, rowsum);
   }
 }
 
@@ -725,37 +755,48 @@ hipError_t launch_affine_embed_rows(const uint8_t *w, int rows, int cols, const 
   return hipGetLastError();
 }
 
+// Batch 1 takes the VALU streaming kernel only for a single very large
+// matrix (LM heads, >= 2^27 weights), where its 1 KiB-per-row loads keep the
+// most bytes in flight (151936 x 1024: 5.2-5.4 TB/s against ~4.0 for the
+// matrix-core kernel); below that the matrix-core kernel's K split gives
+// more waves.
+static bool use_m1(const AffineGroup &g, int cols, int m) {
+  return g.n == 1 && m == 1 && (int64_t)g.rows[0] * cols >= ((int64_t)1 << 27);
+}
+
+template <bool F16, int PRO>
+static hipError_t launch_m1(const AffineGroup &g, int cols, const uint16_t *x,
+                            const GemvPrologue &pro, hipStream_t stream) {
+  const uint8_t *w = g.w[0];
+  uint16_t *y = g.y[0];
+  const int rows = g.rows[0];
+  // waves: about two register groups of items each, at most 4 workgroups
+  // of 8 waves per CU
+  int cus = device_cus();
+  if (cus < 1) cus = 256;
+  const int64_t items = (int64_t)rows * ((cols + 1023) / 1024);
+  int64_t wgs = (items + 2 * kG * kM1Waves - 1) / (2 * kG * kM1Waves);
+  if (wgs > 4 * (int64_t)cus) wgs = 4 * (int64_t)cus;
+  if (wgs < 1) wgs = 1;
+  const size_t lds = (size_t)((cols + 1023) / 1024) * 1024 * 4;
+  hipLaunchKernelGGL((affine_gemv_m1_kernel<F16, PRO>), dim3((unsigned)wgs), dim3(kM1Threads),
+                     lds, stream, w, rows, cols, x, y, pro);
+  return hipGetLastError();
+}
+
 hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m, bool f16,
                               hipStream_t stream) {
   const GemvPrologue none = {};
+  if (use_m1(g, cols, m))
+    return f16 ? launch_m1<true, 0>(g, cols, x, none, stream)
+               : launch_m1<false, 0>(g, cols, x, none, stream);
   if (f16) return launch_mfma<ActF16>(g, cols, x, m, none, stream);
-  // Batch 1 takes the VALU streaming kernel only for a single very large
-  // matrix (LM heads, >= 2^27 weights), where its 1 KiB-per-row loads keep
-  // the most bytes in flight (151936 x 1024: 5.2-5.4 TB/s against ~4.0 for
-  // the matrix-core kernel); below that the matrix-core kernel's K split
-  // gives more waves.
-  if (g.n == 1 && m == 1 && (int64_t)g.rows[0] * cols >= ((int64_t)1 << 27)) {
-    const uint8_t *w = g.w[0];
-    uint16_t *y = g.y[0];
-    const int rows = g.rows[0];
-    // waves: about two register groups of items each, at most 4 workgroups
-    // of 8 waves per CU
-    int cus = device_cus();
-    if (cus < 1) cus = 256;
-    const int64_t items = (int64_t)rows * ((cols + 1023) / 1024);
-    int64_t wgs = (items + 2 * kG * kM1Waves - 1) / (2 * kG * kM1Waves);
-    if (wgs > 4 * (int64_t)cus) wgs = 4 * (int64_t)cus;
-    if (wgs < 1) wgs = 1;
-    const size_t lds = (size_t)((cols + 1023) / 1024) * 1024 * 4;
-    hipLaunchKernelGGL(affine_gemv_m1_kernel, dim3((unsigned)wgs), dim3(kM1Threads), lds,
-                       stream, w, rows, cols, x, y);
-    return hipGetLastError();
-  }
   return launch_mfma<ActBf16>(g, cols, x, m, none, stream);
 }
 
 hipError_t launch_affine_gemv_pro(AffineGroup g, int cols, const uint16_t *x,
                                   const GemvPrologue &pro, hipStream_t stream) {
+  if (pro.kind == 1 && use_m1(g, cols, 1)) return launch_m1<true, 1>(g, cols, x, pro, stream);
   if (pro.kind == 1) return launch_mfma<ActF16, 1>(g, cols, x, 1, pro, stream);
   if (pro.kind == 2) return launch_mfma<ActF16, 2>(g, cols, x, 1, pro, stream);
   return launch_mfma<ActF16>(g, cols, x, 1, pro, stream);
