@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kQW = 8;                 // waves per workgroup
 constexpr int kQThreads = kQW * kWave;
-constexpr int kQU = 2;                 // steps per register group
+constexpr int kQU = 1;                 // steps per register group (2 and 4 measured slower)
 constexpr int kQLdsBudget = 64 * 1024;
 
 template <int R>
