@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kQW = 8;                 // waves per workgroup
 constexpr int kQThreads = kQW * kWave;
+constexpr int kQMaxSplit = kQW < 8 ? kQW : 8;  // waves one row's steps are split over
 constexpr int kQU = 1;                 // steps per register group (2 and 4 measured slower)
 constexpr int kQLdsBudget = 64 * 1024;
 
@@ -188,6 +189,7 @@ __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][
 template <int MT, int R, int KS, bool EPI>
 __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
     const Q40Group grp, int cols, const float *__restrict__ x_, int t0, int m) {
+  static_assert(KS >= 1 && KS <= kQW, "a row's split needs one wave per part");
   constexpr int SLOTS = kQW / KS;
   __shared__ float red[KS > 1 ? kQW * MT * R * 8 : 1];
   extern __shared__ __attribute__((aligned(16))) float qsh[];
@@ -215,9 +217,10 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   ci.s = cc.s = S.sa;
   int li = n, lc = n;
   QGroup<R> A, B;
-  // x staging: thread i copies block i of x (8 x 16 bytes) and its sum;
-  // MT * bpr <= 512 by the LDS budget.  The first register group of weights
-  // is issued between the x loads and their use, so both are in flight.
+  // x staging: thread i copies block i of x (8 x 16 bytes) and its sum, and
+  // blocks i + kQThreads, ... after it when there are more blocks than
+  // threads.  The first register group of weights is issued between the
+  // first x loads and their use, so both are in flight.
   const int nblk = MT * bpr;
   const int bi = min((int)threadIdx.x, nblk - 1);
   const int bt = bi / bpr, bb = bi - bt * bpr;
@@ -237,6 +240,20 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
       *(floatx4 *)(xs + 32 * bi + 4 * k) = v;
     }
     xsum[bi] = sum;
+  }
+  for (int b = threadIdx.x + kQThreads; b < nblk; b += kQThreads) {
+    const int t = b / bpr, bk = b - t * bpr;
+    const bool live = t0 + t < m;
+    const QD_GLOBAL floatx4 *p =
+        (const QD_GLOBAL floatx4 *)(x + (size_t)min(t0 + t, m - 1) * cols + 32 * bk);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const floatx4 v = live ? p[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+      sum += (v[0] + v[1]) + (v[2] + v[3]);
+      *(floatx4 *)(xs + 32 * b + 4 * k) = v;
+    }
+    xsum[b] = sum;
   }
   // LDS writes done, then the barrier (the weight loads stay in flight)
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -311,7 +328,7 @@ hipError_t launch_q_ks(const Q40Group &g, int cols, const float *x, int t0, int 
   return hipGetLastError();
 }
 
-// KS: split a row's steps over up to 8 waves until the launch gives about
+// KS: split a row's steps over up to kQMaxSplit waves until the launch gives about
 // kQTargetWaves waves (each wave keeping at least one register group);
 // KS = 1 walks row groups grid-stride with kQStreamWgsPerCu workgroups per CU.
 constexpr int kQTargetWaves = 4096;
@@ -327,7 +344,7 @@ hipError_t launch_q_mt(Q40Group g, int cols, const float *x, int t0, int m,
   const int steps = cols / 256;
   const long ngroups = g.tile0[g.n];
   int ks = 1;
-  while (ks < 8 && ngroups * ks < kQTargetWaves && steps / (2 * ks) >= kQU) ks *= 2;
+  while (ks < kQMaxSplit && ngroups * ks < kQTargetWaves && steps / (2 * ks) >= kQU) ks *= 2;
   if (ks == 1) {
     int cus = device_cus();
     if (cus < 1) cus = 256;
@@ -336,21 +353,21 @@ hipError_t launch_q_mt(Q40Group g, int cols, const float *x, int t0, int m,
     return launch_q_ks<MT, R, 1, EPI>(g, cols, x, t0, m, (int)grid, stream);
   }
   const int grid = (int)((ngroups * ks + kQW - 1) / kQW);
-  switch (ks) {
-    case 2: return launch_q_ks<MT, R, 2, EPI>(g, cols, x, t0, m, grid, stream);
-    case 4: return launch_q_ks<MT, R, 4, EPI>(g, cols, x, t0, m, grid, stream);
-    default: return launch_q_ks<MT, R, 8, EPI>(g, cols, x, t0, m, grid, stream);
-  }
+  if constexpr (kQMaxSplit >= 2)
+    if (ks == 2) return launch_q_ks<MT, R, 2, EPI>(g, cols, x, t0, m, grid, stream);
+  if constexpr (kQMaxSplit >= 4)
+    if (ks == 4) return launch_q_ks<MT, R, 4, EPI>(g, cols, x, t0, m, grid, stream);
+  if constexpr (kQMaxSplit >= 8)
+    if (ks == 8) return launch_q_ks<MT, R, 8, EPI>(g, cols, x, t0, m, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
                             hipStream_t stream) {
-  // tokens per pass limited by the LDS copy of x (fp32 plus block sums) and
-  // by one x block per thread for the staging
-  int cap = kQLdsBudget / (cols * 4 + cols / 8);
-  if (cap * (cols / 32) > kQThreads) cap = kQThreads / (cols / 32);
+  // tokens per pass limited by the LDS copy of x (fp32 plus block sums)
+  const int cap = kQLdsBudget / (cols * 4 + cols / 8);
   // kernels specialised for a plain product (no bias, no GELU)
   bool epi = g.gelu != 0;
   for (int k = 0; k < g.n; ++k) epi = epi || g.bias[k] != nullptr;

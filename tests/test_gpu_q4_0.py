@@ -66,7 +66,7 @@ def test_quantize_special_values():
 
 @pytest.mark.parametrize("rows,cols,m", [
     (2048, 512, 1), (512, 2048, 1), (2048, 512, 4), (512, 2048, 4),
-    (1280, 1280, 1), (5120, 1280, 1), (1280, 5120, 1),
+    (1280, 1280, 1), (5120, 1280, 1), (1280, 5120, 1), (1280, 5120, 4),
     (1, 256, 1), (9, 256, 3), (100, 768, 16), (37, 2816, 5),
     # the widest input the GEMV takes (8192 columns)
     (97, 8192, 4), (33, 8192, 16),
