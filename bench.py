@@ -704,7 +704,7 @@ def row_qwen3_decoder_step(qd):
     logits = torch.empty(spec.vocab, dtype=torch.float16, device=DEV)
     g = capture(lambda: qd.qwen3_step_run(model, ws, wsb, x, pos, logits, advance=True))
     out = {"model": spec.name, "layers": spec.layers, "weight_bytes": wbytes,
-           "launches_per_token": spec.layers * 6 + 1}
+           "launches_per_token": spec.layers * (5 if spec.kv_heads <= 8 else 6) + 1}
     for ctx in ctxs:
         pos.fill_(ctx)
         torch.cuda.synchronize()

@@ -416,8 +416,9 @@ typedef struct {
 } qd_qwen3_model;
 
 /* Bytes of the step workspace for this model (0 if the model is not
- * supported): one error word, the f16 scratch rows and the attention
- * partials. */
+ * supported): one error word, the f16 scratch rows, the attention partials
+ * and, with at most 8 K/V heads, kv_heads fp32 rows of hidden entries (the
+ * o projection's partial sums, one row per K/V head). */
 size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model);
 
 /* Qwen3AsrMetalEngine::step for one row: x (device, f16 [hidden], 16-byte
@@ -426,7 +427,10 @@ size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model);
  * the K/V rows appended at cache row p, decode attention over rows [0, p],
  * the o GEMV, residual add, rmsnorm, the gate/up GEMVs (one launch),
  * silu*mul, the down GEMV, residual add -- leaving the new residual row in
- * x.  When logits (device, f16 [vocab], 2-byte aligned) is not NULL, the
+ * x.  With at most 8 K/V heads the o GEMV runs inside the attention's
+ * combine as one fp32 partial per K/V head over that head's input columns,
+ * summed in head order and rounded to f16 by the next launch; the o output
+ * is then that sum instead of one fp32 sum over all columns.  When logits (device, f16 [vocab], 2-byte aligned) is not NULL, the
  * final norm and the tied LM-head GEMV write the next-token logits.  With
  * advance = 1, *position is incremented at the end of the step.  The
  * kernels read p from device memory, allocate nothing and launch no memset,

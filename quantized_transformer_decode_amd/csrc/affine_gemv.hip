@@ -47,6 +47,7 @@ namespace {
 
 constexpr int kMW = 8;
 constexpr int kMThreads = kMW * kWave;
+constexpr int kMaxDparts = 8;  // partial rows a step prologue sums (one per K/V head)
 
 // Activation type of the matrix-core kernel: x and y BF16 (the configs) or
 // f16 (the page's Metal GEMV); scales and biases are BF16 in both.
@@ -326,20 +327,47 @@ __device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_
       const int i = min(t + k * kMThreads, chunks - 1);
       wv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
     }
+    u32x4 xv[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      xv[k] = *(const QD_GLOBAL u32x4 *)(x + 8 * min(t + k * kMThreads, chunks - 1));
+    if (pro.dparts) {
+      // delta = f16(dparts[0] + dparts[1] + ...), in that order, staged in
+      // LDS as f16 (the norm's row overwrites it after the next barrier)
+      const QD_GLOBAL float *dp = gp(pro.dparts);
+      for (int c4 = t; c4 < cols / 4; c4 += kMThreads) {
+        floatx4 v[kMaxDparts];
+#pragma unroll
+        for (int j = 0; j < kMaxDparts; ++j)
+          v[j] = *(const QD_GLOBAL floatx4 *)(dp + (size_t)min(j, pro.nparts - 1) * cols + 4 * c4);
+        floatx4 sum = v[0];
+#pragma unroll
+        for (int j = 1; j < kMaxDparts; ++j)
+          if (j < pro.nparts) sum += v[j];
+        u32x2 h;
+        h.x = (uint32_t)f32_to_f16(sum[0]) | ((uint32_t)f32_to_f16(sum[1]) << 16);
+        h.y = (uint32_t)f32_to_f16(sum[2]) | ((uint32_t)f32_to_f16(sum[3]) << 16);
+        *(u32x2 *)(xl + 8 * c4) = h;
+      }
+      __syncthreads();
+    }
+    const bool has_delta = pro.delta || pro.dparts;
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int i = t + k * kMThreads;
       if (i < chunks) {
-        const u32x4 xv = *(const QD_GLOBAL u32x4 *)(x + 8 * i);
         u32x4 dv = {0u, 0u, 0u, 0u};
-        if (pro.delta) dv = *(const QD_GLOBAL u32x4 *)(gp(pro.delta) + 8 * i);
+        if (pro.dparts)
+          dv = *(const u32x4 *)(xl + 16 * i);
+        else if (pro.delta)
+          dv = *(const QD_GLOBAL u32x4 *)(gp(pro.delta) + 8 * i);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          a[k][e] = pro.delta ? round_f16(half_of(xv, e) + half_of(dv, e)) : half_of(xv, e);
+          a[k][e] = has_delta ? round_f16(half_of(xv[k], e) + half_of(dv, e)) : half_of(xv[k], e);
           ss = fmaf(a[k][e], a[k][e], ss);
         }
-        if (pro.delta && pro.x_out && blockIdx.x == 0)
+        if (has_delta && pro.x_out && blockIdx.x == 0)
           *(QD_GLOBAL u32x4 *)(gp(pro.x_out) + 8 * i) = pack_halves(a[k]);
       }
     }
@@ -796,7 +824,10 @@ hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
 
 hipError_t launch_affine_gemv_pro(AffineGroup g, int cols, const uint16_t *x,
                                   const GemvPrologue &pro, hipStream_t stream) {
-  if (pro.kind == 1 && use_m1(g, cols, 1)) return launch_m1<true, 1>(g, cols, x, pro, stream);
+  if (pro.kind == 1 && pro.dparts && (pro.nparts < 1 || pro.nparts > kMaxDparts))
+    return hipErrorInvalidValue;
+  if (pro.kind == 1 && !pro.dparts && use_m1(g, cols, 1))
+    return launch_m1<true, 1>(g, cols, x, pro, stream);
   if (pro.kind == 1) return launch_mfma<ActF16, 1>(g, cols, x, 1, pro, stream);
   if (pro.kind == 2) return launch_mfma<ActF16, 2>(g, cols, x, 1, pro, stream);
   return launch_mfma<ActF16>(g, cols, x, 1, pro, stream);

@@ -425,6 +425,125 @@ __global__ __launch_bounds__(kAttThreads) void attention_combine_kernel(
                             gp(out) + (size_t)h * D);
 }
 
+// Combine, then the o projection (decoder step).  Workgroup (s, j) merges
+// the chunks of the G query heads of K/V head j exactly as
+// attention_combine_kernel does (the same fp32 order, the row rounded to f16
+// as the page stores it), then multiplies that row -- columns
+// [j * G * D, (j + 1) * G * D) of the o projection's input -- by the same
+// columns of rows [s * kCoRows, ...) of the affine-INT8 o weights:
+//   opart[j][n] = sum_g (scale[n][g] * sum_k q[n][k] a[k] + bias[n][g] * sum_k a[k]).
+// The o output of the page is f16(sum_j opart[j][n]), summed in j order by
+// the next kernel's prologue; nothing is accumulated across workgroups.  The
+// weight loads are issued first, so they are in flight during the combine.
+constexpr int kCoThreads = 512;
+constexpr int kCoPasses = 2;  // weight rows per lane
+
+template <int D, int G>
+__global__ __launch_bounds__(kCoThreads) void attention_combine_o_kernel(
+    const float *__restrict__ part, int stride, const int *__restrict__ pos_dev, int capacity,
+    int rows_per_wave, const uint8_t *__restrict__ wo, int rows, int cols,
+    float *__restrict__ opart) {
+  constexpr int E = G * D;                           // elements of the K/V head's row slice
+  constexpr int EW = E < kCoThreads ? E : kCoThreads;
+  constexpr int SL = kCoThreads / EW;                // chunk slices side by side
+  constexpr int EPT = E / EW;                        // elements per thread
+  constexpr int LPR = E / 16;                        // lanes per weight row (16 codes each)
+  constexpr int RPP = kCoThreads / LPR;              // rows per pass
+  __shared__ float sm[SL][EW], sl[SL][EW], so[SL][EW];
+  __shared__ __attribute__((aligned(16))) float av[E];
+  const int t = threadIdx.x, j = blockIdx.y;
+  const int u = t % LPR;
+  const int groups = cols / 64;
+  const QD_GLOBAL uint8_t *w = gp(wo);
+  const QD_GLOBAL uint16_t *sc = (const QD_GLOBAL uint16_t *)(w + (size_t)rows * cols);
+  const size_t boff = (size_t)rows * groups;
+  const int c0 = j * E + 16 * u;                     // first column of this lane
+  const int gi = c0 / 64;
+  u32x4 q[kCoPasses];
+  float scale[kCoPasses], bias[kCoPasses];
+#pragma unroll
+  for (int p = 0; p < kCoPasses; ++p) {
+    const int n = min(blockIdx.x * (kCoPasses * RPP) + p * RPP + t / LPR, rows - 1);
+    q[p] = *(const QD_GLOBAL u32x4 *)(w + (size_t)n * cols + c0);
+    scale[p] = bf16_to_f32(sc[(size_t)n * groups + gi]);
+    bias[p] = bf16_to_f32(sc[boff + (size_t)n * groups + gi]);
+  }
+  const int pos = gp(pos_dev)[0];
+  if (pos < 0 || pos >= capacity) return;  // the first kernel has set the error word
+  const int nchunks = (pos + kAttWaves * rows_per_wave) / (kAttWaves * rows_per_wave);
+  const int slice = t / EW, e0 = t % EW;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = e0 + k * EW;
+    const int h = e / D, i = e % D;
+    const QD_GLOBAL float *ph = gp(part) + (size_t)(j * G + h) * stride * (D + 2);
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int cb = slice; cb < nchunks; cb += kCombBatch * SL) {
+      float mc[kCombBatch], lc[kCombBatch], oc[kCombBatch];
+#pragma unroll
+      for (int v = 0; v < kCombBatch; ++v) {
+        const int c = min(cb + v * SL, nchunks - 1);
+        const QD_GLOBAL float *pc = ph + (size_t)c * (D + 2);
+        mc[v] = pc[0];
+        lc[v] = pc[1];
+        oc[v] = pc[2 + i];
+      }
+      float mb = m;
+#pragma unroll
+      for (int v = 0; v < kCombBatch; ++v)
+        if (cb + v * SL < nchunks) mb = fmaxf(mb, mc[v]);
+      const float a = m == -INFINITY ? 0.f : __expf(m - mb);
+      l *= a;
+      o *= a;
+#pragma unroll
+      for (int v = 0; v < kCombBatch; ++v) {
+        const float wgt = (cb + v * SL < nchunks && mc[v] != -INFINITY) ? __expf(mc[v] - mb) : 0.f;
+        l = fmaf(lc[v], wgt, l);
+        o = fmaf(oc[v], wgt, o);
+      }
+      m = mb;
+    }
+    if constexpr (SL > 1) {
+      sm[slice][e0] = m;
+      sl[slice][e0] = l;
+      so[slice][e0] = o;
+      __syncthreads();
+      if (slice == 0) {
+        for (int r = 1; r < SL; ++r) {
+          const float m2 = sm[r][e0], l2 = sl[r][e0], o2 = so[r][e0];
+          const float mm = fmaxf(m, m2);
+          const float a = m == -INFINITY ? 0.f : __expf(m - mm);
+          const float b = m2 == -INFINITY ? 0.f : __expf(m2 - mm);
+          l = l * a + l2 * b;
+          o = o * a + o2 * b;
+          m = mm;
+        }
+        av[e] = f16_to_f32(f32_to_f16(o / l));
+      }
+    } else {
+      av[e] = f16_to_f32(f32_to_f16(o / l));
+    }
+  }
+  __syncthreads();
+  const float4 *ap = (const float4 *)(av + 16 * u);
+  const float4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
+  const float s16 = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w)) +
+                    ((a2.x + a2.y) + (a2.z + a2.w)) + ((a3.x + a3.y) + (a3.z + a3.w));
+#pragma unroll
+  for (int p = 0; p < kCoPasses; ++p) {
+    const uint4 qq = {q[p].x, q[p].y, q[p].z, q[p].w};
+    float v = fmaf(scale[p], dot16(qq, a0, a1, a2, a3), bias[p] * s16);
+    v = group_sum<LPR>(v);
+    const int n = blockIdx.x * (kCoPasses * RPP) + p * RPP + t / LPR;
+    if (u == 0 && n < rows) gp(opart)[(size_t)j * rows + n] = v;
+  }
+}
+
+template <int D, int G>
+int combine_o_rows_per_wg() {
+  return kCoPasses * (kCoThreads / (G * D / 16));
+}
+
 template <int D, int G, bool F16>
 hipError_t launch_att(const AttentionArgs &a, hipStream_t stream) {
   // with a device position the chunk grid covers the whole cache
@@ -455,6 +574,18 @@ hipError_t launch_att(const AttentionArgs &a, hipStream_t stream) {
                        a.capacity, a.part, a.out, none);
   else if (!F16)
     return hipErrorInvalidValue;
+  if (a.wo) {
+    if constexpr (F16) {
+      if (!a.pos_dev || a.wo_cols != a.heads * D || a.wo_rows < 1) return hipErrorInvalidValue;
+      const int rpw = combine_o_rows_per_wg<D, G>();
+      hipLaunchKernelGGL((attention_combine_o_kernel<D, G>),
+                         dim3((a.wo_rows + rpw - 1) / rpw, a.kv_heads), dim3(kCoThreads), 0,
+                         stream, a.part, p.nchunks, a.pos_dev, a.capacity, p.rows_per_wave,
+                         a.wo, a.wo_rows, a.wo_cols, a.opart);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL((attention_combine_kernel<D, F16>), dim3(a.kv_heads * G),
                      dim3(kAttThreads), 0, stream, a.part, p.nchunks, p.nchunks, a.pos_dev,
                      a.capacity, p.rows_per_wave, a.out);

@@ -651,7 +651,7 @@ qd_status attention_decode(const void *q, const void *k_cache, const void *v_cac
   if (overlap(out, qb, workspace, (size_t)need)) return QD_EINVAL;
   qd_status st = check_device();
   if (st != QD_OK) return st;
-  qd::AttentionArgs a;
+  qd::AttentionArgs a = {};
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k_cache;
   a.v = (const uint16_t *)v_cache;
@@ -741,8 +741,13 @@ namespace {
 
 // Byte offsets of the step workspace's parts (each 256-byte aligned).
 struct StepLayout {
-  size_t err, xalt, q, kbuf, vbuf, attn, delta, gate, up, part, total;
+  size_t err, xalt, q, kbuf, vbuf, attn, delta, gate, up, part, opart, total;
 };
+
+// The o projection runs inside the attention's combine when the gate/up
+// prologue can sum its per-K/V-head partial rows.
+constexpr int64_t kStepMaxOParts = 8;
+bool step_fused_o(const qd_qwen3_model &m) { return m.kv_heads <= kStepMaxOParts; }
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
@@ -774,6 +779,7 @@ StepLayout qwen3_layout(const qd_qwen3_model &m) {
   L.gate = take(m.inter * 2);
   L.up = take(m.inter * 2);
   L.part = take((size_t)attention_decode_workspace_bytes(m.heads, m.kv_heads, m.head_dim));
+  L.opart = take(step_fused_o(m) ? (size_t)m.kv_heads * m.hidden * 4 : 0);
   L.total = o;
   return L;
 }
@@ -842,6 +848,7 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
   uint16_t *kbuf = (uint16_t *)(ws + L.kbuf), *vbuf = (uint16_t *)(ws + L.vbuf);
   uint16_t *attn = (uint16_t *)(ws + L.attn), *delta = (uint16_t *)(ws + L.delta);
   uint16_t *gate = (uint16_t *)(ws + L.gate), *up = (uint16_t *)(ws + L.up);
+  float *opart = (float *)(ws + L.opart);
   // The residual row alternates between the caller's x and a scratch row:
   // a fused residual add reads one and writes the other, so no workgroup
   // reads a row that another is rewriting.  A step has 2 * n_layers adds,
@@ -893,7 +900,7 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     qr.eps = m.eps;
     qr.theta = m.theta;
     qr.err = err;
-    qd::AttentionArgs a;
+    qd::AttentionArgs a = {};
     a.q = q;
     a.k = (const uint16_t *)ly.k_cache;
     a.v = (const uint16_t *)ly.v_cache;
@@ -909,17 +916,33 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     a.pos_dev = pos;
     a.capacity = (int)m.capacity;
     a.qkr = &qr;
+    const bool fused_o = step_fused_o(m);
+    if (fused_o) {
+      // the o projection inside the combine: one fp32 partial row per K/V head
+      a.wo = (const uint8_t *)ly.o;
+      a.wo_rows = hid;
+      a.wo_cols = qw;
+      a.opart = opart;
+    }
     QD_TRY(qd::launch_attention_decode(a, s));
-    qd::AffineGroup go = {};
-    go.n = 1;
-    go.w[0] = (const uint8_t *)ly.o;
-    go.y[0] = delta;
-    go.rows[0] = hid;
-    QD_TRY(qd::launch_affine_gemv(go, qw, attn, 1, true, s));
-    // residual add + post-attention RMSNorm, fused into the gate/up GEMVs
+    if (!fused_o) {
+      qd::AffineGroup go = {};
+      go.n = 1;
+      go.w[0] = (const uint8_t *)ly.o;
+      go.y[0] = delta;
+      go.rows[0] = hid;
+      QD_TRY(qd::launch_affine_gemv(go, qw, attn, 1, true, s));
+    }
+    // residual add (o = f16 of the partials' sum) + post-attention RMSNorm,
+    // fused into the gate/up GEMVs
     qd::GemvPrologue pp = {};
     pp.kind = 1;
-    pp.delta = delta;
+    if (fused_o) {
+      pp.dparts = opart;
+      pp.nparts = KV;
+    } else {
+      pp.delta = delta;
+    }
     pp.w = (const uint16_t *)ly.post_norm;
     pp.x_out = res[cur ^ 1];
     pp.eps = m.eps;

@@ -48,6 +48,9 @@ hipError_t launch_affine_gemv(AffineGroup g, int cols, const uint16_t *x, int m,
 struct GemvPrologue {
   int kind;
   const uint16_t *delta, *w, *up;
+  // kind 1 alternative to delta: f16(sum over nparts fp32 rows dparts[j][cols])
+  const float *dparts;
+  int nparts;
   uint16_t *x_out;
   int *advance;
   float eps;
@@ -99,6 +102,13 @@ struct AttentionArgs {
   const int *pos_dev;
   int capacity;
   const AttentionQkRope *qkr;
+  // Optional (f16, device position): the combine also applies the o
+  // projection (affine-INT8 g64, wo_rows x wo_cols, wo_cols = heads *
+  // head_dim) and writes opart[kv_heads][wo_rows] (fp32 partial rows, one
+  // per K/V head) instead of out.
+  const uint8_t *wo;
+  int wo_rows, wo_cols;
+  float *opart;
 };
 // Rows per wave and chunks of the window [kv_start, length) (host only).
 struct AttentionPlan {

@@ -344,9 +344,10 @@ def test_qwen3_step_workspace_and_errors():
     wb = qd.qwen3_step_workspace_bytes
     m = _qwen3()
     n = wb(m)
-    # error word, normed, q, k, v, attn, delta, gate, up (each 256-padded), partials
+    # error word, normed, q, k, v, attn, delta, gate, up (each 256-padded),
+    # attention partials, fp32 o-projection partial rows (one per K/V head)
     rows = 256 + 2048 + 4096 + 2048 + 2048 + 4096 + 2048 + 6144 + 6144
-    assert n == rows + qd.attention_decode_workspace_bytes(16, 8, 128)
+    assert n == rows + qd.attention_decode_workspace_bytes(16, 8, 128) + 8 * 1024 * 4
     for bad in (dict(hidden=1000), dict(head_dim=96), dict(heads=24), dict(inter=16384),
                 dict(capacity=0), dict(vocab=0), dict(n_layers=0)):
         assert wb(_qwen3(**bad)) == 0, bad

@@ -384,10 +384,11 @@ def test_step_without_logits_odd_layers_advancing():
 
 
 @pytest.mark.parametrize("heads,kv_heads,head_dim", [(4, 4, 64), (8, 2, 64), (16, 2, 128),
-                                                     (8, 1, 128)])
+                                                     (8, 1, 128), (16, 16, 64)])
 def test_step_head_groupings(heads, kv_heads, head_dim):
     # 1, 4 and 8 query heads per K/V head (the fused attention prologue's
-    # other instances), one layer, positions 0..69: with a 4096-row cache the
+    # other instances; 16 K/V heads take the o projection as its own GEMV
+    # after the combine), one layer, positions 0..69: with a 4096-row cache the
     # attention chunks hold 32 (d 128) or 64 (d 64) rows, so the window
     # crosses chunk boundaries and the appended row moves between chunks
     spec = synth.Qwen3Spec(f"qwen3-g{heads // kv_heads}-d{head_dim}", 256, heads, kv_heads,
