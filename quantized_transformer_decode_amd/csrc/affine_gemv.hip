@@ -311,35 +311,64 @@ __device__ __forceinline__ u32x4 pack_halves(const float (&v)[8]) {
 // The transformed input row (m = 1, f16) into LDS, in stage_x's layout
 // (GemvPrologue): kind 1 the residual add and RMSNorm, kind 2 SiLU-mul.
 // cols <= 8192: at most two 8-value chunks per thread.
+// The prologue's global inputs, loaded before the first buffer of weights
+// is issued: the memory wait for them then leaves the weight loads in
+// flight, and the prologue's arithmetic and barriers overlap the weight
+// stream.  PRO 1: x, delta (or the first four columns of each partial row)
+// and the norm weights; PRO 2: gate (in xv) and up (in dv).
+constexpr int kProCpt = 2;  // 8-element chunks per thread (cols <= 8192)
+struct ProIn {
+  u32x4 xv[kProCpt], dv[kProCpt], wv[kProCpt];
+  floatx4 pv[kMaxDparts];
+};
+
 template <int PRO>
-__device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_t *x, int cols,
-                                            const GemvPrologue &pro) {
-  constexpr int CPT = 2;
+__device__ __forceinline__ void pro_load(ProIn &in, const QD_GLOBAL uint16_t *x, int cols,
+                                         const GemvPrologue &pro) {
+  const int chunks = cols >> 3;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < kProCpt; ++k) {
+    const int i = min(t + k * kMThreads, chunks - 1);
+    in.xv[k] = *(const QD_GLOBAL u32x4 *)(x + 8 * i);
+    if constexpr (PRO == 1) {
+      in.wv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
+      if (pro.delta) in.dv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.delta) + 8 * i);
+    } else {
+      in.dv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.up) + 8 * i);
+    }
+  }
+  if constexpr (PRO == 1) {
+    if (pro.dparts) {
+      const int c4 = min(t, cols / 4 - 1);
+#pragma unroll
+      for (int j = 0; j < kMaxDparts; ++j)
+        in.pv[j] = *(const QD_GLOBAL floatx4 *)(gp(pro.dparts) +
+                                                 (size_t)min(j, pro.nparts - 1) * cols + 4 * c4);
+    }
+  }
+}
+
+template <int PRO>
+__device__ __forceinline__ void stage_x_pro(uint8_t *xl, int cols, const GemvPrologue &pro,
+                                            const ProIn &in) {
+  constexpr int CPT = kProCpt;
   const int chunks = cols >> 3;
   const int t = threadIdx.x;
   float a[CPT][8];
   if constexpr (PRO == 1) {
     __shared__ float red[kMW];
-    // the norm weights are loaded with x and delta (one memory round trip)
-    u32x4 wv[CPT];
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int i = min(t + k * kMThreads, chunks - 1);
-      wv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
-    }
-    u32x4 xv[CPT];
-#pragma unroll
-    for (int k = 0; k < CPT; ++k)
-      xv[k] = *(const QD_GLOBAL u32x4 *)(x + 8 * min(t + k * kMThreads, chunks - 1));
     if (pro.dparts) {
       // delta = f16(dparts[0] + dparts[1] + ...), in that order, staged in
       // LDS as f16 (the norm's row overwrites it after the next barrier)
-      const QD_GLOBAL float *dp = gp(pro.dparts);
       for (int c4 = t; c4 < cols / 4; c4 += kMThreads) {
         floatx4 v[kMaxDparts];
 #pragma unroll
         for (int j = 0; j < kMaxDparts; ++j)
-          v[j] = *(const QD_GLOBAL floatx4 *)(dp + (size_t)min(j, pro.nparts - 1) * cols + 4 * c4);
+          v[j] = c4 == t ? in.pv[j]
+                         : *(const QD_GLOBAL floatx4 *)(gp(pro.dparts) +
+                                                        (size_t)min(j, pro.nparts - 1) * cols +
+                                                        4 * c4);
         floatx4 sum = v[0];
 #pragma unroll
         for (int j = 1; j < kMaxDparts; ++j)
@@ -361,10 +390,11 @@ __device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_
         if (pro.dparts)
           dv = *(const u32x4 *)(xl + 16 * i);
         else if (pro.delta)
-          dv = *(const QD_GLOBAL u32x4 *)(gp(pro.delta) + 8 * i);
+          dv = in.dv[k];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          a[k][e] = has_delta ? round_f16(half_of(xv[k], e) + half_of(dv, e)) : half_of(xv[k], e);
+          a[k][e] = has_delta ? round_f16(half_of(in.xv[k], e) + half_of(dv, e))
+                              : half_of(in.xv[k], e);
           ss = fmaf(a[k][e], a[k][e], ss);
         }
         if (has_delta && pro.x_out && blockIdx.x == 0)
@@ -382,7 +412,7 @@ __device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_
     for (int k = 0; k < CPT; ++k) {
       const int i = t + k * kMThreads;
       if (i < chunks) {
-        const uint32_t we[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
+        const uint32_t we[4] = {in.wv[k].x, in.wv[k].y, in.wv[k].z, in.wv[k].w};
         float n[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -396,12 +426,10 @@ __device__ __forceinline__ void stage_x_pro(uint8_t *xl, const QD_GLOBAL uint16_
     for (int k = 0; k < CPT; ++k) {
       const int i = t + k * kMThreads;
       if (i < chunks) {
-        const u32x4 gv = *(const QD_GLOBAL u32x4 *)(x + 8 * i);
-        const u32x4 uv = *(const QD_GLOBAL u32x4 *)(gp(pro.up) + 8 * i);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float g = half_of(gv, e);
-          a[k][e] = g / (1.f + expf(-g)) * half_of(uv, e);
+          const float g = half_of(in.xv[k], e);
+          a[k][e] = g / (1.f + expf(-g)) * half_of(in.dv[k], e);
         }
         *(u32x4 *)(xl + 16 * i) = pack_halves(a[k]);
       }
@@ -453,13 +481,26 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   MGroup<R, U, CH, Act> A, B;
   const MCursor c0 = ci;
   const int l0 = li;
-  // the first buffer's codes and scales are in flight while x is staged
-  if (n > 0) mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+  // the first buffer's codes and scales are in flight while x is staged;
+  // a prologue's inputs are loaded first, so that waiting for them does not
+  // wait for the weights
+  ProIn pin;
+  if constexpr (XL && PRO != 0) {
+    pro_load<PRO>(pin, x, cols, pro);
+    // the prologue in both branches: after a join of paths with different
+    // numbers of loads in flight, the memory waits would be counted for
+    // the path with fewer (and wait for the weights here too)
+    if (n > 0) {
+      mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      stage_x_pro<PRO>(xl, cols, pro, pin);
+    } else {
+      stage_x_pro<PRO>(xl, cols, pro, pin);
+    }
+  } else if (n > 0) {
+    mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+  }
   if constexpr (XL) {
-    if constexpr (PRO == 0)
-      stage_x(xl, x, m, cols);
-    else
-      stage_x_pro<PRO>(xl, x, cols, pro);
+    if constexpr (PRO == 0) stage_x(xl, x, m, cols);
     // LDS writes done, then the barrier (global loads stay in flight)
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // the first buffer read the untransformed x from memory

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
   const size_t row = (size_t)kv_heads * D;  // elements per cache row
 
   // The rows of this wave: loads of the next rows are issued before the
-  // current ones are computed (the first ones before q is prepared).
+  // current ones are computed (the first ones before q is prepared, after
+  // the loads of the q/k prologue).
   const int t0 = kv_start + (c * kAttWaves + wave) * rows_per_wave;
   const int t1 = min(t0 + rows_per_wave, length);
   u32x4 kw[kAttUnroll], vw[kAttUnroll];
@@ -225,8 +226,6 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
       vw[u] = *(const QD_GLOBAL u32x4 *)(vc + off);
     }
   };
-  if (t0 < t1) issue(t0);
-
   // this lane's 8 dimensions of each query head, fp32, pre-scaled
   float qf[G][8];
   // QKR: the new K/V row of head j, for the chunk that holds it
@@ -234,6 +233,8 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
   const int pos = length - 1;
   const bool mine = QKR && (pos - kv_start) / (kAttWaves * rows_per_wave) == c;
   if constexpr (QKR) {
+    // The prologue's loads go first: waiting for them then leaves the cache
+    // rows in flight, and the angles, norms and barriers below overlap them.
     __shared__ float cs[2][D / 2];
     u32x4 qraw[G], kraw, vraw;
     const u32x4 wq = *(const QD_GLOBAL u32x4 *)(gp(qkr.q_w) + 8 * sub);
@@ -247,41 +248,55 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
       vraw = *(const QD_GLOBAL u32x4 *)(gp(qkr.v_src) + (size_t)j * D + 8 * sub);
       wk = *(const QD_GLOBAL u32x4 *)(gp(qkr.k_w) + 8 * sub);
     }
-    if (threadIdx.x < D / 2) {
-      // angle pos * theta^(-2i/d) and its reduction to [-pi, pi] in fp64
-      // (a position of tens of thousands times the frequency needs it), the
-      // sine and cosine of the reduced angle in fp32
-      constexpr double kTwoPi = 6.283185307179586;
-      const double ang = (double)pos * exp2(-2.0 * threadIdx.x / (double)D * log2((double)qkr.theta));
-      const float r = (float)(ang - kTwoPi * rint(ang / kTwoPi));
-      float sn, cn;
-      sincosf(r, &sn, &cn);
-      cs[0][threadIdx.x] = cn;
-      cs[1][threadIdx.x] = sn;
-    }
-    __syncthreads();
+    auto prologue = [&]() {
+      if (threadIdx.x < D / 2) {
+        // angle pos * theta^(-2i/d) and its reduction to [-pi, pi] in fp64
+        // (a position of tens of thousands times the frequency needs it),
+        // the sine and cosine of the reduced angle in fp32
+        constexpr double kTwoPi = 6.283185307179586;
+        const double ang =
+            (double)pos * exp2(-2.0 * threadIdx.x / (double)D * log2((double)qkr.theta));
+        const float r = (float)(ang - kTwoPi * rint(ang / kTwoPi));
+        float sn, cn;
+        sincosf(r, &sn, &cn);
+        cs[0][threadIdx.x] = cn;
+        cs[1][threadIdx.x] = sn;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      unpack8<true>(qraw[h], qf[h]);
-      norm_rope8<D>(qf[h], wq, sub, qkr.eps, cs);
-    }
-    if (kwave) {
-      float kx[8];
-      unpack8<true>(kraw, kx);
-      norm_rope8<D>(kx, wk, sub, qkr.eps, cs);
-      const u32x4 kp = pack8_f16(kx);
-      const size_t off = (size_t)pos * kv_heads * D + (size_t)j * D + 8 * sub;
-      *(QD_GLOBAL u32x4 *)(gp((uint16_t *)k_) + off) = kp;
-      *(QD_GLOBAL u32x4 *)(gp((uint16_t *)v_) + off) = vraw;
-      *(u32x4 *)(knew + 8 * sub) = kp;
-      *(u32x4 *)(vnew + 8 * sub) = vraw;
-    }
-    __syncthreads();
+      for (int h = 0; h < G; ++h) {
+        unpack8<true>(qraw[h], qf[h]);
+        norm_rope8<D>(qf[h], wq, sub, qkr.eps, cs);
+      }
+      if (kwave) {
+        float kx[8];
+        unpack8<true>(kraw, kx);
+        norm_rope8<D>(kx, wk, sub, qkr.eps, cs);
+        const u32x4 kp = pack8_f16(kx);
+        const size_t off = (size_t)pos * kv_heads * D + (size_t)j * D + 8 * sub;
+        *(QD_GLOBAL u32x4 *)(gp((uint16_t *)k_) + off) = kp;
+        *(QD_GLOBAL u32x4 *)(gp((uint16_t *)v_) + off) = vraw;
+        *(u32x4 *)(knew + 8 * sub) = kp;
+        *(u32x4 *)(vnew + 8 * sub) = vraw;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[h][i] *= scale;
+        for (int i = 0; i < 8; ++i) qf[h][i] *= scale;
+    };
+    // in both branches: after a join of paths with different numbers of
+    // loads in flight the memory waits would be counted for the path with
+    // fewer, and the prologue would wait for the cache rows too (a wave's
+    // barrier instructions count the same on either path)
+    if (t0 < t1) {
+      issue(t0);
+      prologue();
+    } else {
+      prologue();
+    }
   } else {
+    if (t0 < t1) issue(t0);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       unpack8<F16>(*(const QD_GLOBAL u32x4 *)(q + (size_t)(j * G + h) * D + 8 * sub), qf[h]);
