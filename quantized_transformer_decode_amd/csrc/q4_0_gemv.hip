@@ -229,31 +229,41 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   floatx4 xv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) xv[k] = xp[k];
-  if (n > 0) qg_issue<R>(A, ci, S, grp, lane, li);
-  if ((int)threadIdx.x < nblk) {
-    const bool live = t0 + bt < m;
-    float sum = 0.f;
+  auto stage = [&]() {
+    if ((int)threadIdx.x < nblk) {
+      const bool live = t0 + bt < m;
+      float sum = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const floatx4 v = live ? xv[k] : floatx4{0.f, 0.f, 0.f, 0.f};
-      sum += (v[0] + v[1]) + (v[2] + v[3]);
-      *(floatx4 *)(xs + 32 * bi + 4 * k) = v;
+      for (int k = 0; k < 8; ++k) {
+        const floatx4 v = live ? xv[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+        sum += (v[0] + v[1]) + (v[2] + v[3]);
+        *(floatx4 *)(xs + 32 * bi + 4 * k) = v;
+      }
+      xsum[bi] = sum;
     }
-    xsum[bi] = sum;
-  }
-  for (int b = threadIdx.x + kQThreads; b < nblk; b += kQThreads) {
-    const int t = b / bpr, bk = b - t * bpr;
-    const bool live = t0 + t < m;
-    const QD_GLOBAL floatx4 *p =
-        (const QD_GLOBAL floatx4 *)(x + (size_t)min(t0 + t, m - 1) * cols + 32 * bk);
-    float sum = 0.f;
+    for (int b = threadIdx.x + kQThreads; b < nblk; b += kQThreads) {
+      const int t = b / bpr, bk = b - t * bpr;
+      const bool live = t0 + t < m;
+      const QD_GLOBAL floatx4 *p =
+          (const QD_GLOBAL floatx4 *)(x + (size_t)min(t0 + t, m - 1) * cols + 32 * bk);
+      float sum = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const floatx4 v = live ? p[k] : floatx4{0.f, 0.f, 0.f, 0.f};
-      sum += (v[0] + v[1]) + (v[2] + v[3]);
-      *(floatx4 *)(xs + 32 * b + 4 * k) = v;
+      for (int k = 0; k < 8; ++k) {
+        const floatx4 v = live ? p[k] : floatx4{0.f, 0.f, 0.f, 0.f};
+        sum += (v[0] + v[1]) + (v[2] + v[3]);
+        *(floatx4 *)(xs + 32 * b + 4 * k) = v;
+      }
+      xsum[b] = sum;
     }
-    xsum[b] = sum;
+  };
+  // the staging in both branches: after a join of paths with different
+  // numbers of loads in flight the memory waits would be counted for the
+  // path with fewer, and the x stores would wait for the weights too
+  if (n > 0) {
+    qg_issue<R>(A, ci, S, grp, lane, li);
+    stage();
+  } else {
+    stage();
   }
   // LDS writes done, then the barrier (the weight loads stay in flight)
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
