@@ -252,10 +252,17 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
       if (threadIdx.x < D / 2) {
         // angle pos * theta^(-2i/d) and its reduction to [-pi, pi] in fp64
         // (a position of tens of thousands times the frequency needs it),
-        // the sine and cosine of the reduced angle in fp32
+        // the sine and cosine of the reduced angle in fp32; theta^(-2i/d) is
+        // (theta^(-2/d))^i by binary powering (i < 64: at most six squarings,
+        // a relative error of about 1e-15)
         constexpr double kTwoPi = 6.283185307179586;
-        const double ang =
-            (double)pos * exp2(-2.0 * threadIdx.x / (double)D * log2((double)qkr.theta));
+        double f = 1.0, b = qkr.freq_ratio;
+#pragma unroll
+        for (int e = 0; e < 6; ++e) {
+          if ((threadIdx.x >> e) & 1) f *= b;
+          b *= b;
+        }
+        const double ang = (double)pos * f;
         const float r = (float)(ang - kTwoPi * rint(ang / kTwoPi));
         float sn, cn;
         sincosf(r, &sn, &cn);

@@ -899,6 +899,7 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     qr.k_w = (const uint16_t *)ly.k_norm;
     qr.eps = m.eps;
     qr.theta = m.theta;
+    qr.freq_ratio = std::pow((double)m.theta, -2.0 / (double)d);
     qr.err = err;
     qd::AttentionArgs a = {};
     a.q = q;

@@ -90,6 +90,7 @@ hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
 struct AttentionQkRope {
   const uint16_t *k_src, *v_src, *q_w, *k_w;
   float eps, theta;
+  double freq_ratio;  // theta^(-2 / head_dim) in fp64 (host)
   unsigned *err;
 };
 struct AttentionArgs {
