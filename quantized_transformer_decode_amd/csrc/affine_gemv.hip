@@ -647,6 +647,7 @@ hipError_t launch_mfma(const AffineGroup &g, int cols, const uint16_t *x, int m,
 
 constexpr int kG = 2;
 constexpr int kM1Threads = 512;
+constexpr int kM1Cpt = 2;  // 8-element pieces of x per thread (cols <= 8192)
 constexpr int kM1Waves = kM1Threads / kWave;
 
 struct M1Group {
@@ -728,33 +729,81 @@ __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
     uint16_t *__restrict__ y_, const GemvPrologue pro) {
   extern __shared__ __attribute__((aligned(16))) float xl[];  // chunks*1024, xswz layout
   const int chunks = (cols + 1023) >> 10;
-  if constexpr (PRO == 1) {
-    __shared__ float red[kM1Waves];
-    float ss = 0.f;
-    for (int e = threadIdx.x; e < cols; e += kM1Threads) {
-      float a = f16_to_f32(x[e]);
-      if (pro.delta) {
-        a = round_f16(a + f16_to_f32(gp(pro.delta)[e]));
-        if (pro.x_out && blockIdx.x == 0) gp(pro.x_out)[e] = f32_to_f16(a);
-      }
-      xl[xswz(e)] = a;
-      ss = fmaf(a, a, ss);
-    }
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
+  // x (with PRO 1 also delta and the norm weights) as 16-byte pieces of 8
+  // elements, every load issued before any is used, and before the first
+  // weights: the staging then costs one memory round trip, under the
+  // weight stream
+  const int c8 = cols >> 3, t = threadIdx.x;
+  u32x4 xv[kM1Cpt], dv[kM1Cpt], wv[kM1Cpt];
 #pragma unroll
-    for (int w = 0; w < kM1Waves; ++w) tot += red[w];
-    const float inv = 1.f / sqrtf(tot / (float)cols + pro.eps);
-    for (int e = threadIdx.x; e < cols; e += kM1Threads)
-      xl[xswz(e)] = round_f16(xl[xswz(e)] * inv * bf16_to_f32(gp(pro.w)[e]));
-    if (pro.advance && blockIdx.x == 0 && threadIdx.x == 0) gp(pro.advance)[0] += 1;
-  } else {
-    for (int e = threadIdx.x; e < cols; e += kM1Threads)
-      xl[xswz(e)] = F16 ? f16_to_f32(x[e]) : bf16_to_f32(x[e]);
+  for (int k = 0; k < kM1Cpt; ++k) {
+    const int i = min(t + k * kM1Threads, c8 - 1);
+    xv[k] = *(const QD_GLOBAL u32x4 *)(gp(x) + 8 * i);
+    if constexpr (PRO == 1) {
+      wv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.w) + 8 * i);
+      if (pro.delta) dv[k] = *(const QD_GLOBAL u32x4 *)(gp(pro.delta) + 8 * i);
+    }
   }
-  __syncthreads();
+  auto put8 = [&](int i, const float (&v)[8]) {
+    *(floatx4 *)(xl + xswz(8 * i)) = floatx4{v[0], v[1], v[2], v[3]};
+    *(floatx4 *)(xl + xswz(8 * i + 4)) = floatx4{v[4], v[5], v[6], v[7]};
+  };
+  auto stage = [&]() {
+    if constexpr (PRO == 1) {
+      __shared__ float red[kM1Waves];
+      float a[kM1Cpt][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < kM1Cpt; ++k) {
+        const int i = t + k * kM1Threads;
+        if (i < c8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            a[k][e] = pro.delta ? round_f16(half_of(xv[k], e) + half_of(dv[k], e))
+                                : half_of(xv[k], e);
+            ss = fmaf(a[k][e], a[k][e], ss);
+          }
+          if (pro.delta && pro.x_out && blockIdx.x == 0)
+            *(QD_GLOBAL u32x4 *)(gp(pro.x_out) + 8 * i) = pack_halves(a[k]);
+        }
+      }
+      ss = wave_sum(ss);
+      if ((t & 63) == 0) red[t >> 6] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kM1Waves; ++w) tot += red[w];
+      const float inv = 1.f / sqrtf(tot / (float)cols + pro.eps);
+#pragma unroll
+      for (int k = 0; k < kM1Cpt; ++k) {
+        const int i = t + k * kM1Threads;
+        if (i < c8) {
+          const uint32_t we[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            v[e] = round_f16(a[k][e] * inv * bf16_to_f32((we[e >> 1] >> (16 * (e & 1))) & 0xffffu));
+          put8(i, v);
+        }
+      }
+      if (pro.advance && blockIdx.x == 0 && t == 0) gp(pro.advance)[0] += 1;
+    } else {
+#pragma unroll
+      for (int k = 0; k < kM1Cpt; ++k) {
+        const int i = t + k * kM1Threads;
+        if (i < c8) {
+          const uint32_t xe[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t b = (xe[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            v[e] = F16 ? f16_to_f32(b) : bf16_to_f32(b);
+          }
+          put8(i, v);
+        }
+      }
+    }
+  };
   const QD_GLOBAL uint8_t *w = gp(w_);
   QD_GLOBAL uint16_t *y = gp(y_);
   const int lane = threadIdx.x & 63;
@@ -763,10 +812,19 @@ __global__ __launch_bounds__(kM1Threads) void affine_gemv_m1_kernel(
   const int lo = uni((int)(((int64_t)rows * gw) / nw));
   const int hi = uni((int)(((int64_t)rows * (gw + 1)) / nw));
   const int n = uni((hi - lo) * chunks);
+  M1Group A, B;
+  // the staging in both branches: after a join of paths with different
+  // numbers of loads in flight the memory waits would be counted for the
+  // path with fewer, and the staging would wait for the first weights
+  if (n > 0) {
+    m1_issue(A, w, rows, cols, chunks, lo, n, 0, lane);
+    stage();
+  } else {
+    stage();
+  }
+  __syncthreads();
   if (n == 0) return;
   float rowsum = 0.f;
-  M1Group A, B;
-  m1_issue(A, w, rows, cols, chunks, lo, n, 0, lane);
   for (int i = 0; i < n; i += 2 * kG) {
     m1_issue(B, w, rows, cols, chunks, lo, n, i + kG < n ? i + kG : i, lane);
     m1_compute<F16>(A, cols, chunks, lo, n, i, lane, xl, y, rowsum);
