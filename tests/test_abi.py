@@ -348,6 +348,11 @@ def test_qwen3_step_workspace_and_errors():
     # attention partials, fp32 o-projection partial rows (one per K/V head)
     rows = 256 + 2048 + 4096 + 2048 + 2048 + 4096 + 2048 + 6144 + 6144
     assert n == rows + qd.attention_decode_workspace_bytes(16, 8, 128) + 8 * 1024 * 4
+    # more than 8 K/V heads: the o projection is its own GEMV, no partial rows
+    # (q, attn 16 x 64 x 2; k, v 16 x 64 x 2: the same padded sizes as above)
+    n16 = wb(_qwen3(heads=16, kv_heads=16, head_dim=64))
+    rows16 = 256 + 2048 + 2048 + 2048 + 2048 + 2048 + 2048 + 6144 + 6144
+    assert n16 == rows16 + qd.attention_decode_workspace_bytes(16, 16, 64)
     for bad in (dict(hidden=1000), dict(head_dim=96), dict(heads=24), dict(inter=16384),
                 dict(capacity=0), dict(vocab=0), dict(n_layers=0)):
         assert wb(_qwen3(**bad)) == 0, bad
