@@ -458,7 +458,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_combine_kernel(
 // the next kernel's prologue; nothing is accumulated across workgroups.  The
 // weight loads are issued first, so they are in flight during the combine.
 constexpr int kCoThreads = 512;
-constexpr int kCoPasses = 2;  // weight rows per lane
+constexpr int kCoPasses = 1;  // weight rows per lane (2 and 4 measured slower)
 
 template <int D, int G>
 __global__ __launch_bounds__(kCoThreads) void attention_combine_o_kernel(
