@@ -36,6 +36,23 @@ constexpr int kAttUnroll = 2;      // row loads in flight per lane (K and V each
 constexpr int kAttTargetWgs = 512; // about two workgroups per CU of a 256-CU device
 constexpr int kAttSingleRowsPerWave = 32;  // windows up to 4 * 32 rows: a single chunk
 
+// With a device position the grid (gchunks chunks per K/V head) is sized for
+// the whole cache, and the chunk length follows the live window of len rows:
+// about 1.5 sqrt(len) rows, at least 32 (and at most gchunks chunks), in
+// whole row loads per wave.  Measured in the decoder step, the best length
+// grows with the window: 32-row chunks at 128 rows, 64 at 1024, 96 at 4096
+// (64, 128 and 256 are slower there).  Every kernel of a call derives it the
+// same way.
+template <int D>
+__device__ __forceinline__ int att_dev_rows_per_wave(int len, int gchunks) {
+  constexpr int step = (kWave / (D / 8)) * kAttUnroll;
+  int rows = max(32, (int)(1.5f * sqrtf((float)len)));
+  rows = max(rows, (len + gchunks - 1) / gchunks);
+  const int want = (rows + kAttWaves - 1) / kAttWaves;
+  // wave-uniform: kept in a scalar register, so the row loop stays scalar
+  return uni(max(step, (want + step - 1) / step * step));
+}
+
 template <bool F16>
 __device__ __forceinline__ float to_f32(uint32_t bits) {
   return F16 ? f16_to_f32(bits) : bf16_to_f32(bits);
@@ -201,6 +218,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
     }
     kv_start = 0;
     length = pos + 1;
+    rows_per_wave = att_dev_rows_per_wave<D>(length, nchunks);
     if (c * kAttWaves * rows_per_wave >= length) return;
   }
   const QD_GLOBAL uint16_t *q = gp(q_);
@@ -432,7 +450,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
 
 // out[h] from the nchunks partials of query head h (chunk stride `stride`),
 // one workgroup per head; with pos_dev, nchunks follows from the window
-// [0, *pos_dev + 1) and rows_per_wave.
+// [0, *pos_dev + 1) (att_dev_rows_per_wave).
 template <int D, bool F16>
 __global__ __launch_bounds__(kAttThreads) void attention_combine_kernel(
     const float *__restrict__ part, int stride, int nchunks, const int *__restrict__ pos_dev,
@@ -441,6 +459,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_combine_kernel(
   if (pos_dev) {
     const int pos = gp(pos_dev)[0];
     if (pos < 0 || pos >= capacity) return;
+    rows_per_wave = att_dev_rows_per_wave<D>(pos + 1, stride);
     nchunks = (pos + kAttWaves * rows_per_wave) / (kAttWaves * rows_per_wave);
   }
   combine_chunks<D, F16>(gp(part) + (size_t)h * stride * (D + 2), nchunks,
@@ -492,6 +511,7 @@ __global__ __launch_bounds__(kCoThreads) void attention_combine_o_kernel(
   }
   const int pos = gp(pos_dev)[0];
   if (pos < 0 || pos >= capacity) return;  // the first kernel has set the error word
+  rows_per_wave = att_dev_rows_per_wave<D>(pos + 1, stride);
   const int nchunks = (pos + kAttWaves * rows_per_wave) / (kAttWaves * rows_per_wave);
   const int slice = t / EW, e0 = t % EW;
 #pragma unroll
