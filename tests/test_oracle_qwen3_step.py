@@ -165,3 +165,242 @@ def test_f16_step_stores_f16_values_near_the_exact_step():
     # the f16 buffers move the result by rounding-sized amounts only
     assert oracle.normwise_error(x16, x64) < 2e-3
     assert oracle.normwise_error(l16, l64) < 2e-3
+
+
+# ---- the f16 buffer model, pinned by the page's own buffer list -------------
+#
+# turbospark-runtime 0.3.0, src/qwen3_asr_metal.rs -- `Work` and
+# `ensure_work` allocate every activation buffer of the step (x, normed, q,
+# attn, delta, gate, up, logits and the per-layer K/V caches) as 16-bit words;
+# `Qwen3AsrMetalEngine::step` encodes one kernel per op, each reading and
+# writing those buffers (the per-head norms, the RoPE and the SiLU-mul in
+# place).  The machine below executes that encoder list literally on
+# numpy float16 arrays: whatever an encoder writes is stored in a 16-bit
+# buffer, so the rounding points follow from the buffers' type, not from a
+# list of roundings.  Each encoder's arithmetic is the exact (f64) value of
+# its inputs (the page does not give kernel internals).  The oracle's f16
+# step must match it bit for bit.
+
+class _PageBuffers:
+    """The step's scratch as the page allocates it: f16 words."""
+
+    def __init__(self, spec, capacity, n_layers):
+        hid, qw, kw = spec.hidden, spec.heads * spec.head_dim, spec.kv_heads * spec.head_dim
+        h = lambda n: np.zeros(n, dtype=np.float16)
+        self.x, self.normed, self.q, self.attn = h(hid), h(hid), h(qw), h(qw)
+        self.delta, self.gate, self.up = h(hid), h(spec.inter), h(spec.inter)
+        self.logits = h(spec.vocab)
+        self.k = [np.zeros((capacity, kw), dtype=np.float16) for _ in range(n_layers)]
+        self.v = [np.zeros((capacity, kw), dtype=np.float16) for _ in range(n_layers)]
+
+
+class _PageMachine:
+    """Encoders of the step on f16 buffers; arithmetic in f64 from the
+    buffers' values; a store into a buffer is a store into float16."""
+
+    def __init__(self, spec, om, capacity):
+        self.spec, self.om = spec, om
+        self.dense = {}
+        self.buf = _PageBuffers(spec, capacity, len(om["layers"]))
+
+    def _w(self, blob, rows, cols):
+        key = id(blob)
+        if key not in self.dense:
+            self.dense[key] = reference_np.affine_dense(blob, rows, cols)
+        return self.dense[key]
+
+    # encode_dequant_int8_gemv_resident: y = W x
+    def gemv(self, blob, rows, cols, src, dst):
+        dst[...] = self._w(blob, rows, cols) @ src.astype(np.float64)
+
+    # encode_rms_norm_bf16w(_perhead): per row of `width` elements
+    def rms_norm(self, src, w, dst, width):
+        a = src.astype(np.float64).reshape(-1, width)
+        inv = 1.0 / np.sqrt((a * a).sum(axis=1, keepdims=True) / width + self.om["eps"])
+        dst[...] = (a * inv * np.asarray(w)[None, :]).reshape(dst.shape)
+
+    # encode_rope_neox_subdim with rotary width = head_dim, in place
+    def rope(self, buf, position, heads):
+        d = self.spec.head_dim
+        a = buf.astype(np.float64).reshape(heads, d)
+        i = np.arange(d // 2, dtype=np.float64)
+        z = (a[:, : d // 2] + 1j * a[:, d // 2:]) * np.exp(
+            1j * position * self.om["theta"] ** (-2.0 * i / d))
+        buf[...] = np.concatenate([z.real, z.imag], axis=1).reshape(-1)
+
+    # encode_attention_decode over rows [0, position]
+    def attention(self, layer, position):
+        s = self.spec
+        grp = s.heads // s.kv_heads
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(s.head_dim)))
+        q = self.buf.q.astype(np.float64).reshape(s.heads, s.head_dim)
+        K = self.buf.k[layer][: position + 1].astype(np.float64).reshape(-1, s.kv_heads,
+                                                                          s.head_dim)
+        V = self.buf.v[layer][: position + 1].astype(np.float64).reshape(-1, s.kv_heads,
+                                                                          s.head_dim)
+        out = np.empty((s.heads, s.head_dim))
+        for h in range(s.heads):
+            sc = K[:, h // grp, :] @ q[h] * scale
+            e = np.exp(sc - sc.max())
+            out[h] = (e / e.sum()) @ V[:, h // grp, :]
+        self.buf.attn[...] = out.reshape(-1)
+
+    def step(self, row, position, logit_rows):
+        s, om, b = self.spec, self.om, self.buf
+        hid, H, KV, d, inter = s.hidden, s.heads, s.kv_heads, s.head_dim, s.inter
+        b.x[...] = row                                   # write_buffer_bytes(x, row)
+        for li, L in enumerate(om["layers"]):
+            kr, vr = b.k[li][position], b.v[li][position]  # (cache, kv_row)
+            self.rms_norm(b.x, L["in_norm"], b.normed, hid)
+            self.gemv(L["q"], H * d, hid, b.normed, b.q)
+            self.gemv(L["k"], KV * d, hid, b.normed, kr)
+            self.gemv(L["v"], KV * d, hid, b.normed, vr)
+            self.rms_norm(b.q, L["q_norm"], b.q, d)
+            self.rms_norm(kr, L["k_norm"], kr, d)
+            self.rope(b.q, position, H)
+            self.rope(kr, position, KV)
+            self.attention(li, position)
+            self.gemv(L["o"], hid, H * d, b.attn, b.delta)
+            b.x[...] = b.x.astype(np.float64) + b.delta   # encode_residual_add
+            self.rms_norm(b.x, L["post_norm"], b.normed, hid)
+            self.gemv(L["gate"], inter, hid, b.normed, b.gate)
+            self.gemv(L["up"], inter, hid, b.normed, b.up)
+            g, u = b.gate.astype(np.float64), b.up.astype(np.float64)
+            b.gate[...] = g / (1.0 + np.exp(-g)) * u      # encode_silu_mul, in place
+            self.gemv(L["down"], hid, inter, b.gate, b.delta)
+            b.x[...] = b.x.astype(np.float64) + b.delta
+        self.rms_norm(b.x, om["final_norm"], b.normed, hid)
+        self.gemv(om["embed"], s.vocab, hid, b.normed, b.logits)
+        lg = b.logits.astype(np.float64)
+        return b.x.astype(np.float64), lg if logit_rows is None else lg[logit_rows]
+
+
+def _machine_vs_step(step_fn, spec, om, rows, positions):
+    """Run the page machine and `step_fn` (the oracle's qwen3_step or a
+    mutant of it) over the same rows; True when every stored value agrees
+    bit for bit (residual row, logits, every layer's new K/V rows)."""
+    cap = max(positions) + 1
+    pm = _PageMachine(spec, om, cap)
+    kc, vc = empty_caches(spec, cap, len(om["layers"]))
+    sel = np.arange(0, spec.vocab, 7)
+    for row, pos in zip(rows, positions):
+        mx, ml = pm.step(row, pos, sel)
+        ox, ol = step_fn(row, pos, om, kc, vc, f16=True, logit_rows=sel)
+        same = np.array_equal(mx, ox) and np.array_equal(ml, ol)
+        for li in range(len(om["layers"])):
+            same &= np.array_equal(pm.buf.k[li][pos].astype(np.float64), kc[li][pos].reshape(-1))
+            same &= np.array_equal(pm.buf.v[li][pos].astype(np.float64), vc[li][pos].reshape(-1))
+        if not same:
+            return False
+    return True
+
+
+def _pin_inputs():
+    spec = synth.QWEN3_TINY_STEP
+    om = oracle_model(spec, synth.qwen3_model(spec))
+    # rows that are not f16 numbers, so the store into x itself rounds; the
+    # third position is far from 0 so the RoPE angles are large
+    rows = np.random.default_rng(6).standard_normal((3, spec.hidden)) * 0.5
+    return spec, om, rows, [0, 1, 3]
+
+
+def test_f16_step_equals_the_page_buffer_machine():
+    spec, om, rows, positions = _pin_inputs()
+    assert _machine_vs_step(oracle.qwen3_step, spec, om, rows, positions)
+
+
+def _rounding_mutants():
+    """Variants of oracle.qwen3_step with one of its f16 roundings dropped or
+    done in BF16 instead, built from its source (the mistakes a reading of
+    the page's buffers could make)."""
+    import ast
+    import inspect
+    import textwrap
+
+    src = textwrap.dedent(inspect.getsource(oracle.qwen3_step))
+    tree = ast.parse(src)
+    sites = [n for n in ast.walk(tree)
+             if isinstance(n, ast.Call) and isinstance(n.func, ast.Name) and n.func.id == "r"]
+    assert len(sites) >= 15, len(sites)
+
+    def bf16(v):
+        return synth.bf16_bits_to_f32(synth.to_bf16_bits(
+            np.asarray(v, dtype=np.float64).astype(np.float32))).astype(np.float64)
+
+    for i in range(len(sites)):
+        for kind in ("drop", "bf16"):
+            t = ast.parse(src)
+            calls = [n for n in ast.walk(t) if isinstance(n, ast.Call) and
+                     isinstance(n.func, ast.Name) and n.func.id == "r"]
+            c = calls[i]
+            what = f"{kind} r() at line {c.lineno}: {ast.unparse(c)[:60]}"
+
+            class Swap(ast.NodeTransformer):
+                def visit_Call(self, node):
+                    self.generic_visit(node)
+                    if node is c:
+                        if kind == "drop":
+                            return node.args[0]
+                        return ast.Call(func=ast.Name("_round_bf16", ast.Load()),
+                                        args=node.args, keywords=[])
+                    return node
+
+            t = ast.fix_missing_locations(Swap().visit(t))
+            ns = dict(vars(oracle))
+            ns["_round_bf16"] = bf16
+            exec(compile(t, "<mutant>", "exec"), ns)
+            yield what, ns["qwen3_step"]
+
+
+def _caught(fn, spec, om, rows, positions):
+    """A mutant is caught when the pin sees a difference, or when it stops
+    with an error (a GEMV of the f16 step refuses inputs that are not f16
+    numbers: a dropped rounding in front of it cannot pass unnoticed)."""
+    try:
+        return not _machine_vs_step(fn, spec, om, rows, positions)
+    except AssertionError:
+        return True
+
+
+def test_buffer_machine_pin_catches_every_rounding_mutant():
+    # every stored-buffer rounding of the oracle matters to the pin: dropping
+    # any one of them, or doing it in BF16, breaks bit equality with the
+    # page machine
+    spec, om, rows, positions = _pin_inputs()
+    survivors = [what for what, fn in _rounding_mutants()
+                 if not _caught(fn, spec, om, rows, positions)]
+    assert not survivors, survivors
+
+
+def _step_with(**replace):
+    import inspect
+    import textwrap
+    ns = dict(vars(oracle))
+    ns.update(replace)
+    exec(compile(textwrap.dedent(inspect.getsource(oracle.qwen3_step)), "<mutant>", "exec"), ns)
+    return ns["qwen3_step"]
+
+
+def test_buffer_machine_pin_catches_an_extra_rounding():
+    # roundings where the page stores nothing must break the pin too: the
+    # attention's scores kept in f16, or the norm's mean square reduced in f16
+    spec, om, rows, positions = _pin_inputs()
+
+    def attention_f16_scores(q, k, v, length, scale, kv_start=0):
+        group = q.shape[0] // k.shape[1]
+        out = np.empty_like(q)
+        for h in range(q.shape[0]):
+            s = oracle.round_f16(scale * (k[kv_start:length, h // group, :] @ q[h]))
+            p = np.exp(s - s.max())
+            out[h] = (p / p.sum()) @ v[kv_start:length, h // group, :]
+        return out
+
+    def rms_norm_f16_mean(x, w, eps):
+        x = np.asarray(x, dtype=np.float64)
+        ms = oracle.round_f16(np.mean(x * x, axis=-1, keepdims=True))
+        return x / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+    assert _caught(_step_with(attention_decode=attention_f16_scores), spec, om, rows, positions)
+    assert _caught(_step_with(rms_norm=rms_norm_f16_mean), spec, om, rows, positions)
+    # and the unmutated copy built the same way still passes
+    assert not _caught(_step_with(), spec, om, rows, positions)
