@@ -416,10 +416,36 @@ typedef struct {
 } qd_qwen3_model;
 
 /* Bytes of the step workspace for this model (0 if the model is not
- * supported): one error word, the f16 scratch rows, the attention partials
- * and, with at most 8 K/V heads, kv_heads fp32 rows of hidden entries (the
- * o projection's partial sums, one row per K/V head). */
+ * supported): one error word, the f16 scratch rows, the attention partials,
+ * with at most 8 K/V heads kv_heads fp32 rows of hidden entries (the o
+ * projection's partial sums, one row per K/V head), and the rotated q row. */
 size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model);
+
+/* The step's scratch rows inside the workspace (the page's `Work` buffers
+ * that the fused kernels still store).  After a step they hold the last
+ * layer's values:
+ *   QD_QWEN3_BUF_Q      f16 [heads*head_dim]  q GEMV output, before its norm and RoPE
+ *   QD_QWEN3_BUF_K      f16 [kv_heads*head_dim]  k GEMV output, before its norm and RoPE
+ *   QD_QWEN3_BUF_V      f16 [kv_heads*head_dim]  v GEMV output
+ *   QD_QWEN3_BUF_QROPE  f16 [heads*head_dim]  q after its per-head norm and RoPE
+ *                       (the page's q buffer after encode_rope_neox_subdim)
+ *   QD_QWEN3_BUF_ATTN   f16 [heads*head_dim]  attention output
+ *   QD_QWEN3_BUF_OPART  fp32 [kv_heads][hidden]  the o projection's partial rows,
+ *                       one per K/V head (kv_heads <= 8)
+ *   QD_QWEN3_BUF_GATE   f16 [inter]  gate GEMV output (before SiLU)
+ *   QD_QWEN3_BUF_UP     f16 [inter]  up GEMV output
+ *   QD_QWEN3_BUF_DELTA  f16 [hidden]  down GEMV output (the o output when
+ *                       kv_heads > 8, until the down GEMV overwrites it)
+ *   QD_QWEN3_BUF_XALT   f16 [hidden]  the residual row after the attention block
+ * Returns the byte offset of that row in the workspace, or -1 when the
+ * model is not supported or the buffer is not used for this model.
+ * Host-only arithmetic (no device call). */
+enum {
+  QD_QWEN3_BUF_Q = 0, QD_QWEN3_BUF_K = 1, QD_QWEN3_BUF_V = 2, QD_QWEN3_BUF_ATTN = 3,
+  QD_QWEN3_BUF_OPART = 4, QD_QWEN3_BUF_GATE = 5, QD_QWEN3_BUF_UP = 6, QD_QWEN3_BUF_DELTA = 7,
+  QD_QWEN3_BUF_XALT = 8, QD_QWEN3_BUF_QROPE = 9
+};
+int64_t qwen3_step_workspace_offset(const qd_qwen3_model *model, int32_t buffer);
 
 /* Qwen3AsrMetalEngine::step for one row: x (device, f16 [hidden], 16-byte
  * aligned) goes through every layer at p = *position (device int32) --

@@ -62,3 +62,19 @@ def q4_0_quantize(w: np.ndarray, rows: int, cols: int) -> np.ndarray:
     stream = out.reshape(-1)
     pad = (-stream.size) % 4
     return np.concatenate([stream, np.zeros(pad, dtype=np.uint8)])
+
+
+def affine_dense_sub(blob: np.ndarray, rows: int, cols: int, row_sel, col_sel) -> np.ndarray:
+    """The dequantised entries w[r, c] = q * scale + bias for the rows
+    `row_sel` (all if None) and columns `col_sel`, in f64."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    g = cols // GROUP
+    rs = np.arange(rows) if row_sel is None else np.asarray(row_sel, dtype=np.int64)
+    cs = np.asarray(col_sel, dtype=np.int64)
+    codes = blob[: rows * cols].reshape(rows, cols)[np.ix_(rs, cs)].astype(np.float64)
+    sc = blob[rows * cols: rows * cols + rows * g * 2].view(np.uint16).reshape(rows, g)
+    bi = blob[rows * cols + rows * g * 2: rows * cols + 2 * rows * g * 2].view(
+        np.uint16).reshape(rows, g)
+    s = bf16_bits_to_f64(sc[np.ix_(rs, cs // GROUP)])
+    b = bf16_bits_to_f64(bi[np.ix_(rs, cs // GROUP)])
+    return codes * s + b

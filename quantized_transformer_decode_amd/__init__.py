@@ -36,6 +36,7 @@ EXPORTS = (
     "attention_decode_workspace_bytes", "attention_decode",
     "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16",
     "qwen3_step_workspace_bytes", "qwen3_step_run", "qwen3_step_check",
+    "qwen3_step_workspace_offset",
 )
 
 
@@ -156,6 +157,8 @@ def lib() -> ctypes.CDLL:
         L.qwen3_step_workspace_bytes.restype = SZ
         L.qwen3_step_run.argtypes = [MP, P, SZ, P, P, P, ctypes.c_int32, P]
         L.qwen3_step_check.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+        L.qwen3_step_workspace_offset.argtypes = [MP, ctypes.c_int32]
+        L.qwen3_step_workspace_offset.restype = I64
         L.attention_decode_workspace_bytes.restype = I64
         L.attention_decode.argtypes = [P, P, P, I64, I64, I64, I64, I64, ctypes.c_float,
                                        ctypes.c_int32, P, P, SZ, P]
@@ -353,6 +356,16 @@ def qwen3_model(hidden, heads, kv_heads, head_dim, inter, vocab, capacity, eps, 
 
 def qwen3_step_workspace_bytes(model) -> int:
     return int(lib().qwen3_step_workspace_bytes(ctypes.byref(model)))
+
+
+QWEN3_BUFFERS = {"q": 0, "k": 1, "v": 2, "attn": 3, "opart": 4, "gate": 5, "up": 6,
+                 "delta": 7, "xalt": 8, "qrope": 9}
+
+
+def qwen3_step_workspace_offset(model, buffer: str) -> int:
+    """Byte offset of one of the step's scratch rows in its workspace (-1:
+    not used for this model)."""
+    return int(lib().qwen3_step_workspace_offset(ctypes.byref(model), QWEN3_BUFFERS[buffer]))
 
 
 def qwen3_step_run(model, workspace, workspace_bytes: int, x, position, logits=None,

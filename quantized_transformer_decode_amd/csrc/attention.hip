@@ -293,6 +293,14 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
         unpack8<true>(qraw[h], qf[h]);
         norm_rope8<D>(qf[h], wq, sub, qkr.eps, cs);
       }
+      // the rotated q rows, as the page's q buffer holds them after the RoPE
+      // (one row slot of the first chunk's first wave stores them)
+      if (qkr.q_out && c == 0 && wave == 0 && grp == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          *(QD_GLOBAL u32x4 *)(gp(qkr.q_out) + (size_t)(j * G + h) * D + 8 * sub) =
+              pack8_f16(qf[h]);
+      }
       if (kwave) {
         float kx[8];
         unpack8<true>(kraw, kx);
@@ -483,7 +491,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kCoThreads) void attention_combine_o_kernel(
     const float *__restrict__ part, int stride, const int *__restrict__ pos_dev, int capacity,
     int rows_per_wave, const uint8_t *__restrict__ wo, int rows, int cols,
-    float *__restrict__ opart) {
+    float *__restrict__ opart, uint16_t *__restrict__ attn_out) {
   constexpr int E = G * D;                           // elements of the K/V head's row slice
   constexpr int EW = E < kCoThreads ? E : kCoThreads;
   constexpr int SL = kCoThreads / EW;                // chunk slices side by side
@@ -567,6 +575,10 @@ __global__ __launch_bounds__(kCoThreads) void attention_combine_o_kernel(
     }
   }
   __syncthreads();
+  // the attention row of this K/V head's query heads, as the page's attn
+  // buffer holds it (the first row block stores it)
+  if (attn_out && blockIdx.x == 0)
+    for (int e = t; e < E; e += kCoThreads) gp(attn_out)[(size_t)j * E + e] = f32_to_f16(av[e]);
   const float4 *ap = (const float4 *)(av + 16 * u);
   const float4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
   const float s16 = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w)) +
@@ -623,7 +635,7 @@ hipError_t launch_att(const AttentionArgs &a, hipStream_t stream) {
       hipLaunchKernelGGL((attention_combine_o_kernel<D, G>),
                          dim3((a.wo_rows + rpw - 1) / rpw, a.kv_heads), dim3(kCoThreads), 0,
                          stream, a.part, p.nchunks, a.pos_dev, a.capacity, p.rows_per_wave,
-                         a.wo, a.wo_rows, a.wo_cols, a.opart);
+                         a.wo, a.wo_rows, a.wo_cols, a.opart, a.out);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;

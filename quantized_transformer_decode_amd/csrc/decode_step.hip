@@ -242,7 +242,9 @@ __device__ __forceinline__ void compute(const Group &g, const StepOp *ops, int l
         if (lane == 0) wk.op.y[wk.row - wk.op.row_base] = f32_to_bf16(rowsum);
         rowsum = 0.f;
       }
-      walk_next(wk, ops);
+      // past the group's last valid item there is no next descriptor to read
+      // (after the plan's last op the table ends)
+      if (g.i0 + k + 1 < wk.n) walk_next(wk, ops);
     }
   }
 }

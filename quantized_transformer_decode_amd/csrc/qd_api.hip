@@ -741,7 +741,7 @@ namespace {
 
 // Byte offsets of the step workspace's parts (each 256-byte aligned).
 struct StepLayout {
-  size_t err, xalt, q, kbuf, vbuf, attn, delta, gate, up, part, opart, total;
+  size_t err, xalt, q, kbuf, vbuf, attn, delta, gate, up, part, opart, qrope, total;
 };
 
 // The o projection runs inside the attention's combine when the gate/up
@@ -780,6 +780,7 @@ StepLayout qwen3_layout(const qd_qwen3_model &m) {
   L.up = take(m.inter * 2);
   L.part = take((size_t)attention_decode_workspace_bytes(m.heads, m.kv_heads, m.head_dim));
   L.opart = take(step_fused_o(m) ? (size_t)m.kv_heads * m.hidden * 4 : 0);
+  L.qrope = take(qw * 2);
   L.total = o;
   return L;
 }
@@ -791,6 +792,25 @@ extern "C" {
 size_t qwen3_step_workspace_bytes(const qd_qwen3_model *model) {
   if (!model || !qwen3_shape_ok(*model)) return 0;
   return qwen3_layout(*model).total;
+}
+
+int64_t qwen3_step_workspace_offset(const qd_qwen3_model *model, int32_t buffer) {
+  if (!model || !qwen3_shape_ok(*model)) return -1;
+  const StepLayout L = qwen3_layout(*model);
+  const bool fo = step_fused_o(*model);
+  switch (buffer) {
+    case QD_QWEN3_BUF_Q: return (int64_t)L.q;
+    case QD_QWEN3_BUF_K: return (int64_t)L.kbuf;
+    case QD_QWEN3_BUF_V: return (int64_t)L.vbuf;
+    case QD_QWEN3_BUF_ATTN: return (int64_t)L.attn;
+    case QD_QWEN3_BUF_OPART: return fo ? (int64_t)L.opart : -1;
+    case QD_QWEN3_BUF_GATE: return (int64_t)L.gate;
+    case QD_QWEN3_BUF_UP: return (int64_t)L.up;
+    case QD_QWEN3_BUF_DELTA: return (int64_t)L.delta;
+    case QD_QWEN3_BUF_XALT: return (int64_t)L.xalt;
+    case QD_QWEN3_BUF_QROPE: return (int64_t)L.qrope;
+    default: return -1;
+  }
 }
 
 qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t workspace_bytes,
@@ -892,7 +912,8 @@ qd_status qwen3_step_run(const qd_qwen3_model *model, void *workspace, size_t wo
     if (l > 0) cur ^= 1;
     // per-head norms + RoPE of q and the new K row, and the K/V append at
     // row p, fused into the attention's first kernel
-    qd::AttentionQkRope qr;
+    qd::AttentionQkRope qr = {};
+    qr.q_out = (uint16_t *)(ws + L.qrope);
     qr.k_src = kbuf;
     qr.v_src = vbuf;
     qr.q_w = (const uint16_t *)ly.q_norm;

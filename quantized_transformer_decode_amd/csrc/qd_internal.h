@@ -89,6 +89,7 @@ hipError_t launch_q4_0_quantize(const float *w, int64_t n_blocks, uint8_t *out,
 // position outside the cache sets bit 1 of *err.
 struct AttentionQkRope {
   const uint16_t *k_src, *v_src, *q_w, *k_w;
+  uint16_t *q_out;    // optional: the normed, rotated q rows (f16 [heads][head_dim])
   float eps, theta;
   double freq_ratio;  // theta^(-2 / head_dim) in fp64 (host)
   unsigned *err;
@@ -106,7 +107,7 @@ struct AttentionArgs {
   // Optional (f16, device position): the combine also applies the o
   // projection (affine-INT8 g64, wo_rows x wo_cols, wo_cols = heads *
   // head_dim) and writes opart[kv_heads][wo_rows] (fp32 partial rows, one
-  // per K/V head) instead of out.
+  // per K/V head); out, when not null, still receives the attention row.
   const uint8_t *wo;
   int wo_rows, wo_cols;
   float *opart;

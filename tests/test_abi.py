@@ -347,12 +347,13 @@ def test_qwen3_step_workspace_and_errors():
     # error word, normed, q, k, v, attn, delta, gate, up (each 256-padded),
     # attention partials, fp32 o-projection partial rows (one per K/V head)
     rows = 256 + 2048 + 4096 + 2048 + 2048 + 4096 + 2048 + 6144 + 6144
-    assert n == rows + qd.attention_decode_workspace_bytes(16, 8, 128) + 8 * 1024 * 4
+    # ... and the rotated q row
+    assert n == rows + qd.attention_decode_workspace_bytes(16, 8, 128) + 8 * 1024 * 4 + 4096
     # more than 8 K/V heads: the o projection is its own GEMV, no partial rows
     # (q, attn 16 x 64 x 2; k, v 16 x 64 x 2: the same padded sizes as above)
     n16 = wb(_qwen3(heads=16, kv_heads=16, head_dim=64))
     rows16 = 256 + 2048 + 2048 + 2048 + 2048 + 2048 + 2048 + 6144 + 6144
-    assert n16 == rows16 + qd.attention_decode_workspace_bytes(16, 16, 64)
+    assert n16 == rows16 + qd.attention_decode_workspace_bytes(16, 16, 64) + 2048
     for bad in (dict(hidden=1000), dict(head_dim=96), dict(heads=24), dict(inter=16384),
                 dict(capacity=0), dict(vocab=0), dict(n_layers=0)):
         assert wb(_qwen3(**bad)) == 0, bad
@@ -426,3 +427,25 @@ def test_valid_args_reach_device_check():
     m = _qwen3()
     assert _call("qwen3_step_run", ctypes.byref(m), WS, qd.qwen3_step_workspace_bytes(m),
                  0x7fa000000000, 0x7fb000000000, None, 1, None) == qd.QD_EDEVICE
+
+
+def test_qwen3_step_workspace_offsets():
+    # the scratch rows lie inside the workspace, 256-byte aligned, disjoint
+    m = _qwen3()
+    total = qd.qwen3_step_workspace_bytes(m)
+    sizes = {"q": 4096, "k": 2048, "v": 2048, "attn": 4096, "opart": 8 * 1024 * 4,
+             "gate": 6144, "up": 6144, "delta": 2048, "xalt": 2048, "qrope": 4096}
+    spans = []
+    for name, size in sizes.items():
+        off = qd.qwen3_step_workspace_offset(m, name)
+        assert off >= 256 and off % 256 == 0 and off + size <= total, name
+        spans.append((off, off + size))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    # with more than 8 K/V heads there are no partial rows
+    m16 = _qwen3(heads=16, kv_heads=16, head_dim=64)
+    assert qd.qwen3_step_workspace_offset(m16, "opart") == -1
+    assert qd.qwen3_step_workspace_offset(m16, "attn") > 0
+    assert qd.qwen3_step_workspace_offset(_qwen3(hidden=1000), "q") == -1
+    assert qd.lib().qwen3_step_workspace_offset(ctypes.byref(m), 10) == -1
+    assert qd.lib().qwen3_step_workspace_offset(None, 0) == -1
