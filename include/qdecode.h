@@ -55,7 +55,8 @@ typedef enum {
   QD_EALIGN = 3,  /* pointer misaligned for the kernel's vector loads/stores  */
   QD_EDEVICE = 4, /* no current HIP device, or it is not gfx950               */
   QD_EHIP = 5,    /* the HIP runtime reported an error; see qd_last_hip_error */
-  QD_ESTEP = 6    /* a decode-step launch reported an error word (see _step_check) */
+  QD_ESTEP = 6,   /* a decode-step launch reported an error word (see _step_check) */
+  QD_ESCRATCH = 7 /* the call needs more than the library's static scratch holds */
 } qd_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -350,6 +351,25 @@ qd_status attention_decode(const void *q, const void *k_cache, const void *v_cac
                            int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t length,
                            int64_t kv_start, float scale, int32_t f16, void *out,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* attention_decode for callers that cannot allocate (code under HIP graph
+ * capture, serving loops that forbid allocation, harnesses without an
+ * allocator): the same operation, arguments and errors as attention_decode
+ * without the workspace.  The chunk partials go to a scratch buffer inside
+ * the library -- a static device array of ATTENTION_NOALLOC_SCRATCH_BYTES
+ * (4 MiB) that every device the library runs on holds until the process
+ * ends.  A head shape whose attention_decode_workspace_bytes exceeds it is
+ * rejected with QD_ESCRATCH before any HIP call.  This call allocates
+ * nothing (no hipMalloc, no library routine that allocates); the first call
+ * on a device looks the array's address up once.  All calls on one device
+ * share the array and nothing in it needs to start at zero, but calls that
+ * may overlap in time on one device (different streams, or different host
+ * threads without ordering) race on it: order them on one stream. */
+#define ATTENTION_NOALLOC_SCRATCH_BYTES (4u << 20)
+qd_status attention_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                   int64_t heads, int64_t kv_heads, int64_t head_dim,
+                                   int64_t length, int64_t kv_start, float scale, int32_t f16,
+                                   void *out, void *stream);
 
 /* ---- the decoder step around the GEMVs ------------------------------------ */
 

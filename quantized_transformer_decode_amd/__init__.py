@@ -20,7 +20,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqdecode.so")
 
-QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_EDEVICE, QD_EHIP, QD_ESTEP = range(7)
+QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_EDEVICE, QD_EHIP, QD_ESTEP, QD_ESCRATCH = range(8)
 
 # every function declared in include/qdecode.h
 EXPORTS = (
@@ -36,7 +36,7 @@ EXPORTS = (
     "attention_decode_workspace_bytes", "attention_decode",
     "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16",
     "qwen3_step_workspace_bytes", "qwen3_step_run", "qwen3_step_check",
-    "qwen3_step_workspace_offset",
+    "qwen3_step_workspace_offset", "attention_decode_noalloc",
 )
 
 
@@ -162,6 +162,8 @@ def lib() -> ctypes.CDLL:
         L.attention_decode_workspace_bytes.restype = I64
         L.attention_decode.argtypes = [P, P, P, I64, I64, I64, I64, I64, ctypes.c_float,
                                        ctypes.c_int32, P, P, SZ, P]
+        L.attention_decode_noalloc.argtypes = [P, P, P, I64, I64, I64, I64, I64,
+                                               ctypes.c_float, ctypes.c_int32, P, P]
         for n in ("affine_i8_g64_pack", "qgemv_affine_i8_g64", "qgemv_q4_0",
                   "qgemv_affine_i8_g64_group", "qgemv_q4_0_group",
                   "qgemm_q4_0_prefill", "q4_0_quantize", "qgemv_affine_i8_g64_step_plan",
@@ -169,7 +171,7 @@ def lib() -> ctypes.CDLL:
                   "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
                   "qlinear_q4_0_gemv", "qlinear_q4_0_gemm", "attention_decode",
                   "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16", "qwen3_step_run",
-                  "qwen3_step_check"):
+                  "qwen3_step_check", "attention_decode_noalloc"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -314,6 +316,16 @@ def attention_decode(q, k_cache, v_cache, heads: int, kv_heads: int, head_dim: i
         _ptr(q), _ptr(k_cache), _ptr(v_cache), heads, kv_heads, head_dim, length, kv_start,
         float(scale), 1 if f16 else 0, _ptr(out), _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def attention_decode_noalloc(q, k_cache, v_cache, heads: int, kv_heads: int, head_dim: int,
+                             length: int, kv_start: int, scale: float, out, f16: bool = True,
+                             stream=None) -> None:
+    """attention_decode with the chunk partials in the library's static
+    scratch (no workspace argument; nothing is allocated)."""
+    _check("attention_decode_noalloc", lib().attention_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), heads, kv_heads, head_dim, length, kv_start,
+        float(scale), 1 if f16 else 0, _ptr(out), _stream(stream)))
 
 
 def rmsnorm_f16(x, delta, w, n: int, eps: float, out, stream=None) -> None:

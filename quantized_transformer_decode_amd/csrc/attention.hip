@@ -24,6 +24,8 @@
 // one workgroup's chain of memory round trips costs more than the second
 // launch.)  Inside the decoder step, the first kernel also takes over the
 // per-head q/k RMSNorm + RoPE and the K/V cache append (QKR).
+#include <atomic>
+
 #include "qd_device.h"
 #include "qd_internal.h"
 
@@ -657,6 +659,38 @@ hipError_t launch_att_g(const AttentionArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Chunk partials of attention_decode_noalloc: a file-scope device array (one
+// copy per device, alive until the process ends) instead of a caller
+// workspace.  Host code never names it: its address on the current device
+// comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoallocScratchBytes = 4u << 20;
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch[kMaxScratchDevices];
+}  // namespace
+
+size_t attention_noalloc_scratch_bytes() { return kNoallocScratchBytes; }
+
+hipError_t attention_noalloc_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // the current device's copy of the array (two threads racing here get
+    // the same address)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 AttentionPlan attention_plan(int64_t kv_heads, int64_t window, int head_dim) {
   // whole loads of rows per wave, about kAttTargetWgs workgroups in all

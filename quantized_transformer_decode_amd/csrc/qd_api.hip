@@ -207,6 +207,7 @@ const char *qd_status_string(int status) {
     case QD_EDEVICE: return "QD_EDEVICE: no current HIP device, or it is not gfx950";
     case QD_EHIP: return "QD_EHIP: the HIP runtime reported an error";
     case QD_ESTEP: return "QD_ESTEP: a decode-step launch reported a wait time-out or grid mismatch";
+    case QD_ESCRATCH: return "QD_ESCRATCH: the shape needs more than the library's static scratch buffer";
     default: return "QD_UNKNOWN";
   }
 }
@@ -626,37 +627,34 @@ int64_t attention_decode_workspace_bytes(int64_t heads, int64_t kv_heads, int64_
   return heads * qd::attention_max_chunks(kv_heads) * (head_dim + 2) * 4;
 }
 
-qd_status attention_decode(const void *q, const void *k_cache, const void *v_cache,
-                           int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t length,
-                           int64_t kv_start, float scale, int32_t f16, void *out,
-                           void *workspace, size_t workspace_bytes, void *stream) {
-  if (!q || !k_cache || !v_cache || !out || !workspace) return QD_EINVAL;
+}  // extern "C"
+
+// Host-side checks shared by attention_decode and attention_decode_noalloc
+// (the workspace's own checks are the caller's); fills the kernels'
+// arguments except the partials' buffer.  *need = the partials' bytes.
+static qd_status attention_args(const void *q, const void *k_cache, const void *v_cache,
+                                int64_t heads, int64_t kv_heads, int64_t head_dim,
+                                int64_t length, int64_t kv_start, float scale, int32_t f16,
+                                void *out, qd::AttentionArgs &a, int64_t &need) {
+  if (!q || !k_cache || !v_cache || !out) return QD_EINVAL;
   if (f16 != 0 && f16 != 1) return QD_EINVAL;
   if (!attention_shape_ok(heads, kv_heads, head_dim)) return QD_ESHAPE;
   if (kv_start < 0 || kv_start >= length || length > (int64_t(1) << 30)) return QD_EINVAL;
   if (!std::isfinite(scale)) return QD_EINVAL;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(workspace, 16))
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
     return QD_EALIGN;
-  const int64_t need = attention_decode_workspace_bytes(heads, kv_heads, head_dim);
-  if ((int64_t)workspace_bytes < need) return QD_EINVAL;
+  need = attention_decode_workspace_bytes(heads, kv_heads, head_dim);
   const size_t qb = (size_t)heads * head_dim * 2;
   const size_t cb = (size_t)length * kv_heads * head_dim * 2;
   const void *ins[3] = {q, k_cache, v_cache};
   const size_t insz[3] = {qb, cb, cb};
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 3; ++i)
     if (overlap(out, qb, ins[i], insz[i])) return QD_EINVAL;
-    if (overlap(workspace, (size_t)need, ins[i], insz[i])) return QD_EINVAL;
-  }
-  if (overlap(out, qb, workspace, (size_t)need)) return QD_EINVAL;
-  qd_status st = check_device();
-  if (st != QD_OK) return st;
-  qd::AttentionArgs a = {};
+  a = {};
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k_cache;
   a.v = (const uint16_t *)v_cache;
   a.out = (uint16_t *)out;
-  a.part = (float *)workspace;
   a.heads = (int)heads;
   a.kv_heads = (int)kv_heads;
   a.head_dim = (int)head_dim;
@@ -667,7 +665,54 @@ qd_status attention_decode(const void *q, const void *k_cache, const void *v_cac
   a.pos_dev = nullptr;
   a.capacity = 0;
   a.qkr = nullptr;
+  return QD_OK;
+}
+
+extern "C" {
+
+qd_status attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                           int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t length,
+                           int64_t kv_start, float scale, int32_t f16, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (!workspace) return QD_EINVAL;
+  qd::AttentionArgs a;
+  int64_t need = 0;
+  qd_status st = attention_args(q, k_cache, v_cache, heads, kv_heads, head_dim, length,
+                                kv_start, scale, f16, out, a, need);
+  if (st != QD_OK) return st;
+  if (!aligned(workspace, 16)) return QD_EALIGN;
+  if ((int64_t)workspace_bytes < need) return QD_EINVAL;
+  const size_t qb = (size_t)heads * head_dim * 2;
+  const size_t cb = (size_t)length * kv_heads * head_dim * 2;
+  const void *ins[3] = {q, k_cache, v_cache};
+  const size_t insz[3] = {qb, cb, cb};
+  for (int i = 0; i < 3; ++i)
+    if (overlap(workspace, (size_t)need, ins[i], insz[i])) return QD_EINVAL;
+  if (overlap(out, qb, workspace, (size_t)need)) return QD_EINVAL;
+  st = check_device();
+  if (st != QD_OK) return st;
+  a.part = (float *)workspace;
   hipError_t e = qd::launch_attention_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status attention_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                   int64_t heads, int64_t kv_heads, int64_t head_dim,
+                                   int64_t length, int64_t kv_start, float scale, int32_t f16,
+                                   void *out, void *stream) {
+  qd::AttentionArgs a;
+  int64_t need = 0;
+  qd_status st = attention_args(q, k_cache, v_cache, heads, kv_heads, head_dim, length,
+                                kv_start, scale, f16, out, a, need);
+  if (st != QD_OK) return st;
+  if ((uint64_t)need > qd::attention_noalloc_scratch_bytes()) return QD_ESCRATCH;
+  st = check_device();
+  if (st != QD_OK) return st;
+  void *scratch = nullptr;
+  hipError_t e = qd::attention_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e);
+  a.part = (float *)scratch;
+  e = qd::launch_attention_decode(a, (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 

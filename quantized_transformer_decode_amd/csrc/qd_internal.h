@@ -120,6 +120,11 @@ AttentionPlan attention_plan(int64_t kv_heads, int64_t window, int head_dim);
 // Upper bound of nchunks over every window (host only).
 int64_t attention_max_chunks(int64_t kv_heads);
 hipError_t launch_attention_decode(const AttentionArgs &a, hipStream_t stream);
+// The library's static scratch for the chunk partials of the allocation-free
+// attention entry point: its size, and its address on the current device
+// (looked up once per device with hipGetSymbolAddress).
+size_t attention_noalloc_scratch_bytes();
+hipError_t attention_noalloc_scratch(void **ptr);
 
 // Small ops of the decoder step (decoder_ops.hip), f16 buffers, BF16 norm
 // weights.  add_rmsnorm: a = x, or f16(x + delta) stored to x_out (which may

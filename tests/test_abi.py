@@ -449,3 +449,32 @@ def test_qwen3_step_workspace_offsets():
     assert qd.qwen3_step_workspace_offset(_qwen3(hidden=1000), "q") == -1
     assert qd.lib().qwen3_step_workspace_offset(ctypes.byref(m), 10) == -1
     assert qd.lib().qwen3_step_workspace_offset(None, 0) == -1
+
+
+def test_errors_attention_decode_noalloc():
+    # the same host-side checks as attention_decode (no workspace), and
+    # QD_ESCRATCH for a head shape whose partials exceed the static scratch
+    f = "attention_decode_noalloc"
+
+    def call(q=A, k=B, v=C, heads=16, kvh=8, d=128, n=100, s=0, scale=0.088, f16=1, out=OUT):
+        return _call(f, q, k, v, heads, kvh, d, n, s, ctypes.c_float(scale), f16, out, None)
+
+    for bad in ({"q": None}, {"k": None}, {"v": None}, {"out": None}):
+        assert call(**bad) == qd.QD_EINVAL
+    assert call(f16=2) == qd.QD_EINVAL
+    assert call(heads=24) == qd.QD_ESHAPE
+    assert call(d=96) == qd.QD_ESHAPE
+    assert call(n=0) == qd.QD_EINVAL
+    assert call(s=100) == qd.QD_EINVAL
+    assert call(scale=float("nan")) == qd.QD_EINVAL
+    assert call(q=A + 8) == qd.QD_EALIGN
+    assert call(out=B + 4096) == qd.QD_EINVAL         # output inside the K cache
+    limit = 4 << 20
+    assert qd.attention_decode_workspace_bytes(1024, 128, 128) <= limit
+    assert call(heads=1024, kvh=128) == qd.QD_EDEVICE  # fits: stops at the device check
+    big = qd.attention_decode_workspace_bytes(8192, 1024, 128)
+    assert big > limit
+    assert call(heads=8192, kvh=1024) == qd.QD_ESCRATCH
+    assert qd.attention_decode_workspace_bytes(32768, 4096, 64) > limit
+    assert call(heads=32768, kvh=4096, d=64) == qd.QD_ESCRATCH
+    assert qd.lib().qd_status_string(qd.QD_ESCRATCH).startswith(b"QD_ESCRATCH")
