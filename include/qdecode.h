@@ -167,7 +167,7 @@ qd_status affine_i8_g64_embed_rows(const void *w_packed, int64_t rows, int64_t c
  * qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step. */
 typedef struct {
   const void *w_packed; /* device, affine blob [rows, cols], 16-byte aligned */
-  const void *x_bf16;   /* device, BF16 [m, cols], 2-byte aligned          */
+  const void *x_bf16;   /* device, BF16 [m, cols], 16-byte aligned         */
   void *y_bf16;         /* device, BF16 [m, rows], 2-byte aligned          */
   int64_t rows, cols;   /* rows >= 1; cols % 64 == 0, 64 <= cols <= 8192   */
   int64_t stage;
@@ -192,8 +192,8 @@ size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
  * returning.  Requirements beyond those of each op: m == 1; ops[0].stage ==
  * 0 and each op's stage equals its predecessor's or one more; ops of one
  * stage share cols; per stage sum(m*ceil(cols/1024)*1024) <= 16384 and
- * sum(m*cols) <= 64 * (compute units of the device) (QD_ESHAPE; the second
- * bound only binds on parts with fewer than 256 CUs); no op's output
+ * sum(m*cols) <= 128 * (compute units of the device) (QD_ESHAPE; the second
+ * bound only binds on parts with fewer than 128 CUs); no op's output
  * overlaps any op's weights or input, or the workspace (QD_EINVAL /
  * QD_ESHAPE / QD_EALIGN as for the single GEMV).  The workspace, weights and inputs must
  * stay valid while runs are in flight. */
@@ -206,7 +206,9 @@ qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
  * every workgroup must be able to be resident, so do not run it concurrently
  * with kernels that occupy whole CUs indefinitely).  Launches nothing else,
  * allocates nothing, and may be captured in a HIP graph.  Runs planned on
- * the same workspace must not overlap in time. */
+ * the same workspace must not overlap in time.  After a run that reported an
+ * error (qgemv_affine_i8_g64_step_check), plan again before the next run:
+ * the workspace's arrival counts no longer match. */
 qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream);
 
 /* Synchronises `stream`, reads the workspace's error word into *error_bits

@@ -9,15 +9,23 @@
 // stream never stops: compute waves load the next stage's weights into
 // registers before waiting for the current stage's input.
 //
-// Exchange between stages.  Inputs travel as tagged 32-bit words
-// (stage tag << 16 | BF16 bits) written through to the device coherence
-// point with agent-scope stores and polled with agent-scope loads, so one
-// store/load round trip carries both the data and the "ready" signal.  A
-// workgroup publishes its slice of stage s+1's inputs only after all of its
-// compute waves are done with stage s; a consumer therefore sees a complete
-// input only once every workgroup has finished stage s.  Tags are
-// (epoch + stage) mod 2^16 with the epoch advanced by the stage count per
-// launch, so a word left from the previous launch never matches.
+// Exchange between stages.  After all of its compute waves are done with
+// stage s, a workgroup stores its slice of stage s+1's input (dense words,
+// two BF16 each) with agent-scope stores, waits for their acknowledgement,
+// and arrives at the stage's barrier: one agent-scope atomic on the counter
+// of its group (workgroup b -> group b % 8, one group per XCD); the group's
+// last arrival increments the stage's global counter, and the last of those
+// writes the stage's tag into every workgroup's own 128-byte release line.
+// Each workgroup polls only its own line, then reads the inputs it needs
+// with agent-scope loads (all in flight at once).  No line is polled by
+// more than one workgroup and no counter takes more than 32 atomics per
+// stage: a single shared counter or flag array, polled by every workgroup,
+// measured about twice as slow per stage on this part.  Tags are epoch +
+// stage with the epoch advanced by the stage count per launch; counters
+// only grow (each launch adds the same amounts, so arrivals are counted
+// modulo the group sizes), so nothing is cleared between launches or graph
+// replays.  The first stage's input is read straight from the ops' inputs,
+// which are written before the launch.
 //
 // Workgroup layout: wave 0 is the poller (publishes, polls the next input
 // into LDS as fp32, hands it to the compute waves through an LDS flag);
@@ -74,6 +82,7 @@ constexpr int kPubRing = 32;  // stages of publish values kept in LDS ahead of u
 struct Shared {
   int xready;        // stages whose input is staged in LDS
   int done;          // compute-wave stage completions
+  int arrived;       // stages whose barrier this workgroup has arrived at
   uint32_t epoch;
   uint32_t pub[kPubRing][64];  // this workgroup's slice of stage s's input at [s % kPubRing]
 };
@@ -289,35 +298,56 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
     }
   };
 
-  // Two register groups in flight: while one is consumed the next is loading.
-  // The prefetch is issued unconditionally (at the end of the stream it
-  // re-reads the current group) so the wait before each consume is exact.
+  auto wait_arrived = [&](int t) {
+    unsigned spins = 0;
+    while (lds_ld(&sh->arrived) < t) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kLdsSpinLimit) {
+        if (lane == 0) atomicOr(err, 4u);
+        break;
+      }
+    }
+  };
+
+  // Two register groups: while one is consumed the next is loading.  Inside
+  // a stage the next group is issued before the current one is consumed.
+  // The first group of the next stage is issued only once this workgroup
+  // has arrived at that stage's barrier: the burst then drains while the
+  // barrier completes, instead of queueing in front of the loads on the
+  // hand-off's critical path (the input read, the arrival, the release
+  // poll), which this CU issues through the same memory pipeline.  Both
+  // paths compute in their own branch, so each waits for exactly the loads
+  // it consumes.
   Cursor c = normalize(stages, n_stages, Cursor{0, 0}, gw, nw);
+  auto run = [&](Group &cur, Group &nxt) -> bool {
+    const Cursor n1 = normalize(stages, n_stages, Cursor{c.s, c.i + G}, gw, nw);
+    if (n1.s == c.s) {
+      issue(nxt, ops, stages, n1, gw, nw, lane);
+      enter(c.s);
+      compute(cur, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
+    } else {
+      enter(c.s);
+      compute(cur, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
+      if (n1.s >= n_stages) return false;
+      signal_done_through(sh, signalled, n1.s);  // as soon as a stage is finished
+      wait_arrived(c.s + 1);
+      issue(nxt, ops, stages, n1, gw, nw, lane);
+    }
+    c = n1;
+    return true;
+  };
   if (c.s < n_stages) {
     issue(A, ops, stages, c, gw, nw, lane);
-    while (true) {
-      const Cursor n1 = normalize(stages, n_stages, Cursor{c.s, c.i + G}, gw, nw);
-      issue(B, ops, stages, n1.s < n_stages ? n1 : c, gw, nw, lane);
-      enter(c.s);
-      compute(A, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
-      if (n1.s >= n_stages) break;
-      signal_done_through(sh, signalled, n1.s);  // as soon as a stage is finished
-      c = n1;
-      const Cursor n2 = normalize(stages, n_stages, Cursor{c.s, c.i + G}, gw, nw);
-      issue(A, ops, stages, n2.s < n_stages ? n2 : c, gw, nw, lane);
-      enter(c.s);
-      compute(B, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
-      if (n2.s >= n_stages) break;
-      signal_done_through(sh, signalled, n2.s);
-      c = n2;
+    while (run(A, B) && run(B, A)) {
     }
   }
   signal_done_through(sh, signalled, n_stages);
 }
 
-// This workgroup's slice of a stage's inputs (all ops back to back, m*cols
-// words each): words [a, b) with a = j * 2^lg, at most 64 words, one per
-// lane.  Loaded ahead of time so the publish itself is a single store.
+// This workgroup's slice of a stage's input words (all ops back to back,
+// m*cols/2 words each, two BF16 per word): words [a, b) with a = j * 2^lg,
+// at most 64 words, one per lane.  Loaded ahead of time so that publishing
+// is an LDS read and a store.
 struct PubSlice {
   int a, b;
   uint32_t v;  // word a + lane
@@ -325,9 +355,10 @@ struct PubSlice {
 
 __device__ __forceinline__ uint32_t input_word(const StepOp *ops, const StepStage &st, int m,
                                                int i) {
-  const int w = m * st.cols;
+  const int w = m * st.cols / 2;  // words per op
   const int k = i / w;
-  return (uint32_t)gp(ops[st.op0 + k].x)[i - k * w];
+  const QD_GLOBAL uint32_t *x = (const QD_GLOBAL uint32_t *)gp(ops[st.op0 + k].x);
+  return x[i - k * w];
 }
 
 __device__ __forceinline__ PubSlice pub_load(const StepOp *ops, const StepStage &st, int m,
@@ -340,33 +371,21 @@ __device__ __forceinline__ PubSlice pub_load(const StepOp *ops, const StepStage 
   return p;
 }
 
-// Everything the poller needs to poll one stage's input and to publish its
-// own slice of it, resolved from the tables one stage ahead (scalar loads
-// are never on the critical path).
-constexpr int kReplicas = 8;  // copies of each published slice (one per XCD)
-
+// Everything the poller needs to read one stage's input and to publish its
+// own slice of it, resolved from the tables one stage ahead.
 struct StagePlan {
-  const uint64_t *src;  // this workgroup's replica of the staging, 64-bit words
-  uint32_t *stg;        // staging, as words (publishing)
-  int f0, f1;           // 64-bit words this workgroup polls: [f0, f1)
+  uint32_t *data;       // the stage's input words
+  int f0, f1;           // 64-bit words this workgroup reads: [f0, f1)
   int k0, k1;           // ops (within the stage) those words belong to
-  int wpo;              // words per op
+  int epo;              // input elements per op
   int xstride;          // LDS floats per op (whole 1024-column chunks)
   int pa, pb;           // this workgroup's published words [pa, pb)
-  int rstride;          // words between replicas
 };
 
 __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepStage &st, int m) {
   StagePlan p;
-  // replicas are spaced by one 64-word line per slice; within a replica the
-  // words are dense (word i at offset i)
-  const int nsl = ((int)st.words + (1 << st.lg) - 1) >> st.lg;
-  p.rstride = nsl * 64;
-  // workgroups are dispatched round-robin over the XCDs: blockIdx % 8 reads
-  // the replica that only the workgroups of its own XCD read
-  p.src = (const uint64_t *)(st.stg + (blockIdx.x % kReplicas) * p.rstride);
-  p.stg = st.stg;
-  p.wpo = m * st.cols;
+  p.data = st.data;
+  p.epo = m * st.cols;
   p.xstride = st.chunks * 1024;
   int lo, hi, lo2, hi2;
   wave_rows(st, blockIdx.x * NCW, gridDim.x * NCW, lo, hi);
@@ -377,99 +396,132 @@ __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepSta
   } else {
     p.k0 = op_of_row(ops, st, lo) - st.op0;
     p.k1 = op_of_row(ops, st, hi2 - 1) - st.op0;
-    p.f0 = (p.k0 * p.wpo) >> 1;
-    p.f1 = ((p.k1 + 1) * p.wpo) >> 1;
+    p.f0 = (p.k0 * p.epo) >> 2;
+    p.f1 = ((p.k1 + 1) * p.epo) >> 2;
   }
   p.pa = (int)blockIdx.x << st.lg;
   p.pb = min(p.pa + (1 << st.lg), (int)st.words);
   return p;
 }
 
-// Poll the part of a stage's input that this workgroup needs (the inputs of
-// the ops its compute waves touch) into LDS as fp32; returns false on
-// time-out.  Up to B 64-bit words per lane are in flight per batch.
-__device__ bool poll_stage(const StagePlan &pp, uint32_t tag, float *dst, int lane,
-                           bool aborted) {
-  constexpr int B = 24;
-  bool ok = true;
-  for (int base = pp.f0; base < pp.f1; base += 64 * B) {
-    uint64_t v[B];
-    unsigned polls = 0;
-    while (true) {
+// Four input elements (one 64-bit word) into LDS as fp32 (xswz layout).
+__device__ __forceinline__ void stage4(const StagePlan &pp, float *dst, int f, uint64_t v) {
+  // elements 4f .. 4f+3 lie in one op (each op's input is a multiple of 64
+  // elements) and land as one float4
+  const int e = 4 * f;
+  int k = pp.k0;
+  while (k < pp.k1 && e >= (k + 1) * pp.epo) ++k;
+  const int r = e - k * pp.epo;
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  *(float4 *)(dst + k * pp.xstride + xswz(r)) =
+      make_float4(bf16_to_f32(lo & 0xffffu), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffffu),
+                  bf16_to_f32(hi >> 16));
+}
+
+// A released stage input into LDS: agent-scope loads of the published
+// words (every load of an op in flight at once), then each lane's 64-bit
+// words go to LDS as float4s.  Lane l takes words l, l + 64, ... of each
+// op, so its LDS addresses advance by a constant: no per-element search.
+__device__ void read_stage(const StagePlan &pp, float *dst, int lane) {
+  constexpr int B = 16;
+  const uint64_t *src = (const uint64_t *)pp.data;
+  const int wpo = pp.epo >> 2;  // 64-bit words per op (a multiple of 16)
+  for (int k = pp.k0; k <= pp.k1; ++k) {
+    const uint64_t *op = src + (size_t)k * wpo;
+    float *od = dst + k * pp.xstride;
+    for (int base = 0; base < wpo; base += 64 * B) {
+      uint64_t v[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) v[b] = ld_agent64(op + min(base + b * 64 + lane, wpo - 1));
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        // only words in range are loaded: clamping the rest to one address
-        // would pile every lane's extra loads onto a single cache line
         const int f = base + b * 64 + lane;
-        v[b] = f < pp.f1
-                   ? ld_agent64(pp.src + f)
-                   : ((uint64_t)tag << 48) | ((uint64_t)tag << 16);
-      }
-      bool ready = true;
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-        ready &= ((uint32_t)(v[b] >> 16) & 0xffffu) == tag &&
-                 ((uint32_t)(v[b] >> 48) & 0xffffu) == tag;
-      if (__all(ready) || aborted) break;
-      if (++polls > kPollLimit) { ok = false; break; }
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const int f = base + b * 64 + lane;
-      if (f < pp.f1) {
-        // words 2f, 2f+1 belong to one op (each op's input has an even
-        // length) and to the same swizzled float pair
-        const int e = 2 * f;
-        int k = pp.k0;  // the op holding word e (no division: ops are few)
-        while (k < pp.k1 && e >= (k + 1) * pp.wpo) ++k;
-        const int r = e - k * pp.wpo;
-        *(float2 *)(dst + k * pp.xstride + xswz(r)) =
-            make_float2(bf16_to_f32((uint32_t)v[b] & 0xffffu),
-                        bf16_to_f32((uint32_t)(v[b] >> 32) & 0xffffu));
+        if (f < wpo) {
+          const uint32_t lo = (uint32_t)v[b], hi = (uint32_t)(v[b] >> 32);
+          *(float4 *)(od + xswz(4 * f)) =
+              make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
+        }
       }
     }
-    if (!ok) return false;
   }
-  return true;
+}
+
+// The first stage's input, straight from the ops' inputs (written before
+// the launch).
+__device__ void read_first_stage(const StagePlan &pp, const StepOp *ops, const StepStage &st,
+                                 float *dst, int lane) {
+  for (int f = pp.f0 + lane; f < pp.f1; f += 64) {
+    const int e = 4 * f, k = e / pp.epo;
+    stage4(pp, dst, f, *(const QD_GLOBAL uint64_t *)(gp(ops[st.op0 + k].x) + (e - k * pp.epo)));
+  }
+}
+
+// Arrival at the barrier that releases stage s's input: after this
+// workgroup's slice is stored (and acknowledged), one agent-scope atomic on
+// its group's counter; the group's last arrival adds one to the stage's
+// global counter, and the last of those writes the stage's tag into every
+// workgroup's release line.  Counters only grow, so "last" is taken modulo
+// the number of arrivals a launch makes.
+__device__ __forceinline__ void arrive(uint32_t *ctr, uint32_t *rel, int s, uint32_t tag,
+                                       int lane) {
+  const int nwg = gridDim.x;
+  const int g = blockIdx.x % kStepGroups;
+  const unsigned gsz = (unsigned)((nwg - g + kStepGroups - 1) / kStepGroups);
+  unsigned release = 0;
+  if (lane == 0) {
+    uint32_t *line = ctr + (size_t)(s * (kStepGroups + 1) + g) * kStepLine;
+    const unsigned old = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if ((old + 1u) % gsz == 0u) {
+      uint32_t *gl = ctr + (size_t)(s * (kStepGroups + 1) + kStepGroups) * kStepLine;
+      const unsigned o2 = __hip_atomic_fetch_add(gl, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+      release = (o2 + 1u) % (unsigned)kStepGroups == 0u ? 1u : 0u;
+    }
+  }
+  if (__builtin_amdgcn_readfirstlane(release))
+    for (int k = lane; k < nwg; k += kWave) st_agent(rel + (size_t)k * kStepLine, tag);
 }
 
 __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
                             int n_stages, int m, Shared *sh, float *xbuf, int xmax,
-                            uint32_t *err) {
+                            uint32_t *rel, uint32_t *ctr, uint32_t *err) {
   const int lane = threadIdx.x & 63;
   const uint32_t epoch = sh->epoch;
+  const uint32_t *myrel = rel + (size_t)blockIdx.x * kStepLine;
   // after a first time-out this workgroup stops waiting, so a broken run
   // still ends quickly (with the error word set)
   bool aborted = false;
   // The values this workgroup publishes come from the resident inputs; they
   // are loaded kPubRing stages ahead into an LDS ring so that publishing is
   // an LDS read and a store, never a wait on memory.
-  for (int t = 0; t < kPubRing && t < n_stages; ++t) {
+  for (int t = 1; t < kPubRing && t < n_stages; ++t) {
     const PubSlice p = pub_load(ops, stages[t], m, lane);
     sh->pub[t][lane] = p.v;
-  }
-  {
-    const PubSlice p0 = pub_load(ops, stages[0], m, lane);
-    const StagePlan q0 = stage_plan(ops, stages[0], m);
-    if (p0.a + lane < p0.b) {
-      const uint32_t w = ((epoch & 0xffffu) << 16) | p0.v;
-#pragma unroll
-      for (int r = 0; r < kReplicas; ++r)
-        st_agent(q0.stg + r * q0.rstride + q0.pa + lane, w);
-    }
   }
   PubSlice pending;
   int pending_stage = -1;
   StagePlan cur = stage_plan(ops, stages[0], m);
   StagePlan nxt = cur;
   for (int s = 0; s < n_stages; ++s) {
-    const uint32_t tag = (epoch + (uint32_t)s) & 0xffffu;
+    const uint32_t tag = epoch + (uint32_t)s;
     // park the value loaded one stage ago (long since arrived)
     if (pending_stage >= 0) sh->pub[pending_stage % kPubRing][lane] = pending.v;
-    if (!poll_stage(cur, tag, xbuf + (s & 1) * xmax, lane, aborted)) {
-      if (lane == 0) atomicOr(err, 1u);
-      aborted = true;
+    if (s > 0 && !aborted) {
+      unsigned polls = 0;
+      while (__builtin_amdgcn_readfirstlane(ld_agent(myrel)) != tag) {
+        if (++polls > kPollLimit) {
+          if (lane == 0) atomicOr(err, 1u);
+          aborted = true;
+          break;
+        }
+      }
     }
+    if (s == 0)
+      read_first_stage(cur, ops, stages[0], xbuf, lane);
+    else
+      read_stage(cur, xbuf + (s & 1) * xmax, lane);
     // hand the staged input to the compute waves (LDS executes this wave's
     // data writes before the flag write)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -494,13 +546,16 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
       }
     }
     if (s + 1 < n_stages) {
-      const uint32_t t1 = ((epoch + (uint32_t)s + 1) & 0xffffu) << 16;
-      if (nxt.pa + lane < nxt.pb) {
-        const uint32_t w = t1 | sh->pub[(s + 1) % kPubRing][lane];
-#pragma unroll
-        for (int r = 0; r < kReplicas; ++r)
-          st_agent(nxt.stg + r * nxt.rstride + nxt.pa + lane, w);
-      }
+      if (nxt.pa + lane < nxt.pb)
+        st_agent(nxt.data + nxt.pa + lane, sh->pub[(s + 1) % kPubRing][lane]);
+      // the slice is acknowledged (visible device-wide) before the arrival
+      // that may release it
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      arrive(ctr, rel, s + 1, tag + 1u, lane);
+      // the compute waves may now issue the next stage's weights
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0) __hip_atomic_store(&sh->arrived, s + 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     cur = nxt;
   }
@@ -508,7 +563,8 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
 
 __global__ __launch_bounds__(kThreads) void affine_step_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
-    int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ err) {
+    int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
+    uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
   if ((int)gridDim.x != nwg) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, 8u);
     return;
@@ -518,11 +574,12 @@ __global__ __launch_bounds__(kThreads) void affine_step_kernel(
   if (threadIdx.x == 0) {
     sh.xready = 0;
     sh.done = 0;
+    sh.arrived = 0;
     sh.epoch = ld_agent(epoch_word);
   }
   __syncthreads();
   if (threadIdx.x < kWave)
-    poller_wave(ops, stages, n_stages, m, &sh, xbuf, xmax, err);
+    poller_wave(ops, stages, n_stages, m, &sh, xbuf, xmax, rel, ctr, err);
   else
     compute_wave(ops, stages, n_stages, &sh, xbuf, xmax, err);
   __syncthreads();
@@ -534,8 +591,9 @@ __global__ __launch_bounds__(kThreads) void affine_step_kernel(
 int step_threads() { return kThreads; }
 
 hipError_t launch_affine_step(const StepOp *ops, const StepStage *stages, int n_stages, int m,
-                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *err,
-                              size_t lds_bytes, hipStream_t stream) {
+                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel,
+                              uint32_t *ctr, uint32_t *err, size_t lds_bytes,
+                              hipStream_t stream) {
   if (lds_bytes > 65536) {
     hipError_t e = hipFuncSetAttribute((const void *)affine_step_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -543,7 +601,7 @@ hipError_t launch_affine_step(const StepOp *ops, const StepStage *stages, int n_
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(affine_step_kernel, dim3(nwg), dim3(kThreads), lds_bytes, stream, ops,
-                     stages, n_stages, m, xmax, nwg, epoch_word, err);
+                     stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
   return hipGetLastError();
 }
 

@@ -99,18 +99,14 @@ bool affine_shape_ok(int64_t rows, int64_t cols) {
 
 constexpr int kMaxStageWords = 16384;  // LDS: two fp32 copies of a stage input
 constexpr int kMinStepWgs = 32;        // smallest grid a plan supports
-constexpr int kStepReplicas = 8;       // copies of each published slice (kernel's kReplicas)
-
-// log2 of the slice length for a stage input of `words` words over `nwg`
-// publishers: the smallest power of two >= ceil(words / nwg), within [2, 64].
+// log2 of the slice length for a stage input of `words` 32-bit words over
+// `nwg` publishers: the smallest power of two >= ceil(words / nwg), within
+// [1, 64] words (one per lane of the publishing wave).
 int step_lg(int64_t words, int nwg) {
   const int64_t per = (words + nwg - 1) / nwg;
   int lg = 1;
   while ((int64_t(1) << lg) < per) ++lg;
   return lg;
-}
-int64_t step_slices(int64_t words, int nwg) {
-  return (words + (int64_t(1) << step_lg(words, nwg)) - 1) >> step_lg(words, nwg);
 }
 constexpr int64_t kMaxStepOps = 65536;
 
@@ -127,7 +123,7 @@ qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
     if (!o.w_packed || !o.x_bf16 || !o.y_bf16) return QD_EINVAL;
     if (o.rows < 1 || o.rows > kMaxRows || o.cols < 1) return QD_EINVAL;
     if (o.cols % 64 != 0 || o.cols > kMaxGemvCols) return QD_ESHAPE;
-    if (!aligned(o.w_packed, 16) || !aligned(o.x_bf16, 2) || !aligned(o.y_bf16, 2))
+    if (!aligned(o.w_packed, 16) || !aligned(o.x_bf16, 16) || !aligned(o.y_bf16, 2))
       return QD_EALIGN;
     if (i == 0) {
       if (o.stage != 0) return QD_EINVAL;
@@ -164,29 +160,31 @@ qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
   return QD_OK;
 }
 
-// Staging bytes for a grid of nwg workgroups: per stage and replica, room for
-// one 256-byte line per slice of 2^lg words (the words themselves are
-// stored densely at the start of that room).
-// Each workgroup publishes at most 64 words of a stage's input (one per
-// lane), so a stage input may hold at most 64 words per workgroup.
+// Each workgroup publishes at most 64 words (128 BF16 values) of a stage's
+// input, one per lane, so a stage input may hold at most 128 values per
+// workgroup.
 bool step_fits_grid(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
   int64_t i = 0;
   while (i < n_ops) {
-    int64_t j = i, words = 0;
-    while (j < n_ops && ops[j].stage == ops[i].stage) words += m * ops[j++].cols;
-    if (words > (int64_t)64 * nwg) return false;
+    int64_t j = i, values = 0;
+    while (j < n_ops && ops[j].stage == ops[i].stage) values += m * ops[j++].cols;
+    if (values > (int64_t)128 * nwg) return false;
     i = j;
   }
   return true;
 }
 
-size_t step_staging_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
-  size_t bytes = 0;
+// Bytes after the tables: one release line per workgroup, the arrival
+// counter lines, and each stage's dense input (256-byte aligned).
+size_t step_exchange_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg,
+                           int n_stages) {
+  size_t bytes = align256((size_t)nwg * 128) +
+                 align256((size_t)n_stages * (qd::kStepGroups + 1) * 128);
   int64_t i = 0;
   while (i < n_ops) {
-    int64_t j = i, words = 0;
-    while (j < n_ops && ops[j].stage == ops[i].stage) words += m * ops[j++].cols;
-    bytes += (size_t)step_slices(words, nwg) * 256 * kStepReplicas;
+    int64_t j = i, values = 0;
+    while (j < n_ops && ops[j].stage == ops[i].stage) values += m * ops[j++].cols;
+    bytes += align256((size_t)values * 2);
     i = j;
   }
   return bytes;
@@ -481,7 +479,7 @@ size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
   if (check_device() != QD_OK) return 0;
   const int nwg = current_cus();
   if (nwg < kMinStepWgs || !step_fits_grid(ops, n_ops, m, nwg)) return 0;
-  return bytes + step_staging_bytes(ops, n_ops, m, nwg);
+  return bytes + step_exchange_bytes(ops, n_ops, m, nwg, ns);
 }
 
 qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
@@ -507,15 +505,18 @@ qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
   const int nwg = current_cus();
   if (nwg < kMinStepWgs) return QD_EDEVICE;
   if (!step_fits_grid(ops, n_ops, m, nwg)) return QD_ESHAPE;
-  need += step_staging_bytes(ops, n_ops, m, nwg);
+  need += step_exchange_bytes(ops, n_ops, m, nwg, ns);
   if (workspace_bytes < need) return QD_EINVAL;
 
-  // host image of header + tables; staging words start zeroed (tag 0 is
-  // never expected: the epoch starts at 1)
+  // host image of header + tables; release lines and counters start zeroed
+  // (tag 0 is never expected: the epoch starts at 1)
   const size_t ops_off = sizeof(qd::StepHeader);
   const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * n_ops);
-  const size_t stg_off = stages_off + align256(sizeof(qd::StepStage) * ns);
-  std::vector<uint8_t> img(stg_off, 0);
+  const size_t rel_off = stages_off + align256(sizeof(qd::StepStage) * ns);
+  const size_t ctr_off = rel_off + align256((size_t)nwg * 128);
+  const size_t data_off = ctr_off + align256((size_t)ns * (qd::kStepGroups + 1) * 128);
+  const size_t stg_off = rel_off;
+  std::vector<uint8_t> img(rel_off, 0);
   qd::StepHeader *h = (qd::StepHeader *)img.data();
   qd::StepOp *dops = (qd::StepOp *)(img.data() + ops_off);
   qd::StepStage *dst = (qd::StepStage *)(img.data() + stages_off);
@@ -527,32 +528,35 @@ qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
   h->xmax = xmax;
   h->ops_off = (uint32_t)ops_off;
   h->stages_off = (uint32_t)stages_off;
+  h->rel_off = (uint32_t)rel_off;
+  h->ctr_off = (uint32_t)ctr_off;
+  h->data_off = (uint32_t)data_off;
   h->lds_bytes = (uint32_t)(2 * (size_t)xmax * 4);
   h->epoch = 1;
   h->error = 0;
-  size_t stg = stg_off;
+  size_t data = data_off;
   int s = -1;
   for (int64_t i = 0; i < n_ops; ++i) {
     const qd_affine_gemv_op &o = ops[i];
     if ((int)o.stage != s) {
       s = (int)o.stage;
-      int64_t words = 0;
-      for (int64_t j = i; j < n_ops && ops[j].stage == o.stage; ++j) words += m * ops[j].cols;
-      dst[s].stg = (uint32_t *)((uint8_t *)workspace + stg);
+      int64_t values = 0;
+      for (int64_t j = i; j < n_ops && ops[j].stage == o.stage; ++j) values += m * ops[j].cols;
+      dst[s].data = (uint32_t *)((uint8_t *)workspace + data);
       dst[s].op0 = (int32_t)i;
       dst[s].nops = 0;
       dst[s].rows_total = 0;
       dst[s].cols = (int32_t)o.cols;
       dst[s].chunks = (int32_t)((o.cols + 1023) / 1024);
-      dst[s].words = (uint16_t)words;
-      dst[s].lg = (uint16_t)step_lg(words, nwg);
-      stg += (size_t)step_slices(words, nwg) * 256 * kStepReplicas;
+      dst[s].words = (uint16_t)(values / 2);
+      dst[s].lg = (uint16_t)step_lg(values / 2, nwg);
+      data += align256((size_t)values * 2);
     }
     qd::StepOp &d = dops[i];
     d.w = (const uint8_t *)o.w_packed;
     d.x = (const uint16_t *)o.x_bf16;
     d.y = (uint16_t *)o.y_bf16;
-    d.stg = (uint32_t *)((uint8_t *)workspace + stg);
+    d.unused = nullptr;
     d.rows = (int32_t)o.rows;
     d.cols = (int32_t)o.cols;
     d.stage = s;
@@ -589,9 +593,12 @@ qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream) {
   const size_t ops_off = sizeof(qd::StepHeader);
   const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * plan->n_ops);
   qd::StepHeader *h = (qd::StepHeader *)ws;  // device address; never dereferenced here
+  const size_t rel_off = stages_off + align256(sizeof(qd::StepStage) * plan->n_stages);
+  const size_t ctr_off = rel_off + align256((size_t)plan->nwg * 128);
   hipError_t e = qd::launch_affine_step(
       (const qd::StepOp *)(ws + ops_off), (const qd::StepStage *)(ws + stages_off),
-      plan->n_stages, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch, &h->error,
+      plan->n_stages, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch,
+      (uint32_t *)(ws + rel_off), (uint32_t *)(ws + ctr_off), &h->error,
       (size_t)plan->lds_bytes, (hipStream_t)stream);
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }

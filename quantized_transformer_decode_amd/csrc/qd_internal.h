@@ -154,7 +154,8 @@ struct StepOp;
 struct StepStage;
 int step_threads();
 hipError_t launch_affine_step(const StepOp *ops, const StepStage *stages, int n_stages, int m,
-                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *err,
-                              size_t lds_bytes, hipStream_t stream);
+                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel,
+                              uint32_t *ctr, uint32_t *err, size_t lds_bytes,
+                              hipStream_t stream);
 
 }  // namespace qd
