@@ -7,148 +7,92 @@
 // one block's partial product P exactly up to fp32 accumulation; the f16
 // delta is applied to P in fp32 (rounding d*(q-8) to BF16 instead would cost
 // up to 2^-9 relative error per weight).  One fp32 multiply-add per output
-// per block is exactly the VALU rate that matches the MFMA rate, so the
-// kernel interleaves the MFMAs of block b with the delta scaling of block
-// b-1's partial products.
+// per block matches the MFMA's own rate; the VALU does it for block b-1
+// while the matrix core runs block b.  (Splitting each weight into two exact
+// BF16 halves instead doubles the MFMAs and the LDS reads per output, and
+// measured slower.)
 //
-// Up to four products that share x go in one launch (the q/k/v of a layer,
-// 3 x 1280 output columns instead of 1280): their column tiles are numbered
-// back to back and each workgroup looks up its matrix.  The q_linear
-// epilogue (f32 bias, gelu_tanh for fc1) is applied at the store.
+// Up to four products that share x go in one launch (the q/k/v of a layer):
+// their column tiles are numbered back to back and each workgroup looks up
+// its matrix.  The q_linear epilogue (f32 bias, gelu_tanh for fc1) is
+// applied at the store.
 //
-// Tiling: a 256-thread workgroup owns a BM (frames) x BN (weight rows)
-// output tile, 64 x 64 by default; its four waves are 2 x 2, each
-// BM/2 x BN/2.  Each LDS stage covers 128 columns of K (four Q4_0 blocks):
-// x [BM][128] BF16 and the dequantised codes [BN][128] BF16, rows padded by
-// 16 bytes so the 16 rows a fragment read touches fall in different banks;
-// the deltas [BN][4] fp32.  Stages are double-buffered: the global loads of
-// stage s+1 are in flight while stage s is computed.  64 x 64 tiles give
-// ~2 workgroups per CU on a 1500 x 1280 output (the LDS, 70 KiB per
-// workgroup, allows two) -- larger tiles leave the chip underfilled at
-// Whisper-large shapes and smaller ones repeat the dequantisation.
+// Tiling.  A workgroup owns a (32 x WAVES) frames x 64 weight rows output
+// tile; wave w owns frames 32w..32w+31 and all 64 rows (2 x 4 MFMA tiles).
+// The waves split the frames only, so each wave's x tile is its own: it is
+// loaded in whole cache lines and re-read from a wave-private LDS tile in
+// fragment order.  The 64 rows' codes are shared: each stage (128
+// columns of K = four Q4_0 blocks) the workgroup converts the raw blocks
+// once into exact BF16 codes in LDS ([64][128 + 8], the padding spreading a
+// fragment read's 16 rows over all banks) with the deltas in fp32
+// ([64][4]), and every wave reads its B fragments there.
+//
+// Pipeline, one barrier per stage.  After the barrier of stage s, a wave
+// issues the loads of its x tile of stage s+1 and of the raw blocks of stage
+// s+2 (two register sets of these; the loop is unrolled twice so that no set
+// is copied), computes stage s from its x tile in LDS and codes buffer s%2
+// while converting the raw blocks of stage s+1 into the other buffer (which
+// the barrier has just freed: every wave is past stage s-1), and finally
+// stores the x tile of stage s+1 over its own.
 #include "qd_device.h"
 #include "qd_internal.h"
-
-#ifndef QD_GEMM_BM
-#define QD_GEMM_BM 64
-#define QD_GEMM_BN 64
-#endif
 
 namespace qd {
 namespace {
 
-constexpr int kThreads = 256;
-#ifndef QD_GEMM_BK
-#define QD_GEMM_BK 128
-#endif
-constexpr int BK = QD_GEMM_BK;          // K columns per stage
-constexpr int NB = BK / 32;             // Q4_0 blocks per stage
-constexpr int CPR = BK / 8;             // 16-byte x chunks per tile row per stage
-constexpr int LDA = BK + 8;             // LDS row stride in bf16
-
-template <int BM, int BN>
-struct Tile {
-  static constexpr int A_ELEMS = BM * LDA;
-  static constexpr int B_ELEMS = BN * LDA;
-  static constexpr int STAGE_BYTES = (A_ELEMS + B_ELEMS) * 2 + BN * NB * 4;
-  static constexpr int TM = BM / 32;    // 16x16 MFMA tiles per wave along M
-  static constexpr int TN = BN / 32;    // ... along N (waves are 2 x 2)
-  static constexpr int XCH = BM * CPR / kThreads;  // x 16-byte chunks per thread
-  static constexpr int WB = BN * NB / kThreads;   // weight blocks per thread (<= 1)
-};
+constexpr int BN = 64;                 // weight rows per workgroup tile
+constexpr int BK = 128;                // K columns per stage
+constexpr int NB = BK / 32;            // Q4_0 blocks per stage
+constexpr int LDB = BK + 8;            // codes row stride in BF16 (272 bytes)
+constexpr int TM = 2, TN = 4;          // 16 x 16 MFMA tiles per wave
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 
-// (q - 8) of four nibbles (one nibble per byte of `v`, bytes in element
-// order) as four BF16 in two dwords: small integers are exact in BF16.
-__device__ __forceinline__ u32x2v codes4_bf16(uint32_t v) {
-  const floatx4 f = {ubyte<0>(v) - 8.f, ubyte<1>(v) - 8.f, ubyte<2>(v) - 8.f,
-                     ubyte<3>(v) - 8.f};
+// (q - 8) of four nibbles (one per byte of `n`, bytes in element order) as
+// four BF16 in two dwords.  Byte k is placed in the mantissa of 2^23
+// (v_perm_b32: bits 0x4b0000qq = 2^23 + q exactly), 2^23 + 8 is subtracted
+// exactly, and the small integer converts exactly to BF16.
+__device__ __forceinline__ u32x2v codes4_bf16(uint32_t n) {
+  floatx4 f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    f[k] = __builtin_bit_cast(float, __builtin_amdgcn_perm(0x4b000000u, n, 0x070c0c00u | k)) -
+           8388616.0f;
   return __builtin_bit_cast(u32x2v, __builtin_convertvector(f, bf16x4));
 }
 
-template <int BM, int BN>
-struct Stage {
-  uint4 xa[Tile<BM, BN>::XCH];  // this thread's x chunks (16 bytes each)
-  uint32_t w[5];                // this thread's Q4_0 block window
-  uint32_t fb;                  // flat index parity | 2 if the row is past the end
-  bool has_w;                   // this thread loads a weight block
+// This wave's LDS writes complete, then a workgroup barrier.  No release
+// fence: a fence would also wait for the global loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One stage of this wave's 32 frames in flight: load j brings frames
+// 4j..4j+3, 256 bytes each (16 lanes per frame).
+struct XRegs {
+  u32x4 a[8];
+};
+// The 20-byte window around the Q4_0 block this thread converts.
+struct RawRegs {
+  u32x4 w4;
+  uint32_t w1;
 };
 
-// Global loads of one stage: x rows m0.., columns k0..k0+127; the weight
-// block (row n0 + tid/NB, block kb0 + tid%NB).
-template <int BM, int BN>
-__device__ __forceinline__ void stage_load(Stage<BM, BN> &st, const QD_GLOBAL uint16_t *x,
-                                           const QD_GLOBAL uint8_t *w, int m, int rows,
-                                           int cols, int m0, int n0, int kb0, int tid) {
-#pragma unroll
-  for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
-    const int c = tid + i * kThreads;  // 16-byte chunk of the BM x 2*BK-byte tile
-    const int r = c / CPR, ch = c % CPR;
-    // frames past m read frame m-1: they only feed output rows that are
-    // never stored
-    const int row = min(m0 + r, m - 1);
-    const u32x4 v = *(const QD_GLOBAL u32x4 *)(x + (size_t)row * cols + kb0 * 32 + ch * 8);
-    st.xa[i] = make_uint4(v.x, v.y, v.z, v.w);
-  }
-  st.has_w = tid < BN * NB;
-  const int r = (tid / NB) % BN, b = tid % NB;
-  int n = n0 + r;
-  if (n >= rows) n = rows - 1;  // clamped rows are zeroed at the store
-  const size_t flat = (size_t)n * (cols >> 5) + kb0 + b;
-  // 20-byte window holding the block's 18 bytes: starts 2 bytes early for
-  // odd flat indices (still inside the previous block) and on the block for
-  // even ones (the 2 bytes past it exist: an even block is never the last
-  // one, the block count per row being a multiple of 8)
-  const QD_GLOBAL uint32_t *p =
-      (const QD_GLOBAL uint32_t *)(w + 18 * flat - 2 * (flat & 1));
-#pragma unroll
-  for (int i = 0; i < 5; ++i) st.w[i] = p[i];
-  st.fb = (uint32_t)(flat & 1) | (n0 + r >= rows ? 2u : 0u);
-}
+template <int WAVES, bool MULTI, bool EPI>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void q4_0_gemm_kernel(
+    const Q40Group grp, int cols, const uint16_t *__restrict__ x, int m) {
+  constexpr int THREADS = WAVES * 64;
+  constexpr int BM = WAVES * 32;
+  constexpr int H = THREADS / (BN * NB);  // threads per block of a stage: 1 or 2
+  static_assert(H == 1 || H == 2, "one block or half a block per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t codes[2][BN * LDB];
+  __shared__ __attribute__((aligned(16))) float deltas[2][BN * NB];
+  // each wave's x tile of the current stage: 32 frames x 16 chunks of 8
+  // BF16, chunk c of frame r stored at position c ^ (r % 16)
+  __shared__ __attribute__((aligned(16))) u32x4 xs[WAVES][32 * 16];
 
-template <int BM, int BN>
-__device__ __forceinline__ void stage_store(const Stage<BM, BN> &st, uint16_t *As, uint16_t *Bs,
-                                            float *Ds, int tid) {
-#pragma unroll
-  for (int i = 0; i < Tile<BM, BN>::XCH; ++i) {
-    const int c = tid + i * kThreads;
-    const int r = c / CPR, ch = c % CPR;
-    *(uint4 *)(As + r * LDA + ch * 8) = st.xa[i];
-  }
-  if (!st.has_w) return;
-  const int r = tid / NB, b = tid % NB;
-  const bool odd = st.fb & 1, dead = st.fb & 2;
-  // d: bytes 0-1 of the block; nibble bytes 2..17
-  const uint32_t dbits = odd ? (st.w[0] >> 16) : (st.w[0] & 0xffffu);
-  uint32_t nib[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    nib[k] = odd ? st.w[k + 1] : __builtin_amdgcn_alignbyte(st.w[k + 1], st.w[k], 2);
-  uint32_t lo[8], hi[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // dword k: elements 4k..4k+3 in the low nibbles, 16+4k.. in the high
-    const uint32_t v = dead ? 0x88888888u : nib[k];
-    const u32x2v cl = codes4_bf16(v & 0x0f0f0f0fu), ch = codes4_bf16((v >> 4) & 0x0f0f0f0fu);
-    lo[2 * k] = cl.x;
-    lo[2 * k + 1] = cl.y;
-    hi[2 * k] = ch.x;
-    hi[2 * k + 1] = ch.y;
-  }
-  uint4 *dst = (uint4 *)(Bs + r * LDA + b * 32);
-  dst[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);  // elements 0..7
-  dst[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);  // 8..15
-  dst[2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);  // 16..23
-  dst[3] = make_uint4(hi[4], hi[5], hi[6], hi[7]);  // 24..31
-  Ds[r * NB + b] = dead ? 0.f : f16_to_f32(dbits);
-}
-
-template <int BM, int BN, bool MULTI, bool EPI>
-__global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
-    const Q40Group grp, int cols, const uint16_t *__restrict__ x_, int m) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // this workgroup's matrix: column tiles are numbered back to back (a
   // single matrix takes its descriptor at fixed offsets)
   const int bx = blockIdx.x;
@@ -159,25 +103,95 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
       if (i < grp.n && bx >= grp.tile0[i]) k = i;
     k = uni(k);
   }
-  const QD_GLOBAL uint8_t *w = gp(grp.w[k]);
+  const uint8_t *w = grp.w[k];
   const int rows = grp.rows[k];
   QD_GLOBAL float *y = gp(grp.y[k]);
   const float *bias = grp.bias[k];
-  const QD_GLOBAL uint16_t *x = gp(x_);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uni(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM;
   const int n0 = (bx - grp.tile0[k]) * BN;
   const int nstages = cols / BK;
+  const int nb = cols >> 5;  // Q4_0 blocks per weight row (a multiple of 8)
+  const int mrem = min(m - m0, BM), rrem = min(rows - n0, BN);
 
-  using T = Tile<BM, BN>;
-  constexpr int TM = T::TM, TN = T::TN;
-  auto As = [&](int buf) { return (uint16_t *)(smem + buf * T::STAGE_BYTES); };
-  auto Bs = [&](int buf) { return (uint16_t *)(smem + buf * T::STAGE_BYTES) + T::A_ELEMS; };
-  auto Ds = [&](int buf) {
-    return (float *)(smem + buf * T::STAGE_BYTES + (T::A_ELEMS + T::B_ELEMS) * 2);
+  // Buffer descriptors over this tile's frames and weight rows; per-stage
+  // offsets go in the scalar offset, so the loads take no vector address
+  // arithmetic.
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(x + (size_t)m0 * cols), 0, mrem * cols * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(w + (size_t)n0 * nb * 18), 0, rrem * nb * 18, kRsrcWord3);
+  const int kc = lane >> 4;  // this lane's chunk (8 K indices) of a block
+  // x loads cover whole cache lines: lane l of load j reads chunk l % 16
+  // of frame 4j + l / 16 (a fragment-shaped load would touch 16 frames'
+  // half lines per instruction, twice the line traffic of the memory
+  // pipeline); frames past m read the tile's last frame: they only feed
+  // outputs never stored
+  int xoff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = min(wave * 32 + 4 * j + (lane >> 4), mrem - 1);
+    xoff[j] = r * cols * 2 + (lane & 15) * 16;
+  }
+  u32x4 *xw = xs[wave];
+  // where this lane's loads land in the wave's LDS tile
+  int xput[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    xput[j] = r * 16 + ((lane & 15) ^ (r & 15));
+  }
+  // the block this thread converts: row cr, block cb of each stage
+  const int cu = tid / H, ch = tid % H;
+  const int cr = cu >> 2, cb = cu & 3;
+  const bool cdead = cr >= rrem;  // past the matrix: loads its last row, zeroed
+  // 20-byte window holding the block's 18 bytes: 2 bytes early for odd
+  // blocks (the block then starts at byte 2 of a dword), on the block for
+  // even ones (an even block is never a row's last, so the 2 bytes past it
+  // exist); with an even block count per row the parity is cb's
+  const int cflat = min(cr, rrem - 1) * nb + cb;
+  const int woff = 18 * cflat - 2 * (cb & 1);
+  const bool codd = cb & 1;
+
+  auto load_x = [&](XRegs &X, int s) {
+    const int so = uni(s * BK * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      X.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j], so, 0));
+  };
+  // the wave's LDS tile is its own: its DS operations run in order, so the
+  // tile is rewritten right after the wave's last fragment read of it
+  auto put_x = [&](const XRegs &X) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xw[xput[j]] = X.a[j];
+  };
+  auto load_raw = [&](RawRegs &R, int s) {
+    const int so = uni(s * NB * 18);
+    R.w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, woff, so, 0));
+    R.w1 = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 16, so, 0);
+  };
+
+  // Quarter i of the conversion of this thread's raw block into buffer buf:
+  // dword i of the nibbles (elements 4i..4i+3 in the low nibbles, 16+4i..
+  // in the high ones) as exact BF16 codes q - 8; quarter 0 also stores the
+  // f16 delta (bytes 0-1 of the block) as fp32.
+  auto convert_part = [&](const RawRegs &R, int buf, int i) {
+    const uint32_t wv[5] = {R.w4.x, R.w4.y, R.w4.z, R.w4.w, R.w1};
+    uint32_t v = codd ? wv[i + 1] : __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], 2);
+    v = cdead ? 0x88888888u : v;
+    uint16_t *row = &codes[buf][cr * LDB + cb * 32 + 4 * i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (H == 2 && h != ch) continue;
+      const u32x2v cv = codes4_bf16(h ? (v >> 4) & 0x0f0f0f0fu : v & 0x0f0f0f0fu);
+      *(u32x2v *)(row + 16 * h) = cv;
+    }
+    if (i == 0 && ch == 0) {
+      const uint32_t dbits = codd ? (wv[0] >> 16) : (wv[0] & 0xffffu);
+      deltas[buf][cr * NB + cb] = cdead ? 0.f : f16_to_f32(dbits);
+    }
   };
 
   floatx4 acc[TM][TN];
@@ -185,71 +199,120 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int kq = (lane >> 4) * 8;  // this lane's 8 K indices within a block
-  const int arow = wm * (BM / 2) + (lane & 15);
-  const int bcol = wn * (BN / 2) + (lane & 15);
-  // the bias of this lane's output columns, loaded before the K loop
-  float bj[TN];
+  // the partial products of the last block computed, scaled (by dprev)
+  // while the next block's MFMAs run -- across stages too
+  floatx4 pprev[TM][TN];
+  float dprev[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int n = n0 + bcol + j * 16;
-    bj[j] = (EPI && bias && n < rows) ? ((const QD_GLOBAL float *)bias)[n] : 0.f;
+    dprev[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) pprev[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  auto scale_prev = [&]() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] += dprev[j] * pprev[i][j];
+  };
 
-  // One stage from LDS buffer `buf`: per block, TM x TN MFMAs of the exact
-  // codes, then the previous block's partial products scaled by its deltas.
-  auto compute = [&](int buf) {
-    const uint16_t *A = As(buf);
-    const uint16_t *Bm = Bs(buf);
-    const float *D = Ds(buf);
-    floatx4 p[2][TM][TN];  // partial products of two blocks in flight
+  // One stage from codes buffer buf, interleaved with the conversion of the
+  // next stage's raw blocks (R) into the other buffer.  Per block: the B
+  // fragments of the next block are read, the block's TM x TN MFMAs issue
+  // one by one, and between them the VALU scales the previous block's
+  // partial products and converts a quarter of the raw block, so the matrix
+  // core and the VALU work at the same time within the wave.
+  auto compute = [&](int buf, const RawRegs &R) {
+    const uint16_t *B = codes[buf] + (lane & 15) * LDB + kc * 8;
+    // A fragment (i, b): frame 16i + lane % 16, chunk 4b + lane / 16
+    auto afrag = [&](int i, int b) {
+      return __builtin_bit_cast(bf16x8, xw[(16 * i + (lane & 15)) * 16 + ((4 * b + kc) ^ (lane & 15))]);
+    };
+    bf16x8 af[2][TM];
+    const float *D = deltas[buf] + (lane & 15) * NB;
+    floatx4 dv[TN];  // deltas of the stage's blocks, per column tile
+    bf16x8 bfr[2][TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      dv[j] = *(const floatx4 *)(D + j * 16 * NB);
+      bfr[0][j] = *(const bf16x8 *)(B + j * 16 * LDB);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = afrag(i, 0);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      bf16x8 af[TM], bfr[TN];
+      if (b + 1 < NB) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8 *)(A + (arow + i * 16) * LDA + b * 32 + kq);
+        for (int j = 0; j < TN; ++j)
+          bfr[(b + 1) & 1][j] = *(const bf16x8 *)(B + j * 16 * LDB + (b + 1) * 32);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *(const bf16x8 *)(Bm + (bcol + j * 16) * LDA + b * 32 + kq);
+        for (int i = 0; i < TM; ++i) af[(b + 1) & 1][i] = afrag(i, b + 1);
+      }
+      floatx4 p[TM][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          p[b & 1][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              af[i], bfr[j], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      if (b > 0) {  // scale the previous block while this block's MFMAs run
+          p[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af[b & 1][i], bfr[b & 1][j],
+              floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      scale_prev();
+      convert_part(R, buf ^ 1, b);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float dj = D[(bcol + j * 16) * NB + (b - 1)];
+      for (int j = 0; j < TN; ++j) {
+        dprev[j] = dv[j][b];
 #pragma unroll
-          for (int i = 0; i < TM; ++i) acc[i][j] += dj * p[(b - 1) & 1][i][j];
-        }
+        for (int i = 0; i < TM; ++i) pprev[i][j] = p[i][j];
       }
     }
+    // instruction order: per block, the next block's B reads, then each
+    // MFMA followed by a share of the VALU work, then the code stores
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN + TM, 0);  // DS read
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const float dj = D[(bcol + j * 16) * NB + (NB - 1)];
+    for (int b = 0; b < NB; ++b) {
+      if (b > 0) __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);  // DS read
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][j] += dj * p[(NB - 1) & 1][i][j];
+      for (int t = 0; t < TM * TN; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);  // DS write
     }
   };
 
-  // Double-buffered: the global loads of stage s+1 are in flight while stage
-  // s is computed from LDS, then go to the other LDS buffer.
-  Stage<BM, BN> st;
-  stage_load(st, x, w, m, rows, cols, m0, n0, 0, tid);
-  stage_store(st, As(0), Bs(0), Ds(0), tid);
-  __syncthreads();
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nstages) stage_load(st, x, w, m, rows, cols, m0, n0, (s + 1) * NB, tid);
-    compute(buf);
-    if (s + 1 < nstages) stage_store(st, As(buf ^ 1), Bs(buf ^ 1), Ds(buf ^ 1), tid);
-    __syncthreads();
+  XRegs X;
+  RawRegs R0, R1;
+  auto step = [&](int s, const RawRegs &Rc, RawRegs &Rl) {
+    lds_barrier();  // codes of stage s visible; buffer (s+1)%2 free
+    // Past the last stage the loads repeat it and the conversion writes a
+    // buffer nobody reads: with no branch, the loop body (two stages; the
+    // stage count is even, K being a multiple of 256) is one basic block,
+    // so the loads stay ahead of the compute instead of being sunk to their
+    // use, and the compiler counts the loads in flight exactly.
+    load_x(X, min(s + 1, nstages - 1));
+    load_raw(Rl, min(s + 2, nstages - 1));
+    __builtin_amdgcn_sched_barrier(0);  // issue them before the compute
+    compute(s & 1, Rc);
+    put_x(X);  // x of stage s+1, once the wave has read stage s's
+  };
+  load_x(X, 0);
+  load_raw(R0, 0);
+  load_raw(R1, min(1, nstages - 1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) convert_part(R0, 0, i);
+  put_x(X);
+  for (int s = 0; s < nstages; s += 2) {
+    step(s, R1, R0);
+    step(s + 1, R0, R1);
   }
+  scale_prev();
 
+  float bj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + j * 16 + (lane & 15);
+    bj[j] = (EPI && bias && n < rows) ? ((const QD_GLOBAL float *)bias)[n] : 0.f;
+  }
   // C layout of a 16x16 f32 MFMA tile: lane holds rows 4*(lane/16)+v of
   // column lane%16.
   auto store = [&](auto act) {
@@ -257,10 +320,10 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + bcol + j * 16;
+        const int n = n0 + j * 16 + (lane & 15);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int t = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + v;
+          const int t = m0 + wave * 32 + i * 16 + (lane >> 4) * 4 + v;
           if (t < m && n < rows)
             y[(size_t)t * rows + n] = EPI ? act(acc[i][j][v] + bj[j]) : acc[i][j][v];
         }
@@ -272,24 +335,19 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemm_kernel(
     store([](float v) { return v; });
 }
 
-template <int BM, int BN, bool MULTI, bool EPI>
+template <int WAVES, bool MULTI, bool EPI>
 hipError_t launch_tile(Q40Group g, int cols, const uint16_t *x, int m, hipStream_t stream) {
-  const size_t lds = 2 * (size_t)Tile<BM, BN>::STAGE_BYTES;
-  static bool attr_set = false;  // the limit is per function; setting it twice is harmless
-  if (!attr_set && lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)q4_0_gemm_kernel<BM, BN, MULTI, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   g.tile0[0] = 0;
   for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + BN - 1) / BN;
   for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
+  constexpr int BM = WAVES * 32;
   dim3 grid(g.tile0[g.n], (m + BM - 1) / BM);
-  hipLaunchKernelGGL((q4_0_gemm_kernel<BM, BN, MULTI, EPI>), grid, dim3(kThreads), lds, stream, g,
+  hipLaunchKernelGGL((q4_0_gemm_kernel<WAVES, MULTI, EPI>), grid, dim3(WAVES * 64), 0, stream, g,
                      cols, x, m);
   return hipGetLastError();
 }
+
+constexpr int kWaves = 4;
 
 }  // namespace
 
@@ -299,10 +357,10 @@ hipError_t launch_q4_0_gemm(Q40Group g, int cols, const uint16_t *x, int m,
   bool epi = g.gelu != 0;
   for (int k = 0; k < g.n; ++k) epi = epi || g.bias[k] != nullptr;
   if (g.n > 1)
-    return epi ? launch_tile<QD_GEMM_BM, QD_GEMM_BN, true, true>(g, cols, x, m, stream)
-               : launch_tile<QD_GEMM_BM, QD_GEMM_BN, true, false>(g, cols, x, m, stream);
-  return epi ? launch_tile<QD_GEMM_BM, QD_GEMM_BN, false, true>(g, cols, x, m, stream)
-             : launch_tile<QD_GEMM_BM, QD_GEMM_BN, false, false>(g, cols, x, m, stream);
+    return epi ? launch_tile<kWaves, true, true>(g, cols, x, m, stream)
+               : launch_tile<kWaves, true, false>(g, cols, x, m, stream);
+  return epi ? launch_tile<kWaves, false, true>(g, cols, x, m, stream)
+             : launch_tile<kWaves, false, false>(g, cols, x, m, stream);
 }
 
 }  // namespace qd
