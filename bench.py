@@ -211,6 +211,18 @@ class DecodeStep:
         self.blobs = self.xs = self.ys = None
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(step: DecodeStep):
     """The oracle on one full decode step (all 197 GEMVs, every row) on all
     host cores; its outputs are compared with the GPU's timed buffers."""
@@ -229,7 +241,8 @@ def cpu_baseline(step: DecodeStep):
         half = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126))) - 8)
         worst = max(worst, float(np.maximum(np.abs(got - ref) - half, 0).max() / np.abs(ref).max()))
     return {
-        "value": 1.0 / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "value": 1.0 / dt, "unit": "tokens/s", "cores": cores, "cpu_model": cpu_model(),
+        "kind": "oracle",
         "sample": "one full decode step: all 197 GEMVs, every output row, f64 (%.2f s wall)" % dt,
         "weight_GBps": step.weight_bytes / dt / 1e9,
         "parity_vs_timed_gpu_buffers": "ok" if worst <= 1e-5 else "FAIL (excess %.3g)" % worst,
@@ -312,7 +325,7 @@ def cpu_baseline_rows():
     out["whisper_large_decoder"] = {
         "tokens_per_s": 1.0 / (32 * dt), "weight_GBps": db / dt / 1e9,
         "sample": "one decoder layer's six GEMVs at M = 1 (%.3f s), times 32 layers" % dt}
-    return {"cores": cores, "kind": "oracle", "configs": out}
+    return {"cores": cores, "cpu_model": cpu_model(), "kind": "oracle", "configs": out}
 
 
 # ---- rows ------------------------------------------------------------------------
@@ -334,11 +347,36 @@ def row_affine_gemv_1024(qd):
                           for i in range(ncopy)])
     warm = event_time(gw.replay, 5, 2) / ncopy
     cold = event_time(gc.replay, 5, 2) / ncopy
+    single = single_launch_cold(lambda i: qd.qgemv_affine_i8_g64(copies[i], rows, cols, x, y, 1),
+                                ncopy)
     return {"shape": "1024x1024, M=1", "weight_bytes": nbytes,
+            "us_single_launch_cold": single,
             "us_per_gemv_warm": warm * 1e3, "us_per_gemv_cold": cold * 1e3,
             "GBps_cold": nbytes / (cold * 1e-3) / 1e9,
             "hbm_peak_frac_cold": nbytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "note": "back-to-back launches in one HIP graph; cold rotates 482 copies (537 MB)"}
+            "note": "throughput: back-to-back launches in one HIP graph; cold rotates 482 "
+                    "copies (537 MB); single launch: one launch alone on an idle GPU, its "
+                    "weights last touched 537 MB earlier"}
+
+
+def single_launch_cold(launch, ncopy, trials=25):
+    """Time of one launch alone on an idle stream, from HIP events recorded
+    just before and after it (so it includes the dispatch latency, not only
+    the kernel), on a copy of the weights untouched for the last `ncopy`
+    copies; median and min over `trials`, in microseconds."""
+    import torch
+    times = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for t in range(trials):
+        i = (t * 97) % ncopy
+        torch.cuda.synchronize()
+        e0.record()
+        launch(i)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    times.sort()
+    return {"median": times[len(times) // 2], "min": times[0], "trials": trials}
 
 
 def row_affine_lm_head(qd):
@@ -429,8 +467,14 @@ def row_q4_0_ffn_pair(qd):
         gw, gc = capture(lambda: launch(False)), capture(lambda: launch(True))
         warm = event_time(gw.replay, 3, 1) / npair
         cold = event_time(gc.replay, 3, 1) / npair
-        out[f"M{m}"] = {"us_per_pair_warm": warm * 1e3, "us_per_pair_cold": cold * 1e3,
+        single = single_launch_cold(
+            lambda i: [qd.qgemv_q4_0(cp[i], r, c, xs[k], ys[k], m)
+                       for k, (r, c, wq, cp) in enumerate(mats)], npair)
+        out[f"M{m}"] = {"us_single_launch_pair_cold": single,
+                        "us_per_pair_warm": warm * 1e3, "us_per_pair_cold": cold * 1e3,
                         "GBps_cold": pair_bytes / (cold * 1e-3) / 1e9}
+    out["note"] = ("throughput: pairs back to back in one HIP graph; single launch: the two "
+                   "GEMVs alone on an idle GPU (HIP events around both), weights cold")
     return out
 
 
@@ -594,12 +638,45 @@ def row_whisper_large_decoder(qd, layers):
                 i += 1
     gl = capture(linear)
     ms_lin = event_time(gl.replay, 20, 3)
+    # variant with the cross-attention q and o of every layer (1280 x 1280
+    # each; the cross-attention k and v run over the encoder frames with the
+    # prefill GEMM): 8 matrices per layer, 192 launches
+    cross = []
+    for layer in range(len(layers)):
+        for k, name in enumerate(("cross_q", "cross_o")):
+            wq = q4_0_from_f32(qd, synth.w_f32(1280, 1280, key=(5, layer, 200 + k)), 1280, 1280)
+            x = torch.from_numpy(synth.x_f32(1, 1280, key=(5, layer, 300 + k))).to(DEV)
+            cross.append((layer, wq, x, torch.empty((1, 1280), device=DEV)))
+    wb_cross = wb + sum(qd.q4_0_bytes(1280, 1280) for _ in cross)
+
+    def with_cross():
+        i = 0
+        layer = 0
+        while i < len(ops):
+            qd.qgemv_q4_0_group([(w, y, r) for _, w, r, _, _, y in ops[i:i + 3]],
+                                ops[i][3], ops[i][4], 1)
+            _, w, r, c, x, y = ops[i + 3]  # self-attention o
+            qd.qgemv_q4_0(w, r, c, x, y, 1)
+            for _, wq, x, y in cross[2 * layer:2 * layer + 2]:
+                qd.qgemv_q4_0(wq, 1280, 1280, x, y, 1)
+            for _, w, r, c, x, y in ops[i + 4:i + 6]:  # fc1, fc2
+                qd.qgemv_q4_0(w, r, c, x, y, 1)
+            i += 6
+            layer += 1
+    gx = capture(with_cross)
+    ms_x = event_time(gx.replay, 20, 3)
+    del cross
     return {"gemvs": len(ops), "weight_bytes": wb, "ms_per_step": ms,
             "tokens_per_s": 1000.0 / ms, "weight_GBps": wb / (ms * 1e-3) / 1e9,
             "hbm_peak_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "variant": "128 launches (q, k, v grouped) in a HIP graph",
             "ms_per_step_192_launches": ms192,
-            "ms_per_step_q_linear": ms_lin}
+            "ms_per_step_q_linear": ms_lin,
+            "with_cross_q_o": {"weight_bytes": wb_cross, "ms_per_step": ms_x,
+                               "weight_GBps": wb_cross / (ms_x * 1e-3) / 1e9,
+                               "hbm_peak_frac": wb_cross / (ms_x * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                               "variant": "8 matrices per layer (plus cross-attention q, o), "
+                                          "192 launches in a HIP graph"}}
 
 
 def row_q4_0_bake(qd):
