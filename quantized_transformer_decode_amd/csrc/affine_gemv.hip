@@ -106,20 +106,41 @@ struct MItem {
   int trow;                      // first row of the tile in its matrix
 };
 
+// Every field of the group descriptor, loaded at the kernel's start: the
+// compiler would otherwise load some of them only inside the first branch,
+// after the first ones had arrived -- a dependent round trip before the
+// first weight load.
+__device__ __forceinline__ void group_args_now(const AffineGroup &g) {
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i)
+    __asm__ volatile("" ::"s"(g.w[i]), "s"(g.y[i]), "s"(g.rows[i]), "s"(g.tile0[i]));
+  __asm__ volatile("" ::"s"(g.tile0[kMaxGroup]), "s"(g.n), "s"(g.grid), "s"(g.ntiles));
+}
+
+// The descriptor fields of matrix k are picked by selects over constant
+// indices: indexing the kernel-argument arrays with k would cost one
+// dependent scalar-load round trip per lookup before the first weight load.
 template <int R>
 __device__ __forceinline__ MItem item_of_tile(const AffineGroup &grp, int cols, int groups,
                                               int tile) {
-  int k = 0;
+  int rows = grp.rows[0], t0 = 0;
+  const uint8_t *w = grp.w[0];
+  uint16_t *y = grp.y[0];
 #pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i)
-    if (i < grp.n && tile >= grp.tile0[i]) k = i;
+  for (int i = 1; i < kMaxGroup; ++i) {
+    const bool in = i < grp.n && tile >= grp.tile0[i];
+    rows = in ? grp.rows[i] : rows;
+    w = in ? grp.w[i] : w;
+    y = in ? grp.y[i] : y;
+    t0 = in ? grp.tile0[i] : t0;
+  }
   MItem it;
-  it.rows = grp.rows[k];
-  it.w = gp(grp.w[k]);
+  it.rows = rows;
+  it.w = gp(w);
   it.sc = (const QD_GLOBAL uint16_t *)(it.w + (size_t)it.rows * cols);
-  it.y = gp(grp.y[k]);
+  it.y = gp(y);
   it.boff = (size_t)it.rows * groups;
-  it.trow = (tile - grp.tile0[k]) * 16 * R;
+  it.trow = (tile - t0) * 16 * R;
   return it;
 }
 
@@ -443,10 +464,12 @@ template <int R, int U, int KS, bool CH, bool XL, class Act, int PRO>
 __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     const AffineGroup grp, int cols, const uint16_t *__restrict__ x_, int m,
     const GemvPrologue pro) {
+  group_args_now(grp);
   constexpr int SLOTS = kMW / KS;
   __shared__ float red[KS > 1 ? kMW * R * kWave * 4 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t xsh[];  // x (XL)
   uint8_t *xl = xsh;
+  __asm__ volatile("" ::"s"(x_), "s"(cols), "s"(m));
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
   const int slot = wave / KS, split = wave % KS;
@@ -459,8 +482,8 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   S.ga = uni(unit * (units * split / KS));
   S.gb = uni(unit * (units * (split + 1) / KS));
   S.ts0 = blockIdx.x * SLOTS + slot;
-  S.stride = gridDim.x * SLOTS;
-  const int ntiles = grp.tile0[grp.n];
+  S.stride = grp.grid * SLOTS;  // the grid size as an argument: gridDim is one more load
+  const int ntiles = grp.ntiles;
   int tiles_mine = 0;
   if (S.ts0 < ntiles) tiles_mine = KS == 1 ? (ntiles - 1 - S.ts0) / S.stride + 1 : 1;
   const int n = uni(tiles_mine * (S.gb - S.ga));
@@ -576,8 +599,11 @@ hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int
       raised = true;
     }
   }
+  AffineGroup ga = g;
+  ga.grid = grid;
+  ga.ntiles = g.tile0[g.n];
   hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act, PRO>), dim3(grid),
-                     dim3(kMThreads), lds, stream, g, cols, x, m, pro);
+                     dim3(kMThreads), lds, stream, ga, cols, x, m, pro);
   return hipGetLastError();
 }
 

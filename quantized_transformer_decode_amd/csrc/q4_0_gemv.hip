@@ -52,18 +52,42 @@ struct QItem {
   int trow;             // first row of the row group in its matrix
 };
 
+// Every field of the group descriptor, loaded at the kernel's start: the
+// compiler would otherwise load some of them only inside the first branch,
+// after the first ones had arrived -- a dependent round trip before the
+// first weight load.
+__device__ __forceinline__ void q_args_now(const Q40Group &g) {
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i)
+    __asm__ volatile("" ::"s"(g.w[i]), "s"(g.y[i]), "s"(g.bias[i]), "s"(g.rows[i]),
+                     "s"(g.tile0[i]));
+  __asm__ volatile("" ::"s"(g.tile0[kMaxGroup]), "s"(g.n), "s"(g.gelu), "s"(g.grid),
+                   "s"(g.ntiles));
+}
+
+// Matrix k's fields by selects over constant indices (indexing the
+// kernel-argument arrays with k would be a dependent scalar load).
 template <int R>
 __device__ __forceinline__ QItem q_item(const Q40Group &grp, int rg) {
-  int k = 0;
+  const uint8_t *w = grp.w[0];
+  float *y = grp.y[0];
+  const float *bias = grp.bias[0];
+  int rows = grp.rows[0], t0 = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i)
-    if (i < grp.n && rg >= grp.tile0[i]) k = i;
+  for (int i = 1; i < kMaxGroup; ++i) {
+    const bool in = i < grp.n && rg >= grp.tile0[i];
+    w = in ? grp.w[i] : w;
+    y = in ? grp.y[i] : y;
+    bias = in ? grp.bias[i] : bias;
+    rows = in ? grp.rows[i] : rows;
+    t0 = in ? grp.tile0[i] : t0;
+  }
   QItem it;
-  it.w = gp(grp.w[k]);
-  it.y = gp(grp.y[k]);
-  it.bias = grp.bias[k];
-  it.rows = grp.rows[k];
-  it.trow = (rg - grp.tile0[k]) * 8 * R;
+  it.w = gp(w);
+  it.y = gp(y);
+  it.bias = bias;
+  it.rows = rows;
+  it.trow = (rg - t0) * 8 * R;
   return it;
 }
 
@@ -190,6 +214,8 @@ template <int MT, int R, int KS, bool EPI>
 __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
     const Q40Group grp, int cols, const float *__restrict__ x_, int t0, int m) {
   static_assert(KS >= 1 && KS <= kQW, "a row's split needs one wave per part");
+  q_args_now(grp);
+  __asm__ volatile("" ::"s"(x_), "s"(cols), "s"(t0), "s"(m));
   constexpr int SLOTS = kQW / KS;
   __shared__ float red[KS > 1 ? kQW * MT * R * 8 : 1];
   extern __shared__ __attribute__((aligned(16))) float qsh[];
@@ -206,8 +232,8 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   S.sa = uni(steps * split / KS);
   S.sb = uni(steps * (split + 1) / KS);
   S.rg0 = blockIdx.x * SLOTS + slot;
-  S.stride = gridDim.x * SLOTS;
-  const int ngroups = grp.tile0[grp.n];
+  S.stride = grp.grid * SLOTS;  // the grid size as an argument: gridDim is one more load
+  const int ngroups = grp.ntiles;
   int mine = 0;
   if (S.rg0 < ngroups) mine = KS == 1 ? (ngroups - 1 - S.rg0) / S.stride + 1 : 1;
   const int n = uni(mine * (S.sb - S.sa));
@@ -333,8 +359,11 @@ hipError_t launch_q_ks(const Q40Group &g, int cols, const float *x, int t0, int 
       raised = true;
     }
   }
+  Q40Group ga = g;
+  ga.grid = grid;
+  ga.ntiles = g.tile0[g.n];
   hipLaunchKernelGGL((q4_0_gemv_kernel<MT, R, KS, EPI>), dim3(grid), dim3(kQThreads), lds, stream,
-                     g, cols, x, t0, m);
+                     ga, cols, x, t0, m);
   return hipGetLastError();
 }
 

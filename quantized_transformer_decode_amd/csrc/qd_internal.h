@@ -21,6 +21,8 @@ struct AffineGroup {
   int rows[kMaxGroup];
   int tile0[kMaxGroup + 1];
   int n;
+  int grid;    // workgroups of the launch (set by the launcher)
+  int ntiles;  // tile0[n] (set by the launcher)
 };
 // Q4_0 products of one launch, each with an optional f32 bias [rows] added
 // to its outputs and, with gelu, gelu_tanh applied after it (q_linear).
@@ -32,6 +34,8 @@ struct Q40Group {
   int tile0[kMaxGroup + 1];
   int n;
   int gelu;
+  int grid;    // workgroups of the launch (set by the GEMV launcher)
+  int ntiles;  // tile0[n] (set by the GEMV launcher)
 };
 
 // x and y BF16, or f16 with f16 = true (scales and biases BF16 in both).
