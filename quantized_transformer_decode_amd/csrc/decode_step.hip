@@ -191,11 +191,10 @@ __device__ __forceinline__ void walk_next(Walk &w, const StepOp *ops) {
 // past a row's end re-read its first chunk): the compiler can then wait for
 // exactly this group's loads before it is consumed, instead of for every
 // load in flight (which would include the next group's prefetch).
-__device__ __forceinline__ void issue(Group &g, const StepOp *ops, const StepStage *stages,
-                                      Cursor c, int gw, int nw, int lane) {
+__device__ __forceinline__ void issue_walk(Group &g, const StepOp *ops, Walk wk, Cursor c,
+                                           int lane) {
   c.s = uni(c.s);
   c.i = uni(c.i);
-  Walk wk = walk_start(ops, stages[c.s], c, gw, nw);
   g.start = wk;
   g.i0 = c.i;
   g.s = c.s;
@@ -215,6 +214,13 @@ __device__ __forceinline__ void issue(Group &g, const StepOp *ops, const StepSta
     g.bi[k] = sc[(size_t)wk.op.rows * groups + gi];
     if (c.i + k + 1 < wk.n) walk_next(wk, ops);
   }
+}
+
+__device__ __forceinline__ void issue(Group &g, const StepOp *ops, const StepStage *stages,
+                                      Cursor c, int gw, int nw, int lane) {
+  c.s = uni(c.s);
+  c.i = uni(c.i);
+  issue_walk(g, ops, walk_start(ops, stages[c.s], c, gw, nw), c, lane);
 }
 
 // Compute one group (the items issue() loaded).  rowsum carries a row's
@@ -330,8 +336,11 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
       compute(cur, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
       if (n1.s >= n_stages) return false;
       signal_done_through(sh, signalled, n1.s);  // as soon as a stage is finished
+      // the next stage's schedule lookups (dependent scalar loads) while the
+      // hand-off completes; only the weight loads wait for the arrival
+      const Walk wn = walk_start(ops, stages[uni(n1.s)], n1, gw, nw);
       wait_arrived(c.s + 1);
-      issue(nxt, ops, stages, n1, gw, nw, lane);
+      issue_walk(nxt, ops, wn, n1, lane);
     }
     c = n1;
     return true;
