@@ -201,6 +201,14 @@ __global__ __launch_bounds__(kAttThreads) void attention_partial_kernel(
     int kv_start, int length, int rows_per_wave, float scale, const int *__restrict__ pos_dev,
     int capacity, float *__restrict__ part, uint16_t *__restrict__ out_,
     const AttentionQkRope qkr) {
+  // every argument loaded at the start (one scalar round trip): loaded where
+  // first used, some would follow the position read as a second round trip
+  __asm__ volatile("" ::"s"(q_), "s"(k_), "s"(v_), "s"(kv_heads), "s"(kv_start), "s"(length),
+                   "s"(rows_per_wave), "s"(scale), "s"(pos_dev), "s"(capacity), "s"(part),
+                   "s"(out_));
+  __asm__ volatile("" ::"s"(qkr.k_src), "s"(qkr.v_src), "s"(qkr.q_w), "s"(qkr.k_w),
+                   "s"(qkr.q_out), "s"(qkr.eps), "s"(qkr.theta), "s"(qkr.freq_ratio),
+                   "s"(qkr.err));
   constexpr int LPP = D / 8;         // lanes per cached row
   constexpr int PPS = kWave / LPP;   // rows per wave load
   __shared__ float red[kAttWaves][G][10][LPP];
@@ -494,6 +502,9 @@ __global__ __launch_bounds__(kCoThreads) void attention_combine_o_kernel(
     const float *__restrict__ part, int stride, const int *__restrict__ pos_dev, int capacity,
     int rows_per_wave, const uint8_t *__restrict__ wo, int rows, int cols,
     float *__restrict__ opart, uint16_t *__restrict__ attn_out) {
+  // every argument loaded at the start (one scalar round trip)
+  __asm__ volatile("" ::"s"(part), "s"(stride), "s"(pos_dev), "s"(capacity), "s"(rows_per_wave),
+                   "s"(wo), "s"(rows), "s"(cols), "s"(opart), "s"(attn_out));
   constexpr int E = G * D;                           // elements of the K/V head's row slice
   constexpr int EW = E < kCoThreads ? E : kCoThreads;
   constexpr int SL = kCoThreads / EW;                // chunk slices side by side
