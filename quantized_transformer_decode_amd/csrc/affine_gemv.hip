@@ -571,13 +571,12 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   }
 }
 
-#ifndef QD_AFFINE_MFMA_R
-#define QD_AFFINE_MFMA_R 1
-#endif
-#ifndef QD_AFFINE_TARGET_WAVES
-#define QD_AFFINE_TARGET_WAVES 4096
-#define QD_AFFINE_STREAM_WGS 2
-#endif
+// Matrix-core kernel shape: 16-row tiles (R = 1); K is split until a launch
+// has about 4096 waves; the streaming walk (KS = 1) runs two workgroups per
+// CU.
+constexpr int kAffineR = 1;
+constexpr int kAffineTargetWaves = 4096;
+constexpr int kAffineStreamWgsPerCu = 2;
 
 // x goes to LDS when its padded copy fits this budget (two workgroups per
 // CU then still fit the 160 KiB of LDS).
@@ -586,7 +585,7 @@ constexpr int kXlBudget = 72 * 1024;
 template <int KS, bool CH, bool XL, class Act, int PRO>
 hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
                           const GemvPrologue &pro, hipStream_t stream) {
-  constexpr int R = QD_AFFINE_MFMA_R;
+  constexpr int R = kAffineR;
   constexpr int U = CH ? 4 : 2;
   const size_t lds = XL ? (size_t)m * (2 * cols + 16) : 0;
   if (lds > 48 * 1024) {  // above the default dynamic-LDS limit: raise it once
@@ -628,9 +627,9 @@ hipError_t launch_mfma_ch(AffineGroup g, int cols, const uint16_t *x, int m,
   // KS: split K over up to 8 waves until the launch gives about
   // kTargetWaves waves (each wave keeping at least one buffer of groups);
   // KS = 1 walks tiles grid-stride with kStreamWgsPerCu workgroups per CU.
-  constexpr int kTargetWaves = QD_AFFINE_TARGET_WAVES;
-  constexpr int kStreamWgsPerCu = QD_AFFINE_STREAM_WGS;
-  constexpr int R = QD_AFFINE_MFMA_R;
+  constexpr int kTargetWaves = kAffineTargetWaves;
+  constexpr int kStreamWgsPerCu = kAffineStreamWgsPerCu;
+  constexpr int R = kAffineR;
   g.tile0[0] = 0;
   for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + 16 * R - 1) / (16 * R);
   for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
