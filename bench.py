@@ -809,7 +809,7 @@ ROWS = ("affine_gemv_1024", "affine_lm_head", "affine_f16", "q4_0_ffn_pair", "qw
 # device-to-device copy of known size; the summary records the sha256 of the
 # kernel's sources at measurement time and is ignored once they change.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "affine_step_kernel_qwen3_0_6b_traffic.md")
-STEP_SOURCES = ("decode_step.hip", "qd_step.h", "qd_device.h")
+STEP_SOURCES = ("decode_step.hip", "qd_step.h", "qd_device.h", "affine_gemv.hip", "qd_api.hip")
 
 
 def step_source_sha():
@@ -822,7 +822,8 @@ def step_source_sha():
 
 
 def recorded_traffic():
-    """bytes per launch of affine_step_kernel, or None if absent or stale."""
+    """HBM bytes per step (the step kernel and the streamed LM head), or None
+    if absent or stale."""
     try:
         with open(TRAFFIC_FILE) as fh:
             text = fh.read()
@@ -954,6 +955,10 @@ def main():
         variant = ("one persistent launch per step (one workgroup per CU); stage s+1 "
                    "reads its inputs only after every workgroup finished stage s")
         kernel, launches = "affine_step_kernel", 1
+        if step.plan.tail:
+            variant += ("; the last stage (the LM head, one GEMV) streams as a second "
+                        "launch after it")
+            kernel = "affine_step_kernel+affine_gemv_m1_kernel"
     else:
         ms, wall = ms_graph, None
         dist = step_distribution(g.replay, min(args.steps, 200), cur)
@@ -1006,7 +1011,7 @@ def main():
         "roofline": {
             "kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": recorded_traffic() if kernel == "affine_step_kernel" else None,
+            "traffic": recorded_traffic() if kernel.startswith("affine_step_kernel") else None,
             "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
         },
     }

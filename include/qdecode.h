@@ -173,13 +173,23 @@ typedef struct {
   int64_t stage;
 } qd_affine_gemv_op;
 
-/* Host-side handle filled by _step_plan (caller-owned plain data). */
+/* Host-side handle filled by _step_plan (caller-owned plain data).  When
+ * the last stage is a single GEMV of at least 2^27 weights (an LM head),
+ * `tail` is 1 and that GEMV is kept here: _step_run streams it with the
+ * single-GEMV kernel after the persistent kernel (which then runs the other
+ * stages), because one matrix streamed by the persistent kernel's
+ * whole-chip stage reaches about half the bandwidth of the streaming
+ * kernel. */
 typedef struct {
   void *workspace;
   int32_t nwg;        /* workgroups = CUs of the planning device */
   int32_t lds_bytes;
   int32_t n_ops, n_stages, m;
   uint32_t magic;
+  int32_t tail;       /* 1: the last stage runs as a separate streaming GEMV */
+  const void *tail_w, *tail_x;
+  void *tail_y;
+  int64_t tail_rows, tail_cols;
 } qd_step_plan;
 
 /* Workspace bytes needed by _step_plan for these ops (0 if invalid). */
@@ -204,11 +214,13 @@ qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
 
 /* Enqueues the whole step as ONE persistent kernel (one workgroup per CU;
  * every workgroup must be able to be resident, so do not run it concurrently
- * with kernels that occupy whole CUs indefinitely).  Launches nothing else,
- * allocates nothing, and may be captured in a HIP graph.  Runs planned on
- * the same workspace must not overlap in time.  After a run that reported an
- * error (qgemv_affine_i8_g64_step_check), plan again before the next run:
- * the workspace's arrival counts no longer match. */
+ * with kernels that occupy whole CUs indefinitely) and, with plan->tail,
+ * the last stage's GEMV as a second launch on the same stream (it starts
+ * after the persistent kernel has finished every other stage).  Launches
+ * nothing else, allocates nothing, and may be captured in a HIP graph.  Runs
+ * planned on the same workspace must not overlap in time.  After a run that
+ * reported an error (qgemv_affine_i8_g64_step_check), plan again before the
+ * next run: the workspace's arrival counts no longer match. */
 qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream);
 
 /* Synchronises `stream`, reads the workspace's error word into *error_bits

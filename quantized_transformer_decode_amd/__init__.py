@@ -87,7 +87,10 @@ class StepPlan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("nwg", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("n_ops", ctypes.c_int32),
                 ("n_stages", ctypes.c_int32), ("m", ctypes.c_int32),
-                ("magic", ctypes.c_uint32)]
+                ("magic", ctypes.c_uint32), ("tail", ctypes.c_int32),
+                ("tail_w", ctypes.c_void_p), ("tail_x", ctypes.c_void_p),
+                ("tail_y", ctypes.c_void_p), ("tail_rows", ctypes.c_int64),
+                ("tail_cols", ctypes.c_int64)]
 
 
 class QDError(RuntimeError):

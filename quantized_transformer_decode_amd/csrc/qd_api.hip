@@ -99,6 +99,8 @@ bool affine_shape_ok(int64_t rows, int64_t cols) {
 
 constexpr int kMaxStageWords = 16384;  // LDS: two fp32 copies of a stage input
 constexpr int kMinStepWgs = 32;        // smallest grid a plan supports
+// a last stage of one GEMV of at least this many weights runs as its own launch
+constexpr int64_t kStepTailWeights = (int64_t)1 << 27;
 // log2 of the slice length for a stage input of `words` 32-bit words over
 // `nwg` publishers: the smallest power of two >= ceil(words / nwg), within
 // [1, 64] words (one per lane of the publishing wave).
@@ -577,6 +579,16 @@ qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
   plan->n_stages = ns;
   plan->m = (int32_t)m;
   plan->magic = qd::kStepMagic;
+  // a last stage of one very large GEMV streams faster as its own launch
+  const qd_affine_gemv_op &last = ops[n_ops - 1];
+  const bool tail = ns > 1 && (n_ops == 1 || ops[n_ops - 2].stage != last.stage) &&
+                    last.rows * last.cols >= kStepTailWeights;
+  plan->tail = tail ? 1 : 0;
+  plan->tail_w = tail ? last.w_packed : nullptr;
+  plan->tail_x = tail ? last.x_bf16 : nullptr;
+  plan->tail_y = tail ? last.y_bf16 : nullptr;
+  plan->tail_rows = tail ? last.rows : 0;
+  plan->tail_cols = tail ? last.cols : 0;
   return QD_OK;
 }
 
@@ -584,7 +596,10 @@ qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream) {
   if (!plan || !plan->workspace || plan->magic != qd::kStepMagic || plan->nwg < 1 ||
       plan->lds_bytes < 8 || plan->lds_bytes > 2 * kMaxStageWords * 4 ||
       plan->lds_bytes % 8 != 0 || plan->n_ops < 1 || plan->n_stages < 1 ||
-      plan->n_stages > plan->n_ops || plan->m != 1)
+      plan->n_stages > plan->n_ops || plan->m != 1 || plan->tail < 0 || plan->tail > 1 ||
+      (plan->tail && (plan->n_stages < 2 || !plan->tail_w || !plan->tail_x || !plan->tail_y ||
+                      plan->tail_rows < 1 || plan->tail_cols < 64 || plan->tail_cols % 64 ||
+                      plan->tail_cols > kMaxGemvCols)))
     return QD_EINVAL;
   qd_status st = check_device();
   if (st != QD_OK) return st;
@@ -597,9 +612,18 @@ qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream) {
   const size_t ctr_off = rel_off + align256((size_t)plan->nwg * 128);
   hipError_t e = qd::launch_affine_step(
       (const qd::StepOp *)(ws + ops_off), (const qd::StepStage *)(ws + stages_off),
-      plan->n_stages, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch,
+      plan->n_stages - plan->tail, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch,
       (uint32_t *)(ws + rel_off), (uint32_t *)(ws + ctr_off), &h->error,
       (size_t)plan->lds_bytes, (hipStream_t)stream);
+  if (e == hipSuccess && plan->tail) {
+    qd::AffineGroup g = {};
+    g.n = 1;
+    g.w[0] = (const uint8_t *)plan->tail_w;
+    g.y[0] = (uint16_t *)plan->tail_y;
+    g.rows[0] = (int)plan->tail_rows;
+    e = qd::launch_affine_gemv(g, (int)plan->tail_cols, (const uint16_t *)plan->tail_x, 1, false,
+                               (hipStream_t)stream);
+  }
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }
 

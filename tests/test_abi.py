@@ -471,7 +471,8 @@ def test_errors_attention_decode_noalloc():
     assert call(out=B + 4096) == qd.QD_EINVAL         # output inside the K cache
     limit = 4 << 20
     assert qd.attention_decode_workspace_bytes(1024, 128, 128) <= limit
-    assert call(heads=1024, kvh=128) == qd.QD_EDEVICE  # fits: stops at the device check
+    if not _gpu_visible():  # fits: stops at the device check (a GPU would run it)
+        assert call(heads=1024, kvh=128) == qd.QD_EDEVICE
     big = qd.attention_decode_workspace_bytes(8192, 1024, 128)
     assert big > limit
     assert call(heads=8192, kvh=1024) == qd.QD_ESCRATCH

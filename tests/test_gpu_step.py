@@ -98,6 +98,38 @@ def test_step_graph_replays():
         st.check(what=f"replay {rep}")
 
 
+# a last stage of one GEMV of >= 2^27 weights runs as a second, streaming
+# launch (plan.tail); one exactly at the threshold and one below it
+TAIL = [(130, 256, 0), (64, 256, 0), (256, 1024, 1), (131072, 1024, 2)]
+NO_TAIL = [(130, 256, 0), (256, 1024, 1), (131071, 1024, 2)]
+
+
+def test_step_streamed_last_stage_eager_and_graph():
+    print("step tail", flush=True)
+    st = Step(TAIL, key=24)
+    assert st.plan.tail == 1 and st.plan.tail_rows == 131072 and st.plan.tail_cols == 1024
+    st.run()
+    st.check(sample_rows=64, what="tail eager")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            qd.qgemv_affine_i8_g64_step_run(st.plan)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for y in st.ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert qd.qgemv_affine_i8_g64_step_check(st.plan) == 0
+        st.check(sample_rows=64, what=f"tail replay {rep}")
+    nt = Step(NO_TAIL, key=25)
+    assert nt.plan.tail == 0
+    nt.run()
+    nt.check(sample_rows=64, what="below the tail threshold")
+
+
 def test_step_qwen3_0_6b_full_size_sampled():
     # the full 197-GEMV step of the Qwen3-0.6B-shaped decoder; every GEMV is
     # checked on sampled rows
@@ -105,6 +137,7 @@ def test_step_qwen3_0_6b_full_size_sampled():
     shapes = [(rows, cols, stage) for (_, _, rows, cols, stage)
               in synth.decode_step_matrices(synth.QWEN3_0_6B)]
     st = Step(shapes, key=23)
+    assert st.plan.tail == 1  # the 151936 x 1024 LM head streams on its own
     for _ in range(3):
         st.run()
     st.check(sample_rows=48, what="qwen3-0.6b")
