@@ -166,11 +166,7 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH, A> &G, MCursor &c, con
                                          int &left) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if constexpr (XL) {
-      const uint8_t *xp = xl + xloff + 128 * c.g;
-      G.xa[u] = *(const typename A::vec *)(xp);
-      G.xb[u] = *(const typename A::vec *)(xp + 16);
-    } else {
+    if constexpr (!XL) {  // with XL, mg_compute reads x from LDS
       const QD_GLOBAL uint8_t *xg = (const QD_GLOBAL uint8_t *)(x + 64 * c.g);
       G.xa[u] = __builtin_bit_cast(typename A::vec, *(const QD_GLOBAL u32x4 *)(xg + xoff));
       G.xb[u] = __builtin_bit_cast(typename A::vec, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
@@ -202,20 +198,6 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH, A> &G, MCursor &c, con
   }
 }
 
-// The x part of a buffer issued before x was staged, again from LDS (a
-// prologue's row exists only there): the same walk as mg_issue's.
-template <int R, int U, bool CH, class A>
-__device__ __forceinline__ void mg_reload_x(MGroup<R, U, CH, A> &G, MCursor c, const MShape &S,
-                                            const uint8_t *xl, uint32_t xloff, int left) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint8_t *xp = xl + xloff + 128 * c.g;
-    G.xa[u] = *(const typename A::vec *)(xp);
-    G.xb[u] = *(const typename A::vec *)(xp + 16);
-    mc_next(c, S, left);
-  }
-}
-
 // Output of one finished tile (KS = 1): lane holds tokens 4*(lane/16)+v of
 // weight row lane%16 of each 16-row block.
 template <int R, class A>
@@ -237,10 +219,11 @@ __device__ __forceinline__ void mg_store(floatx4 (&acc)[R], const MShape &S,
 
 // Items past the end of the walk (padding up to a whole buffer) are
 // computed with zero scale and bias.
-template <int R, int U, bool CH, bool STORE, class A>
+template <int R, int U, bool CH, bool STORE, bool XL, class A>
 __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH, A> &G, floatx4 (&acc)[R],
                                            MCursor &c, const MShape &S, const AffineGroup &grp,
-                                           int &left, int m, int lane, typename A::vec ones) {
+                                           int &left, int m, int lane, typename A::vec ones,
+                                           const uint8_t *xl, uint32_t xloff) {
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   const int src4 = (4 * (lane & 15) + (lane >> 4)) * 4;
   const int srcs = (lane & 15) * 4, srcb = srcs + 64;
@@ -248,8 +231,20 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH, A> &G, floatx4
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int valid = left > 0;  // wave-uniform
-    floatx4 Sx = A::mfma(G.xa[u], ones, z);
-    Sx = A::mfma(G.xb[u], ones, Sx);
+    // x from LDS here rather than with the loads: holding every group's x
+    // fragments in registers from issue to use cost 64 VGPRs, one workgroup
+    // per CU instead of two (151936 x 1024 at M = 4: 3.9 -> 4.4 TB/s)
+    typename A::vec xa, xb;
+    if constexpr (XL) {
+      const uint8_t *xp = xl + xloff + 128 * c.g;
+      xa = *(const typename A::vec *)(xp);
+      xb = *(const typename A::vec *)(xp + 16);
+    } else {
+      xa = G.xa[u];
+      xb = G.xb[u];
+    }
+    floatx4 Sx = A::mfma(xa, ones, z);
+    Sx = A::mfma(xb, ones, Sx);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // lane 16*g4 + n takes row n's quarter g4 from lane 4*n + g4
@@ -258,8 +253,8 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH, A> &G, floatx4
                        (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.y),
                        (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.z),
                        (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)ql.w)};
-      floatx4 P = A::mfma(G.xa[u], A::codes(q.x, q.y), z);
-      P = A::mfma(G.xb[u], A::codes(q.z, q.w), P);
+      floatx4 P = A::mfma(xa, A::codes(q.x, q.y), z);
+      P = A::mfma(xb, A::codes(q.z, q.w), P);
       float s, b;
       if constexpr (CH) {
         if ((u & 1) == 0) {
@@ -502,8 +497,6 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   ci.g = cc.g = S.ga;
   int li = n, lc = n;
   MGroup<R, U, CH, Act> A, B;
-  const MCursor c0 = ci;
-  const int l0 = li;
   // the first buffer's codes and scales are in flight while x is staged;
   // a prologue's inputs are loaded first, so that waiting for them does not
   // wait for the weights
@@ -514,21 +507,18 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     // numbers of loads in flight, the memory waits would be counted for
     // the path with fewer (and wait for the weights here too)
     if (n > 0) {
-      mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
       stage_x_pro<PRO>(xl, cols, pro, pin);
     } else {
       stage_x_pro<PRO>(xl, cols, pro, pin);
     }
   } else if (n > 0) {
-    mg_issue<R, U, CH, false, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+    mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
   }
   if constexpr (XL) {
     if constexpr (PRO == 0) stage_x(xl, x, m, cols);
     // LDS writes done, then the barrier (global loads stay in flight)
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // the first buffer read the untransformed x from memory
-    if constexpr (PRO != 0)
-      if (n > 0) mg_reload_x<R, U, CH, Act>(A, c0, S, xl, xloff, l0);
   }
   if (n > 0) {
     // Loads are never conditional (the compiler then waits for exactly the
@@ -536,17 +526,17 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     // is issued before the current one is consumed.
     for (;;) {
       if (lc <= U) {
-        mg_compute<R, U, CH, KS == 1, Act>(A, acc, cc, S, grp, lc, m, lane, ones);
+        mg_compute<R, U, CH, KS == 1, XL, Act>(A, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
         break;
       }
       mg_issue<R, U, CH, XL, Act>(B, ci, S, grp, x, xoff, xl, xloff, lane, li);
-      mg_compute<R, U, CH, KS == 1, Act>(A, acc, cc, S, grp, lc, m, lane, ones);
+      mg_compute<R, U, CH, KS == 1, XL, Act>(A, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
       if (lc <= U) {
-        mg_compute<R, U, CH, KS == 1, Act>(B, acc, cc, S, grp, lc, m, lane, ones);
+        mg_compute<R, U, CH, KS == 1, XL, Act>(B, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
         break;
       }
       mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
-      mg_compute<R, U, CH, KS == 1, Act>(B, acc, cc, S, grp, lc, m, lane, ones);
+      mg_compute<R, U, CH, KS == 1, XL, Act>(B, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
     }
   }
   if constexpr (KS > 1) {
