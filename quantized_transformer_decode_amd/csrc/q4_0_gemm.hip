@@ -27,6 +27,13 @@
 // fragment read's 16 rows over all banks) with the deltas in fp32
 // ([64][4]), and every wave reads its B fragments there.
 //
+// Launches with fewer output tiles than two per CU (the 1280-row matrices
+// of a Whisper-large layer: 240 tiles at 1500 frames) run eight waves per
+// workgroup instead: two K parts of four waves, each with its own codes
+// buffers, the second part's partial tile added to the first's through LDS
+// at the end -- two waves per SIMD instead of one (1280 x 1280: 18.0 ->
+// 16.7 us, 1280 x 5120: 56.0 -> 49.0 us).
+//
 // Pipeline, one barrier per stage.  After the barrier of stage s, a wave
 // issues the loads of its x tile of stage s+1 and of the raw blocks of stage
 // s+2 (two register sets of these; the loop is unrolled twice so that no set
@@ -75,20 +82,24 @@ struct XRegs {
   u32x4 a[8];
 };
 // The 20-byte window around the Q4_0 block this thread converts.
+constexpr int kWaves = 4;  // waves per K part
+
 struct RawRegs {
   u32x4 w4;
   uint32_t w1;
 };
 
-template <int WAVES, bool MULTI, bool EPI>
+template <int WAVES, int KS, bool MULTI, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void q4_0_gemm_kernel(
     const Q40Group grp, int cols, const uint16_t *__restrict__ x, int m) {
-  constexpr int THREADS = WAVES * 64;
-  constexpr int BM = WAVES * 32;
-  constexpr int H = THREADS / (BN * NB);  // threads per block of a stage: 1 or 2
+  constexpr int FW = WAVES / KS;          // waves per K part (each 32 frames)
+  constexpr int PTHREADS = FW * 64;       // threads per K part
+  constexpr int BM = FW * 32;
+  constexpr int H = PTHREADS / (BN * NB);  // threads per block of a stage: 1 or 2
   static_assert(H == 1 || H == 2, "one block or half a block per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t codes[2][BN * LDB];
-  __shared__ __attribute__((aligned(16))) float deltas[2][BN * NB];
+  static_assert(KS == 1 || KS == 2, "K in one or two parts");
+  __shared__ __attribute__((aligned(16))) uint16_t codes_all[KS][2][BN * LDB];
+  __shared__ __attribute__((aligned(16))) float deltas_all[KS][2][BN * NB];
   // each wave's x tile of the current stage: 32 frames x 16 chunks of 8
   // BF16, chunk c of frame r stored at position c ^ (r % 16)
   __shared__ __attribute__((aligned(16))) u32x4 xs[WAVES][32 * 16];
@@ -107,12 +118,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const int rows = grp.rows[k];
   QD_GLOBAL float *y = gp(grp.y[k]);
   const float *bias = grp.bias[k];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uni(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = uni((int)threadIdx.x >> 6);
+  // K part of this wave, and its place among the part's waves
+  const int part = KS == 1 ? 0 : uni(wave / FW);
+  const int fw = KS == 1 ? wave : uni(wave - part * FW);
+  const int tid = (int)threadIdx.x - part * PTHREADS;
+  uint16_t(&codes)[2][BN * LDB] = codes_all[part];
+  float(&deltas)[2][BN * NB] = deltas_all[part];
   const int m0 = blockIdx.y * BM;
   const int n0 = (bx - grp.tile0[k]) * BN;
-  const int nstages = cols / BK;
+  const int nstages = cols / BK / KS;     // stages of this part
+  const int sbase = part * nstages;        // its first stage
   const int nb = cols >> 5;  // Q4_0 blocks per weight row (a multiple of 8)
   const int mrem = min(m - m0, BM), rrem = min(rows - n0, BN);
 
@@ -132,7 +149,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   int xoff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = min(wave * 32 + 4 * j + (lane >> 4), mrem - 1);
+    const int r = min(fw * 32 + 4 * j + (lane >> 4), mrem - 1);
     xoff[j] = r * cols * 2 + (lane & 15) * 16;
   }
   u32x4 *xw = xs[wave];
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const bool codd = cb & 1;
 
   auto load_x = [&](XRegs &X, int s) {
-    const int so = uni(s * BK * 2);
+    const int so = uni((sbase + s) * BK * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       X.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j], so, 0));
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int j = 0; j < 8; ++j) xw[xput[j]] = X.a[j];
   };
   auto load_raw = [&](RawRegs &R, int s) {
-    const int so = uni(s * NB * 18);
+    const int so = uni((sbase + s) * NB * 18);
     R.w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, woff, so, 0));
     R.w1 = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 16, so, 0);
   };
@@ -301,11 +318,34 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int i = 0; i < 4; ++i) convert_part(R0, 0, i);
   put_x(X);
-  for (int s = 0; s < nstages; s += 2) {
+  int s = 0;
+  for (; s + 1 < nstages; s += 2) {
     step(s, R1, R0);
     step(s + 1, R0, R1);
   }
+  if (s < nstages) step(s, R1, R0);  // an odd stage count (K in two parts)
   scale_prev();
+  if constexpr (KS == 2) {
+    // part 1 hands its partial tile to part 0 through LDS (over the codes
+    // buffers, free once every wave is past its last stage)
+    float *red = reinterpret_cast<float *>(&codes_all[0][0][0]);
+    static_assert(sizeof(codes_all) >= FW * TM * TN * 4 * 64 * sizeof(float), "LDS for the partial tiles");
+    __syncthreads();
+    if (part == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          *(floatx4 *)(red + (((fw * TM + i) * TN + j) * 64 + lane) * 4) = acc[i][j];
+    }
+    __syncthreads();
+    if (part == 1) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] += *(const floatx4 *)(red + (((fw * TM + i) * TN + j) * 64 + lane) * 4);
+  }
 
   float bj[TN];
 #pragma unroll
@@ -323,7 +363,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         const int n = n0 + j * 16 + (lane & 15);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int t = m0 + wave * 32 + i * 16 + (lane >> 4) * 4 + v;
+          const int t = m0 + fw * 32 + i * 16 + (lane >> 4) * 4 + v;
           if (t < m && n < rows)
             y[(size_t)t * rows + n] = EPI ? act(acc[i][j][v] + bj[j]) : acc[i][j][v];
         }
@@ -335,19 +375,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     store([](float v) { return v; });
 }
 
-template <int WAVES, bool MULTI, bool EPI>
-hipError_t launch_tile(Q40Group g, int cols, const uint16_t *x, int m, hipStream_t stream) {
-  g.tile0[0] = 0;
-  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + BN - 1) / BN;
-  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
-  constexpr int BM = WAVES * 32;
-  dim3 grid(g.tile0[g.n], (m + BM - 1) / BM);
-  hipLaunchKernelGGL((q4_0_gemm_kernel<WAVES, MULTI, EPI>), grid, dim3(WAVES * 64), 0, stream, g,
-                     cols, x, m);
+template <int WAVES, int KS, bool MULTI, bool EPI>
+hipError_t launch_tile(const Q40Group &g, int cols, const uint16_t *x, int m, dim3 grid,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((q4_0_gemm_kernel<WAVES, KS, MULTI, EPI>), grid, dim3(WAVES * 64), 0, stream,
+                     g, cols, x, m);
   return hipGetLastError();
 }
 
-constexpr int kWaves = 4;
+// Launches with fewer output tiles than two per CU split K in two parts
+// inside each workgroup (eight waves: two waves per SIMD instead of one);
+// the parts' partial tiles are summed in LDS.
+template <bool MULTI, bool EPI>
+hipError_t launch_tiles(Q40Group g, int cols, const uint16_t *x, int m, hipStream_t stream) {
+  g.tile0[0] = 0;
+  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + BN - 1) / BN;
+  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
+  constexpr int BM = kWaves * 32;
+  const dim3 grid(g.tile0[g.n], (m + BM - 1) / BM);
+  int cus = device_cus();
+  if (cus < 1) cus = 256;
+  if ((long)grid.x * grid.y < 2L * cus)
+    return launch_tile<2 * kWaves, 2, MULTI, EPI>(g, cols, x, m, grid, stream);
+  return launch_tile<kWaves, 1, MULTI, EPI>(g, cols, x, m, grid, stream);
+}
 
 }  // namespace
 
@@ -357,10 +408,10 @@ hipError_t launch_q4_0_gemm(Q40Group g, int cols, const uint16_t *x, int m,
   bool epi = g.gelu != 0;
   for (int k = 0; k < g.n; ++k) epi = epi || g.bias[k] != nullptr;
   if (g.n > 1)
-    return epi ? launch_tile<kWaves, true, true>(g, cols, x, m, stream)
-               : launch_tile<kWaves, true, false>(g, cols, x, m, stream);
-  return epi ? launch_tile<kWaves, false, true>(g, cols, x, m, stream)
-             : launch_tile<kWaves, false, false>(g, cols, x, m, stream);
+    return epi ? launch_tiles<true, true>(g, cols, x, m, stream)
+               : launch_tiles<true, false>(g, cols, x, m, stream);
+  return epi ? launch_tiles<false, true>(g, cols, x, m, stream)
+             : launch_tiles<false, false>(g, cols, x, m, stream);
 }
 
 }  // namespace qd
