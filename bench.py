@@ -25,7 +25,8 @@ part of the path on its own workload:
   qwen3_1_7b_step        Qwen3-1.7B-shaped decode step at M = 1, 4, 10, 16
                          (graphs of one launch per stage: same-input GEMVs grouped)
   whisper_large_prefill  one Whisper-large layer's six projections at 1500 frames
-  whisper_large_decoder  32 layers x 6 Q4_0 GEMVs at batch 1 (q, k, v grouped)
+  whisper_large_decoder  32 layers x 6 Q4_0 GEMVs at batch 1 (one persistent launch;
+                         also 128 launches with q, k, v grouped)
   q4_0_bake              f32 -> Q4_0 of one Whisper-large layer
 All inputs are seeded synthetic data of the pages' shapes (see synth/).
 """
@@ -616,7 +617,19 @@ def row_whisper_large_decoder(qd, layers):
                 qd.qgemv_q4_0(w, r, c, x, y, 1)
                 i += 1
     g = capture(grouped)
-    ms = event_time(g.replay, 20, 3)
+    ms_graph = event_time(g.replay, 20, 3)
+    # the same 192 GEMVs as one persistent launch (128 stages: q, k, v share
+    # a stage)
+    stage_of = {"q": 0, "k": 0, "v": 0, "o": 1, "fc1": 2, "fc2": 3}
+    sops = qd.make_q4_0_ops((w, x, y, r, c, 4 * (i // 6) + stage_of[name])
+                            for i, (name, w, r, c, x, y) in enumerate(ops))
+    nbytes = qd.qgemv_q4_0_step_workspace_bytes(sops, 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    plan = qd.qgemv_q4_0_step_plan(sops, 1, ws, nbytes)
+    gp_ = capture(lambda: qd.qgemv_q4_0_step_run(plan))
+    ms_pers = event_time(gp_.replay, 20, 3)
+    assert qd.qgemv_q4_0_step_check(plan) == 0
+    ms = min(ms_graph, ms_pers)
     g192 = capture(lambda: [qd.qgemv_q4_0(w, r, c, x, y, 1) for _, w, r, c, x, y in ops])
     ms192 = event_time(g192.replay, 20, 3)
     # the same step as the page's q_linear calls: biases (none for k) and
@@ -669,7 +682,9 @@ def row_whisper_large_decoder(qd, layers):
     return {"gemvs": len(ops), "weight_bytes": wb, "ms_per_step": ms,
             "tokens_per_s": 1000.0 / ms, "weight_GBps": wb / (ms * 1e-3) / 1e9,
             "hbm_peak_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "variant": "128 launches (q, k, v grouped) in a HIP graph",
+            "variant": ("one persistent launch (128 stages)" if ms_pers <= ms_graph
+                        else "128 launches (q, k, v grouped) in a HIP graph"),
+            "ms_persistent_step": ms_pers, "ms_128_launches": ms_graph,
             "ms_per_step_192_launches": ms192,
             "ms_per_step_q_linear": ms_lin,
             "with_cross_q_o": {"weight_bytes": wb_cross, "ms_per_step": ms_x,

@@ -190,6 +190,7 @@ typedef struct {
   const void *tail_w, *tail_x;
   void *tail_y;
   int64_t tail_rows, tail_cols;
+  int32_t format;     /* 0: affine-INT8 g64 plan, 1: Q4_0 plan (qgemv_q4_0_step_*) */
 } qd_step_plan;
 
 /* Workspace bytes needed by _step_plan for these ops (0 if invalid). */
@@ -229,6 +230,42 @@ qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream);
  * not match the plan. */
 qd_status qgemv_affine_i8_g64_step_check(const qd_step_plan *plan,
                                          uint32_t *error_bits, void *stream);
+
+/* The same single-launch step for Q4_0 GEMVs (the projections of a Whisper
+ * decoder layer in decoder order: fuel-transformers 0.19.1,
+ * lazy_quantized_whisper.rs -- decoder_layer applies q, k, v, then o, then
+ * fc1, then fc2): y[m, rows] = x[m, cols] W^T with the operation, layouts and
+ * f32 arithmetic of qgemv_q4_0 (no bias or GELU: q_linear's epilogue stays
+ * with qlinear_q4_0_gemv).  Stage rules as qd_affine_gemv_op. */
+typedef struct {
+  const void *w_q4_0; /* device, Q4_0 stream [rows, cols], 16-byte aligned   */
+  const float *x;     /* device, f32 [m, cols], 16-byte aligned             */
+  float *y;           /* device, f32 [m, rows], 4-byte aligned              */
+  int64_t rows, cols; /* rows >= 1; cols % 256 == 0, 256 <= cols <= 8192    */
+  int64_t stage;
+} qd_q4_0_gemv_op;
+
+/* Workspace bytes needed by qgemv_q4_0_step_plan for these ops (0 if
+ * invalid). */
+size_t qgemv_q4_0_step_workspace_bytes(const qd_q4_0_gemv_op *ops, int64_t n_ops, int64_t m);
+
+/* As qgemv_affine_i8_g64_step_plan, for Q4_0 ops: m == 1; ops of one stage
+ * share cols; per stage sum(m*ceil(cols/2048)*2048) <= 16384 and
+ * sum(m*cols) <= 64 * (compute units of the device) (QD_ESHAPE); no output
+ * may overlap any op's weights, input or output, or the workspace
+ * (QD_EINVAL).  Sets plan->format = 1 and plan->tail = 0 (every stage runs in
+ * the persistent kernel). */
+qd_status qgemv_q4_0_step_plan(const qd_q4_0_gemv_op *ops, int64_t n_ops, int64_t m,
+                               void *workspace, size_t workspace_bytes, qd_step_plan *plan,
+                               void *stream);
+
+/* Enqueues a Q4_0 plan as ONE persistent kernel, with the guarantees and
+ * limits of qgemv_affine_i8_g64_step_run.  QD_EINVAL for a plan of the other
+ * format (and _step_run of the affine format rejects a Q4_0 plan). */
+qd_status qgemv_q4_0_step_run(const qd_step_plan *plan, void *stream);
+
+/* qgemv_affine_i8_g64_step_check for a Q4_0 plan (same error bits). */
+qd_status qgemv_q4_0_step_check(const qd_step_plan *plan, uint32_t *error_bits, void *stream);
 
 /* ---- ggml Q4_0 ------------------------------------------------------------ */
 

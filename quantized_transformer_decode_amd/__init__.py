@@ -37,6 +37,8 @@ EXPORTS = (
     "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16",
     "qwen3_step_workspace_bytes", "qwen3_step_run", "qwen3_step_check",
     "qwen3_step_workspace_offset", "attention_decode_noalloc",
+    "qgemv_q4_0_step_workspace_bytes", "qgemv_q4_0_step_plan", "qgemv_q4_0_step_run",
+    "qgemv_q4_0_step_check",
 )
 
 
@@ -90,7 +92,13 @@ class StepPlan(ctypes.Structure):
                 ("magic", ctypes.c_uint32), ("tail", ctypes.c_int32),
                 ("tail_w", ctypes.c_void_p), ("tail_x", ctypes.c_void_p),
                 ("tail_y", ctypes.c_void_p), ("tail_rows", ctypes.c_int64),
-                ("tail_cols", ctypes.c_int64)]
+                ("tail_cols", ctypes.c_int64), ("format", ctypes.c_int32)]
+
+
+class Q40GemvOp(ctypes.Structure):
+    """qd_q4_0_gemv_op"""
+    _fields_ = [("w_q4_0", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("stage", ctypes.c_int64)]
 
 
 class QDError(RuntimeError):
@@ -142,6 +150,12 @@ def lib() -> ctypes.CDLL:
         L.qgemv_affine_i8_g64_step_plan.argtypes = [OPS, I64, I64, P, SZ, PLAN, P]
         L.qgemv_affine_i8_g64_step_run.argtypes = [PLAN, P]
         L.qgemv_affine_i8_g64_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
+        QOPS = ctypes.POINTER(Q40GemvOp)
+        L.qgemv_q4_0_step_workspace_bytes.argtypes = [QOPS, I64, I64]
+        L.qgemv_q4_0_step_workspace_bytes.restype = SZ
+        L.qgemv_q4_0_step_plan.argtypes = [QOPS, I64, I64, P, SZ, PLAN, P]
+        L.qgemv_q4_0_step_run.argtypes = [PLAN, P]
+        L.qgemv_q4_0_step_check.argtypes = [PLAN, ctypes.POINTER(ctypes.c_uint32), P]
         L.qd_stream_read.argtypes = [P, SZ, P, P]
         L.qgemv_affine_i8_g64_f16.argtypes = [P, I64, I64, P, P, I64, P]
         LIN = ctypes.POINTER(Q40LinearItem)
@@ -174,7 +188,8 @@ def lib() -> ctypes.CDLL:
                   "qd_stream_read", "qgemv_affine_i8_g64_f16", "affine_i8_g64_embed_rows",
                   "qlinear_q4_0_gemv", "qlinear_q4_0_gemm", "attention_decode",
                   "rmsnorm_f16", "qk_norm_rope_f16", "silu_mul_f16", "qwen3_step_run",
-                  "qwen3_step_check", "attention_decode_noalloc"):
+                  "qwen3_step_check", "attention_decode_noalloc", "qgemv_q4_0_step_plan",
+                  "qgemv_q4_0_step_run", "qgemv_q4_0_step_check"):
             getattr(L, n).restype = I
         _lib = L
     return _lib
@@ -437,6 +452,43 @@ def qgemv_affine_i8_g64_step_plan(ops, m, workspace, workspace_bytes: int,
 def qgemv_affine_i8_g64_step_run(plan: StepPlan, stream=None) -> None:
     _check("qgemv_affine_i8_g64_step_run",
            lib().qgemv_affine_i8_g64_step_run(ctypes.byref(plan), _stream(stream)))
+
+
+def make_q4_0_ops(specs):
+    """specs: iterable of (w_q4_0, x_f32, y_f32, rows, cols, stage) with
+    tensors or raw device addresses -> ctypes array of Q40GemvOp."""
+    specs = list(specs)
+    arr = (Q40GemvOp * len(specs))()
+    for i, (w, x, y, rows, cols, stage) in enumerate(specs):
+        arr[i] = Q40GemvOp(_ptr(w), _ptr(x), _ptr(y), rows, cols, stage)
+    return arr
+
+
+def qgemv_q4_0_step_workspace_bytes(ops, m: int = 1) -> int:
+    return int(lib().qgemv_q4_0_step_workspace_bytes(ops, len(ops), m))
+
+
+def qgemv_q4_0_step_plan(ops, m, workspace, workspace_bytes: int, stream=None) -> StepPlan:
+    plan = StepPlan()
+    _check("qgemv_q4_0_step_plan", lib().qgemv_q4_0_step_plan(
+        ops, len(ops), m, _ptr(workspace), workspace_bytes, ctypes.byref(plan),
+        _stream(stream)))
+    return plan
+
+
+def qgemv_q4_0_step_run(plan: StepPlan, stream=None) -> None:
+    _check("qgemv_q4_0_step_run", lib().qgemv_q4_0_step_run(ctypes.byref(plan), _stream(stream)))
+
+
+def qgemv_q4_0_step_check(plan: StepPlan, stream=None) -> int:
+    """Synchronise and return the step's error word (raises QDError if set)."""
+    bits = ctypes.c_uint32(0)
+    st = lib().qgemv_q4_0_step_check(ctypes.byref(plan), ctypes.byref(bits), _stream(stream))
+    if st not in (QD_OK, QD_ESTEP):
+        _check("qgemv_q4_0_step_check", st)
+    if st == QD_ESTEP:
+        raise QDError(f"qgemv_q4_0_step_check (error bits {bits.value:#x})", st)
+    return bits.value
 
 
 def qgemv_affine_i8_g64_step_check(plan: StepPlan, stream=None) -> int:

@@ -1,5 +1,6 @@
 // decode_step.hip -- one persistent launch for a whole decode step's
-// affine-INT8 g64 GEMVs, in stage order (M = 1).
+// GEMVs, in stage order (M = 1): affine-INT8 g64 ops (BF16), or Q4_0 ops
+// (f32, the Whisper decoder's projections).
 //
 // turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step
 // encodes every projection GEMV of a generated token, in decoder order, into
@@ -26,6 +27,13 @@
 // modulo the group sizes), so nothing is cleared between launches or graph
 // replays.  The first stage's input is read straight from the ops' inputs,
 // which are written before the launch.
+//
+// Q4_0 ops: a work item is 64 blocks (2048 columns) of one row, lane l
+// holding block l in the 20-byte window that starts 2 bytes early for odd
+// blocks (the Q4_0 GEMV's load form; a row's block count is a multiple of 8,
+// so a block's parity is its lane's); the staged input goes to LDS as fp32
+// in a layout where lane l's eight float4 of block l are conflict-free; the
+// exchange words are the f32 inputs themselves.
 //
 // Workgroup layout: wave 0 is the poller (publishes, polls the next input
 // into LDS as fp32, hands it to the compute waves through an LDS flag);
@@ -110,9 +118,26 @@ struct Walk {
   OpView op;
 };
 
-struct Group {
+// Columns of one work item: a 1 KiB row chunk of affine codes, or 64 Q4_0
+// blocks.
+template <bool Q4>
+constexpr int kItemCols = Q4 ? 2048 : 1024;
+
+template <bool Q4>
+struct Loads;
+template <>
+struct Loads<false> {
   uint4 q[G];
   uint16_t sc[G], bi[G];  // raw BF16 bits; combined only when consumed
+};
+template <>
+struct Loads<true> {
+  u32x4 w4[G];            // the 20-byte block windows
+  uint32_t w1[G];
+};
+
+template <bool Q4>
+struct Group : Loads<Q4> {
   Walk start;             // where the group begins (kept from the issue)
   int i0, s;              // the group's first item and its stage
 };
@@ -191,7 +216,8 @@ __device__ __forceinline__ void walk_next(Walk &w, const StepOp *ops) {
 // past a row's end re-read its first chunk): the compiler can then wait for
 // exactly this group's loads before it is consumed, instead of for every
 // load in flight (which would include the next group's prefetch).
-__device__ __forceinline__ void issue_walk(Group &g, const StepOp *ops, Walk wk, Cursor c,
+template <bool Q4>
+__device__ __forceinline__ void issue_walk(Group<Q4> &g, const StepOp *ops, Walk wk, Cursor c,
                                            int lane) {
   c.s = uni(c.s);
   c.i = uni(c.i);
@@ -201,22 +227,35 @@ __device__ __forceinline__ void issue_walk(Group &g, const StepOp *ops, Walk wk,
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     const int lrow = wk.row - wk.op.row_base;
-    int col = wk.ch * 1024 + lane * 16;
-    if (col >= wk.op.cols) col = 0;
-    const u32x4 v = __builtin_nontemporal_load(
-        (const QD_GLOBAL u32x4 *)(wk.op.w + (size_t)lrow * wk.op.cols + col));
-    g.q[k] = make_uint4(v.x, v.y, v.z, v.w);
-    const int groups = wk.op.cols >> 6;
-    const QD_GLOBAL uint16_t *sc =
-        (const QD_GLOBAL uint16_t *)(wk.op.w + (size_t)wk.op.rows * wk.op.cols);
-    const size_t gi = (size_t)lrow * groups + (col >> 6);
-    g.sc[k] = sc[gi];
-    g.bi[k] = sc[(size_t)wk.op.rows * groups + gi];
+    if constexpr (Q4) {
+      // block ch*64 + lane of the row (lanes past the row re-read block 0 or
+      // 1, keeping their parity)
+      const int nb = wk.op.cols >> 5;
+      int blk = wk.ch * 64 + lane;
+      if (blk >= nb) blk = lane & 1;
+      const QD_GLOBAL uint8_t *p =
+          wk.op.w + 18 * ((size_t)lrow * nb + blk) - 2 * (lane & 1);
+      g.w4[k] = __builtin_nontemporal_load((const QD_GLOBAL u32x4 *)p);
+      g.w1[k] = __builtin_nontemporal_load((const QD_GLOBAL uint32_t *)(p + 16));
+    } else {
+      int col = wk.ch * 1024 + lane * 16;
+      if (col >= wk.op.cols) col = 0;
+      const u32x4 v = __builtin_nontemporal_load(
+          (const QD_GLOBAL u32x4 *)(wk.op.w + (size_t)lrow * wk.op.cols + col));
+      g.q[k] = make_uint4(v.x, v.y, v.z, v.w);
+      const int groups = wk.op.cols >> 6;
+      const QD_GLOBAL uint16_t *sc =
+          (const QD_GLOBAL uint16_t *)(wk.op.w + (size_t)wk.op.rows * wk.op.cols);
+      const size_t gi = (size_t)lrow * groups + (col >> 6);
+      g.sc[k] = sc[gi];
+      g.bi[k] = sc[(size_t)wk.op.rows * groups + gi];
+    }
     if (c.i + k + 1 < wk.n) walk_next(wk, ops);
   }
 }
 
-__device__ __forceinline__ void issue(Group &g, const StepOp *ops, const StepStage *stages,
+template <bool Q4>
+__device__ __forceinline__ void issue(Group<Q4> &g, const StepOp *ops, const StepStage *stages,
                                       Cursor c, int gw, int nw, int lane) {
   c.s = uni(c.s);
   c.i = uni(c.i);
@@ -226,8 +265,79 @@ __device__ __forceinline__ void issue(Group &g, const StepOp *ops, const StepSta
 // Compute one group (the items issue() loaded).  rowsum carries a row's
 // partial sum across groups.  The walk state comes from the issue, so the
 // only memory this touches is LDS and the weights already in registers.
-__device__ __forceinline__ void compute(const Group &g, const StepOp *ops, int lane,
-                                        const float *xl, float &rowsum) {
+// Q4_0 staging layout inside one 2048-column item: element 32*blk + 4*j4 + r
+// at float4 slot 8*blk + (j4 ^ ((blk >> 1) & 7)).  Lane blk reads its eight
+// slots; sixteen consecutive lanes then cover all 64 banks, and so do the
+// poller's writes of consecutive elements.
+__device__ __forceinline__ int xq4(int e) {
+  const int c = e & ~2047, r = e & 2047;
+  const int blk = r >> 5, j4 = (r >> 2) & 7;
+  return c + ((8 * blk + (j4 ^ ((blk >> 1) & 7))) << 2) + (r & 3);
+}
+
+// One Q4_0 work item: lane l holds block ch*64 + l (20-byte window w, odd
+// parity = lane & 1) against x[32 l .. 32 l + 31] in registers; returns
+// d * (sum_j q_j x_j - 8 * sum_j x_j).
+__device__ __forceinline__ float q4_item(const u32x4 w4, uint32_t w1, int lane,
+                                         const float4 (&xq)[8], float xs) {
+  const uint32_t w[5] = {w4.x, w4.y, w4.z, w4.w, w1};
+  const bool odd = lane & 1;
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t nib = odd ? w[k + 1] : __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);
+    const uint32_t lo = nib & 0x0f0f0f0fu, hi = (nib >> 4) & 0x0f0f0f0fu;
+    // low nibbles: elements 4k..4k+3; high nibbles: 16+4k..16+4k+3
+    s0 = fmaf(ubyte<0>(lo), xq[k].x, s0);
+    s0 = fmaf(ubyte<1>(lo), xq[k].y, s0);
+    s0 = fmaf(ubyte<2>(lo), xq[k].z, s0);
+    s0 = fmaf(ubyte<3>(lo), xq[k].w, s0);
+    s1 = fmaf(ubyte<0>(hi), xq[4 + k].x, s1);
+    s1 = fmaf(ubyte<1>(hi), xq[4 + k].y, s1);
+    s1 = fmaf(ubyte<2>(hi), xq[4 + k].z, s1);
+    s1 = fmaf(ubyte<3>(hi), xq[4 + k].w, s1);
+  }
+  const float d = f16_to_f32(odd ? (w[0] >> 16) : (w[0] & 0xffffu));
+  return d * fmaf(-8.f, xs, s0 + s1);
+}
+
+__device__ __forceinline__ void compute_q4(const Group<true> &g, const StepOp *ops, int lane,
+                                           const float *xl, float &rowsum) {
+  {
+    Walk wk = g.start;
+    int xkey = -1;
+    float4 xq[8];
+    float xs = 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (g.i0 + k < wk.n) {
+        const bool valid = wk.ch * 64 + lane < (wk.op.cols >> 5);
+        const int key = wk.o * 64 + wk.ch;
+        if (key != xkey) {
+          xkey = key;
+          const float *xp = xl + (wk.o - wk.op0) * (wk.chunks * 2048) + wk.ch * 2048;
+          xs = 0.f;
+#pragma unroll
+          for (int j4 = 0; j4 < 8; ++j4) {
+            xq[j4] = *(const float4 *)(xp + ((8 * lane + (j4 ^ ((lane >> 1) & 7))) << 2));
+            xs += (xq[j4].x + xq[j4].y) + (xq[j4].z + xq[j4].w);
+          }
+        }
+        float p = q4_item(g.w4[k], g.w1[k], lane, xq, xs);
+        if (!valid) p = 0.f;
+        rowsum += wave_sum_dpp(p);
+        if (wk.ch == wk.chunks - 1) {
+          if (lane == 0) ((QD_GLOBAL float *)wk.op.y)[wk.row - wk.op.row_base] = rowsum;
+          rowsum = 0.f;
+        }
+        if (g.i0 + k + 1 < wk.n) walk_next(wk, ops);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void compute_affine(const Group<false> &g, const StepOp *ops,
+                                               int lane, const float *xl, float &rowsum) {
   Walk wk = g.start;
   int xkey = -1;
   float4 x0, x1, x2, x3;
@@ -264,6 +374,15 @@ __device__ __forceinline__ void compute(const Group &g, const StepOp *ops, int l
   }
 }
 
+template <bool Q4>
+__device__ __forceinline__ void compute(const Group<Q4> &g, const StepOp *ops, int lane,
+                                        const float *xl, float &rowsum) {
+  if constexpr (Q4)
+    compute_q4(g, ops, lane, xl, rowsum);
+  else
+    compute_affine(g, ops, lane, xl, rowsum);
+}
+
 __device__ __forceinline__ void signal_done_through(Shared *sh, int &signalled, int upto) {
   // mark stages [signalled, upto) done for this wave
   if (signalled < upto) {
@@ -275,6 +394,7 @@ __device__ __forceinline__ void signal_done_through(Shared *sh, int &signalled, 
   }
 }
 
+template <bool Q4>
 __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
                              int n_stages, Shared *sh, const float *xbuf, int xmax,
                              uint32_t *err) {
@@ -288,7 +408,7 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
   int signalled = 0;
   float rowsum = 0.f;
   int have = 0;  // stages known staged
-  Group A, B;
+  Group<Q4> A, B;
 
   auto enter = [&](int s) {
     signal_done_through(sh, signalled, s);
@@ -325,7 +445,7 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
   // paths compute in their own branch, so each waits for exactly the loads
   // it consumes.
   Cursor c = normalize(stages, n_stages, Cursor{0, 0}, gw, nw);
-  auto run = [&](Group &cur, Group &nxt) -> bool {
+  auto run = [&](Group<Q4> &cur, Group<Q4> &nxt) -> bool {
     const Cursor n1 = normalize(stages, n_stages, Cursor{c.s, c.i + G}, gw, nw);
     if (n1.s == c.s) {
       issue(nxt, ops, stages, n1, gw, nw, lane);
@@ -362,21 +482,23 @@ struct PubSlice {
   uint32_t v;  // word a + lane
 };
 
+template <bool Q4>
 __device__ __forceinline__ uint32_t input_word(const StepOp *ops, const StepStage &st, int m,
                                                int i) {
-  const int w = m * st.cols / 2;  // words per op
+  const int w = Q4 ? m * st.cols : m * st.cols / 2;  // words per op (f32, or BF16 pairs)
   const int k = i / w;
   const QD_GLOBAL uint32_t *x = (const QD_GLOBAL uint32_t *)gp(ops[st.op0 + k].x);
   return x[i - k * w];
 }
 
+template <bool Q4>
 __device__ __forceinline__ PubSlice pub_load(const StepOp *ops, const StepStage &st, int m,
                                              int lane) {
   PubSlice p;
   const int words = st.words;
   p.a = (int)blockIdx.x << st.lg;
   p.b = min(p.a + (1 << st.lg), words);
-  p.v = (p.a + lane < p.b) ? input_word(ops, st, m, p.a + lane) : 0u;
+  p.v = (p.a + lane < p.b) ? input_word<Q4>(ops, st, m, p.a + lane) : 0u;
   return p;
 }
 
@@ -391,11 +513,14 @@ struct StagePlan {
   int pa, pb;           // this workgroup's published words [pa, pb)
 };
 
+template <bool Q4>
 __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepStage &st, int m) {
+  // 64-bit exchange words: four BF16 inputs, or two f32 (Q4_0)
+  constexpr int kLgPer64 = Q4 ? 1 : 2;
   StagePlan p;
   p.data = st.data;
   p.epo = m * st.cols;
-  p.xstride = st.chunks * 1024;
+  p.xstride = st.chunks * kItemCols<Q4>;
   int lo, hi, lo2, hi2;
   wave_rows(st, blockIdx.x * NCW, gridDim.x * NCW, lo, hi);
   wave_rows(st, blockIdx.x * NCW + NCW - 1, gridDim.x * NCW, lo2, hi2);
@@ -405,36 +530,42 @@ __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepSta
   } else {
     p.k0 = op_of_row(ops, st, lo) - st.op0;
     p.k1 = op_of_row(ops, st, hi2 - 1) - st.op0;
-    p.f0 = (p.k0 * p.epo) >> 2;
-    p.f1 = ((p.k1 + 1) * p.epo) >> 2;
+    p.f0 = (p.k0 * p.epo) >> kLgPer64;
+    p.f1 = ((p.k1 + 1) * p.epo) >> kLgPer64;
   }
   p.pa = (int)blockIdx.x << st.lg;
   p.pb = min(p.pa + (1 << st.lg), (int)st.words);
   return p;
 }
 
-// Four input elements (one 64-bit word) into LDS as fp32 (xswz layout).
-__device__ __forceinline__ void stage4(const StagePlan &pp, float *dst, int f, uint64_t v) {
-  // elements 4f .. 4f+3 lie in one op (each op's input is a multiple of 64
-  // elements) and land as one float4
-  const int e = 4 * f;
+// One 64-bit input word into LDS as fp32: four BF16 elements (xswz layout),
+// or two f32 elements (Q4_0, xq4 layout).
+template <bool Q4>
+__device__ __forceinline__ void stage_word(const StagePlan &pp, float *dst, int f, uint64_t v) {
+  // the word's elements lie in one op (each op's input is a multiple of 64
+  // elements) and land in one float4 slot
+  const int e = (Q4 ? 2 : 4) * f;
   int k = pp.k0;
   while (k < pp.k1 && e >= (k + 1) * pp.epo) ++k;
   const int r = e - k * pp.epo;
   const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  *(float4 *)(dst + k * pp.xstride + xswz(r)) =
-      make_float4(bf16_to_f32(lo & 0xffffu), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffffu),
-                  bf16_to_f32(hi >> 16));
+  if constexpr (Q4)
+    *(float2 *)(dst + k * pp.xstride + xq4(r)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
+  else
+    *(float4 *)(dst + k * pp.xstride + xswz(r)) =
+        make_float4(bf16_to_f32(lo & 0xffffu), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffffu),
+                    bf16_to_f32(hi >> 16));
 }
 
 // A released stage input into LDS: agent-scope loads of the published
 // words (every load of an op in flight at once), then each lane's 64-bit
 // words go to LDS as float4s.  Lane l takes words l, l + 64, ... of each
 // op, so its LDS addresses advance by a constant: no per-element search.
+template <bool Q4>
 __device__ void read_stage(const StagePlan &pp, float *dst, int lane) {
   constexpr int B = 16;
   const uint64_t *src = (const uint64_t *)pp.data;
-  const int wpo = pp.epo >> 2;  // 64-bit words per op (a multiple of 16)
+  const int wpo = pp.epo >> (Q4 ? 1 : 2);  // 64-bit words per op (a multiple of 16)
   for (int k = pp.k0; k <= pp.k1; ++k) {
     const uint64_t *op = src + (size_t)k * wpo;
     float *od = dst + k * pp.xstride;
@@ -447,9 +578,12 @@ __device__ void read_stage(const StagePlan &pp, float *dst, int lane) {
         const int f = base + b * 64 + lane;
         if (f < wpo) {
           const uint32_t lo = (uint32_t)v[b], hi = (uint32_t)(v[b] >> 32);
-          *(float4 *)(od + xswz(4 * f)) =
-              make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
+          if constexpr (Q4)
+            *(float2 *)(od + xq4(2 * f)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
+          else
+            *(float4 *)(od + xswz(4 * f)) =
+                make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                            __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
         }
       }
     }
@@ -458,11 +592,14 @@ __device__ void read_stage(const StagePlan &pp, float *dst, int lane) {
 
 // The first stage's input, straight from the ops' inputs (written before
 // the launch).
+template <bool Q4>
 __device__ void read_first_stage(const StagePlan &pp, const StepOp *ops, const StepStage &st,
                                  float *dst, int lane) {
+  constexpr int kEsz = Q4 ? 4 : 2;  // bytes per input element
   for (int f = pp.f0 + lane; f < pp.f1; f += 64) {
-    const int e = 4 * f, k = e / pp.epo;
-    stage4(pp, dst, f, *(const QD_GLOBAL uint64_t *)(gp(ops[st.op0 + k].x) + (e - k * pp.epo)));
+    const int e = (Q4 ? 2 : 4) * f, k = e / pp.epo;
+    const QD_GLOBAL uint8_t *x = (const QD_GLOBAL uint8_t *)gp(ops[st.op0 + k].x);
+    stage_word<Q4>(pp, dst, f, *(const QD_GLOBAL uint64_t *)(x + (size_t)(e - k * pp.epo) * kEsz));
   }
 }
 
@@ -493,6 +630,7 @@ __device__ __forceinline__ void arrive(uint32_t *ctr, uint32_t *rel, int s, uint
     for (int k = lane; k < nwg; k += kWave) st_agent(rel + (size_t)k * kStepLine, tag);
 }
 
+template <bool Q4>
 __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
                             int n_stages, int m, Shared *sh, float *xbuf, int xmax,
                             uint32_t *rel, uint32_t *ctr, uint32_t *err) {
@@ -506,12 +644,12 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
   // are loaded kPubRing stages ahead into an LDS ring so that publishing is
   // an LDS read and a store, never a wait on memory.
   for (int t = 1; t < kPubRing && t < n_stages; ++t) {
-    const PubSlice p = pub_load(ops, stages[t], m, lane);
+    const PubSlice p = pub_load<Q4>(ops, stages[t], m, lane);
     sh->pub[t][lane] = p.v;
   }
   PubSlice pending;
   int pending_stage = -1;
-  StagePlan cur = stage_plan(ops, stages[0], m);
+  StagePlan cur = stage_plan<Q4>(ops, stages[0], m);
   StagePlan nxt = cur;
   for (int s = 0; s < n_stages; ++s) {
     const uint32_t tag = epoch + (uint32_t)s;
@@ -528,21 +666,21 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
       }
     }
     if (s == 0)
-      read_first_stage(cur, ops, stages[0], xbuf, lane);
+      read_first_stage<Q4>(cur, ops, stages[0], xbuf, lane);
     else
-      read_stage(cur, xbuf + (s & 1) * xmax, lane);
+      read_stage<Q4>(cur, xbuf + (s & 1) * xmax, lane);
     // hand the staged input to the compute waves (LDS executes this wave's
     // data writes before the flag write)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (lane == 0) __hip_atomic_store(&sh->xready, s + 1, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_WORKGROUP);
     // resolve the next stage while the compute waves work
-    if (s + 1 < n_stages) nxt = stage_plan(ops, stages[s + 1], m);
+    if (s + 1 < n_stages) nxt = stage_plan<Q4>(ops, stages[s + 1], m);
     // load stage s + kPubRing's values; they are parked next iteration in the
     // slot of stage s, which was published at the end of the last iteration
     pending_stage = -1;
     if (s + kPubRing < n_stages) {
-      pending = pub_load(ops, stages[s + kPubRing], m, lane);
+      pending = pub_load<Q4>(ops, stages[s + kPubRing], m, lane);
       pending_stage = s + kPubRing;
     }
     // wait for every compute wave to finish stage s, then publish s+1
@@ -570,10 +708,11 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
   }
 }
 
-__global__ __launch_bounds__(kThreads) void affine_step_kernel(
-    const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
-    int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
-    uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
+template <bool Q4>
+__device__ __forceinline__ void step_body(const StepOp *__restrict__ ops,
+                                          const StepStage *__restrict__ stages, int n_stages,
+                                          int m, int xmax, int nwg, uint32_t *epoch_word,
+                                          uint32_t *rel, uint32_t *ctr, uint32_t *err) {
   if ((int)gridDim.x != nwg) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, 8u);
     return;
@@ -588,29 +727,46 @@ __global__ __launch_bounds__(kThreads) void affine_step_kernel(
   }
   __syncthreads();
   if (threadIdx.x < kWave)
-    poller_wave(ops, stages, n_stages, m, &sh, xbuf, xmax, rel, ctr, err);
+    poller_wave<Q4>(ops, stages, n_stages, m, &sh, xbuf, xmax, rel, ctr, err);
   else
-    compute_wave(ops, stages, n_stages, &sh, xbuf, xmax, err);
+    compute_wave<Q4>(ops, stages, n_stages, &sh, xbuf, xmax, err);
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(epoch_word, sh.epoch + (uint32_t)n_stages);
+}
+
+__global__ __launch_bounds__(kThreads) void affine_step_kernel(
+    const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
+    int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
+    uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
+  step_body<false>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+}
+
+__global__ __launch_bounds__(kThreads) void q4_0_step_kernel(
+    const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
+    int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
+    uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
+  step_body<true>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
 }
 
 }  // namespace
 
 int step_threads() { return kThreads; }
 
-hipError_t launch_affine_step(const StepOp *ops, const StepStage *stages, int n_stages, int m,
-                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel,
-                              uint32_t *ctr, uint32_t *err, size_t lds_bytes,
-                              hipStream_t stream) {
+hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
+                       int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
+                       uint32_t *err, size_t lds_bytes, hipStream_t stream) {
+  const void *fn = q4 ? (const void *)q4_0_step_kernel : (const void *)affine_step_kernel;
   if (lds_bytes > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)affine_step_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(affine_step_kernel, dim3(nwg), dim3(kThreads), lds_bytes, stream, ops,
-                     stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  if (q4)
+    hipLaunchKernelGGL(q4_0_step_kernel, dim3(nwg), dim3(kThreads), lds_bytes, stream, ops,
+                       stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  else
+    hipLaunchKernelGGL(affine_step_kernel, dim3(nwg), dim3(kThreads), lds_bytes, stream, ops,
+                       stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
   return hipGetLastError();
 }
 

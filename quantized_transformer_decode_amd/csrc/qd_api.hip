@@ -114,19 +114,54 @@ constexpr int64_t kMaxStepOps = 65536;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// One GEMV of a decode step, either format (the public op structs differ
+// only in their pointer types).
+struct StepIn {
+  const void *w, *x;
+  void *y;
+  int64_t rows, cols, stage;
+};
+
+// What the two formats' step plans differ in.
+struct StepFormat {
+  bool q4;
+  int elem() const { return q4 ? 4 : 2; }        // bytes per input / output element
+  int chunk() const { return q4 ? 2048 : 1024; } // columns per work item
+  int per_word() const { return q4 ? 1 : 2; }    // input values per 32-bit exchange word
+  size_t weights(int64_t rows, int64_t cols) const {
+    return q4 ? q40_bytes(rows, cols) : affine_bytes(rows, cols);
+  }
+  bool cols_ok(int64_t cols) const {
+    return q4 ? cols % 256 == 0 && cols >= 256 && cols <= kMaxGemvCols
+              : cols % 64 == 0 && cols <= kMaxGemvCols;
+  }
+};
+
+std::vector<StepIn> step_in(const qd_affine_gemv_op *ops, int64_t n_ops) {
+  std::vector<StepIn> v((size_t)n_ops);
+  for (int64_t i = 0; i < n_ops; ++i)
+    v[i] = StepIn{ops[i].w_packed, ops[i].x_bf16, ops[i].y_bf16, ops[i].rows, ops[i].cols,
+                  ops[i].stage};
+  return v;
+}
+std::vector<StepIn> step_in(const qd_q4_0_gemv_op *ops, int64_t n_ops) {
+  std::vector<StepIn> v((size_t)n_ops);
+  for (int64_t i = 0; i < n_ops; ++i)
+    v[i] = StepIn{ops[i].w_q4_0, ops[i].x, ops[i].y, ops[i].rows, ops[i].cols, ops[i].stage};
+  return v;
+}
+
 // Validates a decode-step op list; on success fills the layout sizes.
-qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
+qd_status step_validate(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f,
                         size_t *ws_bytes, int *n_stages, int *xmax) {
   if (!ops || n_ops < 1 || n_ops > kMaxStepOps || m != 1) return QD_EINVAL;
   int stages = 0, cur_words = 0, max_words = 0;
-  size_t staging = 0;
   for (int64_t i = 0; i < n_ops; ++i) {
-    const qd_affine_gemv_op &o = ops[i];
-    if (!o.w_packed || !o.x_bf16 || !o.y_bf16) return QD_EINVAL;
+    const StepIn &o = ops[i];
+    if (!o.w || !o.x || !o.y) return QD_EINVAL;
     if (o.rows < 1 || o.rows > kMaxRows || o.cols < 1) return QD_EINVAL;
-    if (o.cols % 64 != 0 || o.cols > kMaxGemvCols) return QD_ESHAPE;
-    if (!aligned(o.w_packed, 16) || !aligned(o.x_bf16, 16) || !aligned(o.y_bf16, 2))
-      return QD_EALIGN;
+    if (!f.cols_ok(o.cols)) return QD_ESHAPE;
+    if (!aligned(o.w, 16) || !aligned(o.x, 16) || !aligned(o.y, f.elem())) return QD_EALIGN;
     if (i == 0) {
       if (o.stage != 0) return QD_EINVAL;
       stages = 1;
@@ -139,38 +174,38 @@ qd_status step_validate(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m,
     } else {
       return QD_EINVAL;
     }
-    // LDS holds each op's input in whole 1024-column chunks
-    cur_words += (int)(m * ((o.cols + 1023) / 1024) * 1024);
+    // LDS holds each op's input in whole chunks of the format's item width
+    cur_words += (int)(m * ((o.cols + f.chunk() - 1) / f.chunk()) * f.chunk());
     if (cur_words > kMaxStageWords) return QD_ESHAPE;
     if (cur_words > max_words) max_words = cur_words;
   }
   // outputs may not overlap any weights or inputs of the step
   for (int64_t i = 0; i < n_ops; ++i) {
-    const size_t ny = (size_t)m * ops[i].rows * 2;
+    const size_t ny = (size_t)m * ops[i].rows * f.elem();
     for (int64_t j = 0; j < n_ops; ++j) {
-      if (overlap(ops[i].y_bf16, ny, ops[j].w_packed, affine_bytes(ops[j].rows, ops[j].cols)) ||
-          overlap(ops[i].y_bf16, ny, ops[j].x_bf16, (size_t)m * ops[j].cols * 2))
+      if (overlap(ops[i].y, ny, ops[j].w, f.weights(ops[j].rows, ops[j].cols)) ||
+          overlap(ops[i].y, ny, ops[j].x, (size_t)m * ops[j].cols * f.elem()))
         return QD_EINVAL;
-      if (j > i && overlap(ops[i].y_bf16, ny, ops[j].y_bf16, (size_t)m * ops[j].rows * 2))
+      if (j > i && overlap(ops[i].y, ny, ops[j].y, (size_t)m * ops[j].rows * f.elem()))
         return QD_EINVAL;
     }
   }
   *n_stages = stages;
   *xmax = max_words;
   *ws_bytes = sizeof(qd::StepHeader) + align256(sizeof(qd::StepOp) * n_ops) +
-              align256(sizeof(qd::StepStage) * stages) + staging;
+              align256(sizeof(qd::StepStage) * stages);
   return QD_OK;
 }
 
-// Each workgroup publishes at most 64 words (128 BF16 values) of a stage's
-// input, one per lane, so a stage input may hold at most 128 values per
+// Each workgroup publishes at most 64 words of a stage's input, one per
+// lane: at most 128 BF16 values (affine) or 64 f32 values (Q4_0) per
 // workgroup.
-bool step_fits_grid(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg) {
+bool step_fits_grid(const StepIn *ops, int64_t n_ops, int64_t m, int nwg, StepFormat f) {
   int64_t i = 0;
   while (i < n_ops) {
     int64_t j = i, values = 0;
     while (j < n_ops && ops[j].stage == ops[i].stage) values += m * ops[j++].cols;
-    if (values > (int64_t)128 * nwg) return false;
+    if (values > (int64_t)64 * f.per_word() * nwg) return false;
     i = j;
   }
   return true;
@@ -178,18 +213,191 @@ bool step_fits_grid(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int 
 
 // Bytes after the tables: one release line per workgroup, the arrival
 // counter lines, and each stage's dense input (256-byte aligned).
-size_t step_exchange_bytes(const qd_affine_gemv_op *ops, int64_t n_ops, int64_t m, int nwg,
-                           int n_stages) {
+size_t step_exchange_bytes(const StepIn *ops, int64_t n_ops, int64_t m, int nwg, int n_stages,
+                           StepFormat f) {
   size_t bytes = align256((size_t)nwg * 128) +
                  align256((size_t)n_stages * (qd::kStepGroups + 1) * 128);
   int64_t i = 0;
   while (i < n_ops) {
     int64_t j = i, values = 0;
     while (j < n_ops && ops[j].stage == ops[i].stage) values += m * ops[j++].cols;
-    bytes += align256((size_t)values * 2);
+    bytes += align256((size_t)values * f.elem());
     i = j;
   }
   return bytes;
+}
+
+size_t step_workspace_bytes(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f) {
+  size_t bytes = 0;
+  int ns = 0, xmax = 0;
+  if (step_validate(ops, n_ops, m, f, &bytes, &ns, &xmax) != QD_OK) return 0;
+  // the staging layout depends on the grid: one workgroup per CU of the
+  // current device
+  if (check_device() != QD_OK) return 0;
+  const int nwg = current_cus();
+  if (nwg < kMinStepWgs || !step_fits_grid(ops, n_ops, m, nwg, f)) return 0;
+  return bytes + step_exchange_bytes(ops, n_ops, m, nwg, ns, f);
+}
+
+qd_status step_plan(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f, void *workspace,
+                    size_t workspace_bytes, qd_step_plan *plan, void *stream) {
+  if (!workspace || !plan) return QD_EINVAL;
+  size_t need = 0;
+  int ns = 0, xmax = 0;
+  qd_status st = step_validate(ops, n_ops, m, f, &need, &ns, &xmax);
+  if (st != QD_OK) return st;
+  if (!aligned(workspace, 256)) return QD_EALIGN;
+  if (workspace_bytes < need) return QD_EINVAL;  // tables alone; staging checked below
+  for (int64_t i = 0; i < n_ops; ++i) {
+    const StepIn &o = ops[i];
+    if (overlap(workspace, workspace_bytes, o.w, f.weights(o.rows, o.cols)) ||
+        overlap(workspace, workspace_bytes, o.x, (size_t)m * o.cols * f.elem()) ||
+        overlap(workspace, workspace_bytes, o.y, (size_t)m * o.rows * f.elem()))
+      return QD_EINVAL;
+  }
+  st = check_device();
+  if (st != QD_OK) return st;
+  const int nwg = current_cus();
+  if (nwg < kMinStepWgs) return QD_EDEVICE;
+  if (!step_fits_grid(ops, n_ops, m, nwg, f)) return QD_ESHAPE;
+  need += step_exchange_bytes(ops, n_ops, m, nwg, ns, f);
+  if (workspace_bytes < need) return QD_EINVAL;
+
+  // host image of header + tables; release lines and counters start zeroed
+  // (tag 0 is never expected: the epoch starts at 1)
+  const size_t ops_off = sizeof(qd::StepHeader);
+  const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * n_ops);
+  const size_t rel_off = stages_off + align256(sizeof(qd::StepStage) * ns);
+  const size_t ctr_off = rel_off + align256((size_t)nwg * 128);
+  const size_t data_off = ctr_off + align256((size_t)ns * (qd::kStepGroups + 1) * 128);
+  const size_t stg_off = rel_off;
+  std::vector<uint8_t> img(rel_off, 0);
+  qd::StepHeader *h = (qd::StepHeader *)img.data();
+  qd::StepOp *dops = (qd::StepOp *)(img.data() + ops_off);
+  qd::StepStage *dst = (qd::StepStage *)(img.data() + stages_off);
+  h->magic = qd::kStepMagic;
+  h->n_ops = (int32_t)n_ops;
+  h->n_stages = ns;
+  h->m = (int32_t)m;
+  h->nwg = nwg;
+  h->xmax = xmax;
+  h->ops_off = (uint32_t)ops_off;
+  h->stages_off = (uint32_t)stages_off;
+  h->rel_off = (uint32_t)rel_off;
+  h->ctr_off = (uint32_t)ctr_off;
+  h->data_off = (uint32_t)data_off;
+  h->lds_bytes = (uint32_t)(2 * (size_t)xmax * 4);
+  h->epoch = 1;
+  h->error = 0;
+  size_t data = data_off;
+  int s = -1;
+  for (int64_t i = 0; i < n_ops; ++i) {
+    const StepIn &o = ops[i];
+    if ((int)o.stage != s) {
+      s = (int)o.stage;
+      int64_t values = 0;
+      for (int64_t j = i; j < n_ops && ops[j].stage == o.stage; ++j) values += m * ops[j].cols;
+      const int64_t words = values / f.per_word();
+      dst[s].data = (uint32_t *)((uint8_t *)workspace + data);
+      dst[s].op0 = (int32_t)i;
+      dst[s].nops = 0;
+      dst[s].rows_total = 0;
+      dst[s].cols = (int32_t)o.cols;
+      dst[s].chunks = (int32_t)((o.cols + f.chunk() - 1) / f.chunk());
+      dst[s].words = (uint16_t)words;
+      dst[s].lg = (uint16_t)step_lg(words, nwg);
+      data += align256((size_t)values * f.elem());
+    }
+    qd::StepOp &d = dops[i];
+    d.w = (const uint8_t *)o.w;
+    d.x = (const uint16_t *)o.x;
+    d.y = (uint16_t *)o.y;
+    d.unused = nullptr;
+    d.rows = (int32_t)o.rows;
+    d.cols = (int32_t)o.cols;
+    d.stage = s;
+    d.row_base = dst[s].rows_total;
+    dst[s].rows_total += (int32_t)o.rows;
+    dst[s].nops += 1;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, hs);
+  if (e == hipSuccess)
+    e = hipMemsetAsync((uint8_t *)workspace + stg_off, 0, need - stg_off, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e);
+  plan->workspace = workspace;
+  plan->nwg = nwg;
+  plan->lds_bytes = (int32_t)h->lds_bytes;
+  plan->n_ops = (int32_t)n_ops;
+  plan->n_stages = ns;
+  plan->m = (int32_t)m;
+  plan->magic = qd::kStepMagic;
+  plan->format = f.q4 ? 1 : 0;
+  // a last stage of one very large affine GEMV streams faster as its own
+  // launch
+  const StepIn &last = ops[n_ops - 1];
+  const bool tail = !f.q4 && ns > 1 && (n_ops == 1 || ops[n_ops - 2].stage != last.stage) &&
+                    last.rows * last.cols >= kStepTailWeights;
+  plan->tail = tail ? 1 : 0;
+  plan->tail_w = tail ? last.w : nullptr;
+  plan->tail_x = tail ? last.x : nullptr;
+  plan->tail_y = tail ? last.y : nullptr;
+  plan->tail_rows = tail ? last.rows : 0;
+  plan->tail_cols = tail ? last.cols : 0;
+  return QD_OK;
+}
+
+qd_status step_run(const qd_step_plan *plan, bool q4, void *stream) {
+  if (!plan || !plan->workspace || plan->magic != qd::kStepMagic ||
+      plan->format != (q4 ? 1 : 0) || plan->nwg < 1 || plan->lds_bytes < 8 ||
+      plan->lds_bytes > 2 * kMaxStageWords * 4 || plan->lds_bytes % 8 != 0 ||
+      plan->n_ops < 1 || plan->n_stages < 1 || plan->n_stages > plan->n_ops ||
+      plan->m != 1 || plan->tail < 0 || plan->tail > 1 || (q4 && plan->tail) ||
+      (plan->tail && (plan->n_stages < 2 || !plan->tail_w || !plan->tail_x || !plan->tail_y ||
+                      plan->tail_rows < 1 || plan->tail_cols < 64 || plan->tail_cols % 64 ||
+                      plan->tail_cols > kMaxGemvCols)))
+    return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  if (current_cus() != plan->nwg) return QD_EDEVICE;
+  uint8_t *ws = (uint8_t *)plan->workspace;
+  const size_t ops_off = sizeof(qd::StepHeader);
+  const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * plan->n_ops);
+  qd::StepHeader *h = (qd::StepHeader *)ws;  // device address; never dereferenced here
+  const size_t rel_off = stages_off + align256(sizeof(qd::StepStage) * plan->n_stages);
+  const size_t ctr_off = rel_off + align256((size_t)plan->nwg * 128);
+  hipError_t e = qd::launch_step(
+      q4, (const qd::StepOp *)(ws + ops_off), (const qd::StepStage *)(ws + stages_off),
+      plan->n_stages - plan->tail, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch,
+      (uint32_t *)(ws + rel_off), (uint32_t *)(ws + ctr_off), &h->error,
+      (size_t)plan->lds_bytes, (hipStream_t)stream);
+  if (e == hipSuccess && plan->tail) {
+    qd::AffineGroup g = {};
+    g.n = 1;
+    g.w[0] = (const uint8_t *)plan->tail_w;
+    g.y[0] = (uint16_t *)plan->tail_y;
+    g.rows[0] = (int)plan->tail_rows;
+    e = qd::launch_affine_gemv(g, (int)plan->tail_cols, (const uint16_t *)plan->tail_x, 1, false,
+                               (hipStream_t)stream);
+  }
+  return e == hipSuccess ? QD_OK : hip_fail(e);
+}
+
+qd_status step_check(const qd_step_plan *plan, bool q4, uint32_t *error_bits, void *stream) {
+  if (!plan || !plan->workspace || plan->magic != qd::kStepMagic ||
+      plan->format != (q4 ? 1 : 0) || !error_bits)
+    return QD_EINVAL;
+  qd_status st = check_device();
+  if (st != QD_OK) return st;
+  uint32_t v = 0;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&v, (uint8_t *)plan->workspace + offsetof(qd::StepHeader, error),
+                                4, hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e);
+  *error_bits = v;
+  return v ? QD_ESTEP : QD_OK;
 }
 
 }  // namespace
@@ -473,174 +681,51 @@ extern "C" {
 
 size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
                                                 int64_t n_ops, int64_t m) {
-  size_t bytes = 0;
-  int ns = 0, xmax = 0;
-  if (step_validate(ops, n_ops, m, &bytes, &ns, &xmax) != QD_OK) return 0;
-  // the staging layout depends on the grid: one workgroup per CU of the
-  // current device
-  if (check_device() != QD_OK) return 0;
-  const int nwg = current_cus();
-  if (nwg < kMinStepWgs || !step_fits_grid(ops, n_ops, m, nwg)) return 0;
-  return bytes + step_exchange_bytes(ops, n_ops, m, nwg, ns);
+  if (!ops || n_ops < 1 || n_ops > kMaxStepOps) return 0;
+  const std::vector<StepIn> v = step_in(ops, n_ops);
+  return step_workspace_bytes(v.data(), n_ops, m, StepFormat{false});
 }
 
 qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
                                         int64_t n_ops, int64_t m,
                                         void *workspace, size_t workspace_bytes,
                                         qd_step_plan *plan, void *stream) {
-  if (!workspace || !plan) return QD_EINVAL;
-  size_t need = 0;
-  int ns = 0, xmax = 0;
-  qd_status st = step_validate(ops, n_ops, m, &need, &ns, &xmax);
-  if (st != QD_OK) return st;
-  if (!aligned(workspace, 256)) return QD_EALIGN;
-  if (workspace_bytes < need) return QD_EINVAL;  // tables alone; staging checked below
-  for (int64_t i = 0; i < n_ops; ++i) {
-    const qd_affine_gemv_op &o = ops[i];
-    if (overlap(workspace, workspace_bytes, o.w_packed, affine_bytes(o.rows, o.cols)) ||
-        overlap(workspace, workspace_bytes, o.x_bf16, (size_t)m * o.cols * 2) ||
-        overlap(workspace, workspace_bytes, o.y_bf16, (size_t)m * o.rows * 2))
-      return QD_EINVAL;
-  }
-  st = check_device();
-  if (st != QD_OK) return st;
-  const int nwg = current_cus();
-  if (nwg < kMinStepWgs) return QD_EDEVICE;
-  if (!step_fits_grid(ops, n_ops, m, nwg)) return QD_ESHAPE;
-  need += step_exchange_bytes(ops, n_ops, m, nwg, ns);
-  if (workspace_bytes < need) return QD_EINVAL;
-
-  // host image of header + tables; release lines and counters start zeroed
-  // (tag 0 is never expected: the epoch starts at 1)
-  const size_t ops_off = sizeof(qd::StepHeader);
-  const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * n_ops);
-  const size_t rel_off = stages_off + align256(sizeof(qd::StepStage) * ns);
-  const size_t ctr_off = rel_off + align256((size_t)nwg * 128);
-  const size_t data_off = ctr_off + align256((size_t)ns * (qd::kStepGroups + 1) * 128);
-  const size_t stg_off = rel_off;
-  std::vector<uint8_t> img(rel_off, 0);
-  qd::StepHeader *h = (qd::StepHeader *)img.data();
-  qd::StepOp *dops = (qd::StepOp *)(img.data() + ops_off);
-  qd::StepStage *dst = (qd::StepStage *)(img.data() + stages_off);
-  h->magic = qd::kStepMagic;
-  h->n_ops = (int32_t)n_ops;
-  h->n_stages = ns;
-  h->m = (int32_t)m;
-  h->nwg = nwg;
-  h->xmax = xmax;
-  h->ops_off = (uint32_t)ops_off;
-  h->stages_off = (uint32_t)stages_off;
-  h->rel_off = (uint32_t)rel_off;
-  h->ctr_off = (uint32_t)ctr_off;
-  h->data_off = (uint32_t)data_off;
-  h->lds_bytes = (uint32_t)(2 * (size_t)xmax * 4);
-  h->epoch = 1;
-  h->error = 0;
-  size_t data = data_off;
-  int s = -1;
-  for (int64_t i = 0; i < n_ops; ++i) {
-    const qd_affine_gemv_op &o = ops[i];
-    if ((int)o.stage != s) {
-      s = (int)o.stage;
-      int64_t values = 0;
-      for (int64_t j = i; j < n_ops && ops[j].stage == o.stage; ++j) values += m * ops[j].cols;
-      dst[s].data = (uint32_t *)((uint8_t *)workspace + data);
-      dst[s].op0 = (int32_t)i;
-      dst[s].nops = 0;
-      dst[s].rows_total = 0;
-      dst[s].cols = (int32_t)o.cols;
-      dst[s].chunks = (int32_t)((o.cols + 1023) / 1024);
-      dst[s].words = (uint16_t)(values / 2);
-      dst[s].lg = (uint16_t)step_lg(values / 2, nwg);
-      data += align256((size_t)values * 2);
-    }
-    qd::StepOp &d = dops[i];
-    d.w = (const uint8_t *)o.w_packed;
-    d.x = (const uint16_t *)o.x_bf16;
-    d.y = (uint16_t *)o.y_bf16;
-    d.unused = nullptr;
-    d.rows = (int32_t)o.rows;
-    d.cols = (int32_t)o.cols;
-    d.stage = s;
-    d.row_base = dst[s].rows_total;
-    dst[s].rows_total += (int32_t)o.rows;
-    dst[s].nops += 1;
-  }
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, hs);
-  if (e == hipSuccess)
-    e = hipMemsetAsync((uint8_t *)workspace + stg_off, 0, need - stg_off, hs);
-  if (e == hipSuccess) e = hipStreamSynchronize(hs);
-  if (e != hipSuccess) return hip_fail(e);
-  plan->workspace = workspace;
-  plan->nwg = nwg;
-  plan->lds_bytes = (int32_t)h->lds_bytes;
-  plan->n_ops = (int32_t)n_ops;
-  plan->n_stages = ns;
-  plan->m = (int32_t)m;
-  plan->magic = qd::kStepMagic;
-  // a last stage of one very large GEMV streams faster as its own launch
-  const qd_affine_gemv_op &last = ops[n_ops - 1];
-  const bool tail = ns > 1 && (n_ops == 1 || ops[n_ops - 2].stage != last.stage) &&
-                    last.rows * last.cols >= kStepTailWeights;
-  plan->tail = tail ? 1 : 0;
-  plan->tail_w = tail ? last.w_packed : nullptr;
-  plan->tail_x = tail ? last.x_bf16 : nullptr;
-  plan->tail_y = tail ? last.y_bf16 : nullptr;
-  plan->tail_rows = tail ? last.rows : 0;
-  plan->tail_cols = tail ? last.cols : 0;
-  return QD_OK;
+  if (!ops || n_ops < 1 || n_ops > kMaxStepOps) return QD_EINVAL;
+  const std::vector<StepIn> v = step_in(ops, n_ops);
+  return step_plan(v.data(), n_ops, m, StepFormat{false}, workspace, workspace_bytes, plan,
+                   stream);
 }
 
 qd_status qgemv_affine_i8_g64_step_run(const qd_step_plan *plan, void *stream) {
-  if (!plan || !plan->workspace || plan->magic != qd::kStepMagic || plan->nwg < 1 ||
-      plan->lds_bytes < 8 || plan->lds_bytes > 2 * kMaxStageWords * 4 ||
-      plan->lds_bytes % 8 != 0 || plan->n_ops < 1 || plan->n_stages < 1 ||
-      plan->n_stages > plan->n_ops || plan->m != 1 || plan->tail < 0 || plan->tail > 1 ||
-      (plan->tail && (plan->n_stages < 2 || !plan->tail_w || !plan->tail_x || !plan->tail_y ||
-                      plan->tail_rows < 1 || plan->tail_cols < 64 || plan->tail_cols % 64 ||
-                      plan->tail_cols > kMaxGemvCols)))
-    return QD_EINVAL;
-  qd_status st = check_device();
-  if (st != QD_OK) return st;
-  if (current_cus() != plan->nwg) return QD_EDEVICE;
-  uint8_t *ws = (uint8_t *)plan->workspace;
-  const size_t ops_off = sizeof(qd::StepHeader);
-  const size_t stages_off = ops_off + align256(sizeof(qd::StepOp) * plan->n_ops);
-  qd::StepHeader *h = (qd::StepHeader *)ws;  // device address; never dereferenced here
-  const size_t rel_off = stages_off + align256(sizeof(qd::StepStage) * plan->n_stages);
-  const size_t ctr_off = rel_off + align256((size_t)plan->nwg * 128);
-  hipError_t e = qd::launch_affine_step(
-      (const qd::StepOp *)(ws + ops_off), (const qd::StepStage *)(ws + stages_off),
-      plan->n_stages - plan->tail, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch,
-      (uint32_t *)(ws + rel_off), (uint32_t *)(ws + ctr_off), &h->error,
-      (size_t)plan->lds_bytes, (hipStream_t)stream);
-  if (e == hipSuccess && plan->tail) {
-    qd::AffineGroup g = {};
-    g.n = 1;
-    g.w[0] = (const uint8_t *)plan->tail_w;
-    g.y[0] = (uint16_t *)plan->tail_y;
-    g.rows[0] = (int)plan->tail_rows;
-    e = qd::launch_affine_gemv(g, (int)plan->tail_cols, (const uint16_t *)plan->tail_x, 1, false,
-                               (hipStream_t)stream);
-  }
-  return e == hipSuccess ? QD_OK : hip_fail(e);
+  return step_run(plan, false, stream);
 }
 
 qd_status qgemv_affine_i8_g64_step_check(const qd_step_plan *plan,
                                          uint32_t *error_bits, void *stream) {
-  if (!plan || !plan->workspace || plan->magic != qd::kStepMagic || !error_bits)
-    return QD_EINVAL;
-  qd_status st = check_device();
-  if (st != QD_OK) return st;
-  uint32_t v = 0;
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(&v, (uint8_t *)plan->workspace + offsetof(qd::StepHeader, error),
-                                4, hipMemcpyDeviceToHost, hs);
-  if (e == hipSuccess) e = hipStreamSynchronize(hs);
-  if (e != hipSuccess) return hip_fail(e);
-  *error_bits = v;
-  return v ? QD_ESTEP : QD_OK;
+  return step_check(plan, false, error_bits, stream);
+}
+
+size_t qgemv_q4_0_step_workspace_bytes(const qd_q4_0_gemv_op *ops, int64_t n_ops, int64_t m) {
+  if (!ops || n_ops < 1 || n_ops > kMaxStepOps) return 0;
+  const std::vector<StepIn> v = step_in(ops, n_ops);
+  return step_workspace_bytes(v.data(), n_ops, m, StepFormat{true});
+}
+
+qd_status qgemv_q4_0_step_plan(const qd_q4_0_gemv_op *ops, int64_t n_ops, int64_t m,
+                               void *workspace, size_t workspace_bytes, qd_step_plan *plan,
+                               void *stream) {
+  if (!ops || n_ops < 1 || n_ops > kMaxStepOps) return QD_EINVAL;
+  const std::vector<StepIn> v = step_in(ops, n_ops);
+  return step_plan(v.data(), n_ops, m, StepFormat{true}, workspace, workspace_bytes, plan,
+                   stream);
+}
+
+qd_status qgemv_q4_0_step_run(const qd_step_plan *plan, void *stream) {
+  return step_run(plan, true, stream);
+}
+
+qd_status qgemv_q4_0_step_check(const qd_step_plan *plan, uint32_t *error_bits, void *stream) {
+  return step_check(plan, true, error_bits, stream);
 }
 
 }  // extern "C"

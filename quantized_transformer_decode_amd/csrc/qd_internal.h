@@ -153,13 +153,13 @@ hipError_t launch_silu_mul(const uint16_t *gate, const uint16_t *up, uint16_t *o
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink,
                               hipStream_t stream);
 
-// Persistent decode-step kernel (decode_step.hip): one workgroup per CU.
+// Persistent decode-step kernel (decode_step.hip): one workgroup per CU;
+// affine-INT8 g64 ops (BF16 in and out) or, with q4, Q4_0 ops (f32).
 struct StepOp;
 struct StepStage;
 int step_threads();
-hipError_t launch_affine_step(const StepOp *ops, const StepStage *stages, int n_stages, int m,
-                              int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel,
-                              uint32_t *ctr, uint32_t *err, size_t lds_bytes,
-                              hipStream_t stream);
+hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
+                       int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
+                       uint32_t *err, size_t lds_bytes, hipStream_t stream);
 
 }  // namespace qd

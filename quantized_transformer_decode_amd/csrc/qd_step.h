@@ -10,7 +10,7 @@
 //                     reset between launches (every launch adds the same
 //                     amounts, so counts are taken modulo the group sizes)
 //   stage inputs      per stage, its ops' inputs back to back as dense
-//                     32-bit words, two BF16 values each
+//                     32-bit words, two BF16 values each (Q4_0 ops: one f32)
 #pragma once
 #include <stdint.h>
 
@@ -21,9 +21,9 @@ constexpr int kStepLine = 32;                 // 32-bit words per 128-byte line
 constexpr int kStepGroups = 8;                // arrival groups: workgroup b -> b % 8
 
 struct StepOp {            // 64 bytes
-  const uint8_t *w;        // affine blob
-  const uint16_t *x;       // BF16 [m, cols] input
-  uint16_t *y;             // BF16 [m, rows] output
+  const uint8_t *w;        // affine blob, or Q4_0 stream
+  const uint16_t *x;       // BF16 [m, cols] input (Q4_0: f32)
+  uint16_t *y;             // BF16 [m, rows] output (Q4_0: f32)
   const void *unused;
   int32_t rows, cols;
   int32_t stage;
@@ -32,15 +32,16 @@ struct StepOp {            // 64 bytes
 };
 
 // A stage's input (its ops' inputs back to back, `words` 32-bit words of two
-// BF16 each) is split into slices of 2^lg words; workgroup j publishes slice
-// j, words [j*2^lg, (j+1)*2^lg), one word per lane.
+// BF16 each, or of one f32 for Q4_0 ops) is split into slices of 2^lg words;
+// workgroup j publishes slice j, words [j*2^lg, (j+1)*2^lg), one word per
+// lane.
 struct StepStage {         // 32 bytes
   uint32_t *data;          // the stage's input words (dense)
   int32_t op0, nops;       // ops [op0, op0 + nops)
   int32_t rows_total;      // sum of the ops' rows
   int32_t cols;            // shared input width
-  int32_t chunks;          // ceil(cols / 1024)
-  uint16_t words;          // nops * m * cols / 2 (<= 8192)
+  int32_t chunks;          // ceil(cols / 1024) (Q4_0: ceil(cols / 2048))
+  uint16_t words;          // nops * m * cols / 2 (Q4_0: nops * m * cols; <= 16384)
   uint16_t lg;             // log2 of the slice length (1..6)
 };
 

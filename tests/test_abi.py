@@ -429,6 +429,51 @@ def test_valid_args_reach_device_check():
                  0x7fa000000000, 0x7fb000000000, None, 1, None) == qd.QD_EDEVICE
 
 
+def _q4_ops(*specs):
+    arr = (qd.Q40GemvOp * len(specs))()
+    for i, sp in enumerate(specs):
+        arr[i] = qd.Q40GemvOp(*sp)
+    return arr
+
+
+def test_errors_q4_0_step():
+    wb = qd.lib().qgemv_q4_0_step_workspace_bytes
+    ok = (A, B, C, 64, 256, 0)
+    assert wb(None, 1, 1) == 0
+    assert wb(_q4_ops((A, B, C, 64, 128, 0)), 1, 1) == 0       # cols % 256
+    assert wb(_q4_ops(ok), 1, 2) == 0                          # m > 1
+    f = "qgemv_q4_0_step_plan"
+    plan = qd.StepPlan()
+    P_ = ctypes.byref(plan)
+    assert _call(f, None, 1, 1, WS, 1 << 20, P_, None) == qd.QD_EINVAL
+    assert _call(f, _q4_ops(ok), 1, 1, None, 1 << 20, P_, None) == qd.QD_EINVAL
+    assert _call(f, _q4_ops((A, B, C, 64, 128, 0)), 1, 1, WS, 1 << 20, P_, None) == qd.QD_ESHAPE
+    assert _call(f, _q4_ops((A, B, C, 64, 8448, 0)), 1, 1, WS, 1 << 20, P_, None) == qd.QD_ESHAPE
+    assert _call(f, _q4_ops((A, B, C + 2, 64, 256, 0)), 1, 1, WS, 1 << 20, P_, None) == qd.QD_EALIGN
+    assert _call(f, _q4_ops((A, B + 4, C, 64, 256, 0)), 1, 1, WS, 1 << 20, P_, None) == qd.QD_EALIGN
+    assert _call(f, _q4_ops((A, B, C, 64, 256, 1)), 1, 1, WS, 1 << 20, P_, None) == qd.QD_EINVAL
+    assert _call(f, _q4_ops(ok, (D, B, E, 64, 512, 0)), 2, 1, WS, 1 << 20, P_,
+                 None) == qd.QD_ESHAPE                         # one stage, two widths
+    assert _call(f, _q4_ops(ok, (D, B, A + 64, 64, 256, 1)), 2, 1, WS, 1 << 20, P_,
+                 None) == qd.QD_EINVAL                         # output over weights
+    assert _call(f, _q4_ops(ok), 1, 1, WS + 16, 1 << 20, P_, None) == qd.QD_EALIGN
+    assert _call(f, _q4_ops(ok), 1, 1, WS, 64, P_, None) == qd.QD_EINVAL
+    # a plan of one format is refused by the other format's run and check
+    for fmt, run, check in ((1, "qgemv_affine_i8_g64_step_run", "qgemv_affine_i8_g64_step_check"),
+                            (0, "qgemv_q4_0_step_run", "qgemv_q4_0_step_check")):
+        p = qd.StepPlan(workspace=WS, nwg=256, lds_bytes=16384, n_ops=1, n_stages=1, m=1,
+                        magic=0x51445354, tail=0, format=fmt)
+        assert _call(run, ctypes.byref(p), None) == qd.QD_EINVAL
+        assert _call(check, ctypes.byref(p), ctypes.byref(ctypes.c_uint32()), None) == qd.QD_EINVAL
+    # a Q4_0 plan never streams a last stage on its own
+    p = qd.StepPlan(workspace=WS, nwg=256, lds_bytes=16384, n_ops=2, n_stages=2, m=1,
+                    magic=0x51445354, tail=1, tail_w=A, tail_x=B, tail_y=C, tail_rows=64,
+                    tail_cols=256, format=1)
+    assert _call("qgemv_q4_0_step_run", ctypes.byref(p), None) == qd.QD_EINVAL
+    if not _gpu_visible():
+        assert _call(f, _q4_ops(ok), 1, 1, WS, 1 << 20, P_, None) == qd.QD_EDEVICE
+
+
 def test_qwen3_step_workspace_offsets():
     # the scratch rows lie inside the workspace, 256-byte aligned, disjoint
     m = _qwen3()
