@@ -561,32 +561,53 @@ __device__ __forceinline__ void stage_word(const StagePlan &pp, float *dst, int 
 // words (every load of an op in flight at once), then each lane's 64-bit
 // words go to LDS as float4s.  Lane l takes words l, l + 64, ... of each
 // op, so its LDS addresses advance by a constant: no per-element search.
+// NB 64-bit words per lane of one op's input [base, wpo) into LDS: every
+// load issued (clamped to the op's last word, never conditional) before any
+// is consumed, so the whole batch costs one memory round trip.
+template <bool Q4, int NB>
+__device__ __forceinline__ void read_words(const uint64_t *op, float *od, int base, int wpo,
+                                           int lane) {
+  uint64_t v[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) v[b] = ld_agent64(op + min(base + b * 64 + lane, wpo - 1));
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int f = base + b * 64 + lane;
+    if (f < wpo) {
+      const uint32_t lo = (uint32_t)v[b], hi = (uint32_t)(v[b] >> 32);
+      if constexpr (Q4)
+        *(float2 *)(od + xq4(2 * f)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
+      else
+        *(float4 *)(od + xswz(4 * f)) =
+            make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                        __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
+    }
+  }
+}
+
+// A released stage input into LDS: agent-scope loads of the published
+// words, then each lane's 64-bit words go to LDS as fp32.  Lane l takes
+// words l, l + 64, ... of each op, so its LDS addresses advance by a
+// constant: no per-element search.  The batch is sized to the op (one
+// straight-line path per size, chosen before any load is issued): inputs
+// up to 1536 words (a 3072-wide f32 row, a 6144-wide BF16 row) take one
+// memory round trip, a 5120-wide f32 row two.
 template <bool Q4>
 __device__ void read_stage(const StagePlan &pp, float *dst, int lane) {
-  constexpr int B = 16;
   const uint64_t *src = (const uint64_t *)pp.data;
   const int wpo = pp.epo >> (Q4 ? 1 : 2);  // 64-bit words per op (a multiple of 16)
+  const int per_lane = uni((wpo + 63) >> 6);
   for (int k = pp.k0; k <= pp.k1; ++k) {
     const uint64_t *op = src + (size_t)k * wpo;
     float *od = dst + k * pp.xstride;
-    for (int base = 0; base < wpo; base += 64 * B) {
-      uint64_t v[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) v[b] = ld_agent64(op + min(base + b * 64 + lane, wpo - 1));
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int f = base + b * 64 + lane;
-        if (f < wpo) {
-          const uint32_t lo = (uint32_t)v[b], hi = (uint32_t)(v[b] >> 32);
-          if constexpr (Q4)
-            *(float2 *)(od + xq4(2 * f)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
-          else
-            *(float4 *)(od + xswz(4 * f)) =
-                make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                            __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
-        }
-      }
-    }
+    if (per_lane <= 4)
+      read_words<Q4, 4>(op, od, 0, wpo, lane);
+    else if (per_lane <= 8)
+      read_words<Q4, 8>(op, od, 0, wpo, lane);
+    else if (per_lane <= 12)
+      read_words<Q4, 12>(op, od, 0, wpo, lane);
+    else
+      for (int base = 0; base < wpo; base += 64 * 24) read_words<Q4, 24>(op, od, base, wpo, lane);
   }
 }
 
