@@ -37,7 +37,7 @@
 //
 // Workgroup layout: wave 0 is the poller (publishes, polls the next input
 // into LDS as fp32, hands it to the compute waves through an LDS flag);
-// waves 1..NCW compute.  The grid is exactly one workgroup per CU and every
+// waves 1..kNcw compute.  The grid is exactly one workgroup per CU and every
 // workgroup must be resident (the plan records the grid size; a launch with
 // another grid size returns without work and sets the error word).  Every
 // wait is bounded; on time-out the error word is set and the kernel runs to
@@ -50,8 +50,13 @@ namespace qd {
 namespace {
 
 
-constexpr int NCW = 8;             // compute waves per workgroup
-constexpr int kThreads = (NCW + 1) * kWave;
+// Compute waves per workgroup: twelve for affine ops (against eight: the
+// Qwen3-1.7B step 0.868 -> 0.820 ms, the 0.6B step unchanged), eight for
+// Q4_0 ops (twelve: the Whisper-large step 0.70 -> 0.73 ms).
+template <bool Q4>
+constexpr int kNcw = Q4 ? 8 : 12;
+template <bool Q4>
+constexpr int kThreads = (kNcw<Q4> + 1) * kWave;
 // Items (1 KiB row chunks) per register group; two groups are in flight per
 // wave.  Three covers a wave's share of a layer stage of 0.6B-1.7B decoders
 // (1-3 items); larger groups mostly re-read past-the-end items, which delays
@@ -403,8 +408,8 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
   // the schedule is a scalar load (it never waits on the vector-load counter
   // that tracks the weight prefetch)
   const int cw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - 1;
-  const int nw = gridDim.x * NCW;
-  const int gw = blockIdx.x * NCW + cw;
+  const int nw = gridDim.x * kNcw<Q4>;
+  const int gw = blockIdx.x * kNcw<Q4> + cw;
   int signalled = 0;
   float rowsum = 0.f;
   int have = 0;  // stages known staged
@@ -522,6 +527,7 @@ __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepSta
   p.epo = m * st.cols;
   p.xstride = st.chunks * kItemCols<Q4>;
   int lo, hi, lo2, hi2;
+  constexpr int NCW = kNcw<Q4>;
   wave_rows(st, blockIdx.x * NCW, gridDim.x * NCW, lo, hi);
   wave_rows(st, blockIdx.x * NCW + NCW - 1, gridDim.x * NCW, lo2, hi2);
   if (hi2 <= lo) {  // no rows for this workgroup in this stage
@@ -706,7 +712,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
     }
     // wait for every compute wave to finish stage s, then publish s+1
     unsigned spins = 0;
-    while (lds_ld(&sh->done) < (s + 1) * NCW) {
+    while (lds_ld(&sh->done) < (s + 1) * kNcw<Q4>) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kLdsSpinLimit) {
         if (lane == 0) atomicOr(err, 2u);
@@ -755,14 +761,14 @@ __device__ __forceinline__ void step_body(const StepOp *__restrict__ ops,
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(epoch_word, sh.epoch + (uint32_t)n_stages);
 }
 
-__global__ __launch_bounds__(kThreads) void affine_step_kernel(
+__global__ __launch_bounds__(kThreads<false>) void affine_step_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
   step_body<false>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
 }
 
-__global__ __launch_bounds__(kThreads) void q4_0_step_kernel(
+__global__ __launch_bounds__(kThreads<true>) void q4_0_step_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
@@ -771,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void q4_0_step_kernel(
 
 }  // namespace
 
-int step_threads() { return kThreads; }
+int step_threads() { return kThreads<false>; }
 
 hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
                        int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
@@ -783,10 +789,10 @@ hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int 
     if (e != hipSuccess) return e;
   }
   if (q4)
-    hipLaunchKernelGGL(q4_0_step_kernel, dim3(nwg), dim3(kThreads), lds_bytes, stream, ops,
+    hipLaunchKernelGGL(q4_0_step_kernel, dim3(nwg), dim3(kThreads<true>), lds_bytes, stream, ops,
                        stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
   else
-    hipLaunchKernelGGL(affine_step_kernel, dim3(nwg), dim3(kThreads), lds_bytes, stream, ops,
+    hipLaunchKernelGGL(affine_step_kernel, dim3(nwg), dim3(kThreads<false>), lds_bytes, stream, ops,
                        stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
   return hipGetLastError();
 }
