@@ -596,16 +596,21 @@ hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int
   return hipGetLastError();
 }
 
-// Only the streaming walk (KS = 1) stages x: there a workgroup reuses it over
-// many tiles, while a split workgroup reads each element of x once anyway.
-// A prologue always stages (the transformed row exists only in LDS).
+// The streaming walk (KS = 1) stages x: there a workgroup reuses it over
+// many tiles.  A split workgroup reads each element of x once anyway, but
+// with m > 1 its x fragments held in registers from issue to use cost 150
+// VGPRs, one workgroup per CU; staged, they are read at use (107 VGPRs, two
+// per CU: the Qwen3-1.7B step at M = 16 1.155 -> 1.120 ms).  At m = 1 the
+// staging's extra round trip and barrier cost more than that (1024 x 1024:
+// 3.5 -> 4.3 us per launch).  A prologue always stages (the transformed row
+// exists only in LDS).
 template <int KS, bool CH, class Act, int PRO>
 hipError_t launch_mfma_xl(const AffineGroup &g, int cols, const uint16_t *x, int m, int grid,
                           const GemvPrologue &pro, hipStream_t stream) {
   if constexpr (PRO != 0) {
     return launch_mfma_ks<KS, CH, true, Act, PRO>(g, cols, x, m, grid, pro, stream);
   } else {
-    if (KS == 1 && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
+    if ((KS == 1 || m > 1) && (size_t)m * (2 * cols + 16) <= (size_t)kXlBudget)
       return launch_mfma_ks<KS, CH, true, Act, PRO>(g, cols, x, m, grid, pro, stream);
     return launch_mfma_ks<KS, CH, false, Act, PRO>(g, cols, x, m, grid, pro, stream);
   }
