@@ -90,7 +90,7 @@ __device__ __forceinline__ int lds_ld(const int *p) {
 
 // LDS layout of a staged input: each op's input occupies chunks*1024 floats
 // (whole chunks) in the xswz layout.
-constexpr int kPubRing = 32;  // stages of publish values kept in LDS ahead of use
+constexpr int kPubRing = 2;   // stages of publish values kept in LDS ahead of use
 
 struct Shared {
   int xready;        // stages whose input is staged in LDS
@@ -669,11 +669,10 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
   bool aborted = false;
   // The values this workgroup publishes come from the resident inputs; they
   // are loaded kPubRing stages ahead into an LDS ring so that publishing is
-  // an LDS read and a store, never a wait on memory.
-  for (int t = 1; t < kPubRing && t < n_stages; ++t) {
-    const PubSlice p = pub_load<Q4>(ops, stages[t], m, lane);
-    sh->pub[t][lane] = p.v;
-  }
+  // an LDS read and a store, never a wait on memory.  Two stages suffice:
+  // each load runs under a stage's compute.  (A 32-stage ring preloaded
+  // before the first stage cost ~13 us per launch: 31 dependent load
+  // chains before any compute wave could start.)
   PubSlice pending;
   int pending_stage = -1;
   StagePlan cur = stage_plan<Q4>(ops, stages[0], m);
@@ -703,6 +702,13 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
                                       __HIP_MEMORY_SCOPE_WORKGROUP);
     // resolve the next stage while the compute waves work
     if (s + 1 < n_stages) nxt = stage_plan<Q4>(ops, stages[s + 1], m);
+    // stage 1's values, needed at the end of this stage (later stages' come
+    // through the ring below); loaded under stage 0's compute rather than
+    // before the first input is staged
+    if (s == 0 && n_stages > 1) {
+      const PubSlice p = pub_load<Q4>(ops, stages[1], m, lane);
+      sh->pub[1][lane] = p.v;
+    }
     // load stage s + kPubRing's values; they are parked next iteration in the
     // slot of stage s, which was published at the end of the last iteration
     pending_stage = -1;
