@@ -563,10 +563,6 @@ __device__ __forceinline__ void stage_word(const StagePlan &pp, float *dst, int 
                     bf16_to_f32(hi >> 16));
 }
 
-// A released stage input into LDS: agent-scope loads of the published
-// words (every load of an op in flight at once), then each lane's 64-bit
-// words go to LDS as float4s.  Lane l takes words l, l + 64, ... of each
-// op, so its LDS addresses advance by a constant: no per-element search.
 // NB 64-bit words per lane of one op's input [base, wpo) into LDS: every
 // load issued (clamped to the op's last word, never conditional) before any
 // is consumed, so the whole batch costs one memory round trip.
