@@ -28,6 +28,11 @@ constexpr int kQThreads = kQW * kWave;
 constexpr int kQMaxSplit = kQW < 8 ? kQW : 8;  // waves one row's steps are split over
 constexpr int kQU = 1;                 // steps per register group (2 and 4 measured slower)
 constexpr int kQLdsBudget = 64 * 1024;
+// x in LDS: each 32-element block padded to 36 floats, so the eight blocks
+// one read instruction covers (lanes 8r + j, block j) start in different
+// banks (unpadded, blocks 128 bytes apart met four to a bank group: the
+// Whisper-base FFN pair at batch 4 10.3 -> 8.7 us)
+constexpr int kXBlk = 36;
 
 template <int R>
 struct QGroup {
@@ -182,7 +187,7 @@ __device__ __forceinline__ void qg_compute(const QGroup<R> &G, float (&acc)[MT][
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       float dot[R];
-      block_dot<R>(nib, xs + t * cols + 32 * b, dot);
+      block_dot<R>(nib, xs + kXBlk * (t * S.bpr + b), dot);
       const float corr = -8.f * xsum[t * S.bpr + b];
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[t][r] = fmaf(d[r], dot[r] + corr, acc[t][r]);
@@ -219,9 +224,9 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   constexpr int SLOTS = kQW / KS;
   __shared__ float red[KS > 1 ? kQW * MT * R * 8 : 1];
   extern __shared__ __attribute__((aligned(16))) float qsh[];
-  float *xs = qsh;                    // [MT][cols]
+  float *xs = qsh;                    // [MT][bpr] blocks of kXBlk floats
   const int bpr = cols >> 5;
-  float *xsum = qsh + MT * cols;      // [MT][bpr]
+  float *xsum = qsh + MT * bpr * kXBlk;  // [MT][bpr]
   const QD_GLOBAL float *x = gp(x_);
   const int lane = threadIdx.x & 63;
   const int wave = uni(threadIdx.x >> 6);
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
       for (int k = 0; k < 8; ++k) {
         const floatx4 v = live ? xv[k] : floatx4{0.f, 0.f, 0.f, 0.f};
         sum += (v[0] + v[1]) + (v[2] + v[3]);
-        *(floatx4 *)(xs + 32 * bi + 4 * k) = v;
+        *(floatx4 *)(xs + kXBlk * bi + 4 * k) = v;
       }
       xsum[bi] = sum;
     }
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
       for (int k = 0; k < 8; ++k) {
         const floatx4 v = live ? p[k] : floatx4{0.f, 0.f, 0.f, 0.f};
         sum += (v[0] + v[1]) + (v[2] + v[3]);
-        *(floatx4 *)(xs + 32 * b + 4 * k) = v;
+        *(floatx4 *)(xs + kXBlk * b + 4 * k) = v;
       }
       xsum[b] = sum;
     }
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
 template <int MT, int R, int KS, bool EPI>
 hipError_t launch_q_ks(const Q40Group &g, int cols, const float *x, int t0, int m, int grid,
                        hipStream_t stream) {
-  const size_t lds = (size_t)MT * cols * 4 + (size_t)MT * (cols / 32) * 4;
+  const size_t lds = (size_t)MT * (cols / 32) * kXBlk * 4 + (size_t)MT * (cols / 32) * 4;
   if (lds > 48 * 1024) {  // above the default dynamic-LDS limit: raise it once
     static bool raised = false;
     if (!raised) {
@@ -406,7 +411,7 @@ hipError_t launch_q_mt(Q40Group g, int cols, const float *x, int t0, int m,
 hipError_t launch_q4_0_gemv(Q40Group g, int cols, const float *x, int m,
                             hipStream_t stream) {
   // tokens per pass limited by the LDS copy of x (fp32 plus block sums)
-  const int cap = kQLdsBudget / (cols * 4 + cols / 8);
+  const int cap = kQLdsBudget / ((cols / 32) * kXBlk * 4 + cols / 8);
   // kernels specialised for a plain product (no bias, no GELU)
   bool epi = g.gelu != 0;
   for (int k = 0; k < g.n; ++k) epi = epi || g.bias[k] != nullptr;
