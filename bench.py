@@ -23,7 +23,7 @@ part of the path on its own workload:
                          page's Metal dtype) and the device tied-embedding lookup
   q4_0_ffn_pair          Whisper-base FFN pair (fc1 2048x512, fc2 512x2048), M = 1, 4
   qwen3_1_7b_step        Qwen3-1.7B-shaped decode step at M = 1, 4, 10, 16
-                         (graphs of one launch per stage: same-input GEMVs grouped)
+                         (persistent at M <= 4; graphs of one launch per stage)
   whisper_large_prefill  one Whisper-large layer's six projections at 1500 frames
   whisper_large_decoder  32 layers x 6 Q4_0 GEMVs at batch 1 (one persistent launch;
                          also 128 launches with q, k, v grouped)
@@ -481,9 +481,9 @@ def row_q4_0_ffn_pair(qd):
 
 def row_qwen3_1_7b_step(qd):
     """Qwen3-1.7B-shaped decode step (1,827,979,264 weight bytes) at M rows:
-    M = 1 as one persistent launch and as a graph of one launch per stage
-    (the faster is reported), M > 1 as a graph of one launch per stage (113),
-    with the graph of 197 single-GEMV launches alongside."""
+    M <= 4 as one persistent launch and as a graph of one launch per stage
+    (the faster is reported), M = 10, 16 as a graph of one launch per stage
+    (113), with the graph of 197 single-GEMV launches alongside."""
     import synth
     out = {}
     step = DecodeStep(synth.QWEN3_1_7B, m=1, cfg=4)
@@ -508,15 +508,22 @@ def row_qwen3_1_7b_step(qd):
         step.ys = [torch.empty((m, rows), dtype=torch.bfloat16, device=DEV)
                    for (_, _, rows, _, _) in step.mats]
         g = capture(step.run_grouped)
-        ms = event_time(g.replay, 5, 2)
+        msg = event_time(g.replay, 5, 2)
         g197 = capture(step.run_eager)
         ms197 = event_time(g197.replay, 5, 2)
-        out[f"M{m}"] = {"ms_per_step": ms, "tokens_per_s": m * 1000.0 / ms,
-                        "weight_GBps": wb / (ms * 1e-3) / 1e9,
-                        "hbm_peak_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                        "variant": "113 launches (one per stage, grouped same-input GEMVs) "
-                                   "in a HIP graph",
-                        "ms_per_step_197_launches": ms197}
+        row = {"ms_113_stage_launches": msg, "ms_per_step_197_launches": ms197}
+        ms, variant = msg, "113 launches (one per stage, grouped same-input GEMVs) in a HIP graph"
+        if m <= 4:  # the persistent step takes up to four token rows
+            step.plan_step()
+            msp = event_time(step.run_step, 10, 3)
+            row["ms_persistent_step"] = msp
+            if msp < ms:
+                ms, variant = msp, "persistent step"
+        row.update({"ms_per_step": ms, "tokens_per_s": m * 1000.0 / ms,
+                    "weight_GBps": wb / (ms * 1e-3) / 1e9,
+                    "hbm_peak_frac": wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "variant": variant})
+        out[f"M{m}"] = row
     del ys_keep
     step.free()
     out["weight_bytes"] = wb

@@ -200,20 +200,26 @@ size_t qgemv_affine_i8_g64_step_workspace_bytes(const qd_affine_gemv_op *ops,
 /* Validates the ops (host array), writes the step tables into `workspace`
  * (device memory owned by the caller, 256-byte aligned, at least
  * _step_workspace_bytes) and fills *plan.  Synchronises `stream` before
- * returning.  Requirements beyond those of each op: m == 1; ops[0].stage ==
- * 0 and each op's stage equals its predecessor's or one more; ops of one
- * stage share cols; per stage sum(m*ceil(cols/1024)*1024) <= 16384 and
- * sum(m*cols) <= 128 * (compute units of the device) (QD_ESHAPE; the second
- * bound only binds on parts with fewer than 128 CUs); no op's output
- * overlaps any op's weights or input, or the workspace (QD_EINVAL /
- * QD_ESHAPE / QD_EALIGN as for the single GEMV).  The workspace, weights and inputs must
- * stay valid while runs are in flight. */
+ * returning.  m is the number of token rows, 1 <= m <= 4 (QD_EINVAL
+ * otherwise; every op's x is [m, cols] and y [m, rows]).  Requirements
+ * beyond those of each op: ops[0].stage == 0 and each op's stage equals its
+ * predecessor's or one more; ops of one stage share cols; the staged input
+ * of a stage fits a workgroup's LDS -- at m = 1 sum(ceil(cols/1024)*1024)
+ * over the stage's ops <= 16384, at m > 1 the same sum times m over the ops
+ * any one workgroup has rows in (the stage's rows split evenly over the
+ * device's compute units) -- and sum(m*cols) <= 128 * (compute units of the
+ * device) (QD_ESHAPE; the last bound only binds on parts with fewer than
+ * 128 CUs); no op's output overlaps any op's weights or input, or the
+ * workspace (QD_EINVAL / QD_ESHAPE / QD_EALIGN as for the single GEMV).
+ * The workspace, weights and inputs must stay valid while runs are in
+ * flight. */
 qd_status qgemv_affine_i8_g64_step_plan(const qd_affine_gemv_op *ops,
                                         int64_t n_ops, int64_t m,
                                         void *workspace, size_t workspace_bytes,
                                         qd_step_plan *plan, void *stream);
 
-/* Enqueues the whole step as ONE persistent kernel (one workgroup per CU;
+/* Enqueues the whole step as ONE persistent kernel (one workgroup per CU,
+ * one kernel per token-row count;
  * every workgroup must be able to be resident, so do not run it concurrently
  * with kernels that occupy whole CUs indefinitely) and, with plan->tail,
  * the last stage's GEMV as a second launch on the same stream (it starts

@@ -50,13 +50,20 @@ namespace qd {
 namespace {
 
 
-// Compute waves per workgroup: twelve for affine ops (against eight: the
-// Qwen3-1.7B step 0.868 -> 0.820 ms, the 0.6B step unchanged), eight for
-// Q4_0 ops (twelve: the Whisper-large step 0.70 -> 0.73 ms).
-template <bool Q4>
-constexpr int kNcw = Q4 ? 8 : 12;
-template <bool Q4>
-constexpr int kThreads = (kNcw<Q4> + 1) * kWave;
+// Compute waves per workgroup: twelve for affine ops at one token row
+// (against eight: the Qwen3-1.7B step 0.868 -> 0.820 ms, the 0.6B step
+// unchanged), eight for Q4_0 ops (twelve: the Whisper-large step 0.70 ->
+// 0.73 ms) and for several token rows (their x and row sums take registers
+// that twelve waves per CU cannot spare).
+template <bool Q4, int MT>
+constexpr int kNcw = (Q4 || MT > 1) ? 8 : 12;
+template <bool Q4, int MT>
+constexpr int kThreads = (kNcw<Q4, MT> + 1) * kWave;
+// Several token rows stage only the ops a workgroup has rows in (a stage's
+// whole input would not fit in LDS); one row stages every op of the stage at
+// a fixed place (the single-row kernel is at its register limit).
+template <bool Q4, int MT>
+constexpr bool kCompact = MT > 1;
 // Items (1 KiB row chunks) per register group; two groups are in flight per
 // wave.  Three covers a wave's share of a layer stage of 0.6B-1.7B decoders
 // (1-3 items); larger groups mostly re-read past-the-end items, which delays
@@ -88,8 +95,14 @@ __device__ __forceinline__ int lds_ld(const int *p) {
   return v;
 }
 
-// LDS layout of a staged input: each op's input occupies chunks*1024 floats
-// (whole chunks) in the xswz layout.
+// LDS layout of a staged input, op k at (k - kbase) * xstride floats:
+// - one token row: kbase = 0 (every op of the stage), whole 1024-column
+//   chunks of fp32 in the xswz layout (Q4_0: 2048-column items of fp32 in
+//   the xq4 layout);
+// - m > 1 token rows: kbase = the first op this workgroup has rows in, the
+//   BF16 values as published, in the xswz order, token row t at
+//   t * chunks * 1024 elements (fp32 would not fit a 6144-wide input of
+//   four rows twice).
 constexpr int kPubRing = 2;   // stages of publish values kept in LDS ahead of use
 
 struct Shared {
@@ -97,6 +110,7 @@ struct Shared {
   int done;          // compute-wave stage completions
   int arrived;       // stages whose barrier this workgroup has arrived at
   uint32_t epoch;
+  int xk0[2];        // kbase of stage s's staged input, at [s & 1]
   uint32_t pub[kPubRing][64];  // this workgroup's slice of stage s's input at [s % kPubRing]
 };
 
@@ -307,7 +321,7 @@ __device__ __forceinline__ float q4_item(const u32x4 w4, uint32_t w1, int lane,
 }
 
 __device__ __forceinline__ void compute_q4(const Group<true> &g, const StepOp *ops, int lane,
-                                           const float *xl, float &rowsum) {
+                                           const float *xl, int k0, float &rowsum) {
   {
     Walk wk = g.start;
     int xkey = -1;
@@ -320,7 +334,7 @@ __device__ __forceinline__ void compute_q4(const Group<true> &g, const StepOp *o
         const int key = wk.o * 64 + wk.ch;
         if (key != xkey) {
           xkey = key;
-          const float *xp = xl + (wk.o - wk.op0) * (wk.chunks * 2048) + wk.ch * 2048;
+          const float *xp = xl + (wk.o - wk.op0 - k0) * (wk.chunks * 2048) + wk.ch * 2048;
           xs = 0.f;
 #pragma unroll
           for (int j4 = 0; j4 < 8; ++j4) {
@@ -341,51 +355,132 @@ __device__ __forceinline__ void compute_q4(const Group<true> &g, const StepOp *o
   }
 }
 
-__device__ __forceinline__ void compute_affine(const Group<false> &g, const StepOp *ops,
-                                               int lane, const float *xl, float &rowsum) {
-  Walk wk = g.start;
-  int xkey = -1;
-  float4 x0, x1, x2, x3;
-  float xs = 0.f;
+// 16 codes (one 16-byte load) against MT token rows of 16 activations each:
+// the codes converted once.
+template <int MT>
+__device__ __forceinline__ void dot16_rows(const uint4 q, const float4 (&x)[MT][4],
+                                           float (&d)[MT]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-  for (int k = 0; k < G; ++k) {
-    if (g.i0 + k < wk.n) {
-      const bool valid = wk.ch * 1024 + lane * 16 < wk.op.cols;
-      // x depends only on (op, chunk): reload it only when that changes
-      const int key = wk.o * 64 + wk.ch;
-      if (key != xkey) {
-        xkey = key;
-        const float *xp = xl + (wk.o - wk.op0) * (wk.chunks * 1024) + wk.ch * 1024 + lane * 4;
-        x0 = *(const float4 *)(xp);
-        x1 = *(const float4 *)(xp + 256);
-        x2 = *(const float4 *)(xp + 512);
-        x3 = *(const float4 *)(xp + 768);
-        xs = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w)) +
-             ((x2.x + x2.y) + (x2.z + x2.w)) + ((x3.x + x3.y) + (x3.z + x3.w));
-      }
-      const float s = bf16_to_f32(g.sc[k]);
-      const float b = bf16_to_f32(g.bi[k]);
-      float p = fmaf(s, dot16(g.q[k], x0, x1, x2, x3), b * xs);
-      if (!valid) p = 0.f;
-      rowsum += wave_sum_dpp(p);
-      if (wk.ch == wk.chunks - 1) {
-        if (lane == 0) wk.op.y[wk.row - wk.op.row_base] = f32_to_bf16(rowsum);
-        rowsum = 0.f;
-      }
-      // past the group's last valid item there is no next descriptor to read
-      // (after the plan's last op the table ends)
-      if (g.i0 + k + 1 < wk.n) walk_next(wk, ops);
+  for (int t = 0; t < MT; ++t) d[t] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float c0 = ubyte<0>(w[k]), c1 = ubyte<1>(w[k]), c2 = ubyte<2>(w[k]),
+                c3 = ubyte<3>(w[k]);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      d[t] = fmaf(c0, x[t][k].x, d[t]);
+      d[t] = fmaf(c1, x[t][k].y, d[t]);
+      d[t] = fmaf(c2, x[t][k].z, d[t]);
+      d[t] = fmaf(c3, x[t][k].w, d[t]);
     }
   }
 }
 
-template <bool Q4>
+template <int MT>
+__device__ __forceinline__ void compute_affine(const Group<false> &g, const StepOp *ops,
+                                               int lane, const float *xl, int k0,
+                                               float (&rowsum)[MT]) {
+  if constexpr (MT == 1) {
+    Walk wk = g.start;
+    int xkey = -1;
+    float4 x0, x1, x2, x3;
+    float xs = 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (g.i0 + k < wk.n) {
+        const bool valid = wk.ch * 1024 + lane * 16 < wk.op.cols;
+        // x depends only on (op, chunk): reload it only when that changes
+        const int key = wk.o * 64 + wk.ch;
+        if (key != xkey) {
+          xkey = key;
+          const float *xp =
+              xl + (wk.o - wk.op0 - k0) * (wk.chunks * 1024) + wk.ch * 1024 + lane * 4;
+          x0 = *(const float4 *)(xp);
+          x1 = *(const float4 *)(xp + 256);
+          x2 = *(const float4 *)(xp + 512);
+          x3 = *(const float4 *)(xp + 768);
+          xs = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w)) +
+               ((x2.x + x2.y) + (x2.z + x2.w)) + ((x3.x + x3.y) + (x3.z + x3.w));
+        }
+        const float s = bf16_to_f32(g.sc[k]);
+        const float b = bf16_to_f32(g.bi[k]);
+        float p = fmaf(s, dot16(g.q[k], x0, x1, x2, x3), b * xs);
+        if (!valid) p = 0.f;
+        rowsum[0] += wave_sum_dpp(p);
+        if (wk.ch == wk.chunks - 1) {
+          if (lane == 0) wk.op.y[wk.row - wk.op.row_base] = f32_to_bf16(rowsum[0]);
+          rowsum[0] = 0.f;
+        }
+        // past the group's last valid item there is no next descriptor to read
+        // (after the plan's last op the table ends)
+        if (g.i0 + k + 1 < wk.n) walk_next(wk, ops);
+      }
+    }
+  } else {
+    // MT token rows: row t of an op's staged input at t * chunks * 1024
+    Walk wk = g.start;
+    int xkey = -1;
+    float4 x[MT][4];
+    float xs[MT];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (g.i0 + k < wk.n) {
+        const bool valid = wk.ch * 1024 + lane * 16 < wk.op.cols;
+        const int key = wk.o * 64 + wk.ch;
+        if (key != xkey) {
+          xkey = key;
+          const uint16_t *xp = (const uint16_t *)(xl + (wk.o - wk.op0 - k0) *
+                                                           (MT * wk.chunks * 512)) +
+                               wk.ch * 1024 + lane * 4;
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const uint16_t *xt = xp + t * (wk.chunks * 1024);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const u32x2 w = *(const u32x2 *)(xt + 256 * j);
+              x[t][j] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                    __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+            }
+            xs[t] = ((x[t][0].x + x[t][0].y) + (x[t][0].z + x[t][0].w)) +
+                    ((x[t][1].x + x[t][1].y) + (x[t][1].z + x[t][1].w)) +
+                    ((x[t][2].x + x[t][2].y) + (x[t][2].z + x[t][2].w)) +
+                    ((x[t][3].x + x[t][3].y) + (x[t][3].z + x[t][3].w));
+          }
+        }
+        const float s = bf16_to_f32(g.sc[k]);
+        const float b = bf16_to_f32(g.bi[k]);
+        float d[MT];
+        dot16_rows<MT>(g.q[k], x, d);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          float p = fmaf(s, d[t], b * xs[t]);
+          if (!valid) p = 0.f;
+          rowsum[t] += wave_sum_dpp(p);
+        }
+        if (wk.ch == wk.chunks - 1) {
+          if (lane < MT) {
+            float v = rowsum[0];
+#pragma unroll
+            for (int t = 1; t < MT; ++t) v = lane == t ? rowsum[t] : v;
+            wk.op.y[(size_t)lane * wk.op.rows + (wk.row - wk.op.row_base)] = f32_to_bf16(v);
+          }
+#pragma unroll
+          for (int t = 0; t < MT; ++t) rowsum[t] = 0.f;
+        }
+        if (g.i0 + k + 1 < wk.n) walk_next(wk, ops);
+      }
+    }
+  }
+}
+
+template <bool Q4, int MT>
 __device__ __forceinline__ void compute(const Group<Q4> &g, const StepOp *ops, int lane,
-                                        const float *xl, float &rowsum) {
+                                        const float *xl, int k0, float (&rowsum)[MT]) {
   if constexpr (Q4)
-    compute_q4(g, ops, lane, xl, rowsum);
+    compute_q4(g, ops, lane, xl, k0, rowsum[0]);
   else
-    compute_affine(g, ops, lane, xl, rowsum);
+    compute_affine<MT>(g, ops, lane, xl, k0, rowsum);
 }
 
 __device__ __forceinline__ void signal_done_through(Shared *sh, int &signalled, int upto) {
@@ -399,7 +494,7 @@ __device__ __forceinline__ void signal_done_through(Shared *sh, int &signalled, 
   }
 }
 
-template <bool Q4>
+template <bool Q4, int MT>
 __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
                              int n_stages, Shared *sh, const float *xbuf, int xmax,
                              uint32_t *err) {
@@ -408,10 +503,12 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
   // the schedule is a scalar load (it never waits on the vector-load counter
   // that tracks the weight prefetch)
   const int cw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - 1;
-  const int nw = gridDim.x * kNcw<Q4>;
-  const int gw = blockIdx.x * kNcw<Q4> + cw;
+  const int nw = gridDim.x * kNcw<Q4, MT>;
+  const int gw = blockIdx.x * kNcw<Q4, MT> + cw;
   int signalled = 0;
-  float rowsum = 0.f;
+  float rowsum[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) rowsum[t] = 0.f;
   int have = 0;  // stages known staged
   Group<Q4> A, B;
 
@@ -427,6 +524,14 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
         have = s + 1;
       }
     }
+  };
+
+  // the first op of stage s's staged input (read after the stage is staged)
+  auto staged_base = [&](int s) -> int {
+    if constexpr (kCompact<Q4, MT>)
+      return uni(sh->xk0[s & 1]);
+    else
+      return 0;
   };
 
   auto wait_arrived = [&](int t) {
@@ -455,10 +560,10 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
     if (n1.s == c.s) {
       issue(nxt, ops, stages, n1, gw, nw, lane);
       enter(c.s);
-      compute(cur, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
+      compute<Q4, MT>(cur, ops, lane, xbuf + (c.s & 1) * xmax, staged_base(c.s), rowsum);
     } else {
       enter(c.s);
-      compute(cur, ops, lane, xbuf + (c.s & 1) * xmax, rowsum);
+      compute<Q4, MT>(cur, ops, lane, xbuf + (c.s & 1) * xmax, staged_base(c.s), rowsum);
       if (n1.s >= n_stages) return false;
       signal_done_through(sh, signalled, n1.s);  // as soon as a stage is finished
       // the next stage's schedule lookups (dependent scalar loads) while the
@@ -513,21 +618,22 @@ struct StagePlan {
   uint32_t *data;       // the stage's input words
   int f0, f1;           // 64-bit words this workgroup reads: [f0, f1)
   int k0, k1;           // ops (within the stage) those words belong to
+  int kbase;            // the op staged first in LDS: k0, or 0 (one token row)
   int epo;              // input elements per op
   int xstride;          // LDS floats per op (whole 1024-column chunks)
   int pa, pb;           // this workgroup's published words [pa, pb)
 };
 
-template <bool Q4>
+template <bool Q4, int MT>
 __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepStage &st, int m) {
   // 64-bit exchange words: four BF16 inputs, or two f32 (Q4_0)
   constexpr int kLgPer64 = Q4 ? 1 : 2;
   StagePlan p;
   p.data = st.data;
   p.epo = m * st.cols;
-  p.xstride = st.chunks * kItemCols<Q4>;
+  p.xstride = MT == 1 ? st.chunks * kItemCols<Q4> : MT * st.chunks * 512;
   int lo, hi, lo2, hi2;
-  constexpr int NCW = kNcw<Q4>;
+  constexpr int NCW = kNcw<Q4, MT>;
   wave_rows(st, blockIdx.x * NCW, gridDim.x * NCW, lo, hi);
   wave_rows(st, blockIdx.x * NCW + NCW - 1, gridDim.x * NCW, lo2, hi2);
   if (hi2 <= lo) {  // no rows for this workgroup in this stage
@@ -539,6 +645,7 @@ __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepSta
     p.f0 = (p.k0 * p.epo) >> kLgPer64;
     p.f1 = ((p.k1 + 1) * p.epo) >> kLgPer64;
   }
+  p.kbase = kCompact<Q4, MT> ? p.k0 : 0;
   p.pa = (int)blockIdx.x << st.lg;
   p.pb = min(p.pa + (1 << st.lg), (int)st.words);
   return p;
@@ -546,19 +653,34 @@ __device__ __forceinline__ StagePlan stage_plan(const StepOp *ops, const StepSta
 
 // One 64-bit input word into LDS as fp32: four BF16 elements (xswz layout),
 // or two f32 elements (Q4_0, xq4 layout).
-template <bool Q4>
+// Element index in LDS (BF16 units, relative to the op) of element r of an
+// op's MT-row input: token row t = r / cols at t * tstride, then the
+// column's xswz slot (the fp32 layout's order, two bytes per element: lane
+// l's 16 columns of a chunk are its four 8-byte pieces at 4 l + 256 j).
+template <int MT>
+__device__ __forceinline__ int x_pos(int r, int cols, int tstride) {
+  int t = 0;
+#pragma unroll
+  for (int i = 1; i < MT; ++i) t += r >= i * cols;
+  return t * tstride + xswz(r - t * cols);
+}
+
+template <bool Q4, int MT>
 __device__ __forceinline__ void stage_word(const StagePlan &pp, float *dst, int f, uint64_t v) {
-  // the word's elements lie in one op (each op's input is a multiple of 64
-  // elements) and land in one float4 slot
+  // the word's elements lie in one op and one token row (each op's row is a
+  // multiple of 64 elements) and land in one float4 slot
   const int e = (Q4 ? 2 : 4) * f;
   int k = pp.k0;
   while (k < pp.k1 && e >= (k + 1) * pp.epo) ++k;
   const int r = e - k * pp.epo;
   const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  float *od = dst + (k - pp.kbase) * pp.xstride;
   if constexpr (Q4)
-    *(float2 *)(dst + k * pp.xstride + xq4(r)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
+    *(float2 *)(od + xq4(r)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
+  else if constexpr (MT > 1)
+    *(uint64_t *)((uint16_t *)od + x_pos<MT>(r, pp.epo / MT, 2 * pp.xstride / MT)) = v;
   else
-    *(float4 *)(dst + k * pp.xstride + xswz(r)) =
+    *(float4 *)(od + xswz(r)) =
         make_float4(bf16_to_f32(lo & 0xffffu), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffffu),
                     bf16_to_f32(hi >> 16));
 }
@@ -566,9 +688,9 @@ __device__ __forceinline__ void stage_word(const StagePlan &pp, float *dst, int 
 // NB 64-bit words per lane of one op's input [base, wpo) into LDS: every
 // load issued (clamped to the op's last word, never conditional) before any
 // is consumed, so the whole batch costs one memory round trip.
-template <bool Q4, int NB>
+template <bool Q4, int MT, int NB>
 __device__ __forceinline__ void read_words(const uint64_t *op, float *od, int base, int wpo,
-                                           int lane) {
+                                           int cols, int tstride, int lane) {
   uint64_t v[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) v[b] = ld_agent64(op + min(base + b * 64 + lane, wpo - 1));
@@ -580,9 +702,12 @@ __device__ __forceinline__ void read_words(const uint64_t *op, float *od, int ba
       if constexpr (Q4)
         *(float2 *)(od + xq4(2 * f)) = make_float2(__uint_as_float(lo), __uint_as_float(hi));
       else
-        *(float4 *)(od + xswz(4 * f)) =
-            make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                        __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
+        if constexpr (MT > 1)
+          *(uint64_t *)((uint16_t *)od + x_pos<MT>(4 * f, cols, tstride)) = v[b];
+        else
+          *(float4 *)(od + xswz(4 * f)) =
+              make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u));
     }
   }
 }
@@ -594,35 +719,38 @@ __device__ __forceinline__ void read_words(const uint64_t *op, float *od, int ba
 // straight-line path per size, chosen before any load is issued): inputs
 // up to 1536 words (a 3072-wide f32 row, a 6144-wide BF16 row) take one
 // memory round trip, a 5120-wide f32 row two.
-template <bool Q4>
+template <bool Q4, int MT>
 __device__ void read_stage(const StagePlan &pp, float *dst, int lane) {
   const uint64_t *src = (const uint64_t *)pp.data;
   const int wpo = pp.epo >> (Q4 ? 1 : 2);  // 64-bit words per op (a multiple of 16)
   const int per_lane = uni((wpo + 63) >> 6);
+  const int cols = pp.epo / MT, tstride = 2 * pp.xstride / MT;  // tstride: BF16 units
   for (int k = pp.k0; k <= pp.k1; ++k) {
     const uint64_t *op = src + (size_t)k * wpo;
-    float *od = dst + k * pp.xstride;
+    float *od = dst + (k - pp.kbase) * pp.xstride;
     if (per_lane <= 4)
-      read_words<Q4, 4>(op, od, 0, wpo, lane);
+      read_words<Q4, MT, 4>(op, od, 0, wpo, cols, tstride, lane);
     else if (per_lane <= 8)
-      read_words<Q4, 8>(op, od, 0, wpo, lane);
+      read_words<Q4, MT, 8>(op, od, 0, wpo, cols, tstride, lane);
     else if (per_lane <= 12)
-      read_words<Q4, 12>(op, od, 0, wpo, lane);
+      read_words<Q4, MT, 12>(op, od, 0, wpo, cols, tstride, lane);
     else
-      for (int base = 0; base < wpo; base += 64 * 24) read_words<Q4, 24>(op, od, base, wpo, lane);
+      for (int base = 0; base < wpo; base += 64 * 24)
+        read_words<Q4, MT, 24>(op, od, base, wpo, cols, tstride, lane);
   }
 }
 
 // The first stage's input, straight from the ops' inputs (written before
 // the launch).
-template <bool Q4>
+template <bool Q4, int MT>
 __device__ void read_first_stage(const StagePlan &pp, const StepOp *ops, const StepStage &st,
                                  float *dst, int lane) {
   constexpr int kEsz = Q4 ? 4 : 2;  // bytes per input element
   for (int f = pp.f0 + lane; f < pp.f1; f += 64) {
     const int e = (Q4 ? 2 : 4) * f, k = e / pp.epo;
     const QD_GLOBAL uint8_t *x = (const QD_GLOBAL uint8_t *)gp(ops[st.op0 + k].x);
-    stage_word<Q4>(pp, dst, f, *(const QD_GLOBAL uint64_t *)(x + (size_t)(e - k * pp.epo) * kEsz));
+    stage_word<Q4, MT>(pp, dst, f,
+                       *(const QD_GLOBAL uint64_t *)(x + (size_t)(e - k * pp.epo) * kEsz));
   }
 }
 
@@ -653,7 +781,7 @@ __device__ __forceinline__ void arrive(uint32_t *ctr, uint32_t *rel, int s, uint
     for (int k = lane; k < nwg; k += kWave) st_agent(rel + (size_t)k * kStepLine, tag);
 }
 
-template <bool Q4>
+template <bool Q4, int MT>
 __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
                             int n_stages, int m, Shared *sh, float *xbuf, int xmax,
                             uint32_t *rel, uint32_t *ctr, uint32_t *err) {
@@ -671,7 +799,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
   // chains before any compute wave could start.)
   PubSlice pending;
   int pending_stage = -1;
-  StagePlan cur = stage_plan<Q4>(ops, stages[0], m);
+  StagePlan cur = stage_plan<Q4, MT>(ops, stages[0], m);
   StagePlan nxt = cur;
   for (int s = 0; s < n_stages; ++s) {
     const uint32_t tag = epoch + (uint32_t)s;
@@ -688,16 +816,17 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
       }
     }
     if (s == 0)
-      read_first_stage<Q4>(cur, ops, stages[0], xbuf, lane);
+      read_first_stage<Q4, MT>(cur, ops, stages[0], xbuf, lane);
     else
-      read_stage<Q4>(cur, xbuf + (s & 1) * xmax, lane);
+      read_stage<Q4, MT>(cur, xbuf + (s & 1) * xmax, lane);
+    if (kCompact<Q4, MT> && lane == 0) sh->xk0[s & 1] = cur.kbase;
     // hand the staged input to the compute waves (LDS executes this wave's
     // data writes before the flag write)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (lane == 0) __hip_atomic_store(&sh->xready, s + 1, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_WORKGROUP);
     // resolve the next stage while the compute waves work
-    if (s + 1 < n_stages) nxt = stage_plan<Q4>(ops, stages[s + 1], m);
+    if (s + 1 < n_stages) nxt = stage_plan<Q4, MT>(ops, stages[s + 1], m);
     // stage 1's values, needed at the end of this stage (later stages' come
     // through the ring below); loaded under stage 0's compute rather than
     // before the first input is staged
@@ -714,7 +843,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
     }
     // wait for every compute wave to finish stage s, then publish s+1
     unsigned spins = 0;
-    while (lds_ld(&sh->done) < (s + 1) * kNcw<Q4>) {
+    while (lds_ld(&sh->done) < (s + 1) * kNcw<Q4, MT>) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kLdsSpinLimit) {
         if (lane == 0) atomicOr(err, 2u);
@@ -737,7 +866,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
   }
 }
 
-template <bool Q4>
+template <bool Q4, int MT>
 __device__ __forceinline__ void step_body(const StepOp *__restrict__ ops,
                                           const StepStage *__restrict__ stages, int n_stages,
                                           int m, int xmax, int nwg, uint32_t *epoch_word,
@@ -753,49 +882,81 @@ __device__ __forceinline__ void step_body(const StepOp *__restrict__ ops,
     sh.done = 0;
     sh.arrived = 0;
     sh.epoch = ld_agent(epoch_word);
+    sh.xk0[0] = sh.xk0[1] = 0;
   }
   __syncthreads();
   if (threadIdx.x < kWave)
-    poller_wave<Q4>(ops, stages, n_stages, m, &sh, xbuf, xmax, rel, ctr, err);
+    poller_wave<Q4, MT>(ops, stages, n_stages, m, &sh, xbuf, xmax, rel, ctr, err);
   else
-    compute_wave<Q4>(ops, stages, n_stages, &sh, xbuf, xmax, err);
+    compute_wave<Q4, MT>(ops, stages, n_stages, &sh, xbuf, xmax, err);
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(epoch_word, sh.epoch + (uint32_t)n_stages);
 }
 
-__global__ __launch_bounds__(kThreads<false>) void affine_step_kernel(
+__global__ __launch_bounds__((kThreads<false, 1>)) void affine_step_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
-  step_body<false>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  step_body<false, 1>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
 }
 
-__global__ __launch_bounds__(kThreads<true>) void q4_0_step_kernel(
+// m = MT token rows (2..4) of affine ops
+template <int MT>
+__global__ __launch_bounds__((kThreads<false, MT>)) void affine_step_mt_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
-  step_body<true>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  step_body<false, MT>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+}
+
+__global__ __launch_bounds__((kThreads<true, 1>)) void q4_0_step_kernel(
+    const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
+    int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
+    uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
+  step_body<true, 1>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
 }
 
 }  // namespace
 
-int step_threads() { return kThreads<false>; }
+int step_compute_waves(bool q4, int m) {
+  return q4 ? kNcw<true, 1> : m > 1 ? kNcw<false, 2> : kNcw<false, 1>;
+}
+
+bool step_compact(bool q4, int m) { return q4 ? kCompact<true, 1> : kCompact<false, 2> && m > 1; }
 
 hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
                        int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
                        uint32_t *err, size_t lds_bytes, hipStream_t stream) {
-  const void *fn = q4 ? (const void *)q4_0_step_kernel : (const void *)affine_step_kernel;
+  const void *fn;
+  int threads;
+  if (q4) {
+    fn = (const void *)q4_0_step_kernel;
+    threads = kThreads<true, 1>;
+  } else if (m == 1) {
+    fn = (const void *)affine_step_kernel;
+    threads = kThreads<false, 1>;
+  } else if (m == 2) {
+    fn = (const void *)affine_step_mt_kernel<2>;
+    threads = kThreads<false, 2>;
+  } else if (m == 3) {
+    fn = (const void *)affine_step_mt_kernel<3>;
+    threads = kThreads<false, 3>;
+  } else if (m == 4) {
+    fn = (const void *)affine_step_mt_kernel<4>;
+    threads = kThreads<false, 4>;
+  } else {
+    return hipErrorInvalidValue;
+  }
   if (lds_bytes > 65536) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes);
     if (e != hipSuccess) return e;
   }
-  if (q4)
-    hipLaunchKernelGGL(q4_0_step_kernel, dim3(nwg), dim3(kThreads<true>), lds_bytes, stream, ops,
-                       stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
-  else
-    hipLaunchKernelGGL(affine_step_kernel, dim3(nwg), dim3(kThreads<false>), lds_bytes, stream, ops,
-                       stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  void *args[] = {(void *)&ops,  (void *)&stages,     (void *)&n_stages, (void *)&m,
+                  (void *)&xmax, (void *)&nwg,        (void *)&epoch_word, (void *)&rel,
+                  (void *)&ctr,  (void *)&err};
+  hipError_t e = hipLaunchKernel(fn, dim3(nwg), dim3(threads), args, lds_bytes, stream);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

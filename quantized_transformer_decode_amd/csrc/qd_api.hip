@@ -99,6 +99,7 @@ bool affine_shape_ok(int64_t rows, int64_t cols) {
 
 constexpr int kMaxStageWords = 16384;  // LDS: two fp32 copies of a stage input
 constexpr int kMinStepWgs = 32;        // smallest grid a plan supports
+constexpr int kMaxStepRows = 4;        // token rows of an affine step
 // a last stage of one GEMV of at least this many weights runs as its own launch
 constexpr int64_t kStepTailWeights = (int64_t)1 << 27;
 // log2 of the slice length for a stage input of `words` 32-bit words over
@@ -151,11 +152,20 @@ std::vector<StepIn> step_in(const qd_q4_0_gemv_op *ops, int64_t n_ops) {
   return v;
 }
 
+// LDS floats one op's staged input takes: whole chunks of the item width,
+// fp32 for one token row, BF16 (half a float each) for several.
+int64_t step_op_lds_floats(int64_t cols, int64_t m, StepFormat f) {
+  const int64_t items = (cols + f.chunk() - 1) / f.chunk() * f.chunk();
+  return m == 1 ? items : m * items / 2;
+}
+
 // Validates a decode-step op list; on success fills the layout sizes.
 qd_status step_validate(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f,
-                        size_t *ws_bytes, int *n_stages, int *xmax) {
-  if (!ops || n_ops < 1 || n_ops > kMaxStepOps || m != 1) return QD_EINVAL;
-  int stages = 0, cur_words = 0, max_words = 0;
+                        size_t *ws_bytes, int *n_stages) {
+  // several token rows for affine ops (one persistent kernel per row count)
+  if (!ops || n_ops < 1 || n_ops > kMaxStepOps || m < 1 || m > (f.q4 ? 1 : kMaxStepRows))
+    return QD_EINVAL;
+  int stages = 0;
   for (int64_t i = 0; i < n_ops; ++i) {
     const StepIn &o = ops[i];
     if (!o.w || !o.x || !o.y) return QD_EINVAL;
@@ -165,19 +175,15 @@ qd_status step_validate(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat 
     if (i == 0) {
       if (o.stage != 0) return QD_EINVAL;
       stages = 1;
-      cur_words = 0;
     } else if (o.stage == ops[i - 1].stage + 1) {
       stages += 1;
-      cur_words = 0;
     } else if (o.stage == ops[i - 1].stage) {
       if (o.cols != ops[i - 1].cols) return QD_ESHAPE;
     } else {
       return QD_EINVAL;
     }
-    // LDS holds each op's input in whole chunks of the format's item width
-    cur_words += (int)(m * ((o.cols + f.chunk() - 1) / f.chunk()) * f.chunk());
-    if (cur_words > kMaxStageWords) return QD_ESHAPE;
-    if (cur_words > max_words) max_words = cur_words;
+    // LDS holds an op's input in whole chunks of the format's item width
+    if (step_op_lds_floats(o.cols, m, f) > kMaxStageWords) return QD_ESHAPE;
   }
   // outputs may not overlap any weights or inputs of the step
   for (int64_t i = 0; i < n_ops; ++i) {
@@ -191,7 +197,6 @@ qd_status step_validate(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat 
     }
   }
   *n_stages = stages;
-  *xmax = max_words;
   *ws_bytes = sizeof(qd::StepHeader) + align256(sizeof(qd::StepOp) * n_ops) +
               align256(sizeof(qd::StepStage) * stages);
   return QD_OK;
@@ -209,6 +214,38 @@ bool step_fits_grid(const StepIn *ops, int64_t n_ops, int64_t m, int nwg, StepFo
     i = j;
   }
   return true;
+}
+
+// fp32 LDS floats one staged stage input takes at most in a workgroup: with
+// several token rows the ops its rows fall in (the kernel splits each
+// stage's rows evenly over all compute waves, workgroup j holding those of
+// its waves), else every op of the stage; m token rows of whole items each.
+// 0 if some workgroup would need more than the LDS holds.
+int step_lds_floats(const StepIn *ops, int64_t n_ops, int64_t m, int nwg, StepFormat f) {
+  const int64_t ncw = qd::step_compute_waves(f.q4, (int)m);
+  const int64_t nw = (int64_t)nwg * ncw;
+  int64_t worst = 0;
+  int64_t i = 0;
+  while (i < n_ops) {
+    int64_t j = i, total = 0;
+    while (j < n_ops && ops[j].stage == ops[i].stage) total += ops[j++].rows;
+    const int64_t per_op = step_op_lds_floats(ops[i].cols, m, f);
+    for (int64_t g = 0; g < nwg; ++g) {
+      const int64_t lo = total * (g * ncw) / nw, hi = total * ((g + 1) * ncw) / nw;
+      if (hi <= lo) continue;
+      // ops holding rows lo and hi - 1 of the stage's row space
+      int64_t k0 = -1, k1 = -1, base = 0;
+      for (int64_t k = i; k < j; ++k) {
+        if (k0 < 0 && lo < base + ops[k].rows) k0 = k;
+        if (k1 < 0 && hi - 1 < base + ops[k].rows) k1 = k;
+        base += ops[k].rows;
+      }
+      const int64_t need = (qd::step_compact(f.q4, (int)m) ? k1 - k0 + 1 : j - i) * per_op;
+      if (need > worst) worst = need;
+    }
+    i = j;
+  }
+  return worst > kMaxStageWords ? 0 : (int)worst;
 }
 
 // Bytes after the tables: one release line per workgroup, the arrival
@@ -229,13 +266,14 @@ size_t step_exchange_bytes(const StepIn *ops, int64_t n_ops, int64_t m, int nwg,
 
 size_t step_workspace_bytes(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f) {
   size_t bytes = 0;
-  int ns = 0, xmax = 0;
-  if (step_validate(ops, n_ops, m, f, &bytes, &ns, &xmax) != QD_OK) return 0;
+  int ns = 0;
+  if (step_validate(ops, n_ops, m, f, &bytes, &ns) != QD_OK) return 0;
   // the staging layout depends on the grid: one workgroup per CU of the
   // current device
   if (check_device() != QD_OK) return 0;
   const int nwg = current_cus();
   if (nwg < kMinStepWgs || !step_fits_grid(ops, n_ops, m, nwg, f)) return 0;
+  if (step_lds_floats(ops, n_ops, m, nwg, f) == 0) return 0;
   return bytes + step_exchange_bytes(ops, n_ops, m, nwg, ns, f);
 }
 
@@ -243,8 +281,8 @@ qd_status step_plan(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f, v
                     size_t workspace_bytes, qd_step_plan *plan, void *stream) {
   if (!workspace || !plan) return QD_EINVAL;
   size_t need = 0;
-  int ns = 0, xmax = 0;
-  qd_status st = step_validate(ops, n_ops, m, f, &need, &ns, &xmax);
+  int ns = 0;
+  qd_status st = step_validate(ops, n_ops, m, f, &need, &ns);
   if (st != QD_OK) return st;
   if (!aligned(workspace, 256)) return QD_EALIGN;
   if (workspace_bytes < need) return QD_EINVAL;  // tables alone; staging checked below
@@ -260,6 +298,8 @@ qd_status step_plan(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f, v
   const int nwg = current_cus();
   if (nwg < kMinStepWgs) return QD_EDEVICE;
   if (!step_fits_grid(ops, n_ops, m, nwg, f)) return QD_ESHAPE;
+  const int xmax = step_lds_floats(ops, n_ops, m, nwg, f);
+  if (xmax == 0) return QD_ESHAPE;
   need += step_exchange_bytes(ops, n_ops, m, nwg, ns, f);
   if (workspace_bytes < need) return QD_EINVAL;
 
@@ -353,7 +393,8 @@ qd_status step_run(const qd_step_plan *plan, bool q4, void *stream) {
       plan->format != (q4 ? 1 : 0) || plan->nwg < 1 || plan->lds_bytes < 8 ||
       plan->lds_bytes > 2 * kMaxStageWords * 4 || plan->lds_bytes % 8 != 0 ||
       plan->n_ops < 1 || plan->n_stages < 1 || plan->n_stages > plan->n_ops ||
-      plan->m != 1 || plan->tail < 0 || plan->tail > 1 || (q4 && plan->tail) ||
+      plan->m < 1 || plan->m > (q4 ? 1 : kMaxStepRows) || plan->tail < 0 || plan->tail > 1 ||
+      (q4 && plan->tail) ||
       (plan->tail && (plan->n_stages < 2 || !plan->tail_w || !plan->tail_x || !plan->tail_y ||
                       plan->tail_rows < 1 || plan->tail_cols < 64 || plan->tail_cols % 64 ||
                       plan->tail_cols > kMaxGemvCols)))
@@ -378,8 +419,8 @@ qd_status step_run(const qd_step_plan *plan, bool q4, void *stream) {
     g.w[0] = (const uint8_t *)plan->tail_w;
     g.y[0] = (uint16_t *)plan->tail_y;
     g.rows[0] = (int)plan->tail_rows;
-    e = qd::launch_affine_gemv(g, (int)plan->tail_cols, (const uint16_t *)plan->tail_x, 1, false,
-                               (hipStream_t)stream);
+    e = qd::launch_affine_gemv(g, (int)plan->tail_cols, (const uint16_t *)plan->tail_x, plan->m,
+                               false, (hipStream_t)stream);
   }
   return e == hipSuccess ? QD_OK : hip_fail(e);
 }

@@ -157,7 +157,8 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink,
 // affine-INT8 g64 ops (BF16 in and out) or, with q4, Q4_0 ops (f32).
 struct StepOp;
 struct StepStage;
-int step_threads();
+int step_compute_waves(bool q4, int m);  // compute waves per workgroup of the step kernel
+bool step_compact(bool q4, int m);       // LDS holds only a workgroup's ops (else all)
 hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
                        int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
                        uint32_t *err, size_t lds_bytes, hipStream_t stream);

@@ -436,6 +436,23 @@ def _q4_ops(*specs):
     return arr
 
 
+def test_errors_affine_step_rows():
+    ops = (qd.AffineGemvOp * 1)(qd.AffineGemvOp(A, B, C, 64, 256, 0))
+    wb = qd.lib().qgemv_affine_i8_g64_step_workspace_bytes
+    plan = qd.StepPlan()
+    for m in (0, 5):                     # 1..4 token rows
+        assert wb(ops, 1, m) == 0
+        assert _call("qgemv_affine_i8_g64_step_plan", ops, 1, m, WS, 1 << 20, ctypes.byref(plan),
+                     None) == qd.QD_EINVAL
+    p = qd.StepPlan(workspace=WS, nwg=256, lds_bytes=16384, n_ops=1, n_stages=1, m=5,
+                    magic=0x51445354, tail=0, format=0)
+    assert _call("qgemv_affine_i8_g64_step_run", ctypes.byref(p), None) == qd.QD_EINVAL
+    if not _gpu_visible():
+        for m in (1, 4):
+            assert _call("qgemv_affine_i8_g64_step_plan", ops, 1, m, WS, 1 << 20,
+                         ctypes.byref(plan), None) == qd.QD_EDEVICE
+
+
 def test_errors_q4_0_step():
     wb = qd.lib().qgemv_q4_0_step_workspace_bytes
     ok = (A, B, C, 64, 256, 0)

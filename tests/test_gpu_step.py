@@ -17,23 +17,30 @@ pytestmark = pytest.mark.gpu
 
 
 class Step:
-    def __init__(self, shapes, key):
-        """shapes: list of (rows, cols, stage)"""
+    def __init__(self, shapes, key, m=1, share_weights=None):
+        """shapes: list of (rows, cols, stage); m token rows.  share_weights:
+        optional per-op index of an earlier op whose weights it reuses."""
         self.shapes = shapes
+        self.m = m
         self.blobs, self.xbits, self.xs, self.ys = [], [], [], []
         for i, (rows, cols, stage) in enumerate(shapes):
-            tr = synth.affine_triplet(rows, cols, key=(key, i, 0))
-            self.blobs.append(pack_on_device(tr))
-            xb = synth.x_bf16(1, cols, key=(key, i, 1))
+            j = share_weights[i] if share_weights is not None else i
+            if j == i:
+                tr = synth.affine_triplet(rows, cols, key=(key, i, 0))
+                self.blobs.append(pack_on_device(tr))
+            else:
+                self.blobs.append(self.blobs[j])
+            xb = synth.x_bf16(m, cols, key=(key, i, 1))
             self.xbits.append(xb)
             self.xs.append(dev_bf16(xb))
-            self.ys.append(torch.full((1, rows), float("nan"), dtype=torch.bfloat16, device=DEV))
+            self.ys.append(torch.full((m, rows), float("nan"), dtype=torch.bfloat16, device=DEV))
         self.ops = qd.make_ops((b, x, y, r, c, s) for (r, c, s), b, x, y in
                                zip(shapes, self.blobs, self.xs, self.ys))
-        nbytes = qd.qgemv_affine_i8_g64_step_workspace_bytes(self.ops, 1)
+        nbytes = qd.qgemv_affine_i8_g64_step_workspace_bytes(self.ops, m)
         assert nbytes > 0
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
-        self.plan = qd.qgemv_affine_i8_g64_step_plan(self.ops, 1, self.ws, nbytes)
+        self.plan = qd.qgemv_affine_i8_g64_step_plan(self.ops, m, self.ws, nbytes)
+        assert self.plan.m == m
 
     def run(self):
         qd.qgemv_affine_i8_g64_step_run(self.plan)
@@ -47,6 +54,7 @@ class Step:
                     np.random.default_rng(i).integers(0, rows, sample_rows), [0, rows - 1]]))
             ref = oracle.affine_gemv(self.blobs[i].cpu().numpy(), rows, cols, self.xbits[i],
                                      row_sel=sel)
+            assert ref.shape[0] == self.m
             got = host_bf16_f64(self.ys[i])
             if sel is not None:
                 got = got[:, sel]
@@ -160,9 +168,71 @@ def test_step_plan_rejects_bad_ops():
         qd.qgemv_affine_i8_g64_step_plan(qd.make_ops(ok + [(base, base + 131072, base + 300000, 64, 64, 1)]),
                                          1, ws, ws.numel())
     assert e.value.status == qd.QD_EINVAL
-    with pytest.raises(qd.QDError) as e:   # m > 1 not supported by the step kernel
-        qd.qgemv_affine_i8_g64_step_plan(qd.make_ops(ok), 2, ws, ws.numel())
-    assert e.value.status == qd.QD_EINVAL
+    for m in (0, 5):                        # 1..4 token rows
+        with pytest.raises(qd.QDError) as e:
+            qd.qgemv_affine_i8_g64_step_plan(qd.make_ops(ok), m, ws, ws.numel())
+        assert e.value.status == qd.QD_EINVAL
     with pytest.raises(qd.QDError) as e:   # workspace too small
         qd.qgemv_affine_i8_g64_step_plan(qd.make_ops(ok), 1, ws, 512)
     assert e.value.status == qd.QD_EINVAL
+
+
+# Several token rows (one persistent kernel per row count): every op's x is
+# [m, cols] and y [m, rows]; the staged input holds only the ops a
+# workgroup has rows in.
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_step_rows_small_parity_and_relaunch(m):
+    print(f"step m={m} small", flush=True)
+    st = Step(SMALL, key=30 + m, m=m)
+    st.run()
+    st.check(what=f"m={m} first launch")
+    for i, (rows, cols, stage) in enumerate(SMALL):
+        xb = synth.x_bf16(m, cols, key=(35 + m, i, 1))
+        st.xbits[i] = xb
+        st.xs[i].copy_(dev_bf16(xb))
+        st.ys[i].fill_(float("nan"))
+    torch.cuda.synchronize()
+    st.run()
+    st.check(what=f"m={m} second launch")
+
+
+def test_step_rows_graph_and_streamed_tail():
+    # m = 4 with a last stage streamed on its own (the matrix-core GEMV at
+    # four rows), eager and as graph replays
+    print("step m=4 tail", flush=True)
+    st = Step(TAIL, key=39, m=4)
+    assert st.plan.tail == 1
+    st.run()
+    st.check(sample_rows=64, what="m=4 tail eager")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            qd.qgemv_affine_i8_g64_step_run(st.plan)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for y in st.ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert qd.qgemv_affine_i8_g64_step_check(st.plan) == 0
+        st.check(sample_rows=64, what=f"m=4 tail replay {rep}")
+
+
+def test_step_rows_qwen3_1_7b_full_size_sampled():
+    # the full Qwen3-1.7B-shaped step at four token rows (one layer's
+    # matrices shared by all 28 layers), every GEMV checked on sampled rows
+    print("step qwen3-1.7b m=4", flush=True)
+    mats = synth.decode_step_matrices(synth.QWEN3_1_7B)
+    shapes = [(rows, cols, stage) for (_, _, rows, cols, stage) in mats]
+    first = {}
+    share = []
+    for i, (layer, name, rows, cols, stage) in enumerate(mats):
+        first.setdefault(name, i)
+        share.append(first[name])
+    st = Step(shapes, key=40, m=4, share_weights=share)
+    assert st.plan.tail == 1
+    for _ in range(2):
+        st.run()
+    st.check(sample_rows=24, what="qwen3-1.7b m=4")
