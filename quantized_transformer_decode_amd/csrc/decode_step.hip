@@ -1,6 +1,6 @@
 // decode_step.hip -- one persistent launch for a whole decode step's
-// GEMVs, in stage order (M = 1): affine-INT8 g64 ops (BF16), or Q4_0 ops
-// (f32, the Whisper decoder's projections).
+// GEMVs, in stage order: affine-INT8 g64 ops (BF16, 1..4 token rows), or
+// Q4_0 ops (f32, one row: the Whisper decoder's projections).
 //
 // turbospark-runtime 0.3.0, qwen3_asr_metal.rs -- Qwen3AsrMetalEngine::step
 // encodes every projection GEMV of a generated token, in decoder order, into
