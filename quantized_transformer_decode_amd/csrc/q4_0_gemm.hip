@@ -27,6 +27,10 @@
 // fragment read's 16 rows over all banks) with the deltas in fp32
 // ([64][4]), and every wave reads its B fragments there.
 //
+// Launches with many output tiles (at least 7/4 of 128 x 128 per CU: fc1 of
+// a Whisper-large layer at 1500 frames) run a second kernel with 128 x 128
+// workgroup tiles and 64 x 64 wave tiles (below).
+//
 // Launches with fewer output tiles than two per CU (the 1280-row matrices
 // of a Whisper-large layer: 240 tiles at 1500 frames) run eight waves per
 // workgroup instead: two K parts of four waves, each with its own codes
@@ -375,6 +379,250 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     store([](float v) { return v; });
 }
 
+// ---- wide tiles: 128 frames x 128 weight rows per workgroup ----------------
+//
+// Launches with many output tiles (fc1 of a Whisper-large layer: 480 wide
+// tiles at 1500 frames) run 2 x 2 waves of 64 frames x 64 rows each: every
+// B fragment read from LDS feeds four MFMAs and every A fragment four, half
+// the LDS and L2 traffic per MFMA of the 32 x 64 wave tiles above, and the x
+// tile is shared by the two waves of a frame half.  A stage is two Q4_0
+// blocks (64 columns: one cache line of each frame), so that two workgroups
+// fit a CU (72 KB of LDS each, two waves per SIMD).  Each thread converts
+// one raw block per stage into the codes buffer; the x tile is
+// double-buffered in LDS like the codes.  A block's partial product is
+// scaled by its delta four MFMAs after it is issued (a ring of four
+// products), which keeps the scaling off the MFMA's result latency without
+// a second set of 16 accumulators.  (fc1 at 1500 frames: 49 -> 43 us; the
+// 1280-row matrices have only 120 such tiles and keep the kernel above.)
+namespace wide {
+constexpr int BM = 128, BN = 128;
+constexpr int NB = 2;                  // Q4_0 blocks per stage
+constexpr int BK = NB * 32;
+constexpr int CH = BK / 8;             // 16-byte chunks of a frame per stage
+constexpr int LDB = BK + 8;            // codes row stride in BF16 (144 bytes)
+constexpr int TM = 4, TN = 4, NT = TM * TN;
+constexpr int LAG = 4;
+constexpr int kThreads = 256;
+constexpr int XL = BM * CH / kThreads;  // x loads per thread and stage
+
+// Chunk c of frame r in the x tile: rows of 128 bytes, two frames per 64
+// banks; sixteen consecutive frames at one chunk land in sixteen distinct
+// 16-byte bank groups (fragment reads and line-shaped writes alike).
+__device__ __forceinline__ int xslot(int r, int c) { return r * CH + (c ^ ((r >> 1) & 7)); }
+}  // namespace wide
+
+template <bool MULTI, bool EPI>
+__global__ __launch_bounds__(wide::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q4_0_gemm_wide_kernel(
+    const Q40Group grp, int cols, const uint16_t *__restrict__ x, int m) {
+  constexpr int BM = wide::BM, BN = wide::BN, NB = wide::NB, BK = wide::BK, CH = wide::CH;
+  constexpr int LDB = wide::LDB, TM = wide::TM, TN = wide::TN, NT = wide::NT, LAG = wide::LAG;
+  constexpr int XL = wide::XL;
+  using wide::xslot;
+  __shared__ __attribute__((aligned(16))) uint16_t codes[2][BN * LDB];
+  __shared__ __attribute__((aligned(16))) float deltas[2][BN * NB];
+  __shared__ __attribute__((aligned(16))) u32x4 xs[2][BM * CH];
+
+  const int bx = blockIdx.x;
+  int k = 0;
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i)
+      if (i < grp.n && bx >= grp.tile0[i]) k = i;
+    k = uni(k);
+  }
+  const uint8_t *w = grp.w[k];
+  const int rows = grp.rows[k];
+  QD_GLOBAL float *y = gp(grp.y[k]);
+  const float *bias = grp.bias[k];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // this wave's frame and row halves
+  const int m0 = blockIdx.y * BM;
+  const int n0 = (bx - grp.tile0[k]) * BN;
+  const int nstages = cols / BK;
+  const int nb = cols >> 5;
+  const int mrem = min(m - m0, BM), rrem = min(rows - n0, BN);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(x + (size_t)m0 * cols), 0, mrem * cols * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(w + (size_t)n0 * nb * 18), 0, rrem * nb * 18, kRsrcWord3);
+  const int kc = lane >> 4;
+
+  // x: load j brings chunk tid % 8 of frame 32j + tid / 8 (frames past m
+  // read the tile's last frame; they only feed outputs never stored)
+  int xoff[XL], xput[XL];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int r = 32 * j + (tid >> 3);
+    xoff[j] = min(r, mrem - 1) * cols * 2 + (tid & 7) * 16;
+    xput[j] = xslot(r, tid & 7);
+  }
+  // the block this thread converts: row cr, block cb of each stage (the
+  // window and parity rules of the kernel above)
+  const int cr = tid >> 1, cb = tid & 1;
+  const bool cdead = cr >= rrem;
+  const int woff = 18 * (min(cr, rrem - 1) * nb + cb) - 2 * cb;
+  const bool codd = cb;
+
+  auto load_x = [&](u32x4 (&X)[XL], int s) {
+    const int so = uni(s * BK * 2);
+#pragma unroll
+    for (int j = 0; j < XL; ++j)
+      X[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j], so, 0));
+  };
+  auto put_x = [&](const u32x4 (&X)[XL], int buf) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) xs[buf][xput[j]] = X[j];
+  };
+  auto load_raw = [&](RawRegs &R, int s) {
+    const int so = uni(s * NB * 18);
+    R.w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, woff, so, 0));
+    R.w1 = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 16, so, 0);
+  };
+  // quarter i of the raw block: elements 4i..4i+3 and 16+4i..16+4i+3
+  auto convert_part = [&](const RawRegs &R, int buf, int i) {
+    const uint32_t wv[5] = {R.w4.x, R.w4.y, R.w4.z, R.w4.w, R.w1};
+    uint32_t v = codd ? wv[i + 1] : __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], 2);
+    v = cdead ? 0x88888888u : v;
+    uint16_t *row = &codes[buf][cr * LDB + cb * 32 + 4 * i];
+    *(u32x2v *)(row) = codes4_bf16(v & 0x0f0f0f0fu);
+    *(u32x2v *)(row + 16) = codes4_bf16((v >> 4) & 0x0f0f0f0fu);
+    if (i == 0) {
+      const uint32_t dbits = codd ? (wv[0] >> 16) : (wv[0] & 0xffffu);
+      deltas[buf][cr * NB + cb] = cdead ? 0.f : f16_to_f32(dbits);
+    }
+  };
+
+  floatx4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // products issued and not yet scaled; slot q of a stage's last LAG are
+  // tiles NT-LAG+q of its last block, scaled early in the next stage by rd[q]
+  floatx4 ring[LAG];
+  float rd[LAG];
+#pragma unroll
+  for (int q = 0; q < LAG; ++q) {
+    ring[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    rd[q] = 0.f;
+  }
+
+  // One stage from buffers buf, converting the next stage's raw block (R)
+  // into the other codes buffer between the MFMAs.  MFMA u of the stage
+  // (block u / NT, tile u % NT = (i, j) = (t / TN, t % TN)) is followed by
+  // the scaling of product u - LAG.
+  auto compute = [&](int buf, const RawRegs &R) {
+    const uint16_t *B = codes[buf] + (64 * wn + (lane & 15)) * LDB + kc * 8;
+    const u32x4 *XS = xs[buf];
+    auto afrag = [&](int i, int b) {
+      return __builtin_bit_cast(bf16x8, XS[xslot(64 * wm + 16 * i + (lane & 15), 4 * b + kc)]);
+    };
+    const float *D = deltas[buf] + (64 * wn + (lane & 15)) * NB;
+    float2 dv[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) dv[j] = *(const float2 *)(D + j * 16 * NB);
+    bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = *(const bf16x8 *)(B + j * 16 * LDB);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = afrag(i, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[(b + 1) & 1][j] = *(const bf16x8 *)(B + j * 16 * LDB + (b + 1) * 32);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[(b + 1) & 1][i] = afrag(i, b + 1);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int u = b * NT + t, q = u % LAG;
+        const floatx4 pn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            af[b & 1][t / TN], bfr[b & 1][t % TN], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        if (u >= LAG) {
+          const int tt = (u - LAG) % NT;
+          const float2 d = dv[tt % TN];
+          acc[tt] += ((u - LAG) / NT ? d.y : d.x) * ring[q];
+        } else {
+          acc[NT - LAG + u] += rd[q] * ring[q];
+        }
+        ring[q] = pn;
+      }
+      convert_part(R, buf ^ 1, 2 * b);
+      convert_part(R, buf ^ 1, 2 * b + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < LAG; ++q) rd[q] = dv[(NT - LAG + q) % TN].y;
+    // per block: the next block's fragment reads, each MFMA followed by a
+    // share of the VALU work, then the code stores
+    __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);  // DS read
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b > 0) __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);  // DS write
+    }
+  };
+
+  // Stage s: after the barrier, the x loads of stage s+1 and the raw-block
+  // loads of stage s+2 are issued, stage s is computed while stage s+1's raw
+  // blocks are converted, and stage s+1's x goes to the other x buffer
+  // (free: every wave is past stage s-1).  Past the last stage the loads
+  // repeat it, so the two-stage loop body has no branch.
+  u32x4 X[XL];
+  RawRegs R0, R1;
+  auto step = [&](int s, const RawRegs &Rc, RawRegs &Rl) {
+    lds_barrier();
+    load_x(X, min(s + 1, nstages - 1));
+    load_raw(Rl, min(s + 2, nstages - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s & 1, Rc);
+    put_x(X, (s + 1) & 1);
+  };
+  load_x(X, 0);
+  load_raw(R0, 0);
+  load_raw(R1, min(1, nstages - 1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) convert_part(R0, 0, i);
+  put_x(X, 0);
+  int s = 0;
+  for (; s + 1 < nstages; s += 2) {
+    step(s, R1, R0);
+    step(s + 1, R0, R1);
+  }
+  if (s < nstages) step(s, R1, R0);
+#pragma unroll
+  for (int q = 0; q < LAG; ++q) acc[NT - LAG + q] += rd[q] * ring[q];
+
+  float bj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + 64 * wn + j * 16 + (lane & 15);
+    bj[j] = (EPI && bias && n < rows) ? ((const QD_GLOBAL float *)bias)[n] : 0.f;
+  }
+  auto store = [&](auto act) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = n0 + 64 * wn + (t % TN) * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tt = m0 + 64 * wm + (t / TN) * 16 + (lane >> 4) * 4 + v;
+        if (tt < m && n < rows)
+          y[(size_t)tt * rows + n] = EPI ? act(acc[t][v] + bj[t % TN]) : acc[t][v];
+      }
+    }
+  };
+  if (EPI && grp.gelu)
+    store([](float v) { return linear_epilogue(v, nullptr, 0, 1); });
+  else
+    store([](float v) { return v; });
+}
+
 template <int WAVES, int KS, bool MULTI, bool EPI>
 hipError_t launch_tile(const Q40Group &g, int cols, const uint16_t *x, int m, dim3 grid,
                        hipStream_t stream) {
@@ -383,18 +631,29 @@ hipError_t launch_tile(const Q40Group &g, int cols, const uint16_t *x, int m, di
   return hipGetLastError();
 }
 
-// Launches with fewer output tiles than two per CU split K in two parts
-// inside each workgroup (eight waves: two waves per SIMD instead of one);
-// the parts' partial tiles are summed in LDS.
+// Launches with at least 7/4 wide tiles per CU run the wide kernel; the
+// others 128 x 64 tiles, with K split in two parts inside each workgroup
+// (eight waves: two waves per SIMD instead of one) when there are fewer
+// than two tiles per CU, the parts' partial tiles summed in LDS.
 template <bool MULTI, bool EPI>
 hipError_t launch_tiles(Q40Group g, int cols, const uint16_t *x, int m, hipStream_t stream) {
-  g.tile0[0] = 0;
-  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + BN - 1) / BN;
-  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
-  constexpr int BM = kWaves * 32;
-  const dim3 grid(g.tile0[g.n], (m + BM - 1) / BM);
   int cus = device_cus();
   if (cus < 1) cus = 256;
+  long wide_tiles = 0;
+  for (int k = 0; k < g.n; ++k) wide_tiles += (g.rows[k] + wide::BN - 1) / wide::BN;
+  wide_tiles *= (m + wide::BM - 1) / wide::BM;
+  const int bn = 4 * wide_tiles >= 7L * cus ? wide::BN : BN;
+  g.tile0[0] = 0;
+  for (int k = 0; k < g.n; ++k) g.tile0[k + 1] = g.tile0[k] + (g.rows[k] + bn - 1) / bn;
+  for (int k = g.n; k < kMaxGroup; ++k) g.tile0[k + 1] = g.tile0[g.n];
+  if (bn == wide::BN) {
+    const dim3 grid(g.tile0[g.n], (m + wide::BM - 1) / wide::BM);
+    hipLaunchKernelGGL((q4_0_gemm_wide_kernel<MULTI, EPI>), grid, dim3(wide::kThreads), 0, stream,
+                       g, cols, x, m);
+    return hipGetLastError();
+  }
+  constexpr int BM = kWaves * 32;
+  const dim3 grid(g.tile0[g.n], (m + BM - 1) / BM);
   if ((long)grid.x * grid.y < 2L * cus)
     return launch_tile<2 * kWaves, 2, MULTI, EPI>(g, cols, x, m, grid, stream);
   return launch_tile<kWaves, 1, MULTI, EPI>(g, cols, x, m, grid, stream);

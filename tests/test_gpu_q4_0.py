@@ -155,10 +155,29 @@ def test_gemm_whisper_large_1500_sampled(rows, cols):
     x = synth.x_bf16(m, cols, key=(5, 1, rows + cols))
     y = _gemm(wq, rows, cols, x, m)
     rng = np.random.default_rng(rows + cols)
-    ms = np.unique(np.concatenate([rng.integers(0, m, 48), [0, 63, 64, 1407, 1408, 1499]]))
-    rs = np.unique(np.concatenate([rng.integers(0, rows, 192), [0, 63, 64, rows - 1]]))
+    ms = np.unique(np.concatenate([rng.integers(0, m, 48), [0, 63, 64, 127, 128, 1407, 1408, 1499]]))
+    rs = np.unique(np.concatenate([rng.integers(0, rows, 192), [0, 63, 64, 127, 128, rows - 1]]))
     ref = oracle.q4_0_gemm(wq, rows, cols, x, m_sel=ms, row_sel=rs)
     check_f32_output(y[np.ix_(ms, rs)], ref, f"1500x{rows}x{cols}")
+    assert np.isfinite(y).all()
+
+
+def test_gemm_wide_tiles_ragged_sampled():
+    # enough 128 x 128 tiles for the wide kernel (40 x 12 on 256 CUs), with
+    # a ragged last tile in both frames (1499) and weight rows (5000)
+    rows, cols, m = 5000, 1280, 1499
+    print(f"q4_0 gemm wide rows={rows} cols={cols} m={m}", flush=True)
+    w = synth.w_f32(rows, cols, key=(5, 2, rows))
+    wq = oracle.q4_0_quantize(w, rows, cols)
+    x = synth.x_bf16(m, cols, key=(5, 3, m))
+    y = _gemm(wq, rows, cols, x, m)
+    rng = np.random.default_rng(rows)
+    ms = np.unique(np.concatenate([rng.integers(0, m, 40),
+                                   [0, 63, 64, 127, 128, 1407, 1408, 1471, 1472, m - 1]]))
+    rs = np.unique(np.concatenate([rng.integers(0, rows, 160),
+                                   [0, 63, 64, 127, 128, 4991, 4992, 4993, rows - 1]]))
+    ref = oracle.q4_0_gemm(wq, rows, cols, x, m_sel=ms, row_sel=rs)
+    check_f32_output(y[np.ix_(ms, rs)], ref, f"{m}x{rows}x{cols}")
     assert np.isfinite(y).all()
 
 
@@ -224,6 +243,30 @@ def test_qlinear_gemm_parity_full(shapes, cols, m, gelu):
     for k, (wq, b, y, r) in enumerate(zip(wqs, biases, ys, shapes)):
         check_f32_output(y.cpu().numpy(), oracle.q_linear(wq, r, cols, x, b, gelu=gelu),
                          f"item {k} ({r}x{cols})")
+
+
+def test_qlinear_gemm_wide_group_sampled():
+    # two products sharing x with enough wide tiles (20 + 20 column tiles x
+    # 12 frame tiles), biases and gelu_tanh, the second product ragged
+    shapes, cols, m = (2560, 2500), 512, 1500
+    print(f"qlinear gemm wide {shapes} cols={cols} m={m}", flush=True)
+    wqs = [oracle.q4_0_quantize(synth.w_f32(r, cols, key=(15, k, r)), r, cols)
+           for k, r in enumerate(shapes)]
+    biases = [_bias(r, 30 + k) for k, r in enumerate(shapes)]
+    x = synth.x_bf16(m, cols, key=(15, cols, m))
+    ys = [torch.full((m, r), float("nan"), device=DEV) for r in shapes]
+    qd.qlinear_q4_0_gemm([(dev_u8(wq), dev_f32(b), y, r)
+                          for wq, b, y, r in zip(wqs, biases, ys, shapes)],
+                         cols, dev_bf16(x), m, gelu=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(15)
+    ms = np.unique(np.concatenate([rng.integers(0, m, 32), [0, 127, 128, 1407, 1408, m - 1]]))
+    for k, (wq, b, y, r) in enumerate(zip(wqs, biases, ys, shapes)):
+        rs = np.unique(np.concatenate([rng.integers(0, r, 96), [0, 127, 128, r - 1]]))
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all()
+        ref = oracle.q_linear(wq, r, cols, x, b, gelu=True, m_sel=ms, row_sel=rs)
+        check_f32_output(got[np.ix_(ms, rs)], ref, f"item {k} ({r}x{cols})")
 
 
 def test_qlinear_gemm_whisper_qkv_and_fc1_1500_sampled():
