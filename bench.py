@@ -363,13 +363,16 @@ def row_affine_gemv_1024(qd):
 def single_launch_cold(launch, ncopy, trials=25):
     """Time of one launch alone on an idle stream, from HIP events recorded
     just before and after it (so it includes the dispatch latency, not only
-    the kernel), on a copy of the weights untouched for the last `ncopy`
-    copies; median and min over `trials`, in microseconds."""
+    the kernel); median and min over `trials`, in microseconds.  The caller
+    has just streamed the `ncopy` copies in order, so trial t takes copy t:
+    every copy a trial reads was last touched at least ncopy - trials
+    copies earlier (past the MALL for the rows here)."""
     import torch
+    assert trials <= ncopy // 4
     times = []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for t in range(trials):
-        i = (t * 97) % ncopy
+        i = t
         torch.cuda.synchronize()
         e0.record()
         launch(i)
