@@ -158,12 +158,16 @@ __device__ __forceinline__ void mc_next(MCursor &c, const MShape &S, int &left) 
 // Addresses are a wave-uniform base (the tile's first row, the group) plus a
 // 32-bit per-lane offset, so the loads take the scalar-base form.  Rows past
 // the end of the matrix are clamped to its last row.
-template <int R, int U, bool CH, bool XL, class A>
+// ONE: the wave walks a single tile (K split over the waves of a slot), whose
+// matrix and row offsets are resolved once, before the first buffer, rather
+// than per item (about 40 scalar instructions per item, in front of the
+// first weight loads of a launch).
+template <int R, int U, bool CH, bool XL, bool ONE, class A>
 __device__ __forceinline__ void mg_issue(MGroup<R, U, CH, A> &G, MCursor &c, const MShape &S,
                                          const AffineGroup &grp,
                                          const QD_GLOBAL uint16_t *x, uint32_t xoff,
                                          const uint8_t *xl, uint32_t xloff, int lane,
-                                         int &left) {
+                                         int &left, const MItem &it0) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if constexpr (!XL) {  // with XL, mg_compute reads x from LDS
@@ -171,7 +175,7 @@ __device__ __forceinline__ void mg_issue(MGroup<R, U, CH, A> &G, MCursor &c, con
       G.xa[u] = __builtin_bit_cast(typename A::vec, *(const QD_GLOBAL u32x4 *)(xg + xoff));
       G.xb[u] = __builtin_bit_cast(typename A::vec, *(const QD_GLOBAL u32x4 *)(xg + xoff + 16));
     }
-    const MItem it = item_of_tile<R>(grp, S.cols, S.groups, S.ts0 + c.j * S.stride);
+    const MItem it = ONE ? it0 : item_of_tile<R>(grp, S.cols, S.groups, S.ts0 + c.j * S.stride);
     const int trow = it.trow;
     const int lim = it.rows - 1 - trow;  // last valid row offset inside the tile
     const QD_GLOBAL uint8_t *cb = it.w + (size_t)trow * S.cols + 64 * c.g;
@@ -492,6 +496,11 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
   for (int r = 0; r < R; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
   const typename Act::vec ones = __builtin_bit_cast(
       typename Act::vec, u32x4{Act::kOnes, Act::kOnes, Act::kOnes, Act::kOnes});
+  // the single tile of a split wave (KS > 1; past the last tile the wave
+  // has no items and the clamped tile is never read)
+  MItem it0 = {};
+  if constexpr (KS > 1)
+    it0 = item_of_tile<R>(grp, cols, S.groups, min(S.ts0, ntiles - 1));
   MCursor ci, cc;  // issue and compute cursors
   ci.j = cc.j = 0;
   ci.g = cc.g = S.ga;
@@ -507,13 +516,13 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     // numbers of loads in flight, the memory waits would be counted for
     // the path with fewer (and wait for the weights here too)
     if (n > 0) {
-      mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_issue<R, U, CH, XL, (KS > 1), Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li, it0);
       stage_x_pro<PRO>(xl, cols, pro, pin);
     } else {
       stage_x_pro<PRO>(xl, cols, pro, pin);
     }
   } else if (n > 0) {
-    mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+    mg_issue<R, U, CH, XL, (KS > 1), Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li, it0);
   }
   if constexpr (XL) {
     if constexpr (PRO == 0) stage_x(xl, x, m, cols);
@@ -529,13 +538,13 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
         mg_compute<R, U, CH, KS == 1, XL, Act>(A, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
         break;
       }
-      mg_issue<R, U, CH, XL, Act>(B, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_issue<R, U, CH, XL, (KS > 1), Act>(B, ci, S, grp, x, xoff, xl, xloff, lane, li, it0);
       mg_compute<R, U, CH, KS == 1, XL, Act>(A, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
       if (lc <= U) {
         mg_compute<R, U, CH, KS == 1, XL, Act>(B, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
         break;
       }
-      mg_issue<R, U, CH, XL, Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li);
+      mg_issue<R, U, CH, XL, (KS > 1), Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li, it0);
       mg_compute<R, U, CH, KS == 1, XL, Act>(B, acc, cc, S, grp, lc, m, lane, ones, xl, xloff);
     }
   }
