@@ -114,7 +114,8 @@ __device__ __forceinline__ void group_args_now(const AffineGroup &g) {
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i)
     __asm__ volatile("" ::"s"(g.w[i]), "s"(g.y[i]), "s"(g.rows[i]), "s"(g.tile0[i]));
-  __asm__ volatile("" ::"s"(g.tile0[kMaxGroup]), "s"(g.n), "s"(g.grid), "s"(g.ntiles));
+  __asm__ volatile("" ::"s"(g.tile0[kMaxGroup]), "s"(g.n), "s"(g.grid), "s"(g.ntiles),
+                   "s"(g.xdiv));
 }
 
 // The descriptor fields of matrix k are picked by selects over constant
@@ -286,29 +287,27 @@ __device__ __forceinline__ void mg_compute(const MGroup<R, U, CH, A> &G, floatx4
   }
 }
 
-// x [m][cols] (16-bit values) into LDS, rows padded to 2*cols + 16 bytes (the 16
-// token rows of a fragment read then start in different banks).
-__device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x, int m,
-                                        int cols) {
-  const int per_row = cols >> 3;  // 16-byte chunks per row
-  const int chunks = m * per_row;
-  const uint32_t stride = 2u * cols + 16u;
+// x [m][cols] (16-bit values) into LDS, rows padded to 2*cols + 16 bytes (the
+// 16 token rows of a fragment read then start in different banks), 8 chunks
+// of 16 bytes per thread at a time.  Chunk i sits at byte 16 i in global
+// memory (rows are contiguous) and at 16 (i + row) in LDS, with
+// row = i / (cols / 8) by a multiply-high (xdiv): a division by a run-time
+// value would put some forty instructions per chunk in front of the loads.
+// Past the last chunk a thread repeats it (the same bytes to the same
+// place), so the stores need no branch.
+__device__ __forceinline__ void stage_x(uint8_t *xl, const QD_GLOBAL uint16_t *x, int chunks,
+                                        uint32_t xdiv) {
   for (int base = 0; base < chunks; base += 8 * kMThreads) {
     u32x4 v[8];
+    int at[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int i = min(base + k * kMThreads + (int)threadIdx.x, chunks - 1);
-      const int row = i / per_row;
-      v[k] = *(const QD_GLOBAL u32x4 *)(x + (size_t)row * cols + 8 * (i - row * per_row));
+      v[k] = *(const QD_GLOBAL u32x4 *)(x + 8 * i);
+      at[k] = 16 * (i + (int)__umulhi((uint32_t)i, xdiv));
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = base + k * kMThreads + (int)threadIdx.x;
-      if (i < chunks) {
-        const int row = i / per_row;
-        *(u32x4 *)(xl + row * stride + 16 * (i - row * per_row)) = v[k];
-      }
-    }
+    for (int k = 0; k < 8; ++k) *(u32x4 *)(xl + at[k]) = v[k];
   }
 }
 
@@ -328,7 +327,7 @@ __device__ __forceinline__ u32x4 pack_halves(const float (&v)[8]) {
   return r;
 }
 
-// The transformed input row (m = 1, f16) into LDS, in stage_x's layout
+// The transformed input row (m = 1, f16) into LDS, in the layout of the x staging above
 // (GemvPrologue): kind 1 the residual add and RMSNorm, kind 2 SiLU-mul.
 // cols <= 8192: at most two 8-value chunks per thread.
 // The prologue's global inputs, loaded before the first buffer of weights
@@ -521,11 +520,12 @@ __global__ __launch_bounds__(kMThreads) void affine_gemv_mfma_kernel(
     } else {
       stage_x_pro<PRO>(xl, cols, pro, pin);
     }
-  } else if (n > 0) {
-    mg_issue<R, U, CH, XL, (KS > 1), Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li, it0);
+  } else {
+    if (n > 0)
+      mg_issue<R, U, CH, XL, (KS > 1), Act>(A, ci, S, grp, x, xoff, xl, xloff, lane, li, it0);
+    if constexpr (XL) stage_x(xl, x, m * (cols >> 3), grp.xdiv);
   }
   if constexpr (XL) {
-    if constexpr (PRO == 0) stage_x(xl, x, m, cols);
     // LDS writes done, then the barrier (global loads stay in flight)
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
@@ -600,6 +600,8 @@ hipError_t launch_mfma_ks(const AffineGroup &g, int cols, const uint16_t *x, int
   AffineGroup ga = g;
   ga.grid = grid;
   ga.ntiles = g.tile0[g.n];
+  const uint64_t per_row = (uint64_t)cols / 8;
+  ga.xdiv = (uint32_t)(((1ull << 32) + per_row - 1) / per_row);
   hipLaunchKernelGGL((affine_gemv_mfma_kernel<R, U, KS, CH, XL, Act, PRO>), dim3(grid),
                      dim3(kMThreads), lds, stream, ga, cols, x, m, pro);
   return hipGetLastError();

@@ -23,6 +23,9 @@ struct AffineGroup {
   int n;
   int grid;    // workgroups of the launch (set by the launcher)
   int ntiles;  // tile0[n] (set by the launcher)
+  // ceil(2^32 / (cols / 8)): floor(i / (cols / 8)) = umulhi(i, xdiv) for the
+  // 16-byte chunk indices of x (i * cols / 8 < 2^32); set by the launcher
+  uint32_t xdiv;
 };
 // Q4_0 products of one launch, each with an optional f32 bias [rows] added
 // to its outputs and, with gelu, gelu_tanh applied after it (q_linear).
