@@ -252,17 +252,22 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
   // blocks i + kQThreads, ... after it when there are more blocks than
   // threads.  The first register group of weights is issued between the
   // first x loads and their use, so both are in flight.
+  // Block b of the pass (token t0 + b / bpr, block b % bpr of its row) sits
+  // at x + t0 * cols + 32 b, the rows being contiguous; blocks of tokens past
+  // m (b >= nlive) read the last live block and are staged as zeros.  (No
+  // division by the run-time bpr: some forty instructions in front of the
+  // first load.)
   const int nblk = MT * bpr;
+  const int nlive = min(MT, m - t0) * bpr;
+  const QD_GLOBAL float *xt = x + (size_t)t0 * cols;
   const int bi = min((int)threadIdx.x, nblk - 1);
-  const int bt = bi / bpr, bb = bi - bt * bpr;
-  const QD_GLOBAL floatx4 *xp =
-      (const QD_GLOBAL floatx4 *)(x + (size_t)min(t0 + bt, m - 1) * cols + 32 * bb);
+  const QD_GLOBAL floatx4 *xp = (const QD_GLOBAL floatx4 *)(xt + 32 * min(bi, nlive - 1));
   floatx4 xv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) xv[k] = xp[k];
   auto stage = [&]() {
     if ((int)threadIdx.x < nblk) {
-      const bool live = t0 + bt < m;
+      const bool live = bi < nlive;
       float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -273,10 +278,8 @@ __global__ __launch_bounds__(kQThreads) void q4_0_gemv_kernel(
       xsum[bi] = sum;
     }
     for (int b = threadIdx.x + kQThreads; b < nblk; b += kQThreads) {
-      const int t = b / bpr, bk = b - t * bpr;
-      const bool live = t0 + t < m;
-      const QD_GLOBAL floatx4 *p =
-          (const QD_GLOBAL floatx4 *)(x + (size_t)min(t0 + t, m - 1) * cols + 32 * bk);
+      const bool live = b < nlive;
+      const QD_GLOBAL floatx4 *p = (const QD_GLOBAL floatx4 *)(xt + 32 * min(b, nlive - 1));
       float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
