@@ -191,6 +191,9 @@ typedef struct {
   void *tail_y;
   int64_t tail_rows, tail_cols;
   int32_t format;     /* 0: affine-INT8 g64 plan, 1: Q4_0 plan (qgemv_q4_0_step_*) */
+  int32_t group;      /* weight chunks per register group of a compute wave:
+                         4 when the plan's stages give each wave more than
+                         three on average (single-row affine plans), else 3 */
 } qd_step_plan;
 
 /* Workspace bytes needed by _step_plan for these ops (0 if invalid). */

@@ -92,7 +92,8 @@ class StepPlan(ctypes.Structure):
                 ("magic", ctypes.c_uint32), ("tail", ctypes.c_int32),
                 ("tail_w", ctypes.c_void_p), ("tail_x", ctypes.c_void_p),
                 ("tail_y", ctypes.c_void_p), ("tail_rows", ctypes.c_int64),
-                ("tail_cols", ctypes.c_int64), ("format", ctypes.c_int32)]
+                ("tail_cols", ctypes.c_int64), ("format", ctypes.c_int32),
+                ("group", ctypes.c_int32)]
 
 
 class Q40GemvOp(ctypes.Structure):

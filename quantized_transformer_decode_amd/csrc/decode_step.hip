@@ -64,11 +64,13 @@ constexpr int kThreads = (kNcw<Q4, MT> + 1) * kWave;
 // a fixed place (the single-row kernel is at its register limit).
 template <bool Q4, int MT>
 constexpr bool kCompact = MT > 1;
-// Items (1 KiB row chunks) per register group; two groups are in flight per
-// wave.  Three covers a wave's share of a layer stage of 0.6B-1.7B decoders
-// (1-3 items); larger groups mostly re-read past-the-end items, which delays
-// the stage hand-off more than the deeper stream helps the LM-head stage.
-constexpr int G = 3;
+// Items (1 KiB row chunks) per register group, NG: two groups are in flight
+// per wave.  Three covers a wave's share of a layer stage of a 0.6B decoder
+// (1-3 items); larger groups there mostly re-read past-the-end items, which
+// delays the stage hand-off more than the deeper stream helps.  A plan whose
+// stages give the waves more (a 1.7B decoder: up to 8 items in its gate/up
+// stage) takes four, the most the single-row kernel's 128 VGPRs hold.
+constexpr int kGroupItems = 3;
 constexpr unsigned kPollLimit = 1u << 18;   // global polls (~1 us each)
 constexpr unsigned kLdsSpinLimit = 1u << 27;
 
@@ -142,21 +144,21 @@ struct Walk {
 template <bool Q4>
 constexpr int kItemCols = Q4 ? 2048 : 1024;
 
-template <bool Q4>
+template <bool Q4, int NG>
 struct Loads;
-template <>
-struct Loads<false> {
-  uint4 q[G];
-  uint16_t sc[G], bi[G];  // raw BF16 bits; combined only when consumed
+template <int NG>
+struct Loads<false, NG> {
+  uint4 q[NG];
+  uint16_t sc[NG], bi[NG];  // raw BF16 bits; combined only when consumed
 };
-template <>
-struct Loads<true> {
-  u32x4 w4[G];            // the 20-byte block windows
-  uint32_t w1[G];
+template <int NG>
+struct Loads<true, NG> {
+  u32x4 w4[NG];             // the 20-byte block windows
+  uint32_t w1[NG];
 };
 
-template <bool Q4>
-struct Group : Loads<Q4> {
+template <bool Q4, int NG>
+struct Group : Loads<Q4, NG> {
   Walk start;             // where the group begins (kept from the issue)
   int i0, s;              // the group's first item and its stage
 };
@@ -235,8 +237,8 @@ __device__ __forceinline__ void walk_next(Walk &w, const StepOp *ops) {
 // past a row's end re-read its first chunk): the compiler can then wait for
 // exactly this group's loads before it is consumed, instead of for every
 // load in flight (which would include the next group's prefetch).
-template <bool Q4>
-__device__ __forceinline__ void issue_walk(Group<Q4> &g, const StepOp *ops, Walk wk, Cursor c,
+template <bool Q4, int NG>
+__device__ __forceinline__ void issue_walk(Group<Q4, NG> &g, const StepOp *ops, Walk wk, Cursor c,
                                            int lane) {
   c.s = uni(c.s);
   c.i = uni(c.i);
@@ -244,7 +246,7 @@ __device__ __forceinline__ void issue_walk(Group<Q4> &g, const StepOp *ops, Walk
   g.i0 = c.i;
   g.s = c.s;
 #pragma unroll
-  for (int k = 0; k < G; ++k) {
+  for (int k = 0; k < NG; ++k) {
     const int lrow = wk.row - wk.op.row_base;
     if constexpr (Q4) {
       // block ch*64 + lane of the row (lanes past the row re-read block 0 or
@@ -273,8 +275,8 @@ __device__ __forceinline__ void issue_walk(Group<Q4> &g, const StepOp *ops, Walk
   }
 }
 
-template <bool Q4>
-__device__ __forceinline__ void issue(Group<Q4> &g, const StepOp *ops, const StepStage *stages,
+template <bool Q4, int NG>
+__device__ __forceinline__ void issue(Group<Q4, NG> &g, const StepOp *ops, const StepStage *stages,
                                       Cursor c, int gw, int nw, int lane) {
   c.s = uni(c.s);
   c.i = uni(c.i);
@@ -320,7 +322,8 @@ __device__ __forceinline__ float q4_item(const u32x4 w4, uint32_t w1, int lane,
   return d * fmaf(-8.f, xs, s0 + s1);
 }
 
-__device__ __forceinline__ void compute_q4(const Group<true> &g, const StepOp *ops, int lane,
+template <int NG>
+__device__ __forceinline__ void compute_q4(const Group<true, NG> &g, const StepOp *ops, int lane,
                                            const float *xl, int k0, float &rowsum) {
   {
     Walk wk = g.start;
@@ -328,7 +331,7 @@ __device__ __forceinline__ void compute_q4(const Group<true> &g, const StepOp *o
     float4 xq[8];
     float xs = 0.f;
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
+    for (int k = 0; k < NG; ++k) {
       if (g.i0 + k < wk.n) {
         const bool valid = wk.ch * 64 + lane < (wk.op.cols >> 5);
         const int key = wk.o * 64 + wk.ch;
@@ -377,8 +380,8 @@ __device__ __forceinline__ void dot16_rows(const uint4 q, const float4 (&x)[MT][
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void compute_affine(const Group<false> &g, const StepOp *ops,
+template <int MT, int NG>
+__device__ __forceinline__ void compute_affine(const Group<false, NG> &g, const StepOp *ops,
                                                int lane, const float *xl, int k0,
                                                float (&rowsum)[MT]) {
   if constexpr (MT == 1) {
@@ -387,7 +390,7 @@ __device__ __forceinline__ void compute_affine(const Group<false> &g, const Step
     float4 x0, x1, x2, x3;
     float xs = 0.f;
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
+    for (int k = 0; k < NG; ++k) {
       if (g.i0 + k < wk.n) {
         const bool valid = wk.ch * 1024 + lane * 16 < wk.op.cols;
         // x depends only on (op, chunk): reload it only when that changes
@@ -424,7 +427,7 @@ __device__ __forceinline__ void compute_affine(const Group<false> &g, const Step
     float4 x[MT][4];
     float xs[MT];
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
+    for (int k = 0; k < NG; ++k) {
       if (g.i0 + k < wk.n) {
         const bool valid = wk.ch * 1024 + lane * 16 < wk.op.cols;
         const int key = wk.o * 64 + wk.ch;
@@ -474,13 +477,13 @@ __device__ __forceinline__ void compute_affine(const Group<false> &g, const Step
   }
 }
 
-template <bool Q4, int MT>
-__device__ __forceinline__ void compute(const Group<Q4> &g, const StepOp *ops, int lane,
+template <bool Q4, int MT, int NG>
+__device__ __forceinline__ void compute(const Group<Q4, NG> &g, const StepOp *ops, int lane,
                                         const float *xl, int k0, float (&rowsum)[MT]) {
   if constexpr (Q4)
-    compute_q4(g, ops, lane, xl, k0, rowsum[0]);
+    compute_q4<NG>(g, ops, lane, xl, k0, rowsum[0]);
   else
-    compute_affine<MT>(g, ops, lane, xl, k0, rowsum);
+    compute_affine<MT, NG>(g, ops, lane, xl, k0, rowsum);
 }
 
 __device__ __forceinline__ void signal_done_through(Shared *sh, int &signalled, int upto) {
@@ -494,10 +497,13 @@ __device__ __forceinline__ void signal_done_through(Shared *sh, int &signalled, 
   }
 }
 
-template <bool Q4, int MT>
-__device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
-                             int n_stages, Shared *sh, const float *xbuf, int xmax,
-                             uint32_t *err) {
+// (forced inline, as the poller below: two kernels share it, and a call would
+// move the register groups through scratch memory)
+template <bool Q4, int MT, int NG>
+__device__ __forceinline__ void compute_wave(const StepOp *__restrict__ ops,
+                                             const StepStage *__restrict__ stages,
+                                             int n_stages, Shared *sh, const float *xbuf,
+                                             int xmax, uint32_t *err) {
   const int lane = threadIdx.x & 63;
   // wave-uniform values kept in scalar registers, so every table lookup of
   // the schedule is a scalar load (it never waits on the vector-load counter
@@ -510,7 +516,7 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
 #pragma unroll
   for (int t = 0; t < MT; ++t) rowsum[t] = 0.f;
   int have = 0;  // stages known staged
-  Group<Q4> A, B;
+  Group<Q4, NG> A, B;
 
   auto enter = [&](int s) {
     signal_done_through(sh, signalled, s);
@@ -555,15 +561,15 @@ __device__ void compute_wave(const StepOp *__restrict__ ops, const StepStage *__
   // paths compute in their own branch, so each waits for exactly the loads
   // it consumes.
   Cursor c = normalize(stages, n_stages, Cursor{0, 0}, gw, nw);
-  auto run = [&](Group<Q4> &cur, Group<Q4> &nxt) -> bool {
-    const Cursor n1 = normalize(stages, n_stages, Cursor{c.s, c.i + G}, gw, nw);
+  auto run = [&](Group<Q4, NG> &cur, Group<Q4, NG> &nxt) __attribute__((always_inline)) -> bool {
+    const Cursor n1 = normalize(stages, n_stages, Cursor{c.s, c.i + NG}, gw, nw);
     if (n1.s == c.s) {
       issue(nxt, ops, stages, n1, gw, nw, lane);
       enter(c.s);
-      compute<Q4, MT>(cur, ops, lane, xbuf + (c.s & 1) * xmax, staged_base(c.s), rowsum);
+      compute<Q4, MT, NG>(cur, ops, lane, xbuf + (c.s & 1) * xmax, staged_base(c.s), rowsum);
     } else {
       enter(c.s);
-      compute<Q4, MT>(cur, ops, lane, xbuf + (c.s & 1) * xmax, staged_base(c.s), rowsum);
+      compute<Q4, MT, NG>(cur, ops, lane, xbuf + (c.s & 1) * xmax, staged_base(c.s), rowsum);
       if (n1.s >= n_stages) return false;
       signal_done_through(sh, signalled, n1.s);  // as soon as a stage is finished
       // the next stage's schedule lookups (dependent scalar loads) while the
@@ -782,9 +788,11 @@ __device__ __forceinline__ void arrive(uint32_t *ctr, uint32_t *rel, int s, uint
 }
 
 template <bool Q4, int MT>
-__device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__restrict__ stages,
-                            int n_stages, int m, Shared *sh, float *xbuf, int xmax,
-                            uint32_t *rel, uint32_t *ctr, uint32_t *err) {
+__device__ __forceinline__ void poller_wave(const StepOp *__restrict__ ops,
+                                            const StepStage *__restrict__ stages,
+                                            int n_stages, int m, Shared *sh, float *xbuf,
+                                            int xmax, uint32_t *rel, uint32_t *ctr,
+                                            uint32_t *err) {
   const int lane = threadIdx.x & 63;
   const uint32_t epoch = sh->epoch;
   const uint32_t *myrel = rel + (size_t)blockIdx.x * kStepLine;
@@ -866,7 +874,7 @@ __device__ void poller_wave(const StepOp *__restrict__ ops, const StepStage *__r
   }
 }
 
-template <bool Q4, int MT>
+template <bool Q4, int MT, int NG>
 __device__ __forceinline__ void step_body(const StepOp *__restrict__ ops,
                                           const StepStage *__restrict__ stages, int n_stages,
                                           int m, int xmax, int nwg, uint32_t *epoch_word,
@@ -888,16 +896,17 @@ __device__ __forceinline__ void step_body(const StepOp *__restrict__ ops,
   if (threadIdx.x < kWave)
     poller_wave<Q4, MT>(ops, stages, n_stages, m, &sh, xbuf, xmax, rel, ctr, err);
   else
-    compute_wave<Q4, MT>(ops, stages, n_stages, &sh, xbuf, xmax, err);
+    compute_wave<Q4, MT, NG>(ops, stages, n_stages, &sh, xbuf, xmax, err);
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent(epoch_word, sh.epoch + (uint32_t)n_stages);
 }
 
+template <int NG>
 __global__ __launch_bounds__((kThreads<false, 1>)) void affine_step_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
-  step_body<false, 1>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  step_body<false, 1, NG>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
 }
 
 // m = MT token rows (2..4) of affine ops
@@ -906,14 +915,16 @@ __global__ __launch_bounds__((kThreads<false, MT>)) void affine_step_mt_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
-  step_body<false, MT>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  step_body<false, MT, kGroupItems>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr,
+                                    err);
 }
 
 __global__ __launch_bounds__((kThreads<true, 1>)) void q4_0_step_kernel(
     const StepOp *__restrict__ ops, const StepStage *__restrict__ stages, int n_stages,
     int m, int xmax, int nwg, uint32_t *__restrict__ epoch_word, uint32_t *__restrict__ rel,
     uint32_t *__restrict__ ctr, uint32_t *__restrict__ err) {
-  step_body<true, 1>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr, err);
+  step_body<true, 1, kGroupItems>(ops, stages, n_stages, m, xmax, nwg, epoch_word, rel, ctr,
+                                  err);
 }
 
 }  // namespace
@@ -926,14 +937,15 @@ bool step_compact(bool q4, int m) { return q4 ? kCompact<true, 1> : kCompact<fal
 
 hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
                        int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
-                       uint32_t *err, size_t lds_bytes, hipStream_t stream) {
+                       uint32_t *err, size_t lds_bytes, int group, hipStream_t stream) {
   const void *fn;
   int threads;
   if (q4) {
     fn = (const void *)q4_0_step_kernel;
     threads = kThreads<true, 1>;
   } else if (m == 1) {
-    fn = (const void *)affine_step_kernel;
+    fn = group == 4 ? (const void *)affine_step_kernel<4>
+                    : (const void *)affine_step_kernel<kGroupItems>;
     threads = kThreads<false, 1>;
   } else if (m == 2) {
     fn = (const void *)affine_step_mt_kernel<2>;

@@ -374,6 +374,20 @@ qd_status step_plan(const StepIn *ops, int64_t n_ops, int64_t m, StepFormat f, v
   plan->m = (int32_t)m;
   plan->magic = qd::kStepMagic;
   plan->format = f.q4 ? 1 : 0;
+  // register groups of four items for a single-row affine plan whose stages
+  // give each compute wave more than three items on average (the persistent
+  // kernel's stages: the tail, when streamed on its own, does not count)
+  {
+    const int64_t nw = (int64_t)nwg * qd::step_compute_waves(f.q4, (int)m);
+    const int last = ns - ((!f.q4 && ns > 1 && (n_ops == 1 || ops[n_ops - 2].stage !=
+                                                ops[n_ops - 1].stage) &&
+                            ops[n_ops - 1].rows * ops[n_ops - 1].cols >= kStepTailWeights)
+                               ? 1 : 0);
+    int64_t items = 0;
+    for (int64_t i = 0; i < n_ops; ++i)
+      if (ops[i].stage < last) items += ops[i].rows * ((ops[i].cols + f.chunk() - 1) / f.chunk());
+    plan->group = (!f.q4 && m == 1 && last > 0 && items > 3 * nw * (int64_t)last) ? 4 : 3;
+  }
   // a last stage of one very large affine GEMV streams faster as its own
   // launch
   const StepIn &last = ops[n_ops - 1];
@@ -412,7 +426,7 @@ qd_status step_run(const qd_step_plan *plan, bool q4, void *stream) {
       q4, (const qd::StepOp *)(ws + ops_off), (const qd::StepStage *)(ws + stages_off),
       plan->n_stages - plan->tail, plan->m, plan->lds_bytes / 8, plan->nwg, &h->epoch,
       (uint32_t *)(ws + rel_off), (uint32_t *)(ws + ctr_off), &h->error,
-      (size_t)plan->lds_bytes, (hipStream_t)stream);
+      (size_t)plan->lds_bytes, plan->group, (hipStream_t)stream);
   if (e == hipSuccess && plan->tail) {
     qd::AffineGroup g = {};
     g.n = 1;

@@ -164,6 +164,7 @@ int step_compute_waves(bool q4, int m);  // compute waves per workgroup of the s
 bool step_compact(bool q4, int m);       // LDS holds only a workgroup's ops (else all)
 hipError_t launch_step(bool q4, const StepOp *ops, const StepStage *stages, int n_stages, int m,
                        int xmax, int nwg, uint32_t *epoch_word, uint32_t *rel, uint32_t *ctr,
-                       uint32_t *err, size_t lds_bytes, hipStream_t stream);
+                       uint32_t *err, size_t lds_bytes, int group,
+                       hipStream_t stream);  // group: items per register group, 4 or 3
 
 }  // namespace qd
