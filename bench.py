@@ -979,11 +979,11 @@ def main():
             assert qd.qgemv_affine_i8_g64_step_check(step.sweep_plan) == 0
         variant = ("one persistent launch per step (one workgroup per CU); stage s+1 "
                    "reads its inputs only after every workgroup finished stage s")
-        kernel, launches = "affine_step_kernel", 1
+        kernel, launches = f"affine_step_kernel<{step.plan.group}>", 1
         if step.plan.tail:
             variant += ("; the last stage (the LM head, one GEMV) streams as a second "
                         "launch after it")
-            kernel = "affine_step_kernel+affine_gemv_m1_kernel"
+            kernel += "+affine_gemv_m1_kernel"
     else:
         ms, wall = ms_graph, None
         dist = step_distribution(g.replay, min(args.steps, 200), cur)
