@@ -146,9 +146,42 @@ def test_step_qwen3_0_6b_full_size_sampled():
               in synth.decode_step_matrices(synth.QWEN3_0_6B)]
     st = Step(shapes, key=23)
     assert st.plan.tail == 1  # the 151936 x 1024 LM head streams on its own
+    assert st.plan.group == 3  # 1.25 weight chunks per compute wave and stage
     for _ in range(3):
         st.run()
     st.check(sample_rows=48, what="qwen3-0.6b")
+
+
+def test_step_group_of_four_parity_and_relaunch():
+    # stages that give each compute wave more than three weight chunks on
+    # average take register groups of four: gate/up 2 x 6144 x 2048, down
+    # 2048 x 6144, then a 2048 x 2048 GEMV, every output row checked
+    print("step groups of four", flush=True)
+    shapes = [(6144, 2048, 0), (6144, 2048, 0), (2048, 6144, 1), (2048, 2048, 2)]
+    st = Step(shapes, key=29)
+    assert st.plan.group == 4 and st.plan.tail == 0
+    for _ in range(3):
+        st.run()
+    st.check(what="groups of four")
+
+
+def test_step_qwen3_1_7b_full_size_sampled():
+    # the full Qwen3-1.7B-shaped step at one token row (groups of four; one
+    # layer's matrices shared by all 28 layers), every GEMV checked on
+    # sampled rows
+    print("step qwen3-1.7b m=1", flush=True)
+    mats = synth.decode_step_matrices(synth.QWEN3_1_7B)
+    shapes = [(rows, cols, stage) for (_, _, rows, cols, stage) in mats]
+    first = {}
+    share = []
+    for i, (layer, name, rows, cols, stage) in enumerate(mats):
+        first.setdefault(name, i)
+        share.append(first[name])
+    st = Step(shapes, key=41, m=1, share_weights=share)
+    assert st.plan.tail == 1 and st.plan.group == 4
+    for _ in range(2):
+        st.run()
+    st.check(sample_rows=24, what="qwen3-1.7b m=1")
 
 
 def test_step_plan_rejects_bad_ops():
