@@ -524,7 +524,6 @@ __device__ __forceinline__ void compute_wave(const StepOp *__restrict__ ops,
     while (have <= s) {
       have = lds_ld(&sh->xready);
       if (have > s) break;
-      __builtin_amdgcn_s_sleep(1);
       if (++spins > kLdsSpinLimit) {
         if (lane == 0) atomicOr(err, 4u);
         have = s + 1;
@@ -852,7 +851,6 @@ __device__ __forceinline__ void poller_wave(const StepOp *__restrict__ ops,
     // wait for every compute wave to finish stage s, then publish s+1
     unsigned spins = 0;
     while (lds_ld(&sh->done) < (s + 1) * kNcw<Q4, MT>) {
-      __builtin_amdgcn_s_sleep(1);
       if (++spins > kLdsSpinLimit) {
         if (lane == 0) atomicOr(err, 2u);
         break;
